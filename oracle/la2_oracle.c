@@ -1,0 +1,209 @@
+/*
+ * la2_oracle.c -- CPU oracle for causal linear attention (test infrastructure only).
+ *
+ * This file is the slow, plain, fp64 definition that the GPU kernels are checked
+ * against.  Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load it; the product path never does.  It shares no code, header or
+ * constant with the HIP library.
+ *
+ * What it computes (page "Lightning Attention", lizeman.github.io llm-arch-kb,
+ * section 1 "Premise", the numerator of the output equation and the prefix-sum
+ * recurrence S_t = S_{t-1} + phi(k_t) v_t^T):
+ *   - the feature map phi is the identity (same page, section 2, where the
+ *     default configuration is said to use identity phi);
+ *   - no denominator: only the numerator recurrence is computed;
+ *   - an optional per-head decay lam in (0, 1] multiplies the past state:
+ *         S_t = lam * S_{t-1} + k_t v_t^T,      o_t = S_t^T q_t,
+ *     which for lam = 1 is exactly the page's prefix sum.
+ *
+ * Backward (derived from the forward by the chain rule; the pages only state
+ * that the backward is tiled as well -- Lightning Attention-2 abstract, arXiv
+ * 2401.04658 card):
+ *   dq_t = S_t do_t                                  (forward sweep, same S_t)
+ *   R_t  = lam * R_{t+1} + q_t do_t^T,  R_{T+1} = 0  (reverse sweep)
+ *   dk_t = R_t v_t,   dv_t = R_t^T k_t
+ *
+ * The *_rows entry points evaluate the same quantities one output row at a
+ * time from the closed sums
+ *   o_t  = sum_{s<=t} lam^{t-s} (q_t . k_s) v_s
+ *   dq_t = sum_{s<=t} lam^{t-s} (do_t . v_s) k_s
+ *   dk_t = sum_{s>=t} lam^{s-t} (do_s . v_t) q_s
+ *   dv_t = sum_{s>=t} lam^{s-t} (q_s . k_t) do_s
+ * so that single rows of very long sequences can be checked without running
+ * the whole recurrence.
+ *
+ * Layout: every tensor is a contiguous array of chains, each chain a row-major
+ * [T, d] (q, k, dq, dk) or [T, dv] (v, o, do, dv) block of doubles.  lam holds
+ * one decay per chain.  All arithmetic is IEEE fp64; no fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- whole-sequence recurrences --------------------------------------- */
+
+void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                        const double *lam, const double *q, const double *k,
+                        const double *v, double *o)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_chains; ++c) {
+        const double *qc = q + c * T * d;
+        const double *kc = k + c * T * d;
+        const double *vc = v + c * T * dv;
+        double *oc = o + c * T * dv;
+        const double l = lam[c];
+        double *S = (double *)calloc((size_t)(d * dv), sizeof(double)); /* S[i][j], i < d, j < dv */
+        for (int64_t t = 0; t < T; ++t) {
+            const double *kt = kc + t * d, *vt = vc + t * dv, *qt = qc + t * d;
+            /* S_t = lam * S_{t-1} + k_t v_t^T */
+            for (int64_t i = 0; i < d; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = l * S[i * dv + j] + kt[i] * vt[j];
+            /* o_t = S_t^T q_t */
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    acc += S[i * dv + j] * qt[i];
+                oc[t * dv + j] = acc;
+            }
+        }
+        free(S);
+    }
+}
+
+void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                         const double *lam, const double *q, const double *k,
+                         const double *v, const double *dout, double *dq,
+                         double *dk, double *dvo)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_chains; ++c) {
+        const double *qc = q + c * T * d;
+        const double *kc = k + c * T * d;
+        const double *vc = v + c * T * dv;
+        const double *gc = dout + c * T * dv;
+        double *dqc = dq + c * T * d;
+        double *dkc = dk + c * T * d;
+        double *dvc = dvo + c * T * dv;
+        const double l = lam[c];
+        double *S = (double *)calloc((size_t)(d * dv), sizeof(double));
+        /* forward sweep: dq_t = S_t do_t */
+        for (int64_t t = 0; t < T; ++t) {
+            const double *kt = kc + t * d, *vt = vc + t * dv, *gt = gc + t * dv;
+            for (int64_t i = 0; i < d; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = l * S[i * dv + j] + kt[i] * vt[j];
+            for (int64_t i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += S[i * dv + j] * gt[j];
+                dqc[t * d + i] = acc;
+            }
+        }
+        /* reverse sweep: R_t = lam R_{t+1} + q_t do_t^T; dk_t = R_t v_t; dv_t = R_t^T k_t */
+        double *R = S;
+        memset(R, 0, sizeof(double) * (size_t)(d * dv));
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const double *qt = qc + t * d, *gt = gc + t * dv;
+            const double *kt = kc + t * d, *vt = vc + t * dv;
+            for (int64_t i = 0; i < d; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    R[i * dv + j] = l * R[i * dv + j] + qt[i] * gt[j];
+            for (int64_t i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += R[i * dv + j] * vt[j];
+                dkc[t * d + i] = acc;
+            }
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    acc += R[i * dv + j] * kt[i];
+                dvc[t * dv + j] = acc;
+            }
+        }
+        free(S);
+    }
+}
+
+/* ---- single rows from the closed sums (one chain) ---------------------- */
+
+static double dot(const double *a, const double *b, int64_t n)
+{
+    double acc = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        acc += a[i] * b[i];
+    return acc;
+}
+
+/* o rows: out[r, :] = o_{rows[r]} for the chain (q, k, v) with decay lam. */
+void la2_oracle_forward_rows(int64_t T, int64_t d, int64_t dv, double lam,
+                             const double *q, const double *k, const double *v,
+                             int64_t n_rows, const int64_t *rows, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        double *y = out + r * dv;
+        for (int64_t j = 0; j < dv; ++j)
+            y[j] = 0.0;
+        if (t < 0 || t >= T)
+            continue;
+        for (int64_t s = 0; s <= t; ++s) {
+            const double w = pow(lam, (double)(t - s)) * dot(q + t * d, k + s * d, d);
+            for (int64_t j = 0; j < dv; ++j)
+                y[j] += w * v[s * dv + j];
+        }
+    }
+}
+
+/* dq, dk, dv rows for the chain; each output row block is [n_rows, width]. */
+void la2_oracle_backward_rows(int64_t T, int64_t d, int64_t dv, double lam,
+                              const double *q, const double *k, const double *v,
+                              const double *dout, int64_t n_rows,
+                              const int64_t *rows, double *dq_rows,
+                              double *dk_rows, double *dv_rows)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t t = rows[r];
+        double *gq = dq_rows + r * d, *gk = dk_rows + r * d, *gv = dv_rows + r * dv;
+        for (int64_t i = 0; i < d; ++i)
+            gq[i] = gk[i] = 0.0;
+        for (int64_t j = 0; j < dv; ++j)
+            gv[j] = 0.0;
+        if (t < 0 || t >= T)
+            continue;
+        /* dq_t = sum_{s<=t} lam^{t-s} (do_t . v_s) k_s */
+        for (int64_t s = 0; s <= t; ++s) {
+            const double w = pow(lam, (double)(t - s)) * dot(dout + t * dv, v + s * dv, dv);
+            for (int64_t i = 0; i < d; ++i)
+                gq[i] += w * k[s * d + i];
+        }
+        /* dk_t = sum_{s>=t} lam^{s-t} (do_s . v_t) q_s ; dv_t = sum_{s>=t} lam^{s-t} (q_s . k_t) do_s */
+        for (int64_t s = t; s < T; ++s) {
+            const double p = pow(lam, (double)(s - t));
+            const double wk = p * dot(dout + s * dv, v + t * dv, dv);
+            const double wv = p * dot(q + s * d, k + t * d, d);
+            for (int64_t i = 0; i < d; ++i)
+                gk[i] += wk * q[s * d + i];
+            for (int64_t j = 0; j < dv; ++j)
+                gv[j] += wv * dout[s * dv + j];
+        }
+    }
+}
+
+int la2_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,243 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each pin takes an ``oracle.Oracle`` (so the same pins can be run against
+deliberately broken copies of the oracle) and raises AssertionError when the
+oracle disagrees.  None of them re-types the oracle's recurrence: they use
+brute-force masked products, closed forms, library routines (numpy.cumsum,
+scipy.signal.lfilter, torch.autograd), finite differences, invariants and a
+hand-worked example.
+"""
+import json
+import os
+
+import numpy as np
+import scipy.signal
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+LAMS = (1.0, 0.9, 0.42)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max|err| = {err:.3e} (scale {scale:.3e})"
+
+
+def _decay_matrix(T, lam):
+    """D[t, s] = lam^(t-s) for s <= t else 0 (the causal mask M when lam = 1)."""
+    t = np.arange(T)[:, None]
+    s = np.arange(T)[None, :]
+    return np.where(s <= t, lam ** np.clip(t - s, 0, None).astype(np.float64), 0.0)
+
+
+def brute_forward(q, k, v, lam):
+    """O = (Q K^T (.) D_lam) V per chain -- the masked left product over the whole sequence."""
+    B, H, T, _ = q.shape
+    o = np.empty(q.shape[:-1] + (v.shape[-1],))
+    for b in range(B):
+        for h in range(H):
+            D = _decay_matrix(T, lam[h])
+            o[b, h] = ((q[b, h] @ k[b, h].T) * D) @ v[b, h]
+    return o
+
+
+def _setup(seed, B=1, H=3, T=37, d=5, dv=4):
+    q, k, v, do = (_rand((B, H, T, n), seed + i) for i, n in enumerate((d, d, dv, dv)))
+    lam = np.array([LAMS[h % len(LAMS)] for h in range(H)])
+    return q, k, v, do, lam
+
+
+# ---- pins ------------------------------------------------------------------
+
+def pin_golden_handworked(orc):
+    """Hand-worked T = 3, lam = 1/2 example (exact dyadic values)."""
+    g = json.load(open(os.path.join(GOLDEN, "handworked_t3.json")))
+    q, k, v, do = (np.array(g[n], dtype=np.float64)[None, None] for n in ("q", "k", "v", "do"))
+    lam = np.array([g["lam"]])
+    _close(orc.forward(q, k, v, lam)[0, 0], g["o"], 0.0, "golden o")
+    dq, dk, dv = orc.backward(q, k, v, do, lam)
+    _close(dq[0, 0], g["dq"], 0.0, "golden dq")
+    _close(dk[0, 0], g["dk"], 0.0, "golden dk")
+    _close(dv[0, 0], g["dv"], 0.0, "golden dv")
+
+
+def pin_bruteforce_forward(orc):
+    """Recurrence == (Q K^T (.) D_lam) V for lam in {1, 0.9, 0.42}; lam = 1 is the masked product M."""
+    for T in (1, 5, 37, 64):
+        q, k, v, _, lam = _setup(10 + T, T=T)
+        _close(orc.forward(q, k, v, lam), brute_forward(q, k, v, lam), 1e-12, f"fwd T={T}")
+    q, k, v, _, _ = _setup(3, H=2, T=50)
+    _close(orc.forward(q, k, v, None), brute_forward(q, k, v, np.ones(2)), 1e-12, "fwd lam=None")
+
+
+def pin_closed_form_ones(orc):
+    """q = k = v = 1: o_t[j] = d (1 - lam^(t+1)) / (1 - lam), and d (t+1) at lam = 1."""
+    T, d, dv = 40, 6, 3
+    ones_q = np.ones((1, 3, T, d))
+    ones_v = np.ones((1, 3, T, dv))
+    lam = np.array([1.0, 0.9, 0.42])
+    o = orc.forward(ones_q, ones_q, ones_v, lam)
+    t = np.arange(T, dtype=np.float64)
+    for h, l in enumerate(lam):
+        ref = d * (t + 1) if l == 1.0 else d * (1 - l ** (t + 1)) / (1 - l)
+        _close(o[0, h], np.repeat(ref[:, None], dv, 1), 1e-13, f"ones lam={l}")
+
+
+def pin_cumsum_filter(orc):
+    """q_t = k_s = e_1: o = cumsum(v) at lam = 1, and the first-order IIR filter y_t = lam y_{t-1} + v_t otherwise."""
+    T, d, dv = 60, 4, 5
+    e1 = np.zeros((1, 3, T, d))
+    e1[..., 0] = 1.0
+    v = _rand((1, 3, T, dv), 7)
+    lam = np.array([1.0, 0.9, 0.42])
+    o = orc.forward(e1, e1, v, lam)
+    _close(o[0, 0], np.cumsum(v[0, 0], axis=0), 1e-13, "cumsum")
+    for h in (1, 2):
+        ref = scipy.signal.lfilter([1.0], [1.0, -lam[h]], v[0, h], axis=0)
+        _close(o[0, h], ref, 1e-13, f"lfilter lam={lam[h]}")
+
+
+def pin_tile_invariance(orc):
+    """The tile decomposition gives the same result for every tile size, including a ragged last tile."""
+    for T in (37, 100):
+        q, k, v, do, lam = _setup(20 + T, T=T)
+        ref_o = orc.forward(q, k, v, lam)
+        ref_g = orc.backward(q, k, v, do, lam)
+        for blk in (1, 2, 8, 16, 32, 64, 128):
+            _close(orc.tiled_forward(q, k, v, lam, blk), ref_o, 1e-12, f"tiled fwd T={T} T_B={blk}")
+            for a, b, n in zip(orc.tiled_backward(q, k, v, do, lam, blk), ref_g, ("dq", "dk", "dv")):
+                _close(a, b, 1e-12, f"tiled {n} T={T} T_B={blk}")
+
+
+def pin_causality(orc):
+    """Changing row t of k or v leaves o_s (s < t) unchanged; a NaN at row t reaches exactly rows >= t."""
+    q, k, v, _, lam = _setup(31, T=30)
+    o = orc.forward(q, k, v, lam)
+    t = 17
+    k2 = k.copy()
+    k2[:, :, t] += 1.0
+    v2 = v.copy()
+    v2[:, :, t] -= 2.0
+    for kk, vv in ((k2, v), (k, v2)):
+        o2 = orc.forward(q, kk, vv, lam)
+        _close(o2[:, :, :t], o[:, :, :t], 0.0, "causal prefix")
+        assert np.all(np.abs(o2[:, :, t:] - o[:, :, t:]).max(axis=-1) > 0), "rows >= t must change"
+    vn = v.copy()
+    vn[:, :, t] = np.nan
+    on = orc.forward(q, k, vn, lam)
+    assert np.all(np.isfinite(on[:, :, :t])) and np.all(np.isnan(on[:, :, t:])), "NaN reach"
+
+
+def _loss(orc, q, k, v, do, lam):
+    return float(np.sum(orc.forward(q, k, v, lam) * do))
+
+
+def pin_finite_differences(orc):
+    """Backward == central finite differences of L = <o, do> in fp64."""
+    q, k, v, do, lam = _setup(41, B=1, H=3, T=11, d=3, dv=2)
+    grads = orc.backward(q, k, v, do, lam)
+    h = 1e-6
+    for idx, (x, g) in enumerate(zip((q, k, v), grads)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            xp = x.copy()
+            xp[mi] += h
+            xm = x.copy()
+            xm[mi] -= h
+            args = [q, k, v]
+            args[idx] = xp
+            lp = _loss(orc, *args, do, lam)
+            args[idx] = xm
+            lm = _loss(orc, *args, do, lam)
+            num[mi] = (lp - lm) / (2 * h)
+        _close(g, num, 1e-7, f"finite differences arg {idx}")
+
+
+def pin_autograd(orc):
+    """Backward == torch.autograd (float64) through the brute-force masked product."""
+    q, k, v, do, lam = _setup(51, B=2, H=3, T=23, d=4, dv=6)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    T = q.shape[2]
+    D = torch.stack([torch.tensor(_decay_matrix(T, l)) for l in lam])     # [H, T, T]
+    o = torch.matmul(torch.matmul(tq, tk.transpose(-1, -2)) * D, tv)
+    o.backward(torch.tensor(do))
+    dq, dk, dv = orc.backward(q, k, v, do, lam)
+    _close(dq, tq.grad.numpy(), 1e-12, "autograd dq")
+    _close(dk, tk.grad.numpy(), 1e-12, "autograd dk")
+    _close(dv, tv.grad.numpy(), 1e-12, "autograd dv")
+
+
+def pin_inner_products(orc):
+    """o is linear in each of q, k, v, so <Q, dQ> = <K, dK> = <V, dV> = <O, dO>."""
+    q, k, v, do, lam = _setup(61, B=2, H=3, T=45, d=7, dv=5)
+    o = orc.forward(q, k, v, lam)
+    dq, dk, dv = orc.backward(q, k, v, do, lam)
+    ref = float(np.sum(o * do))
+    for x, g, n in ((q, dq, "q"), (k, dk, "k"), (v, dv, "v")):
+        got = float(np.sum(x * g))
+        assert abs(got - ref) <= 1e-11 * max(1.0, abs(ref)), f"<{n}, d{n}> = {got} vs {ref}"
+
+
+def pin_backward_as_forward(orc):
+    """dQ = LA(dO, V, K); dK and dV are the same attention run backwards in time."""
+    q, k, v, do, lam = _setup(71, B=1, H=3, T=33, d=4, dv=6)
+    dq, dk, dv = orc.backward(q, k, v, do, lam)
+    f = lambda x: x[:, :, ::-1].copy()
+    _close(dq, orc.forward(do, v, k, lam), 1e-12, "dq identity")
+    _close(dk, f(orc.forward(f(v), f(do), f(q), lam)), 1e-12, "dk identity")
+    _close(dv, f(orc.forward(f(k), f(q), f(do), lam)), 1e-12, "dv identity")
+
+
+def pin_linearity_and_heads(orc):
+    """o is linear in v, and chains are independent: permuting heads with their decays permutes outputs."""
+    q, k, v, _, lam = _setup(81, B=2, H=3, T=29)
+    v2 = _rand(v.shape, 82)
+    a, b = 0.75, -1.5
+    _close(orc.forward(q, k, a * v + b * v2, lam),
+           a * orc.forward(q, k, v, lam) + b * orc.forward(q, k, v2, lam), 1e-12, "linearity")
+    perm = [2, 0, 1]
+    _close(orc.forward(q[:, perm], k[:, perm], v[:, perm], lam[perm]),
+           orc.forward(q, k, v, lam)[:, perm], 0.0, "head permutation")
+
+
+def pin_rows(orc):
+    """Single rows from the closed sums equal the matching rows of the brute-force product."""
+    q, k, v, do, lam = _setup(91, B=1, H=3, T=41, d=5, dv=3)
+    rows = np.array([0, 1, 17, 39, 40])
+    o = brute_forward(q, k, v, lam)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    D = torch.stack([torch.tensor(_decay_matrix(q.shape[2], l)) for l in lam])
+    torch.matmul(torch.matmul(tq, tk.transpose(-1, -2)) * D, tv).backward(torch.tensor(do))
+    for h in range(3):
+        _close(orc.forward_rows(q[0, h], k[0, h], v[0, h], lam[h], rows), o[0, h, rows], 1e-12, "rows o")
+        gq, gk, gv = orc.backward_rows(q[0, h], k[0, h], v[0, h], do[0, h], lam[h], rows)
+        _close(gq, tq.grad[0, h, rows].numpy(), 1e-12, "rows dq")
+        _close(gk, tk.grad[0, h, rows].numpy(), 1e-12, "rows dk")
+        _close(gv, tv.grad[0, h, rows].numpy(), 1e-12, "rows dv")
+
+
+ALL_PINS = [
+    pin_golden_handworked,
+    pin_bruteforce_forward,
+    pin_closed_form_ones,
+    pin_cumsum_filter,
+    pin_tile_invariance,
+    pin_causality,
+    pin_finite_differences,
+    pin_autograd,
+    pin_inner_products,
+    pin_backward_as_forward,
+    pin_linearity_and_heads,
+    pin_rows,
+]

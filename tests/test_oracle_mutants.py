@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the C oracle and check that some pin catches each.
+
+The mutants are compiled from textual edits of ``oracle/la2_oracle.c`` into a
+temporary directory; the real oracle is never touched.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import pins
+
+SRC = open(obuild.SRC).read()
+
+# (name, original text, mutated text): each is a mistake someone could plausibly make.
+MUTANTS = [
+    ("no_decay_forward",
+     "S[i * dv + j] = l * S[i * dv + j] + kt[i] * vt[j];\n            /* o_t",
+     "S[i * dv + j] = S[i * dv + j] + kt[i] * vt[j];\n            /* o_t"),
+    ("decay_on_current_token",
+     "S[i * dv + j] = l * S[i * dv + j] + kt[i] * vt[j];\n            /* o_t",
+     "S[i * dv + j] = l * (S[i * dv + j] + kt[i] * vt[j]);\n            /* o_t"),
+    ("wrong_operand_readout",
+     "acc += S[i * dv + j] * qt[i];",
+     "acc += S[i * dv + j] * kt[i];"),
+    ("reverse_state_uses_k",
+     "R[i * dv + j] = l * R[i * dv + j] + qt[i] * gt[j];",
+     "R[i * dv + j] = l * R[i * dv + j] + kt[i] * gt[j];"),
+    ("dv_uses_q",
+     "acc += R[i * dv + j] * kt[i];",
+     "acc += R[i * dv + j] * qt[i];"),
+    ("dk_sign",
+     "acc += R[i * dv + j] * vt[j];",
+     "acc -= R[i * dv + j] * vt[j];"),
+    ("dq_forward_no_decay",
+     "S[i * dv + j] = l * S[i * dv + j] + kt[i] * vt[j];\n            for (int64_t i = 0; i < d; ++i) {",
+     "S[i * dv + j] = S[i * dv + j] + kt[i] * vt[j];\n            for (int64_t i = 0; i < d; ++i) {"),
+    ("rows_exponent_off_by_one",
+     "const double w = pow(lam, (double)(t - s)) * dot(q + t * d, k + s * d, d);",
+     "const double w = pow(lam, (double)(t - s + 1)) * dot(q + t * d, k + s * d, d);"),
+    ("rows_dk_wrong_vector",
+     "const double wk = p * dot(dout + s * dv, v + t * dv, dv);",
+     "const double wk = p * dot(dout + t * dv, v + s * dv, dv);"),
+    ("rows_skip_diagonal",
+     "for (int64_t s = 0; s <= t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q",
+     "for (int64_t s = 0; s < t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    assert SRC.count(old) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / f"{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = obuild.compile_oracle(str(src), str(tmp_path / f"{name}.so"))
+    orc = oracle.load(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
