@@ -1,5 +1,19 @@
 """Lightning Attention-2 tiled causal linear attention on MI355X (gfx950).
 
-The HIP library is loaded on first use of the binding; ``inputs`` (seeded
-synthetic workloads) imports without it.
+The HIP library (``lib/libla2.so``, C ABI in ``include/la2.h``) is loaded on
+first use of the binding; ``inputs`` (seeded synthetic workloads) imports
+without it.
 """
+from .binding import (  # noqa: F401
+    LA2Error,
+    LA2Function,
+    backward,
+    forward,
+    la2_abi_version,
+    la2_backward,
+    la2_forward,
+    la2_status_string,
+    la2_workspace_bytes,
+    lightning_attention,
+    load_library,
+)

@@ -1,0 +1,179 @@
+"""Thin ctypes binding of ``include/la2.h``: argument marshalling only.
+
+Every step of the computation runs in the HIP library ``lib/libla2.so``; this
+module only checks tensors, passes their device pointers, sizes and torch's
+current HIP stream, and turns status codes into exceptions.  There is no CPU
+path: if the library is missing or a tensor is not on the GPU, it raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2.so")
+
+LA2_F32 = 0
+LA2_BF16 = 1
+_DTYPES = {torch.float32: LA2_F32, torch.bfloat16: LA2_BF16}
+
+EXPORTS = ("la2_forward", "la2_backward", "la2_workspace_bytes", "la2_status_string", "la2_abi_version")
+
+_lib = None
+
+
+class LA2Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({la2_status_string(status)})")
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes handle of the built HIP library."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.la2_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la2_forward.restype = i32
+    lib.la2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la2_backward.restype = i32
+    lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.la2_workspace_bytes.restype = sz
+    lib.la2_status_string.argtypes = [i32]
+    lib.la2_status_string.restype = ctypes.c_char_p
+    lib.la2_abi_version.argtypes = []
+    lib.la2_abi_version.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def la2_status_string(status):
+    return load_library().la2_status_string(int(status)).decode()
+
+
+def la2_abi_version():
+    return load_library().la2_abi_version()
+
+
+def dtype_code(dtype):
+    try:
+        return _DTYPES[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}; use torch.float32 or torch.bfloat16") from None
+
+
+def la2_workspace_bytes(B, H, T, d, d_v, block, dtype, backward):
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    n = load_library().la2_workspace_bytes(B, H, T, d, d_v, block, code, 1 if backward else 0)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported sizes for la2_workspace_bytes")
+    return n
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _decay_ptr(decay):
+    if decay is None:
+        return None
+    if decay.dtype != torch.float32:
+        raise TypeError("decay must be float32")
+    return _dev_ptr(decay, "decay")
+
+
+def la2_forward(q, k, v, decay, o, block, workspace=None, stream=None):
+    """Enqueue o = attention(q, k, v) on ``stream`` (default: torch's current stream)."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_forward(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
+        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_forward")
+
+
+def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None):
+    """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_backward(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(dout, "dout"),
+        _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
+        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_backward")
+
+
+def _check_same(q, k, v, other=None):
+    for name, t in (("k", k), ("v", v)) + ((("dout", other),) if other is not None else ()):
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, H, T, d] and v [B, H, T, d_v]")
+
+
+def workspace_for(q, v, block, backward):
+    B, H, T, d = q.shape
+    n = la2_workspace_bytes(B, H, T, d, v.shape[-1], block, q.dtype, backward)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def forward(q, k, v, decay=None, block=128, workspace=None):
+    """Allocate o (and the workspace if none is given) and run the forward pass."""
+    _check_same(q, k, v)
+    o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, v, block, False)
+    la2_forward(q, k, v, decay, o, block, workspace)
+    return o
+
+
+def backward(q, k, v, dout, decay=None, block=128, workspace=None):
+    """Allocate (dq, dk, dv) and run the backward pass."""
+    _check_same(q, k, v, dout)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = workspace_for(q, v, block, True)
+    la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace)
+    return dq, dk, dv
+
+
+class LA2Function(torch.autograd.Function):
+    """autograd bridge: forward and backward both run in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, decay=None, block=128):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        ctx.save_for_backward(q, k, v, decay)
+        ctx.block = block
+        return forward(q, k, v, decay, block)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, decay = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, dout.contiguous(), decay, ctx.block)
+        return dq, dk, dv, None, None
+
+
+def lightning_attention(q, k, v, decay=None, block=128):
+    """o = attention(q, k, v) with autograd support."""
+    return LA2Function.apply(q, k, v, decay, block)

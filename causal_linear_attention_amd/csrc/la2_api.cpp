@@ -1,0 +1,216 @@
+// la2_api.cpp -- C ABI of the library: argument checks, work planning, dispatch.
+//
+// Work decomposition.  Chains (batch x head) are independent: the state a tile
+// reads depends only on earlier tiles of the same chain (page "Lightning
+// Attention", lizeman.github.io llm-arch-kb, section 2, Step 1).  Each chain is a
+// serial walk over its tiles, so when there are fewer chains than compute units
+// the sequence is also cut into segments that run on different workgroups:
+//   1. a state-only pass gives each segment's own state delta,
+//   2. a prefix pass chains the deltas into each segment's start state,
+//   3. the output pass runs every segment from its start state.
+// With enough chains only step 3 runs, from a zero state.
+#include <cstdlib>
+#include <cstring>
+
+#include "la2.h"
+#include "la2_internal.h"
+
+namespace {
+
+constexpr int kComputeUnits = 256;   // MI355X: 256 CUs in 8 XCDs
+
+struct Plan {
+    int TB;          // tile length the kernels run with
+    int nseg;        // segments per chain
+    int seg_tiles;   // tiles per segment
+    size_t ws_bytes; // workspace for the segment states
+};
+
+int elem_size(int dtype) { return dtype == LA2_BF16 ? 2 : 4; }
+
+bool block_ok(int dtype, int block) {
+    if (dtype == LA2_BF16) return block == 64 || block == 128 || block == 256;
+    return block == 16 || block == 32 || block == 64;
+}
+
+// Value-slice width a kernel launch uses for a value tensor of width `w`.
+int slice_width(int dtype, int w) { return dtype == LA2_BF16 ? w : 64; }
+
+int check_sizes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0) return LA2_ERR_BAD_SHAPE;
+    // every byte offset must fit comfortably in int64, and grid dimensions in 32 bits
+    const int64_t lim = (int64_t)1 << 40;
+    if (B > lim / H) return LA2_ERR_BAD_SHAPE;
+    const int64_t chains = B * H;
+    if (chains > (int64_t)1 << 24 || T > lim / chains || chains * T > lim / 512) return LA2_ERR_BAD_SHAPE;
+    if (!((d == 64 || d == 128) && (dv == 64 || dv == 128))) return LA2_ERR_UNSUPPORTED;
+    if (!block_ok(dtype, block)) return LA2_ERR_UNSUPPORTED;
+    return LA2_OK;
+}
+
+Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
+    Plan p{};
+    p.TB = dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
+    const int64_t NT = (T + p.TB - 1) / p.TB;
+    const int64_t chains = B * H;
+    const int64_t slices = dv / slice_width(dtype, (int)dv);
+    const int64_t work = chains * slices;
+    int64_t seg_tiles = NT;
+    if (const char *env = std::getenv("LA2_SEGMENT_TILES")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) seg_tiles = v < NT ? v : NT;
+    } else if (work < kComputeUnits && NT > 1) {
+        int64_t nseg = kComputeUnits / work;
+        if (nseg > NT) nseg = NT;
+        seg_tiles = (NT + nseg - 1) / nseg;
+    }
+    p.seg_tiles = (int)seg_tiles;
+    p.nseg = (int)((NT + seg_tiles - 1) / seg_tiles);
+    p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nseg * d * dv * sizeof(float) : 0;
+    return p;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void *p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// One scan of the decomposition: y = attention(a, b, c) in direction `dir`.
+int run_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
+             int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s) {
+    la2::ScanArgs args{};
+    args.a = a;
+    args.b = b;
+    args.c = c;
+    args.y = y;
+    args.decay = decay;
+    args.T = T;
+    args.H = (int)H;
+    args.DVT = W;
+    args.nseg = pl.nseg;
+    args.seg_tiles = pl.seg_tiles;
+    args.chains = (int)chains;
+    const int DV = slice_width(dtype, W);
+    args.nslice = W / DV;
+    auto launch = [&](la2::Mode mode) {
+        return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, mode, s)
+                                 : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
+    };
+    if (pl.nseg > 1) {
+        args.states = static_cast<float *>(ws);
+        // deltas of the segments whose successor (forward) / predecessor (reverse) needs them
+        args.seg_first = dir == la2::Dir::Forward ? 0 : 1;
+        args.seg_count = pl.nseg - 1;
+        if (launch(la2::Mode::StateOnly) != hipSuccess) return LA2_ERR_HIP;
+        if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nseg,
+                                       (int64_t)pl.seg_tiles * pl.TB, (int64_t)D * W, dir, s) != hipSuccess)
+            return LA2_ERR_HIP;
+    }
+    args.seg_first = 0;
+    args.seg_count = pl.nseg;
+    if (launch(la2::Mode::Output) != hipSuccess) return LA2_ERR_HIP;
+    return LA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la2_abi_version(void) { return LA2_ABI_VERSION; }
+
+const char *la2_status_string(int status) {
+    switch (status) {
+        case LA2_OK: return "ok";
+        case LA2_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case LA2_ERR_BAD_SHAPE: return "B, H, T, d and d_v must be positive and the tensors addressable";
+        case LA2_ERR_UNSUPPORTED: return "d, d_v, block or dtype outside the compiled set";
+        case LA2_ERR_MISALIGNED: return "tensor pointers must be 16-byte aligned";
+        case LA2_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
+        case LA2_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than la2_workspace_bytes";
+        case LA2_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                           int backward) {
+    (void)backward;   // forward and backward run scans of the same length and state size
+    if (check_sizes(B, H, T, d, d_v, block, dtype) != LA2_OK) return (size_t)-1;
+    return make_plan(B, H, T, d, d_v, block, dtype).ws_bytes;
+}
+
+int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B, int64_t H,
+                int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
+                void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
+    int st = check_sizes(B, H, T, d, d_v, block, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (workspace && !aligned16(workspace)) ||
+        (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+    const Range ro = range_of(o, nv);
+    if (overlap(ro, range_of(q, nq)) || overlap(ro, range_of(k, nq)) || overlap(ro, range_of(v, nv)) ||
+        (decay && overlap(ro, range_of(decay, (size_t)H * 4))))
+        return LA2_ERR_ALIAS;
+    if (pl.ws_bytes) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return LA2_ERR_WORKSPACE_TOO_SMALL;
+        const Range rw = range_of(workspace, pl.ws_bytes);
+        if (overlap(rw, ro) || overlap(rw, range_of(q, nq)) || overlap(rw, range_of(k, nq)) ||
+            overlap(rw, range_of(v, nv)) || (decay && overlap(rw, range_of(decay, (size_t)H * 4))))
+            return LA2_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run_scan(q, k, v, o, decay, B * H, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s);
+}
+
+int la2_backward(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
+                 void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
+    int st = check_sizes(B, H, T, d, d_v, block, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv) || (workspace && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+    const Range ins[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
+                          range_of(decay, decay ? (size_t)H * 4 : 0)};
+    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv),
+                           range_of(workspace, pl.ws_bytes)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlap(outs[i], ins[j])) return LA2_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return LA2_ERR_ALIAS;
+    }
+    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LA2_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t chains = B * H;
+    const int D = (int)d, DV = (int)d_v;
+    // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k)
+    st = run_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, s);
+    if (st != LA2_OK) return st;
+    // dk_t = R_t v_t           = reverse scan with (v, do, q)
+    st = run_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, workspace, s);
+    if (st != LA2_OK) return st;
+    // dv_t = R_t^T k_t         = reverse scan with (k, q, do)
+    return run_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace, s);
+}
+
+}  // extern "C"

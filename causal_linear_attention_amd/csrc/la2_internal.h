@@ -1,0 +1,49 @@
+// la2_internal.h -- declarations shared by the library's own translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace la2 {
+
+// One launch of the tile-scan kernel over a set of (chain, segment, value-slice)
+// work items.  Roles follow the attention output y_t = sum_s w(t, s) (a_t . b_s) c_s:
+//   a = "query" [chains, T, D], b = "key" [chains, T, D], c = "value" [chains, T, DVT].
+// Forward: (q, k, v) -> o.  Backward: dq = scan(do, v, k); dk = reverse scan(v, do, q);
+// dv = reverse scan(k, q, do)  (the three are fused where a kernel supports it).
+struct ScanArgs {
+    const void *a;
+    const void *b;
+    const void *c;
+    void *y;               // output [chains, T, DVT] (unused in state-only launches)
+    const float *decay;    // [H] or nullptr (lam = 1)
+    float *states;         // fp32 [chains, nseg, D, DVT]: segment start states / segment deltas
+    int64_t T;
+    int H;
+    int DVT;               // full value width (row stride of c and y)
+    int nseg;              // segments per chain
+    int seg_tiles;         // tiles per segment
+    int seg_first;         // first segment index handled by this launch
+    int seg_count;         // segments per chain handled by this launch
+    int nslice;            // value slices per chain (DVT / slice width)
+    int chains;            // B * H
+};
+
+// Kernel families.
+enum class Dir { Forward, Reverse };
+enum class Mode { Output, StateOnly };
+
+// Launchers (return hipGetLastError() after the launch).
+hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
+                            hipStream_t s);
+hipError_t launch_scan_f32(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
+                           hipStream_t s);
+// Turns per-segment deltas into per-segment start states, in place.
+hipError_t launch_segment_prefix(float *states, const float *decay, int chains, int H, int nseg,
+                                 int64_t seg_len, int64_t elems, Dir dir, hipStream_t s);
+
+// Which (D, DV, TB) the kernels are compiled for.
+bool bf16_supported(int D, int DV, int TB);
+bool f32_supported(int D, int DV, int TB);
+
+}  // namespace la2

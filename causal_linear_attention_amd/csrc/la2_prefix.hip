@@ -1,0 +1,52 @@
+// la2_prefix.hip -- chain the per-segment states of a split sequence.
+//
+// When a chain is cut into segments that run on different workgroups, each segment
+// first produces its own state delta (the state it would reach from zero), and this
+// kernel turns the deltas into the state each segment starts from.  The state is the
+// fixed-size summary of everything before the segment (page "Lightning Attention",
+// lizeman.github.io llm-arch-kb, section 2, "Memory footprint": the only persistent
+// state across tiles is the d x d_v matrix S), so the hand-over is one affine step
+// per segment:
+//   forward: S_in[0] = 0,        S_in[p+1] = lam^L S_in[p] + dS[p]
+//   reverse: R_in[last] = 0,     R_in[p-1] = lam^L R_in[p] + dR[p]
+// L is the segment length in positions (every segment except the last is full, and
+// the last one's length only ever multiplies a zero state).
+#include "la2_internal.h"
+
+namespace la2 {
+namespace {
+
+__global__ __launch_bounds__(256) void segment_prefix_kernel(float *states, const float *decay, int H, int nseg,
+                                                             int64_t seg_len, int64_t elems, int reverse) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int chain = blockIdx.y;
+    if (e >= elems) return;
+    const float f = decay ? exp2f((float)seg_len * log2f(decay[chain % H])) : 1.0f;
+    float *base = states + (int64_t)chain * nseg * elems + e;
+    float run = 0.0f;
+    if (!reverse) {
+        for (int p = 0; p < nseg; ++p) {
+            const float d = p < nseg - 1 ? base[(int64_t)p * elems] : 0.0f;
+            base[(int64_t)p * elems] = run;
+            run = fmaf(f, run, d);
+        }
+    } else {
+        for (int p = nseg - 1; p >= 0; --p) {
+            const float d = p > 0 ? base[(int64_t)p * elems] : 0.0f;
+            base[(int64_t)p * elems] = run;
+            run = fmaf(f, run, d);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_segment_prefix(float *states, const float *decay, int chains, int H, int nseg, int64_t seg_len,
+                                 int64_t elems, Dir dir, hipStream_t s) {
+    dim3 grid((unsigned)((elems + 255) / 256), (unsigned)chains);
+    hipLaunchKernelGGL(segment_prefix_kernel, grid, dim3(256), 0, s, states, decay, H, nseg, seg_len, elems,
+                       dir == Dir::Reverse ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace la2

@@ -1,0 +1,106 @@
+/*
+ * la2.h -- C ABI of the MI355X (gfx950) Lightning Attention-2 library.
+ *
+ * Operation.  Causal linear attention with identity feature map, no
+ * denominator and an optional per-head decay lam_h in (0, 1]:
+ *
+ *     S_t = lam_h * S_{t-1} + k_t v_t^T,     o_t = S_t^T q_t,
+ *
+ * i.e. the numerator recurrence of page "Lightning Attention"
+ * (lizeman.github.io llm-arch-kb), section 1, computed the way its section 2
+ * derives: the sequence is cut into tiles of `block` positions; inside a tile
+ * the output is the masked left product (Q_b K_b^T (.) M) V_b (Step 2), across
+ * tiles the right product Q_b S_{b-1} (Step 3), and the d x d_v state is
+ * carried from tile to tile (Step 4).  With lam < 1 the mask M becomes
+ * lam^(i-j) on and below the diagonal, the inter-tile rows are weighted
+ * lam^(i+1) and the state update is S_b = lam^block S_{b-1} +
+ * (diag(lam^(block-1-j)) K_b)^T V_b.  The backward pass ("tiling ... through
+ * both forward and backward", Lightning Attention-2 abstract, arXiv 2401.04658)
+ * produces dQ by the same forward-order scan and dK, dV by the mirrored
+ * reverse-order scan of R_t = lam R_{t+1} + q_t do_t^T.
+ *
+ * Tensors.  Device pointers to contiguous row-major [B, H, T, d] (q, k, dq,
+ * dk) and [B, H, T, d_v] (v, o, dout, dv) arrays of one element type `dtype`,
+ * each 16-byte aligned.  Outputs have the input dtype; accumulation is fp32.
+ * `decay` is a device pointer to H fp32 values in (0, 1], or NULL for lam = 1;
+ * its values are read on the device and not validated (values outside (0, 1]
+ * give unspecified results).
+ *
+ * Supported: d, d_v in {64, 128}; dtype LA2_BF16 with block in {64, 128, 256},
+ * LA2_F32 with block in {16, 32, 64}.  A block of 256 is carried out as two
+ * 128-position sub-tiles with the state handed over between them; the
+ * decomposition gives the same result for any tile size (same page, section 2:
+ * the split into intra- and inter-tile parts holds for every tile length).
+ *
+ * Ownership.  The caller allocates and frees every buffer, including the
+ * workspace (la2_workspace_bytes tells its size; it may be 0, in which case
+ * workspace may be NULL).  The library allocates nothing, never synchronizes,
+ * keeps no state between calls and is safe to call from several threads.
+ *
+ * Execution.  Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns at once.  Outputs and workspace are in use
+ * until the stream reaches that point.
+ *
+ * Errors.  Every entry point returns LA2_OK (0) or a status below.  All
+ * argument checks run before anything is enqueued, so a non-zero status other
+ * than LA2_ERR_HIP means nothing was launched.  Nothing is printed and
+ * nothing aborts.
+ */
+#ifndef LA2_H
+#define LA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA2_ABI_VERSION 1
+
+enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
+
+enum la2_status {
+    LA2_OK = 0,
+    LA2_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    LA2_ERR_BAD_SHAPE = 2,           /* B, H, T, d or d_v <= 0, or sizes overflow */
+    LA2_ERR_UNSUPPORTED = 3,         /* d / d_v / block / dtype outside the compiled set */
+    LA2_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
+    LA2_ERR_ALIAS = 5,               /* an output overlaps an input, another output or the workspace */
+    LA2_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < la2_workspace_bytes(...) or NULL workspace */
+    LA2_ERR_HIP = 7                  /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Forward: o = attention(q, k, v).
+ *   q, k: [B, H, T, d]; v, o: [B, H, T, d_v]; decay: [H] fp32 or NULL.
+ *   block: tile length T_B; dtype: enum la2_dtype.
+ *   workspace: device scratch of at least la2_workspace_bytes(..., 0) bytes,
+ *   used for the per-segment states when a chain is split across workgroups. */
+int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o,
+                int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward: gradients of <o, dout> with respect to q, k and v.
+ *   dout, dv: [B, H, T, d_v]; dq, dk: [B, H, T, d]; other arguments as in la2_forward.
+ *   workspace: at least la2_workspace_bytes(..., 1) bytes. */
+int la2_backward(const void *q, const void *k, const void *v, const float *decay, const void *dout,
+                 void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d,
+                 int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Workspace bytes needed by la2_forward (backward = 0) or la2_backward (backward = 1)
+ * for these sizes; (size_t)-1 for arguments that la2_forward/la2_backward would reject. */
+size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,
+                           int dtype, int backward);
+
+/* Static, human-readable text for a status code. */
+const char *la2_status_string(int status);
+
+/* LA2_ABI_VERSION of the built library. */
+int la2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA2_H */

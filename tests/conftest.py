@@ -11,3 +11,9 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # name the case on the terminal before it touches the GPU
+    sys.__stderr__.write(f"[start] {nodeid}\n")
+    sys.__stderr__.flush()

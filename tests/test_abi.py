@@ -1,0 +1,110 @@
+"""C-ABI library on the CPU: it loads, exports what include/la2.h declares, and
+rejects bad arguments before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import causal_linear_attention_amd as la2
+from causal_linear_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "la2.h")).read()
+
+OK, NULLP, SHAPE, UNSUP, MISAL, ALIAS, WS = 0, 1, 2, 3, 4, 5, 6
+P = 1 << 20          # fake, 16-byte aligned device addresses: validation fails before any use
+MB = 1 << 26
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la2.load_library()
+
+
+def declared_functions():
+    return re.findall(r"^\s*(?:int|size_t|const char \*)\s*(la2_\w+)\s*\(", HEADER, flags=re.M)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    ver = int(re.search(r"#define LA2_ABI_VERSION (\d+)", HEADER).group(1))
+    assert la2.la2_abi_version() == ver
+    for code in range(8):
+        s = la2.la2_status_string(code)
+        assert s and s != "unknown status"
+    assert la2.la2_status_string(99) == "unknown status"
+
+
+def fwd(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, B=1, H=1, T=64, d=64, dv=64, block=64,
+        dtype=1, ws=None, wsb=0):
+    return lib.la2_forward(q, k, v, decay, o, B, H, T, d, dv, block, dtype, ws, wsb, None)
+
+
+def bwd(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, do=P + 3 * MB, dq=P + 4 * MB, dk=P + 5 * MB,
+        dv_=P + 6 * MB, B=1, H=1, T=64, d=64, dv=64, block=64, dtype=1, ws=None, wsb=0):
+    return lib.la2_backward(q, k, v, decay, do, dq, dk, dv_, B, H, T, d, dv, block, dtype, ws, wsb, None)
+
+
+def test_null_pointers(lib):
+    assert fwd(lib, q=None) == NULLP
+    assert fwd(lib, o=None) == NULLP
+    assert bwd(lib, do=None) == NULLP
+    assert bwd(lib, dv_=None) == NULLP
+
+
+def test_bad_shapes(lib):
+    for kw in ({"B": 0}, {"H": -1}, {"T": 0}, {"d": 0}, {"dv": -5}, {"B": 1 << 40, "H": 1 << 30}):
+        assert fwd(lib, **kw) == SHAPE, kw
+        assert bwd(lib, **kw) == SHAPE, kw
+
+
+def test_unsupported(lib):
+    assert fwd(lib, d=96) == UNSUP
+    assert fwd(lib, dv=256) == UNSUP
+    assert fwd(lib, dtype=7) == UNSUP
+    assert fwd(lib, dtype=1, block=32) == UNSUP      # bf16 tiles: 64, 128, 256
+    assert fwd(lib, dtype=0, block=128) == UNSUP     # fp32 tiles: 16, 32, 64
+    assert bwd(lib, block=100) == UNSUP
+
+
+def test_misaligned(lib):
+    assert fwd(lib, q=P + 2) == MISAL
+    assert fwd(lib, o=P + 3 * MB + 8) == MISAL
+    assert fwd(lib, decay=P + 7 * MB + 1) == MISAL
+    assert bwd(lib, dk=P + 5 * MB + 4) == MISAL
+
+
+def test_alias(lib):
+    assert fwd(lib, o=P) == ALIAS                       # o == q
+    assert fwd(lib, o=P + 2 * MB + 64) == ALIAS         # o inside v
+    assert bwd(lib, dq=P + 1 * MB) == ALIAS             # dq == k
+    assert bwd(lib, dk=P + 4 * MB) == ALIAS             # dk == dq
+
+
+def test_workspace(lib):
+    # one chain of 1024 positions is split over workgroups, so it needs segment states
+    n = la2.la2_workspace_bytes(1, 1, 1024, 64, 64, 64, torch.bfloat16, False)
+    assert n > 0
+    assert fwd(lib, T=1024, ws=None, wsb=0) == WS
+    assert fwd(lib, T=1024, ws=P + 8 * MB, wsb=n - 1) == WS
+    assert bwd(lib, T=1024, ws=None, wsb=0) == WS
+    assert fwd(lib, T=1024, ws=P + MB, wsb=n) == ALIAS   # workspace on top of k
+    # enough chains to fill the GPU: no split, no workspace
+    assert la2.la2_workspace_bytes(16, 16, 4096, 128, 128, 128, torch.bfloat16, True) == 0
+    assert lib.la2_workspace_bytes(1, 1, 64, 96, 64, 64, 1, 0) == ctypes.c_size_t(-1).value
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        la2.la2_forward(q, q, q, None, torch.empty_like(q), 64)
+    with pytest.raises(TypeError):
+        la2.forward(q.half(), q.half(), q.half())

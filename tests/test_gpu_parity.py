@@ -1,0 +1,220 @@
+"""HIP path vs the CPU oracle, through the C ABI.
+
+Bars (max|gpu - ref| / max|ref| over each output tensor): 1e-5 for fp32 inputs,
+2e-2 for bf16 inputs.  Small shapes are compared element by element against the
+whole-sequence oracle; the full workload sizes are compared on sampled rows that
+the oracle computes one by one from the closed sums.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_amd as la2
+from causal_linear_attention_amd import inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref)
+    scale = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(np.asarray(got) - ref))) / (scale if scale > 0 else 1.0)
+
+
+def lam_of(x):
+    return None if x["decay"] is None else x["decay"].double().numpy()
+
+
+def run_gpu(x, block, backward=True):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    decay = None if x["decay"] is None else x["decay"].to(DEV)
+    o = la2.forward(q, k, v, decay, block=block)
+    out = {"o": o}
+    if backward:
+        out["dq"], out["dk"], out["dv"] = la2.backward(q, k, v, x["do"].to(DEV), decay, block=block)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_full(x, block, backward=True, tol=None):
+    w = x["workload"]
+    tol = tol or TOL[w.dtype]
+    got = run_gpu(x, block, backward)
+    lam = lam_of(x)
+    args = [f64(x[n]) for n in ("q", "k", "v")]
+    errs = {"o": rel_err(f64(got["o"]), oracle.forward(*args, lam))}
+    if backward:
+        ref = oracle.backward(*args, f64(x["do"]), lam)
+        for n, r in zip(("dq", "dk", "dv"), ref):
+            errs[n] = rel_err(f64(got[n]), r)
+    print(w.name, block, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{w.name} T_B={block} {n}: {e:.3e} > {tol}"
+    return got
+
+
+SMALL = [
+    # (B, H, T, d, dv, dtype, block, decay)
+    (2, 3, 1000, 64, 64, "bf16", 64, "heads"),
+    (2, 3, 1000, 128, 128, "bf16", 128, "heads"),
+    (1, 2, 777, 128, 64, "bf16", 256, "heads"),
+    (1, 2, 500, 64, 128, "bf16", 128, "none"),
+    (1, 1, 4096, 128, 128, "bf16", 128, 0.999),
+    (2, 2, 300, 128, 128, "f32", 64, "heads"),
+    (1, 3, 257, 64, 64, "f32", 16, "heads"),
+    (1, 2, 200, 128, 64, "f32", 32, 0.5),
+    (1, 2, 333, 64, 128, "f32", 64, "none"),
+]
+
+
+@pytest.mark.parametrize("B,H,T,d,dv,dtype,block,decay", SMALL, ids=lambda v: str(v))
+def test_small_shapes(B, H, T, d, dv, dtype, block, decay):
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=B * 1000 + T, decay=decay)
+    check_full(x, block)
+
+
+def test_many_chains_no_split():
+    # 272 chains fill the GPU, so every chain runs as one segment (no workspace)
+    x = inputs.make_random(16, 17, 200, 64, 64, dtype="bf16", seed=5, decay="heads")
+    assert la2.la2_workspace_bytes(16, 17, 200, 64, 64, 64, torch.bfloat16, True) == 0
+    check_full(x, 64)
+
+
+@pytest.mark.parametrize("seg_tiles", ["1", "2", "3"])
+def test_forced_segments(seg_tiles, monkeypatch):
+    monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    x = inputs.make_random(1, 2, 700, 128, 128, dtype="bf16", seed=9, decay="heads")
+    check_full(x, 64)
+
+
+@pytest.mark.parametrize("dtype,blocks", [("bf16", (64, 128, 256)), ("f32", (16, 32, 64))])
+def test_tile_size_invariance(dtype, blocks):
+    x = inputs.make_random(1, 4, 640, 64, 64, dtype=dtype, seed=17, decay="heads")
+    outs = [check_full(x, b) for b in blocks]
+    tol = TOL[dtype]
+    for n in ("o", "dq", "dk", "dv"):
+        for o in outs[1:]:
+            assert rel_err(f64(o[n]), f64(outs[0][n])) <= 2 * tol
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 128, 129])
+def test_edge_lengths(T):
+    x = inputs.make_random(1, 2, T, 128, 128, dtype="bf16", seed=T, decay="heads")
+    check_full(x, 64)
+    xf = inputs.make_random(1, 2, T, 64, 64, dtype="f32", seed=T, decay="heads")
+    check_full(xf, 32)
+
+
+def test_zero_inputs_give_zero():
+    x = inputs.make_random(1, 2, 300, 128, 128, dtype="bf16", seed=1, decay="heads")
+    for n in ("q", "k", "v", "do"):
+        x[n] = torch.zeros_like(x[n])
+    got = run_gpu(x, 128)
+    for n in ("o", "dq", "dk", "dv"):
+        assert torch.count_nonzero(got[n]).item() == 0
+
+
+def test_strong_decay():
+    x = inputs.make_random(1, 2, 500, 64, 64, dtype="bf16", seed=3, decay=0.01)
+    check_full(x, 128)
+
+
+def test_causality_bitwise():
+    x = inputs.make_random(1, 2, 400, 128, 128, dtype="bf16", seed=21, decay="heads")
+    a = run_gpu(x, 128, backward=False)["o"]
+    t = 201
+    for n in ("k", "v"):
+        y = dict(x)
+        y[n] = x[n].clone()
+        y[n][:, :, t] += 1.0
+        b = run_gpu(y, 128, backward=False)["o"]
+        assert torch.equal(a[:, :, :t], b[:, :, :t]), n
+        assert not torch.equal(a[:, :, t:], b[:, :, t:]), n
+
+
+def test_autograd_matches_backward():
+    x = inputs.make_random(1, 2, 300, 64, 64, dtype="bf16", seed=4, decay="heads")
+    q, k, v, do = (x[n].to(DEV).requires_grad_(n != "do") for n in ("q", "k", "v", "do"))
+    decay = x["decay"].to(DEV)
+    o = la2.lightning_attention(q, k, v, decay, 64)
+    o.backward(do)
+    dq, dk, dv = la2.backward(q.detach(), k.detach(), v.detach(), do, decay, 64)
+    assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+
+
+def test_stream_ordering_on_side_stream():
+    x = inputs.make_random(1, 2, 512, 128, 128, dtype="bf16", seed=8, decay="heads")
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    decay = x["decay"].to(DEV)
+    ref = la2.forward(q, k, v, decay, 128)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o = la2.forward(q, k, v, decay, 128)
+    s.synchronize()
+    assert torch.equal(o, ref)
+
+
+# ---- the named workloads at full size --------------------------------------
+
+def test_tiny_fp32_forward():
+    x = inputs.make("tiny_fp32_fwd")
+    check_full(x, x["workload"].block, backward=False)
+
+
+def test_bf16_forward_t2k():
+    x = inputs.make("bf16_fwd_t2k")
+    check_full(x, x["workload"].block, backward=False)
+
+
+def check_sampled(name, chains, n_rows=6, seed=0):
+    """Full-size run in the benchmark's launch configuration; oracle on sampled rows."""
+    x = inputs.make(name)
+    w = x["workload"]
+    got = run_gpu(x, w.block, backward=True)
+    rng = np.random.default_rng(seed)
+    T = w.T
+    fixed = [0, 1, min(T - 1, 127), min(T - 1, 128), T - 2, T - 1]
+    rows = np.unique(np.array(fixed + list(rng.integers(0, T, n_rows))))
+    lam = lam_of(x)
+    errs = {n: [] for n in ("o", "dq", "dk", "dv")}
+    refs = {n: [] for n in errs}
+    gots = {n: [] for n in errs}
+    for b, h in chains:
+        l = 1.0 if lam is None else lam[h]
+        q, k, v, do = (f64(x[n][b, h]) for n in ("q", "k", "v", "do"))
+        refs["o"].append(oracle.forward_rows(q, k, v, l, rows))
+        gq, gk, gv = oracle.backward_rows(q, k, v, do, l, rows)
+        refs["dq"].append(gq)
+        refs["dk"].append(gk)
+        refs["dv"].append(gv)
+        for n in errs:
+            gots[n].append(f64(got[n][b, h, torch.as_tensor(rows)]))
+    for n in errs:
+        e = rel_err(np.stack(gots[n]), np.stack(refs[n]))
+        print(f"{name} {n}: {e:.3e} over {len(chains)} chains x {rows.size} rows", flush=True)
+        assert e <= TOL[w.dtype], f"{name} {n}: {e:.3e}"
+
+
+def test_tnl15b_layer_sampled():
+    check_sampled("tnl15b_layer", [(0, 0), (1, 39), (0, 20), (1, 7)])
+
+
+@pytest.mark.parametrize("name", inputs.SWEEP_NAMES)
+def test_length_sweep_sampled(name):
+    w = inputs.WORKLOADS[name]
+    check_sampled(name, [(0, 0), (w.B - 1, 15), (w.B // 2, 7)])
+
+
+def test_long_context_outliers_sampled():
+    check_sampled("long128k_outliers", [(0, 0), (0, 39), (0, 13)], n_rows=4)
