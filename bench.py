@@ -1,0 +1,195 @@
+"""Throughput of the Lightning Attention-2 forward + backward on one MI355X.
+
+Workload: the fixed-token length sweep -- 131,072 tokens per batch at
+(B, T) = (128, 1K), (32, 4K), (8, 16K), (2, 64K), (1, 128K), H = 16 heads,
+d = d_v = 128, tile T_B = 128, no decay, bf16 in HBM with fp32 accumulation,
+synthetic seeded inputs.  One step is the whole hot path (la2_forward then
+la2_backward) over each of the five batches; every input is resident in HBM
+before the timed region starts.
+
+Prints one JSON line: whole-job tokens/s over the timed steps, the per-length
+tokens/s, the roofline of the dominant kernel measured with HIP events on the
+stream the kernels run on, and the CPU oracle's tokens/s on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--points", default="all", help="comma list of sweep lengths in K (e.g. 1,128) or 'all'")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=64,
+                    help="sequences of the 1K point the oracle runs for the CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """Algorithmic bytes and flops of one forward and one backward over workload w (per call)."""
+    th = w.B * w.H * w.T                      # token-heads
+    e = 2 if w.dtype == "bf16" else 4
+    d = w.d
+    tb = w.block
+    return {
+        "fwd_bytes": th * 4 * d * e,          # read q, k, v; write o
+        "bwd_bytes": th * 7 * d * e,          # read q, k, v, do; write dq, dk, dv
+        "fwd_flops": th * (4 * tb * d + 4 * d * d),
+        "bwd_flops": th * (10 * tb * d + 10 * d * d),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "chains shard across GPUs with no communication, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_linear_attention_amd as la2
+    from causal_linear_attention_amd import inputs
+
+    dev = torch.device("cuda:0")
+    names = inputs.SWEEP_NAMES
+    if args.points != "all":
+        want = {int(p) for p in args.points.split(",")}
+        names = [n for n in names if inputs.WORKLOADS[n].T // 1024 in want]
+
+    # ---- inputs resident in HBM --------------------------------------------
+    cases = []
+    for n in names:
+        x = inputs.make(n)
+        w = x["workload"]
+        q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
+        decay = None if x["decay"] is None else x["decay"].to(dev)
+        ws_n = max(la2.la2_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.block, q.dtype, b) for b in (0, 1))
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+        o = torch.empty_like(v)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        cases.append(dict(w=w, q=q, k=k, v=v, do=do, decay=decay, ws=ws, o=o, dq=dq, dk=dk, dv=dv,
+                          host=x if (w.T == 1024 and not args.no_cpu_baseline) else None))
+        print(f"[bench] {w.name}: B={w.B} T={w.T} workspace={ws_n} B", file=sys.stderr, flush=True)
+        del x
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(record=None):
+        for i, c in enumerate(cases):
+            ev = record[i] if record is not None else None
+            if ev:
+                ev[0].record(stream)
+            la2.la2_forward(c["q"], c["k"], c["v"], c["decay"], c["o"], c["w"].block, c["ws"], stream)
+            if ev:
+                ev[1].record(stream)
+            la2.la2_backward(c["q"], c["k"], c["v"], c["decay"], c["do"], c["dq"], c["dk"], c["dv"],
+                             c["w"].block, c["ws"], stream)
+            if ev:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in cases] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [sum(events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)) / args.steps
+              for i in range(len(cases))]
+    bwd_ms = [sum(events[s][i][1].elapsed_time(events[s][i][2]) for s in range(args.steps)) / args.steps
+              for i in range(len(cases))]
+
+    tokens_per_step = sum(c["w"].tokens for c in cases)
+    value = tokens_per_step * args.steps / wall
+    sweep = {}
+    for c, f, b in zip(cases, fwd_ms, bwd_ms):
+        w = c["w"]
+        alg = algorithmic(w)
+        sweep[f"T={w.T}"] = {
+            "B": w.B, "fwd_ms": round(f, 4), "bwd_ms": round(b, 4),
+            "tokens_per_s": round(w.tokens / ((f + b) * 1e-3), 1),
+            "fwd_GBs": round(alg["fwd_bytes"] / (f * 1e-3) / 1e9, 1),
+            "bwd_GBs": round(alg["bwd_bytes"] / (b * 1e-3) / 1e9, 1),
+            "fwd_bwd_TFLOPs": round((alg["fwd_flops"] + alg["bwd_flops"]) / ((f + b) * 1e-3) / 1e12, 1),
+        }
+    tps = [v["tokens_per_s"] for v in sweep.values()]
+
+    # Dominant kernel: the forward-direction output scan; at the 1K point la2_forward is exactly one
+    # launch of it (2048 chains fill the GPU, no segment split), so its event time is that launch.
+    dom = next((i for i, c in enumerate(cases) if c["ws"] is None), None)
+    roofline = None
+    if dom is not None:
+        w = cases[dom]["w"]
+        alg = algorithmic(w)
+        achieved = alg["fwd_bytes"] / (fwd_ms[dom] * 1e-3) / 1e9
+        roofline = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "scan_bf16_kernel<D=128,DV=128,TB=128,Forward,Output>",
+            "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
+            "avg_launch_ms": round(fwd_ms[dom], 4),
+            "algorithmic_bytes_per_launch": alg["fwd_bytes"],
+            "mfma_TFLOPs": round(alg["fwd_flops"] / (fwd_ms[dom] * 1e-3) / 1e12, 1),
+            "mfma_frac": round(alg["fwd_flops"] / (fwd_ms[dom] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+
+    cpu = None
+    hostc = next((c for c in cases if c["host"] is not None), None)
+    if hostc is not None:
+        import oracle
+        x = hostc["host"]
+        nseq = min(args.cpu_sample_seqs, x["workload"].B)
+        sl = lambda t: t[:nseq].double().numpy()
+        q, k, v, do = (sl(x[n]) for n in ("q", "k", "v", "do"))
+        ta = time.perf_counter()
+        oracle.forward(q, k, v, None)
+        oracle.backward(q, k, v, do, None)
+        tc = time.perf_counter() - ta
+        cpu = {"value": round(nseq * x["workload"].T / tc, 1), "unit": "tokens/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{nseq} sequences x 1024 tokens x 16 heads of the T=1K batch, forward + backward, "
+                         f"fp64 token recurrence, {tc:.1f} s"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fixed-token length sweep: 131072 tokens per batch at (B,T) in "
+                        + ",".join(f"({c['w'].B},{c['w'].T})" for c in cases)
+                        + "; H=16, d=d_v=128, T_B=128, no decay; one step = fwd+bwd over every batch",
+            "tokens_per_step": tokens_per_step, "heads": 16, "d": 128, "d_v": 128, "block": 128,
+            "parallelism": "none (1 GPU)",
+        },
+        "sweep": sweep,
+        "flatness": round(min(tps) / max(tps), 4) if tps else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,6 @@
 // la2_scan_bf16.hip -- bf16 tile-scan kernel of Lightning Attention-2 on gfx950 MFMA.
 //
-// One workgroup (4 waves) owns one (chain, segment, value-slice) work item and walks
+// One workgroup (8 waves, two per SIMD) owns one (chain, segment, value-slice) work item and walks
 // the segment's tiles in order (page "Lightning Attention", lizeman.github.io
 // llm-arch-kb, section 2, Steps 1-4).  Per tile of TB positions it computes
 //
@@ -35,7 +35,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -83,16 +84,15 @@ struct Cfg {
     static constexpr int NTB = TB / 32;          // 32-row blocks of the tile
     static constexpr int NDB = DV / 32;          // 32-column blocks of the value slice
     static constexpr int NKB = D / 32;           // 32-row blocks of the state
-    static constexpr int WPT = 4 / NTB;          // waves sharing one row block
+    static constexpr int WPT = (kWaves / NTB < NDB) ? kWaves / NTB : NDB;   // waves sharing one row block
     static constexpr int ODB = NDB / WPT;        // value blocks of O per wave
-    static constexpr int SPW = NKB * NDB / 4;    // state blocks per wave
-    // global -> register staging
+    static constexpr int NSB = NKB * NDB;        // 32x32 blocks of the state
+    static constexpr int SPW = NSB > kWaves ? NSB / kWaves : 1;   // state blocks per wave
+    // global -> register staging: Q in 16-byte chunks, K and V in 8x8 blocks (one per thread)
     static constexpr int QCH = kOut ? TB * D / 8 : 0;
     static constexpr int QPT = (QCH + kThreads - 1) / kThreads;
     static constexpr int KBLK = (TB / 8) * (D / 8);
-    static constexpr int KPT = (KBLK + kThreads - 1) / kThreads;
     static constexpr int VBLK = (TB / 8) * (DV / 8);
-    static constexpr int VPT = (VBLK + kThreads - 1) / kThreads;
     // LDS carve-up (bf16 elements)
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + (kOut ? TB * D : 0);
@@ -101,16 +101,33 @@ struct Cfg {
     static constexpr int oST = oVT + DV * TB;
     static constexpr int kLds = oST + (kOut ? DV * D : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
-    static_assert(ODB >= 1 && SPW >= 1 && NKB * NDB % 4 == 0, "shape");
+    static_assert(ODB * WPT == NDB && NTB * WPT <= kWaves, "output blocks");
+    static_assert(SPW * kWaves == NSB || (SPW == 1 && NSB <= kWaves), "state blocks");
+    static_assert(KBLK + VBLK <= kThreads, "one staging block per thread");
     static_assert(kLds * 2 <= 160 * 1024, "LDS");
 };
+
+// Row block and part (which ODB value blocks) of O owned by a wave.  Waves w and w + 4
+// share a SIMD; the mapping gives each SIMD one short and one long causal row block.
+template <int NTB, int WPT>
+__device__ __forceinline__ void wave_rows(int wave, int &tb, int &part) {
+    if constexpr (NTB == 4 && WPT == 2) {
+        tb = wave < 4 ? wave : 7 - wave;
+        part = wave < 4 ? 0 : 1;
+    } else if constexpr (NTB == 2 && WPT == 4) {
+        tb = (wave & 1) ^ ((wave >> 2) & 1);
+        part = (wave >> 1) & 3;
+    } else {
+        tb = wave % NTB;
+        part = wave / NTB;
+    }
+}
 
 template <int D, int DV, int TB, Mode MODE>
 struct Staged {
     using C = Cfg<D, DV, TB, MODE>;
     u32x4 q[C::QPT > 0 ? C::QPT : 1];
-    u32x4 k[C::KPT][8];
-    u32x4 v[C::VPT][8];
+    u32x4 blk[8];     // rows of this thread's 8x8 block of K (tid < KBLK) or V (KBLK <= tid < KBLK + VBLK)
 };
 
 template <int D, int DV, int TB, Mode MODE>
@@ -127,24 +144,20 @@ __device__ __forceinline__ void stage_load(Staged<D, DV, TB, MODE> &r, const u16
             r.q[s] = (cid < C::QCH && t < T) ? gload(a + t * D + ch * 8) : zero;
         }
     }
-#pragma unroll
-    for (int s = 0; s < C::KPT; ++s) {
-        const int bid = tid + s * kThreads;
-        const int rg = bid / (D / 8), cc = bid % (D / 8);
+    if (tid < C::KBLK) {
+        const int rg = tid / (D / 8), cc = tid % (D / 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t t = t0 + group_row(rg, i);
-            r.k[s][i] = (bid < C::KBLK && t < T) ? gload(b + t * D + cc * 8) : zero;
+            r.blk[i] = t < T ? gload(b + t * D + cc * 8) : zero;
         }
-    }
-#pragma unroll
-    for (int s = 0; s < C::VPT; ++s) {
-        const int bid = tid + s * kThreads;
+    } else if (tid < C::KBLK + C::VBLK) {
+        const int bid = tid - C::KBLK;
         const int rg = bid / (DV / 8), cc = bid % (DV / 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t t = t0 + group_row(rg, i);
-            r.v[s][i] = (bid < C::VBLK && t < T) ? gload(c + t * DVT + cc * 8) : zero;
+            r.blk[i] = t < T ? gload(c + t * DVT + cc * 8) : zero;
         }
     }
 }
@@ -192,33 +205,47 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
             if (cid < C::QCH) lds_write(smem + C::oQ, lds_off<D>(cid / (D / 8), cid % (D / 8)), r.q[s]);
         }
     }
+    if (tid < C::KBLK) {
+        const int rg = tid / (D / 8), cc = tid % (D / 8);
+        if constexpr (C::kOut) {
 #pragma unroll
-    for (int s = 0; s < C::KPT; ++s) {
-        const int bid = tid + s * kThreads;
-        if (bid < C::KBLK) {
-            const int rg = bid / (D / 8), cc = bid % (D / 8);
-            if constexpr (C::kOut) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) lds_write(smem + C::oK, lds_off<D>(group_row(rg, i), cc), r.k[s][i]);
-            }
-            if (weighted) {
-                float wrow[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = group_row(rg, i);
-                    wrow[i] = exp2f((float)(DIR == Dir::Forward ? TB - 1 - j : j) * l2);
-                }
-                write_transposed_weighted<TB>(smem + C::oKT, r.k[s], wrow, rg, cc);
-            } else {
-                write_transposed<TB>(smem + C::oKT, r.k[s], rg, cc);
-            }
+            for (int i = 0; i < 8; ++i) lds_write(smem + C::oK, lds_off<D>(group_row(rg, i), cc), r.blk[i]);
         }
-    }
+        if (weighted) {
+            float wrow[8];
 #pragma unroll
-    for (int s = 0; s < C::VPT; ++s) {
-        const int bid = tid + s * kThreads;
-        if (bid < C::VBLK) write_transposed<TB>(smem + C::oVT, r.v[s], bid / (DV / 8), bid % (DV / 8));
+            for (int i = 0; i < 8; ++i) {
+                const int j = group_row(rg, i);
+                wrow[i] = exp2f((float)(DIR == Dir::Forward ? TB - 1 - j : j) * l2);
+            }
+            write_transposed_weighted<TB>(smem + C::oKT, r.blk, wrow, rg, cc);
+        } else {
+            write_transposed<TB>(smem + C::oKT, r.blk, rg, cc);
+        }
+    } else if (tid < C::KBLK + C::VBLK) {
+        const int bid = tid - C::KBLK;
+        write_transposed<TB>(smem + C::oVT, r.blk, bid / (DV / 8), bid % (DV / 8));
     }
+}
+
+// 4x4 transpose inside each quad of lanes: on entry lane m of the quad holds x[i] = M[i][m];
+// on exit it holds x[i] = M[m][i].  Two DPP exchanges (lane xor 1, lane xor 2).
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void quad_transpose(float &x0, float &x1, float &x2, float &x3, int lane) {
+    const bool b0 = lane & 1, b1 = lane & 2;
+    float r = dpp_xor1(b0 ? x0 : x1);
+    if (b0) x0 = r; else x1 = r;
+    r = dpp_xor1(b0 ? x2 : x3);
+    if (b0) x2 = r; else x3 = r;
+    r = dpp_xor2(b1 ? x0 : x2);
+    if (b1) x0 = r; else x2 = r;
+    r = dpp_xor2(b1 ? x1 : x3);
+    if (b1) x1 = r; else x3 = r;
 }
 
 template <int D, int DV, int TB, Dir DIR, Mode MODE>
@@ -253,9 +280,12 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const float l2 = has_decay ? log2f(p.decay[chain % p.H]) : 0.0f;
     auto pw = [&](int n) -> float { return has_decay ? exp2f((float)n * l2) : 1.0f; };
 
-    // waves -> blocks
-    const int tb = wave / C::WPT;                 // row block of O and P owned by this wave
-    const int db0 = (wave % C::WPT) * C::ODB;     // first value block of O owned by this wave
+    // waves -> blocks of O (row block tb, value blocks db0 .. db0 + ODB - 1) and of the state
+    int tb, part;
+    wave_rows<C::NTB, C::WPT>(wave, tb, part);
+    const bool o_active = part < C::WPT;
+    const int db0 = part * C::ODB;
+    const bool s_active = wave * C::SPW < C::NSB;
 
     f32x16 sacc[C::SPW];
     const bool init_state = C::kOut && gs != nullptr &&
@@ -266,14 +296,16 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            sacc[s][r] = init_state ? gs[(int64_t)d * p.DVT + nb * 32 + col] : 0.0f;
+            sacc[s][r] = (init_state && s_active) ? gs[(int64_t)d * p.DVT + nb * 32 + col] : 0.0f;
         }
     }
 
     auto tile_of = [&](int it) -> int64_t { return DIR == Dir::Forward ? tile_lo + it : tile_hi - 1 - it; };
 
+    // S^T (bf16) into LDS for the next tile's right product
     auto write_state_lds = [&]() {
         if constexpr (C::kOut) {
+            if (!s_active) return;
 #pragma unroll
             for (int s = 0; s < C::SPW; ++s) {
                 const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
@@ -302,88 +334,102 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         const bool update = (MODE == Mode::StateOnly) || (it + 1 < ntiles);
 
         if constexpr (C::kOut) {
-            const u16 *sQ = smem + C::oQ, *sK = smem + C::oK, *sVT = smem + C::oVT, *sST = smem + C::oST;
-            bf16x8 qf[D / 16];
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) qf[ks] = lds_read(sQ, lds_off<D>(tb * 32 + col, 2 * ks + h));
+            if (o_active) {
+                const u16 *sQ = smem + C::oQ, *sK = smem + C::oK, *sVT = smem + C::oVT, *sST = smem + C::oST;
+                const int qrow = tb * 32 + col;
 
-            f32x16 oacc[C::ODB];
+                f32x16 oacc[C::ODB];
 #pragma unroll
-            for (int n = 0; n < C::ODB; ++n)
+                for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
+                    for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
 
-            // Step 3: inter-tile right product, rows weighted by w_inter
-            if (state_nonzero) {
+                // Step 3: inter-tile right product, rows weighted by w_inter
+                if (state_nonzero) {
+#pragma unroll 2
+                    for (int ks = 0; ks < D / 16; ++ks) {
+                        const bf16x8 qf = lds_read(sQ, lds_off<D>(qrow, 2 * ks + h));
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
+                        for (int n = 0; n < C::ODB; ++n)
+                            oacc[n] = mfma(qf, lds_read(sST, lds_off<D>((db0 + n) * 32 + col, 2 * ks + h)), oacc[n]);
+                    }
+                    if (has_decay) {
 #pragma unroll
-                    for (int n = 0; n < C::ODB; ++n)
-                        oacc[n] = mfma(qf[ks], lds_read(sST, lds_off<D>((db0 + n) * 32 + col, 2 * ks + h)), oacc[n]);
-                if (has_decay) {
+                        for (int r = 0; r < 16; ++r) {
+                            const int i = tb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const float w = pw(DIR == Dir::Forward ? i + 1 : TB - i);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = tb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const float w = pw(DIR == Dir::Forward ? i + 1 : TB - i);
-#pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) oacc[n][r] *= w;
+                            for (int n = 0; n < C::ODB; ++n) oacc[n][r] *= w;
+                        }
                     }
                 }
-            }
 
-            // Step 2: intra-tile masked left product, one 32x32 block of A^T at a time
-            const int ulo = DIR == Dir::Forward ? 0 : tb;
-            const int uhi = DIR == Dir::Forward ? tb : C::NTB - 1;
-            const int tcol = tb * 32 + col;
-            for (int u = ulo; u <= uhi; ++u) {
-                f32x16 acc;
+                // Step 2: intra-tile masked left product, one 32x32 block of A^T at a time
+                const int ulo = DIR == Dir::Forward ? 0 : tb;
+                const int uhi = DIR == Dir::Forward ? tb : C::NTB - 1;
+                const int tcol = tb * 32 + col;
+                for (int u = ulo; u <= uhi; ++u) {
+                    f32x16 acc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+                    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 4
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        acc = mfma(lds_read(sK, lds_off<D>(u * 32 + col, 2 * ks + h)),
+                                   lds_read(sQ, lds_off<D>(qrow, 2 * ks + h)), acc);
+                    bf16x8 pf[2];
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-                    acc = mfma(lds_read(sK, lds_off<D>(u * 32 + col, 2 * ks + h)), qf[ks], acc);
-                bf16x8 pf[2];
+                    for (int r = 0; r < 16; ++r) {
+                        const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
+                        const float v = diff >= 0 ? acc[r] * pw(diff) : 0.0f;
+                        pf[r >> 3][r & 7] = (__bf16)v;
+                    }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
-                    const float v = diff >= 0 ? acc[r] * pw(diff) : 0.0f;
-                    pf[r >> 3][r & 7] = (__bf16)v;
+                    for (int x = 0; x < 2; ++x)
+#pragma unroll
+                        for (int n = 0; n < C::ODB; ++n)
+                            oacc[n] = mfma(pf[x],
+                                           lds_read(sVT, lds_off<TB>((db0 + n) * 32 + col, 4 * u + 2 * x + h)),
+                                           oacc[n]);
                 }
-#pragma unroll
-                for (int x = 0; x < 2; ++x)
-#pragma unroll
-                    for (int n = 0; n < C::ODB; ++n)
-                        oacc[n] = mfma(pf[x], lds_read(sVT, lds_off<TB>((db0 + n) * 32 + col, 4 * u + 2 * x + h)),
-                                       oacc[n]);
-            }
 
-            // store O rows of this wave (bf16, rows beyond T dropped)
+                // store O: a quad transpose gives each lane 4 consecutive columns of one row
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t t = t0 + tb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (t < T) {
+                for (int n = 0; n < C::ODB; ++n) {
 #pragma unroll
-                    for (int n = 0; n < C::ODB; ++n) gy[t * p.DVT + (db0 + n) * 32 + col] = (u16)f32_to_bf16(oacc[n][r]);
+                    for (int j = 0; j < 4; ++j) {
+                        float x0 = oacc[n][4 * j], x1 = oacc[n][4 * j + 1], x2 = oacc[n][4 * j + 2],
+                              x3 = oacc[n][4 * j + 3];
+                        quad_transpose(x0, x1, x2, x3, lane);
+                        const int64_t t = t0 + tb * 32 + 8 * j + 4 * h + (lane & 3);
+                        if (t < T) {
+                            u32x2 pk;
+                            pk[0] = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
+                            pk[1] = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
+                            *reinterpret_cast<u32x2 *>(gy + t * p.DVT + (db0 + n) * 32 + (col & ~3)) = pk;
+                        }
+                    }
                 }
             }
         }
 
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
-            if (has_decay) {
-                const float f = pw(TB);
+            if (s_active) {
+                if (has_decay) {
+                    const float f = pw(TB);
 #pragma unroll
-                for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
-            }
-            const u16 *sKT = smem + C::oKT, *sVT = smem + C::oVT;
+                    for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
+                }
+                const u16 *sKT = smem + C::oKT, *sVT = smem + C::oVT;
+#pragma unroll 2
+                for (int x = 0; x < TB / 16; ++x) {
 #pragma unroll
-            for (int x = 0; x < TB / 16; ++x) {
-#pragma unroll
-                for (int s = 0; s < C::SPW; ++s) {
-                    const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-                    sacc[s] = mfma(lds_read(sKT, lds_off<TB>(kb * 32 + col, 2 * x + h)),
-                                   lds_read(sVT, lds_off<TB>(nb * 32 + col, 2 * x + h)), sacc[s]);
+                    for (int s = 0; s < C::SPW; ++s) {
+                        const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+                        sacc[s] = mfma(lds_read(sKT, lds_off<TB>(kb * 32 + col, 2 * x + h)),
+                                       lds_read(sVT, lds_off<TB>(nb * 32 + col, 2 * x + h)), sacc[s]);
+                    }
                 }
             }
             state_nonzero = true;
@@ -399,13 +445,15 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     }
 
     if constexpr (MODE == Mode::StateOnly) {
+        if (s_active) {
 #pragma unroll
-        for (int s = 0; s < C::SPW; ++s) {
-            const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+            for (int s = 0; s < C::SPW; ++s) {
+                const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                gs[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    gs[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
+                }
             }
         }
     }
