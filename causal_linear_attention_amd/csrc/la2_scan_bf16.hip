@@ -49,6 +49,16 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * RL + ((chunk ^ (row & (NCH - 1))) << 3);
 }
 
+// Same for the transposed tiles (rows are d or d_v indices, chunks hold 8 positions).  Staging
+// writes one column of 8x8 blocks per lane, so a group of lanes hits rows 8 apart; the swizzle
+// folds row bits 3.. into the chunk index so those writes and the MFMA fragment reads (32
+// consecutive rows) both land on distinct banks.
+template <int RL>
+__device__ __forceinline__ int lds_off_t(int row, int chunk) {
+    constexpr int NCH = RL / 8;
+    return row * RL + ((chunk ^ ((row ^ (row >> 3)) & (NCH - 1))) << 3);
+}
+
 __device__ __forceinline__ bf16x8 lds_read(const u16 *s, int off) {
     return *reinterpret_cast<const bf16x8 *>(s + off);
 }
@@ -173,7 +183,7 @@ __device__ __forceinline__ void write_transposed(u16 *sT, const u32x4 (&x)[8], i
             const unsigned int lo = x[2 * m][e >> 1], hi = x[2 * m + 1][e >> 1];
             out[m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
         }
-        lds_write(sT, lds_off<TB>(cc * 8 + e, rg), out);
+        lds_write(sT, lds_off_t<TB>(cc * 8 + e, rg), out);
     }
 }
 
@@ -190,13 +200,12 @@ __device__ __forceinline__ void write_transposed_weighted(u16 *sT, const u32x4 (
             const unsigned int hi = f32_to_bf16(bf16_to_f32(elem(x[2 * m + 1], e)) * wrow[2 * m + 1]);
             out[m] = lo | (hi << 16);
         }
-        lds_write(sT, lds_off<TB>(cc * 8 + e, rg), out);
+        lds_write(sT, lds_off_t<TB>(cc * 8 + e, rg), out);
     }
 }
 
-template <int D, int DV, int TB, Dir DIR, Mode MODE>
-__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid,
-                                            bool weighted, float l2) {
+template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
+__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid, float l2) {
     using C = Cfg<D, DV, TB, MODE>;
     if constexpr (C::kOut) {
 #pragma unroll
@@ -211,12 +220,12 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
 #pragma unroll
             for (int i = 0; i < 8; ++i) lds_write(smem + C::oK, lds_off<D>(group_row(rg, i), cc), r.blk[i]);
         }
-        if (weighted) {
+        if constexpr (DECAY) {
             float wrow[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int j = group_row(rg, i);
-                wrow[i] = exp2f((float)(DIR == Dir::Forward ? TB - 1 - j : j) * l2);
+                wrow[i] = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - j : j) * l2);
             }
             write_transposed_weighted<TB>(smem + C::oKT, r.blk, wrow, rg, cc);
         } else {
@@ -248,7 +257,7 @@ __device__ __forceinline__ void quad_transpose(float &x0, float &x1, float &x2, 
     if (b1) x1 = r; else x3 = r;
 }
 
-template <int D, int DV, int TB, Dir DIR, Mode MODE>
+template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
 __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     using C = Cfg<D, DV, TB, MODE>;
     __shared__ __attribute__((aligned(16))) u16 smem[C::kLds];
@@ -276,9 +285,9 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     u16 *gy = C::kOut ? static_cast<u16 *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
     float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + dv0 : nullptr;
 
-    const bool has_decay = p.decay != nullptr;
-    const float l2 = has_decay ? log2f(p.decay[chain % p.H]) : 0.0f;
-    auto pw = [&](int n) -> float { return has_decay ? exp2f((float)n * l2) : 1.0f; };
+    // lam^n = 2^(n log2 lam) with the hardware exp2 (n >= 0 only, so no overflow; tiny powers flush to 0)
+    const float l2 = DECAY ? log2f(p.decay[chain % p.H]) : 0.0f;
+    auto pw = [&](int n) -> float { return DECAY ? __builtin_amdgcn_exp2f((float)n * l2) : 1.0f; };
 
     // waves -> blocks of O (row block tb, value blocks db0 .. db0 + ODB - 1) and of the state
     int tb, part;
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
     Staged<D, DV, TB, MODE> st;
     stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
-    stage_store<D, DV, TB, DIR, MODE>(st, smem, tid, has_decay, l2);
+    stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
     if (ntiles > 1) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(1) * TB, T, p.DVT, tid);
     if (init_state) write_state_lds();
     __syncthreads();
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                         for (int n = 0; n < C::ODB; ++n)
                             oacc[n] = mfma(qf, lds_read(sST, lds_off<D>((db0 + n) * 32 + col, 2 * ks + h)), oacc[n]);
                     }
-                    if (has_decay) {
+                    if constexpr (DECAY) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int i = tb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -376,20 +385,30 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     for (int ks = 0; ks < D / 16; ++ks)
                         acc = mfma(lds_read(sK, lds_off<D>(u * 32 + col, 2 * ks + h)),
                                    lds_read(sQ, lds_off<D>(qrow, 2 * ks + h)), acc);
+                    // causal decay mask: only the diagonal block has masked entries
                     bf16x8 pf[2];
+                    if (u == tb) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
-                        const float v = diff >= 0 ? acc[r] * pw(diff) : 0.0f;
-                        pf[r >> 3][r & 7] = (__bf16)v;
+                        for (int r = 0; r < 16; ++r) {
+                            const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
+                            const float v = diff >= 0 ? (DECAY ? acc[r] * pw(diff) : acc[r]) : 0.0f;
+                            pf[r >> 3][r & 7] = (__bf16)v;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
+                            pf[r >> 3][r & 7] = (__bf16)(DECAY ? acc[r] * pw(diff) : acc[r]);
+                        }
                     }
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
                         for (int n = 0; n < C::ODB; ++n)
                             oacc[n] = mfma(pf[x],
-                                           lds_read(sVT, lds_off<TB>((db0 + n) * 32 + col, 4 * u + 2 * x + h)),
+                                           lds_read(sVT, lds_off_t<TB>((db0 + n) * 32 + col, 4 * u + 2 * x + h)),
                                            oacc[n]);
                 }
 
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
             if (s_active) {
-                if (has_decay) {
+                if constexpr (DECAY) {
                     const float f = pw(TB);
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
@@ -427,8 +446,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) {
                         const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-                        sacc[s] = mfma(lds_read(sKT, lds_off<TB>(kb * 32 + col, 2 * x + h)),
-                                       lds_read(sVT, lds_off<TB>(nb * 32 + col, 2 * x + h)), sacc[s]);
+                        sacc[s] = mfma(lds_read(sKT, lds_off_t<TB>(kb * 32 + col, 2 * x + h)),
+                                       lds_read(sVT, lds_off_t<TB>(nb * 32 + col, 2 * x + h)), sacc[s]);
                     }
                 }
             }
@@ -438,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         __syncthreads();                       // every wave is done with this tile's LDS
         if (update) write_state_lds();
         if (it + 1 < ntiles) {
-            stage_store<D, DV, TB, DIR, MODE>(st, smem, tid, has_decay, l2);
+            stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
             if (it + 2 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 2) * TB, T, p.DVT, tid);
         }
         __syncthreads();
@@ -462,7 +481,12 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 template <int D, int DV, int TB, Dir DIR, Mode MODE>
 hipError_t launch_one(const ScanArgs &a, hipStream_t s) {
     const int64_t items = (int64_t)a.chains * a.seg_count * a.nslice;
-    hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, MODE>), dim3((unsigned)items), dim3(kThreads), 0, s, a);
+    if (a.decay)
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, MODE, true>), dim3((unsigned)items), dim3(kThreads), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, MODE, false>), dim3((unsigned)items), dim3(kThreads),
+                           0, s, a);
     return hipGetLastError();
 }
 
