@@ -1,8 +1,8 @@
 // la2_scan_bf16.hip -- bf16 tile-scan kernel of Lightning Attention-2 on gfx950 MFMA.
 //
 // One workgroup (8 waves, two per SIMD) owns one (chain, segment, value-slice) work item and walks
-// the segment's tiles in order (page "Lightning Attention", lizeman.github.io
-// llm-arch-kb, section 2, Steps 1-4).  Per tile of TB positions it computes
+// the segment's tiles in order (page "Lightning Attention", lizeman.github.io llm-arch-kb,
+// section 2, Steps 1-4).  Per tile of TB positions it computes
 //
 //   A^T   = K_b Q_b^T                 (Step 2 scores, transposed, fp32 in MFMA accumulators)
 //   P     = causal decay mask of A    (kept in registers; becomes the next MFMA's A operand)
@@ -12,18 +12,19 @@
 // with the decay weights of the token recurrence S_t = lam S_{t-1} + k_t v_t^T:
 //   forward: mask lam^(i-j) for j <= i, w_inter = lam^(i+1),  w_upd = lam^(TB-1-j)
 //   reverse: mask lam^(j-i) for j >= i, w_inter = lam^(TB-i), w_upd = lam^j
-// The reverse direction is the same scan run from the last tile to the first; the
-// backward pass uses it for dK and dV.  All products are v_mfma_f32_32x32x16_bf16.
+// The reverse direction is the same scan run from the last tile to the first; the backward pass
+// uses it for dK and dV.  All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
-// LDS layout (bf16, every row split in 16-byte chunks XOR-swizzled by row index):
-//   sQ  [TB][D]   natural Q tile          (A^T B operand, Q S A operand)
-//   sK  [TB][D]   natural K tile          (A^T A operand)
-//   sKT [D][TB]   weighted K^T            (state update A operand)
-//   sVT [DV][TB]  V^T                     (P V B operand, state update B operand)
-//   sST [DV][D]   S^T rounded to bf16     (Q S B operand)
-// In sKT and sVT the positions of each group of 16 are stored in the order
-// 0-3, 8-11, 4-7, 12-15, which is the order in which one lane of a 32x32 MFMA
-// accumulator holds the rows of P, so P can be fed to the next MFMA directly.
+// LDS holds the tiles in their natural row-major layout, rows split in 16-byte chunks whose
+// position is XOR-swizzled by row:
+//   sQ  [TB][D]   Q tile      (A^T B operand and Q S A operand: plain 16-byte fragment reads)
+//   sK  [TB][D]   K tile      (A^T A operand: plain reads; state-update A operand K^T: transpose reads)
+//   sV  [TB][DV]  V tile      (P V and state-update B operand V: transpose reads)
+//   sST [DV][D]   S^T in bf16 (Q S B operand)
+// Operands that need 8 consecutive positions per lane (K^T, V) come from ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
+// i/4 + 4e, so lanes that address (row R0 + j/4, column C0 + 4 (j%4)) get column C0 + i, rows
+// R0..R0+3.  Each tile is staged global -> registers -> LDS during the second half of the previous one.
 #include "la2_internal.h"
 
 namespace la2 {
@@ -31,6 +32,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
@@ -42,21 +44,15 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Offset (in bf16 elements) of 16-byte chunk `chunk` of row `row` in a [rows][RL] LDS matrix.
+// Element offset of 16-byte chunk `chunk` of row `row` in a row-major [rows][RL] bf16 LDS tile.
+// RL = 128: chunk ^ (row ^ 4 (row & 3)) mod 16 spreads both 32 consecutive rows at one chunk
+// (fragment reads) and rows {r..r+3, r+8..r+11} at four chunks (transpose reads) over all banks.
 template <int RL>
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    constexpr int NCH = RL / 8;
-    return row * RL + ((chunk ^ (row & (NCH - 1))) << 3);
-}
-
-// Same for the transposed tiles (rows are d or d_v indices, chunks hold 8 positions).  Staging
-// writes one column of 8x8 blocks per lane, so a group of lanes hits rows 8 apart; the swizzle
-// folds row bits 3.. into the chunk index so those writes and the MFMA fragment reads (32
-// consecutive rows) both land on distinct banks.
-template <int RL>
-__device__ __forceinline__ int lds_off_t(int row, int chunk) {
-    constexpr int NCH = RL / 8;
-    return row * RL + ((chunk ^ ((row ^ (row >> 3)) & (NCH - 1))) << 3);
+__device__ __forceinline__ int nat_off(int row, int chunk) {
+    if constexpr (RL == 128)
+        return row * 128 + ((chunk ^ ((row ^ ((row & 3) << 2)) & 15)) << 3);
+    else
+        return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 __device__ __forceinline__ bf16x8 lds_read(const u16 *s, int off) {
@@ -67,25 +63,46 @@ __device__ __forceinline__ void lds_write(u16 *s, int off, const u32x4 &v) {
     *reinterpret_cast<u32x4 *>(s + off) = v;
 }
 
-__device__ __forceinline__ u32x4 gload(const u16 *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
+__device__ __forceinline__ s16x4 tr_read(const u16 *s, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(s + off));
 }
 
-__device__ __forceinline__ float bf16_to_f32(unsigned int bits16) {
-    return __uint_as_float(bits16 << 16);
+// MFMA operand fragment (either side) from a natural [positions][RL] tile: lane l gets column
+// n0 + l % 32 and 8 positions.  PERM = false: positions k0 + 8h + 0..7 (h = l / 32), the order
+// of a plain 16-byte read; PERM = true: k0 + {4h..4h+3, 8+4h..8+4h+3}, the order in which an
+// MFMA accumulator lane holds the rows of P.
+template <int RL, bool PERM>
+__device__ __forceinline__ bf16x8 frag_tr(const u16 *s, int k0, int n0, int lane) {
+    const int g = lane >> 4, j = lane & 15, h = g >> 1;
+    const int col = n0 + 16 * (g & 1) + 4 * (j & 3);
+    const int r0 = k0 + (PERM ? 4 * h : 8 * h) + (j >> 2);
+    const int r1 = r0 + (PERM ? 8 : 4);
+    // assemble from whole dwords: per-element 16-bit extraction of the builtin's result is
+    // mis-lowered by this compiler (every element comes out as element 0)
+    const u32x2 a = __builtin_bit_cast(u32x2, tr_read(s, nat_off<RL>(r0, col >> 3) + (col & 7)));
+    const u32x2 b = __builtin_bit_cast(u32x2, tr_read(s, nat_off<RL>(r1, col >> 3) + (col & 7)));
+    const u32x4 w = {a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Buffer resource over `bytes` bytes from `base`: loads past the end return 0 and stores past
+// the end are dropped by the hardware range check, which is what handles a ragged last tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x2 &v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r,
+                                          byte_off, 0, 0);
 }
 
 __device__ __forceinline__ unsigned int f32_to_bf16(float f) {
     return (unsigned int)__builtin_bit_cast(u16, (__bf16)f);
-}
-
-__device__ __forceinline__ unsigned int elem(const u32x4 &x, int e) {
-    return (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-}
-
-// Row (within the tile) of element i of 8-row group rg, in the 0-3,8-11,4-7,12-15 order.
-__device__ __forceinline__ int group_row(int rg, int i) {
-    return 16 * (rg >> 1) + 4 * (rg & 1) + i + (i >= 4 ? 4 : 0);
 }
 
 template <int D, int DV, int TB, Mode MODE>
@@ -98,27 +115,28 @@ struct Cfg {
     static constexpr int ODB = NDB / WPT;        // value blocks of O per wave
     static constexpr int NSB = NKB * NDB;        // 32x32 blocks of the state
     static constexpr int SPW = NSB > kWaves ? NSB / kWaves : 1;   // state blocks per wave
-    // global -> register staging: Q in 16-byte chunks, K and V in 8x8 blocks (one per thread)
+    static constexpr int KS = D / 16;            // contraction steps over d
+    // global -> register staging, 16-byte chunks of the natural tiles
     static constexpr int QCH = kOut ? TB * D / 8 : 0;
-    static constexpr int QPT = (QCH + kThreads - 1) / kThreads;
-    static constexpr int KBLK = (TB / 8) * (D / 8);
-    static constexpr int VBLK = (TB / 8) * (DV / 8);
+    static constexpr int KCH = TB * D / 8;
+    static constexpr int VCH = TB * DV / 8;
+    static constexpr int NQ = (QCH + kThreads - 1) / kThreads;
+    static constexpr int NK = (KCH + kThreads - 1) / kThreads;
+    static constexpr int NV = (VCH + kThreads - 1) / kThreads;
     // LDS carve-up (bf16 elements)
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + (kOut ? TB * D : 0);
-    static constexpr int oKT = oK + (kOut ? TB * D : 0);
-    static constexpr int oVT = oKT + D * TB;
-    static constexpr int oST = oVT + DV * TB;
+    static constexpr int oV = oK + TB * D;
+    static constexpr int oST = oV + TB * DV;
     static constexpr int kLds = oST + (kOut ? DV * D : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
     static_assert(ODB * WPT == NDB && NTB * WPT <= kWaves, "output blocks");
     static_assert(SPW * kWaves == NSB || (SPW == 1 && NSB <= kWaves), "state blocks");
-    static_assert(KBLK + VBLK <= kThreads, "one staging block per thread");
     static_assert(kLds * 2 <= 160 * 1024, "LDS");
 };
 
-// Row block and part (which ODB value blocks) of O owned by a wave.  Waves w and w + 4
-// share a SIMD; the mapping gives each SIMD one short and one long causal row block.
+// Row block and part (which ODB value blocks) of O owned by a wave.  Waves w and w + 4 share a
+// SIMD; the mapping gives each SIMD one short and one long causal row block.
 template <int NTB, int WPT>
 __device__ __forceinline__ void wave_rows(int wave, int &tb, int &part) {
     if constexpr (NTB == 4 && WPT == 2) {
@@ -136,105 +154,63 @@ __device__ __forceinline__ void wave_rows(int wave, int &tb, int &part) {
 template <int D, int DV, int TB, Mode MODE>
 struct Staged {
     using C = Cfg<D, DV, TB, MODE>;
-    u32x4 q[C::QPT > 0 ? C::QPT : 1];
-    u32x4 blk[8];     // rows of this thread's 8x8 block of K (tid < KBLK) or V (KBLK <= tid < KBLK + VBLK)
+    u32x4 q[C::NQ > 0 ? C::NQ : 1];
+    u32x4 k[C::NK];
+    u32x4 v[C::NV];
 };
 
+// Issue the global loads of the tile starting at position t0 into registers (16-byte chunks of
+// the natural row-major tiles).  Nothing waits for them here; rows at or past T read as zero.
 template <int D, int DV, int TB, Mode MODE>
 __device__ __forceinline__ void stage_load(Staged<D, DV, TB, MODE> &r, const u16 *a, const u16 *b,
                                            const u16 *c, int64_t t0, int64_t T, int DVT, int tid) {
     using C = Cfg<D, DV, TB, MODE>;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if constexpr (C::kOut) {
+    if constexpr (C::NQ > 0) {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + t0 * D, (T - t0) * D * 2);
 #pragma unroll
-        for (int s = 0; s < C::QPT; ++s) {
-            const int cid = tid + s * kThreads;
-            const int row = cid / (D / 8), ch = cid % (D / 8);
-            const int64_t t = t0 + row;
-            r.q[s] = (cid < C::QCH && t < T) ? gload(a + t * D + ch * 8) : zero;
+        for (int s = 0; s < C::NQ; ++s) {
+            const int cid = min(tid + s * kThreads, C::QCH - 1);
+            r.q[s] = bload(ra, ((cid / (D / 8)) * D + (cid % (D / 8)) * 8) * 2);
         }
     }
-    if (tid < C::KBLK) {
-        const int rg = tid / (D / 8), cc = tid % (D / 8);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + t0 * D, (T - t0) * D * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t t = t0 + group_row(rg, i);
-            r.blk[i] = t < T ? gload(b + t * D + cc * 8) : zero;
-        }
-    } else if (tid < C::KBLK + C::VBLK) {
-        const int bid = tid - C::KBLK;
-        const int rg = bid / (DV / 8), cc = bid % (DV / 8);
+    for (int s = 0; s < C::NK; ++s) {
+        const int cid = min(tid + s * kThreads, C::KCH - 1);
+        r.k[s] = bload(rb, ((cid / (D / 8)) * D + (cid % (D / 8)) * 8) * 2);
+    }
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(c + t0 * DVT, (T - t0) * DVT * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t t = t0 + group_row(rg, i);
-            r.blk[i] = t < T ? gload(c + t * DVT + cc * 8) : zero;
-        }
+    for (int s = 0; s < C::NV; ++s) {
+        const int cid = min(tid + s * kThreads, C::VCH - 1);
+        r.v[s] = bload(rc, ((cid / (DV / 8)) * DVT + (cid % (DV / 8)) * 8) * 2);
     }
 }
 
-// Transpose an 8x8 block of bf16 (rows in x[0..7]) and write column e as one 16-byte chunk.
-template <int TB>
-__device__ __forceinline__ void write_transposed(u16 *sT, const u32x4 (&x)[8], int rg, int cc) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        u32x4 out;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const unsigned int lo = x[2 * m][e >> 1], hi = x[2 * m + 1][e >> 1];
-            out[m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        lds_write(sT, lds_off_t<TB>(cc * 8 + e, rg), out);
-    }
-}
-
-// Same, with row i of the block scaled by wrow[i] (rounded once to bf16).
-template <int TB>
-__device__ __forceinline__ void write_transposed_weighted(u16 *sT, const u32x4 (&x)[8], const float (&wrow)[8],
-                                                          int rg, int cc) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        u32x4 out;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const unsigned int lo = f32_to_bf16(bf16_to_f32(elem(x[2 * m], e)) * wrow[2 * m]);
-            const unsigned int hi = f32_to_bf16(bf16_to_f32(elem(x[2 * m + 1], e)) * wrow[2 * m + 1]);
-            out[m] = lo | (hi << 16);
-        }
-        lds_write(sT, lds_off_t<TB>(cc * 8 + e, rg), out);
-    }
-}
-
-template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
-__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid, float l2) {
+template <int D, int DV, int TB, Mode MODE>
+__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid) {
     using C = Cfg<D, DV, TB, MODE>;
-    if constexpr (C::kOut) {
 #pragma unroll
-        for (int s = 0; s < C::QPT; ++s) {
-            const int cid = tid + s * kThreads;
-            if (cid < C::QCH) lds_write(smem + C::oQ, lds_off<D>(cid / (D / 8), cid % (D / 8)), r.q[s]);
-        }
+    for (int s = 0; s < C::NQ; ++s) {
+        const int cid = tid + s * kThreads;
+        if (cid < C::QCH) lds_write(smem + C::oQ, nat_off<D>(cid / (D / 8), cid % (D / 8)), r.q[s]);
     }
-    if (tid < C::KBLK) {
-        const int rg = tid / (D / 8), cc = tid % (D / 8);
-        if constexpr (C::kOut) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lds_write(smem + C::oK, lds_off<D>(group_row(rg, i), cc), r.blk[i]);
-        }
-        if constexpr (DECAY) {
-            float wrow[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = group_row(rg, i);
-                wrow[i] = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - j : j) * l2);
-            }
-            write_transposed_weighted<TB>(smem + C::oKT, r.blk, wrow, rg, cc);
-        } else {
-            write_transposed<TB>(smem + C::oKT, r.blk, rg, cc);
-        }
-    } else if (tid < C::KBLK + C::VBLK) {
-        const int bid = tid - C::KBLK;
-        write_transposed<TB>(smem + C::oVT, r.blk, bid / (DV / 8), bid % (DV / 8));
+    for (int s = 0; s < C::NK; ++s) {
+        const int cid = tid + s * kThreads;
+        if (cid < C::KCH) lds_write(smem + C::oK, nat_off<D>(cid / (D / 8), cid % (D / 8)), r.k[s]);
     }
+#pragma unroll
+    for (int s = 0; s < C::NV; ++s) {
+        const int cid = tid + s * kThreads;
+        if (cid < C::VCH) lds_write(smem + C::oV, nat_off<DV>(cid / (DV / 8), cid % (DV / 8)), r.v[s]);
+    }
+}
+
+// Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its
+// global loads, so the next tile's loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // 4x4 transpose inside each quad of lanes: on entry lane m of the quad holds x[i] = M[i][m];
@@ -297,8 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const bool s_active = wave * C::SPW < C::NSB;
 
     f32x16 sacc[C::SPW];
-    const bool init_state = C::kOut && gs != nullptr &&
-                            (DIR == Dir::Forward ? seg > 0 : seg < p.nseg - 1);
+    const bool init_state = C::kOut && gs != nullptr && (DIR == Dir::Forward ? seg > 0 : seg < p.nseg - 1);
 #pragma unroll
     for (int s = 0; s < C::SPW; ++s) {
         const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
@@ -324,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     u32x2 pk;
                     pk[0] = f32_to_bf16(sacc[s][4 * j + 0]) | (f32_to_bf16(sacc[s][4 * j + 1]) << 16);
                     pk[1] = f32_to_bf16(sacc[s][4 * j + 2]) | (f32_to_bf16(sacc[s][4 * j + 3]) << 16);
-                    *reinterpret_cast<u32x2 *>(smem + C::oST + lds_off<D>(nb * 32 + col, d >> 3) + (d & 7)) = pk;
+                    *reinterpret_cast<u32x2 *>(smem + C::oST + nat_off<D>(nb * 32 + col, d >> 3) + (d & 7)) = pk;
                 }
             }
         }
@@ -332,11 +307,11 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
     Staged<D, DV, TB, MODE> st;
     stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
-    stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
-    if (ntiles > 1) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(1) * TB, T, p.DVT, tid);
+    stage_store<D, DV, TB, MODE>(st, smem, tid);
     if (init_state) write_state_lds();
-    __syncthreads();
+    lds_barrier();
 
+    const u16 *sQ = smem + C::oQ, *sK = smem + C::oK, *sV = smem + C::oV, *sST = smem + C::oST;
     bool state_nonzero = init_state;
     for (int it = 0; it < ntiles; ++it) {
         const int64_t t0 = tile_of(it) * TB;
@@ -344,8 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
         if constexpr (C::kOut) {
             if (o_active) {
-                const u16 *sQ = smem + C::oQ, *sK = smem + C::oK, *sVT = smem + C::oVT, *sST = smem + C::oST;
                 const int qrow = tb * 32 + col;
+                auto rdQ = [&](int ks) { return lds_read(sQ, nat_off<D>(qrow, 2 * ks + h)); };
 
                 f32x16 oacc[C::ODB];
 #pragma unroll
@@ -355,12 +330,24 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
                 // Step 3: inter-tile right product, rows weighted by w_inter
                 if (state_nonzero) {
-#pragma unroll 2
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        const bf16x8 qf = lds_read(sQ, lds_off<D>(qrow, 2 * ks + h));
+                    auto rdST = [&](int n, int ks) {
+                        return lds_read(sST, nat_off<D>((db0 + n) * 32 + col, 2 * ks + h));
+                    };
+                    bf16x8 qa = rdQ(0), sa[C::ODB];
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n)
-                            oacc[n] = mfma(qf, lds_read(sST, lds_off<D>((db0 + n) * 32 + col, 2 * ks + h)), oacc[n]);
+                    for (int n = 0; n < C::ODB; ++n) sa[n] = rdST(n, 0);
+#pragma unroll 2
+                    for (int ks = 0; ks < C::KS; ++ks) {
+                        const int kn = ks + 1 < C::KS ? ks + 1 : ks;
+                        const bf16x8 qn = rdQ(kn);
+                        bf16x8 sn[C::ODB];
+#pragma unroll
+                        for (int n = 0; n < C::ODB; ++n) sn[n] = rdST(n, kn);
+#pragma unroll
+                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(qa, sa[n], oacc[n]);
+                        qa = qn;
+#pragma unroll
+                        for (int n = 0; n < C::ODB; ++n) sa[n] = sn[n];
                     }
                     if constexpr (DECAY) {
 #pragma unroll
@@ -378,13 +365,28 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 const int uhi = DIR == Dir::Forward ? tb : C::NTB - 1;
                 const int tcol = tb * 32 + col;
                 for (int u = ulo; u <= uhi; ++u) {
+                    asm volatile("" ::: "memory");   // keep each block's LDS reads inside its iteration
+                    // V fragments of this block (in P's row order) are read first; the A^T chain hides them
+                    bf16x8 vf[2][C::ODB];
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+#pragma unroll
+                        for (int n = 0; n < C::ODB; ++n)
+                            vf[x][n] = frag_tr<DV, true>(sV, u * 32 + 16 * x, (db0 + n) * 32, lane);
                     f32x16 acc;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll 4
-                    for (int ks = 0; ks < D / 16; ++ks)
-                        acc = mfma(lds_read(sK, lds_off<D>(u * 32 + col, 2 * ks + h)),
-                                   lds_read(sQ, lds_off<D>(qrow, 2 * ks + h)), acc);
+                    bf16x8 ka = lds_read(sK, nat_off<D>(u * 32 + col, h)), qa = rdQ(0);
+#pragma unroll
+                    for (int ks = 0; ks < C::KS; ks += 2) {
+                        const bf16x8 kb = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 1) + h)), qb = rdQ(ks + 1);
+                        acc = mfma(ka, qa, acc);
+                        if (ks + 2 < C::KS) {
+                            ka = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 2) + h));
+                            qa = rdQ(ks + 2);
+                        }
+                        acc = mfma(kb, qb, acc);
+                    }
                     // causal decay mask: only the diagonal block has masked entries
                     bf16x8 pf[2];
                     if (u == tb) {
@@ -406,13 +408,12 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n)
-                            oacc[n] = mfma(pf[x],
-                                           lds_read(sVT, lds_off_t<TB>((db0 + n) * 32 + col, 4 * u + 2 * x + h)),
-                                           oacc[n]);
+                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(pf[x], vf[x][n], oacc[n]);
                 }
 
-                // store O: a quad transpose gives each lane 4 consecutive columns of one row
+                // store O: a quad transpose gives each lane 4 consecutive columns of one row; rows at
+                // or past T fall outside the buffer range and are dropped
+                const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * p.DVT, (T - t0) * p.DVT * 2);
 #pragma unroll
                 for (int n = 0; n < C::ODB; ++n) {
 #pragma unroll
@@ -420,17 +421,19 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                         float x0 = oacc[n][4 * j], x1 = oacc[n][4 * j + 1], x2 = oacc[n][4 * j + 2],
                               x3 = oacc[n][4 * j + 3];
                         quad_transpose(x0, x1, x2, x3, lane);
-                        const int64_t t = t0 + tb * 32 + 8 * j + 4 * h + (lane & 3);
-                        if (t < T) {
-                            u32x2 pk;
-                            pk[0] = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
-                            pk[1] = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
-                            *reinterpret_cast<u32x2 *>(gy + t * p.DVT + (db0 + n) * 32 + (col & ~3)) = pk;
-                        }
+                        const int row = tb * 32 + 8 * j + 4 * h + (lane & 3);
+                        u32x2 pk;
+                        pk[0] = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
+                        pk[1] = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
+                        bstore8(ry, (row * p.DVT + (db0 + n) * 32 + (col & ~3)) * 2, pk);
                     }
                 }
             }
         }
+
+        // The next tile's loads go out here, after the register-heavy intra-tile phase, and land in
+        // LDS after this tile's last barrier.
+        if (it + 1 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, tid);
 
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
@@ -440,27 +443,57 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
-                const u16 *sKT = smem + C::oKT, *sVT = smem + C::oVT;
+                auto rdKT = [&](int s, int x) {
+                    bf16x8 f = frag_tr<D, false>(sK, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, lane);
+                    if constexpr (DECAY) {
+                        // weight position t by w_upd, working on whole dwords (two positions each)
+                        u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const int t = 16 * x + 8 * h + 2 * m;
+                            const float lo = __uint_as_float(w[m] << 16) * pw(DIR == Dir::Forward ? TB - 1 - t : t);
+                            const float hi = __uint_as_float(w[m] & 0xffff0000u) *
+                                             pw(DIR == Dir::Forward ? TB - 2 - t : t + 1);
+                            w[m] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                        }
+                        f = __builtin_bit_cast(bf16x8, w);
+                    }
+                    return f;
+                };
+                auto rdV = [&](int s, int x) {
+                    return frag_tr<DV, false>(sV, 16 * x, ((wave * C::SPW + s) % C::NDB) * 32, lane);
+                };
+                bf16x8 ka[C::SPW], va[C::SPW];
+#pragma unroll
+                for (int s = 0; s < C::SPW; ++s) {
+                    ka[s] = rdKT(s, 0);
+                    va[s] = rdV(s, 0);
+                }
 #pragma unroll 2
                 for (int x = 0; x < TB / 16; ++x) {
+                    bf16x8 kn[C::SPW], vn[C::SPW];
+                    const int xn = x + 1 < TB / 16 ? x + 1 : x;
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) {
-                        const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-                        sacc[s] = mfma(lds_read(sKT, lds_off_t<TB>(kb * 32 + col, 2 * x + h)),
-                                       lds_read(sVT, lds_off_t<TB>(nb * 32 + col, 2 * x + h)), sacc[s]);
+                        kn[s] = rdKT(s, xn);
+                        vn[s] = rdV(s, xn);
+                    }
+#pragma unroll
+                    for (int s = 0; s < C::SPW; ++s) sacc[s] = mfma(ka[s], va[s], sacc[s]);
+#pragma unroll
+                    for (int s = 0; s < C::SPW; ++s) {
+                        ka[s] = kn[s];
+                        va[s] = vn[s];
                     }
                 }
             }
             state_nonzero = true;
         }
 
-        __syncthreads();                       // every wave is done with this tile's LDS
+        lds_barrier();                       // every wave is done with this tile's LDS
         if (update) write_state_lds();
-        if (it + 1 < ntiles) {
-            stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
-            if (it + 2 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 2) * TB, T, p.DVT, tid);
-        }
-        __syncthreads();
+        if (it + 1 < ntiles) stage_store<D, DV, TB, MODE>(st, smem, tid);
+        lds_barrier();
     }
 
     if constexpr (MODE == Mode::StateOnly) {
