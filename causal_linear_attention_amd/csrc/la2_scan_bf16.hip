@@ -105,7 +105,7 @@ __device__ __forceinline__ unsigned int f32_to_bf16(float f) {
     return (unsigned int)__builtin_bit_cast(u16, (__bf16)f);
 }
 
-template <int D, int DV, int TB, Mode MODE>
+template <int D, int DV, int TB, Mode MODE, bool DECAY = false>
 struct Cfg {
     static constexpr bool kOut = MODE == Mode::Output;
     static constexpr int NTB = TB / 32;          // 32-row blocks of the tile
@@ -128,7 +128,8 @@ struct Cfg {
     static constexpr int oK = oQ + (kOut ? TB * D : 0);
     static constexpr int oV = oK + TB * D;
     static constexpr int oST = oV + TB * DV;
-    static constexpr int kLds = oST + (kOut ? DV * D : 0);
+    static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
+    static constexpr int kLds = oKW + (DECAY ? TB * D : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
     static_assert(ODB * WPT == NDB && NTB * WPT <= kWaves, "output blocks");
     static_assert(SPW * kWaves == NSB || (SPW == 1 && NSB <= kWaves), "state blocks");
@@ -187,9 +188,9 @@ __device__ __forceinline__ void stage_load(Staged<D, DV, TB, MODE> &r, const u16
     }
 }
 
-template <int D, int DV, int TB, Mode MODE>
-__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid) {
-    using C = Cfg<D, DV, TB, MODE>;
+template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
+__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid, float l2) {
+    using C = Cfg<D, DV, TB, MODE, DECAY>;
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
         const int cid = tid + s * kThreads;
@@ -198,7 +199,20 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
 #pragma unroll
     for (int s = 0; s < C::NK; ++s) {
         const int cid = tid + s * kThreads;
-        if (cid < C::KCH) lds_write(smem + C::oK, nat_off<D>(cid / (D / 8), cid % (D / 8)), r.k[s]);
+        if (cid < C::KCH) {
+            const int row = cid / (D / 8), off = nat_off<D>(row, cid % (D / 8));
+            if constexpr (C::kOut || !DECAY) lds_write(smem + C::oK, off, r.k[s]);
+            if constexpr (DECAY) {
+                // the state update's copy of K: row j scaled by w_upd(j), rounded once to bf16
+                const float w = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - row : row) * l2);
+                u32x4 x = r.k[s];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    x[m] = f32_to_bf16(__uint_as_float(x[m] << 16) * w) |
+                           (f32_to_bf16(__uint_as_float(x[m] & 0xffff0000u) * w) << 16);
+                lds_write(smem + C::oKW, off, x);
+            }
+        }
     }
 #pragma unroll
     for (int s = 0; s < C::NV; ++s) {
@@ -235,7 +249,7 @@ __device__ __forceinline__ void quad_transpose(float &x0, float &x1, float &x2, 
 
 template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
 __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
-    using C = Cfg<D, DV, TB, MODE>;
+    using C = Cfg<D, DV, TB, MODE, DECAY>;
     __shared__ __attribute__((aligned(16))) u16 smem[C::kLds];
 
     const int tid = threadIdx.x;
@@ -307,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
     Staged<D, DV, TB, MODE> st;
     stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
-    stage_store<D, DV, TB, MODE>(st, smem, tid);
+    stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
     if (init_state) write_state_lds();
     lds_barrier();
 
@@ -366,13 +380,16 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 const int tcol = tb * 32 + col;
                 for (int u = ulo; u <= uhi; ++u) {
                     asm volatile("" ::: "memory");   // keep each block's LDS reads inside its iteration
-                    // V fragments of this block (in P's row order) are read first; the A^T chain hides them
+                    // V fragments of this block, in P's row order; in the forward direction they are read
+                    // before the A^T chain, which hides their latency
                     bf16x8 vf[2][C::ODB];
+                    auto rdVF = [&](int x, int n) { return frag_tr<DV, true>(sV, u * 32 + 16 * x, (db0 + n) * 32, lane); };
+                    if constexpr (DIR == Dir::Forward) {
 #pragma unroll
-                    for (int x = 0; x < 2; ++x)
+                        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n)
-                            vf[x][n] = frag_tr<DV, true>(sV, u * 32 + 16 * x, (db0 + n) * 32, lane);
+                            for (int n = 0; n < C::ODB; ++n) vf[x][n] = rdVF(x, n);
+                    }
                     f32x16 acc;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -408,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(pf[x], vf[x][n], oacc[n]);
+                        for (int n = 0; n < C::ODB; ++n)
+                            oacc[n] = mfma(pf[x], DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), oacc[n]);
                 }
 
                 // store O: a quad transpose gives each lane 4 consecutive columns of one row; rows at
@@ -443,22 +461,9 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
+                const u16 *sKU = smem + (DECAY ? C::oKW : C::oK);   // K as used by the update
                 auto rdKT = [&](int s, int x) {
-                    bf16x8 f = frag_tr<D, false>(sK, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, lane);
-                    if constexpr (DECAY) {
-                        // weight position t by w_upd, working on whole dwords (two positions each)
-                        u32x4 w = __builtin_bit_cast(u32x4, f);
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const int t = 16 * x + 8 * h + 2 * m;
-                            const float lo = __uint_as_float(w[m] << 16) * pw(DIR == Dir::Forward ? TB - 1 - t : t);
-                            const float hi = __uint_as_float(w[m] & 0xffff0000u) *
-                                             pw(DIR == Dir::Forward ? TB - 2 - t : t + 1);
-                            w[m] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-                        }
-                        f = __builtin_bit_cast(bf16x8, w);
-                    }
-                    return f;
+                    return frag_tr<D, false>(sKU, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, lane);
                 };
                 auto rdV = [&](int s, int x) {
                     return frag_tr<DV, false>(sV, 16 * x, ((wave * C::SPW + s) % C::NDB) * 32, lane);
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 
         lds_barrier();                       // every wave is done with this tile's LDS
         if (update) write_state_lds();
-        if (it + 1 < ntiles) stage_store<D, DV, TB, MODE>(st, smem, tid);
+        if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
         lds_barrier();
     }
 
