@@ -23,6 +23,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roofline"
+
+# HBM bytes per launch of the forward output kernel at the 1K point, from rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE runs (one counter per run), each scaled by what the same counter reads for a plain
+# 1 GiB device copy (FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000).  Valid only for the kernel source they
+# were taken on; for any other source the roofline reports traffic as null.
+TRAFFIC_KERNEL_SHA256_16 = "7c05b347962bbd83"
+TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573084 * 1024, "write": 525900 * 1024}
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
@@ -36,7 +43,20 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
                     help="sequences of the 1K point the oracle runs for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Five plain copies of 1 GiB: a kernel of known traffic (1 GiB read + 1 GiB written per copy)."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * src.element_size(), "copies": 5}))
 
 
 def algorithmic(w):
@@ -55,6 +75,9 @@ def algorithmic(w):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "chains shard across GPUs with no communication, but no multi-GPU path is built.",
@@ -139,13 +162,18 @@ def main():
     # launch of it (2048 chains fill the GPU, no segment split), so its event time is that launch.
     dom = next((i for i, c in enumerate(cases) if c["ws"] is None), None)
     roofline = None
+    import hashlib
+    src = os.path.join(ROOT, "causal_linear_attention_amd", "csrc", "la2_scan_bf16.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    traffic = (TRAFFIC_BYTES_PER_LAUNCH["fetch"] + TRAFFIC_BYTES_PER_LAUNCH["write"]
+               if sha == TRAFFIC_KERNEL_SHA256_16 else None)
     if dom is not None:
         w = cases[dom]["w"]
         alg = algorithmic(w)
         achieved = alg["fwd_bytes"] / (fwd_ms[dom] * 1e-3) / 1e9
         roofline = {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": "scan_bf16_kernel<D=128,DV=128,TB=128,Forward,Output>",
             "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
             "avg_launch_ms": round(fwd_ms[dom], 4),
