@@ -84,9 +84,8 @@ Range range_of(const void *p, size_t bytes) {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
-// One scan of the decomposition: y = attention(a, b, c) in direction `dir`.
-int run_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
-             int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s) {
+la2::ScanArgs scan_args(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains,
+                        int64_t H, int64_t T, int W, const Plan &pl, int dtype) {
     la2::ScanArgs args{};
     args.a = a;
     args.b = b;
@@ -99,26 +98,44 @@ int run_scan(const void *a, const void *b, const void *c, void *y, const float *
     args.nseg = pl.nseg;
     args.seg_tiles = pl.seg_tiles;
     args.chains = (int)chains;
-    const int DV = slice_width(dtype, W);
-    args.nslice = W / DV;
-    auto launch = [&](la2::Mode mode) {
-        return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, mode, s)
-                                 : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
-    };
-    if (pl.nseg > 1) {
-        args.states = static_cast<float *>(ws);
-        // deltas of the segments whose successor (forward) / predecessor (reverse) needs them
-        args.seg_first = dir == la2::Dir::Forward ? 0 : 1;
-        args.seg_count = pl.nseg - 1;
-        if (launch(la2::Mode::StateOnly) != hipSuccess) return LA2_ERR_HIP;
-        if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nseg,
-                                       (int64_t)pl.seg_tiles * pl.TB, (int64_t)D * W, dir, s) != hipSuccess)
-            return LA2_ERR_HIP;
-    }
+    args.nslice = W / slice_width(dtype, W);
+    return args;
+}
+
+hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, la2::Dir dir, la2::Mode mode,
+                  hipStream_t s) {
+    const int DV = slice_width(dtype, args.DVT);
+    return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, mode, s)
+                             : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
+}
+
+// Segment start states of the scan with key role `b` (width D) and value role `c` (width W) in
+// direction `dir`, written to `ws` ([chains, nseg, D, W] fp32).  Only called for split chains.
+int segment_states(const void *b, const void *c, const float *decay, int64_t chains, int64_t H, int64_t T, int D,
+                   int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s) {
+    la2::ScanArgs args = scan_args(nullptr, b, c, nullptr, decay, chains, H, T, W, pl, dtype);
+    args.states = static_cast<float *>(ws);
+    // deltas of the segments whose successor (forward) / predecessor (reverse) needs them
+    args.seg_first = dir == la2::Dir::Forward ? 0 : 1;
+    args.seg_count = pl.nseg - 1;
+    if (launch(args, D, pl, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
+    if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nseg, (int64_t)pl.seg_tiles * pl.TB,
+                                   (int64_t)D * W, dir, s) != hipSuccess)
+        return LA2_ERR_HIP;
+    return LA2_OK;
+}
+
+// Output pass y = attention(a, b, c) in direction `dir`, every segment starting from the states in
+// `ws` (transposed when states_t) or from zero when the chains are not split.
+int output_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
+                int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, int states_t,
+                hipStream_t s) {
+    la2::ScanArgs args = scan_args(a, b, c, y, decay, chains, H, T, W, pl, dtype);
+    args.states = pl.nseg > 1 ? static_cast<float *>(ws) : nullptr;
+    args.states_t = states_t;
     args.seg_first = 0;
     args.seg_count = pl.nseg;
-    if (launch(la2::Mode::Output) != hipSuccess) return LA2_ERR_HIP;
-    return LA2_OK;
+    return launch(args, D, pl, dtype, dir, la2::Mode::Output, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
 }
 
 }  // namespace
@@ -173,7 +190,13 @@ int la2_forward(const void *q, const void *k, const void *v, const float *decay,
             return LA2_ERR_ALIAS;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return run_scan(q, k, v, o, decay, B * H, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s);
+    const int64_t chains = B * H;
+    if (pl.nseg > 1) {
+        st = segment_states(k, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s);
+        if (st != LA2_OK) return st;
+    }
+    return output_scan(q, k, v, o, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace,
+                       0, s);
 }
 
 int la2_backward(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
@@ -203,14 +226,25 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chains = B * H;
     const int D = (int)d, DV = (int)d_v;
-    // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k)
-    st = run_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, s);
-    if (st != LA2_OK) return st;
-    // dk_t = R_t v_t           = reverse scan with (v, do, q)
-    st = run_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, workspace, s);
-    if (st != LA2_OK) return st;
-    // dv_t = R_t^T k_t         = reverse scan with (k, q, do)
-    return run_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace, s);
+    st = LA2_OK;
+    const bool split = pl.nseg > 1;
+    // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T
+    if (split && (st = segment_states(v, k, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace,
+                                      s)) != LA2_OK)
+        return st;
+    if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 0,
+                          s)) != LA2_OK)
+        return st;
+    // reverse state R_t = lam R_{t+1} + q_t do_t^T, [d, d_v], shared by the dv and dk scans
+    if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace,
+                                      s)) != LA2_OK)
+        return st;
+    // dv_t = R_t^T k_t         = reverse scan with (k, q, do), state R
+    if ((st = output_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace, 0,
+                          s)) != LA2_OK)
+        return st;
+    // dk_t = R_t v_t           = reverse scan with (v, do, q), state R^T: read R transposed
+    return output_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, workspace, 1, s);
 }
 
 }  // extern "C"

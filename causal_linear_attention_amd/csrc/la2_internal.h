@@ -18,6 +18,7 @@ struct ScanArgs {
     void *y;               // output [chains, T, DVT] (unused in state-only launches)
     const float *decay;    // [H] or nullptr (lam = 1)
     float *states;         // fp32 [chains, nseg, D, DVT]: segment start states / segment deltas
+    int states_t;          // 1: output launches read the start states transposed, [chains, nseg, DVT, D]
     int64_t T;
     int H;
     int DVT;               // full value width (row stride of c and y)

@@ -273,7 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const u16 *gb = static_cast<const u16 *>(p.b) + (int64_t)chain * T * D;
     const u16 *gc = static_cast<const u16 *>(p.c) + (int64_t)chain * T * p.DVT + dv0;
     u16 *gy = C::kOut ? static_cast<u16 *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
-    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + dv0 : nullptr;
+    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
+                         : nullptr;
 
     // lam^n = 2^(n log2 lam) with the hardware exp2 (n >= 0 only, so no overflow; tiny powers flush to 0)
     const float l2 = DECAY ? log2f(p.decay[chain % p.H]) : 0.0f;
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            sacc[s][r] = (init_state && s_active) ? gs[(int64_t)d * p.DVT + nb * 32 + col] : 0.0f;
+            const int64_t e = p.states_t ? (int64_t)(nb * 32 + col) * D + d : (int64_t)d * p.DVT + nb * 32 + col;
+            sacc[s][r] = (init_state && s_active) ? gs[e] : 0.0f;
         }
     }
 

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
     const float *gb = static_cast<const float *>(p.b) + (int64_t)chain * T * D;
     const float *gc = static_cast<const float *>(p.c) + (int64_t)chain * T * p.DVT + dv0;
     float *gy = kOut ? static_cast<float *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
-    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + dv0 : nullptr;
+    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
+                         : nullptr;
 
     const bool has_decay = p.decay != nullptr;
     const float l2 = has_decay ? log2f(p.decay[chain % p.H]) : 0.0f;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
 
     const bool init_state = kOut && gs != nullptr && (DIR == Dir::Forward ? seg > 0 : seg < p.nseg - 1);
     for (int e = tid; e < D * DV; e += kThreads)
-        sS[e] = init_state ? gs[(int64_t)(e / DV) * p.DVT + e % DV] : 0.0f;
+        sS[e] = init_state ? gs[p.states_t ? (int64_t)(e % DV) * D + e / DV : (int64_t)(e / DV) * p.DVT + e % DV] : 0.0f;
 
     for (int it = 0; it < ntiles; ++it) {
         const int64_t t0 = (DIR == Dir::Forward ? tile_lo + it : tile_hi - 1 - it) * TB;
