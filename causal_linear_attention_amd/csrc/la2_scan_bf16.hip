@@ -6,7 +6,7 @@
 //
 //   A^T   = K_b Q_b^T                 (Step 2 scores, transposed, fp32 in MFMA accumulators)
 //   P     = causal decay mask of A    (kept in registers; becomes the next MFMA's A operand)
-//   O_b   = diag(w_inter) Q_b S + P V_b   (Step 3 right product plus Step 2 left product)
+//   O_b^T = S^T Q_b^T diag(w_inter) + V_b^T P^T   (Step 3 right + Step 2 left product, as O^T)
 //   S     = lam^TB S + (diag(w_upd) K_b)^T V_b   (Step 4, fp32 accumulators, never leaves chip)
 //
 // with the decay weights of the token recurrence S_t = lam S_{t-1} + k_t v_t^T:
@@ -96,6 +96,11 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x4 &v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           byte_off, 0, 0);
+}
+
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x2 &v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r,
                                           byte_off, 0, 0);
@@ -103,6 +108,15 @@ __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int byte_off, 
 
 __device__ __forceinline__ unsigned int f32_to_bf16(float f) {
     return (unsigned int)__builtin_bit_cast(u16, (__bf16)f);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to a packed pair of bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ unsigned int pack_bf16(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
 }
 
 template <int D, int DV, int TB, Mode MODE, bool DECAY = false>
@@ -129,7 +143,11 @@ struct Cfg {
     static constexpr int oV = oK + TB * D;
     static constexpr int oST = oV + TB * DV;
     static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
-    static constexpr int kLds = oKW + (DECAY ? TB * D : 0);
+    // per-wave staging of its 32 x ODB*32 output block, for full-row stores (no decay: LDS to spare)
+    static constexpr bool kStageO = kOut && !DECAY;
+    static constexpr int OSW = ODB * 32;                     // staged row width (elements)
+    static constexpr int oOS = oKW + (DECAY ? TB * D : 0);
+    static constexpr int kLds = oOS + (kStageO ? kWaves * 32 * OSW : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
     static_assert(ODB * WPT == NDB && NTB * WPT <= kWaves, "output blocks");
     static_assert(SPW * kWaves == NSB || (SPW == 1 && NSB <= kWaves), "state blocks");
@@ -227,26 +245,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 4x4 transpose inside each quad of lanes: on entry lane m of the quad holds x[i] = M[i][m];
-// on exit it holds x[i] = M[m][i].  Two DPP exchanges (lane xor 1, lane xor 2).
-__device__ __forceinline__ float dpp_xor1(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
-__device__ __forceinline__ void quad_transpose(float &x0, float &x1, float &x2, float &x3, int lane) {
-    const bool b0 = lane & 1, b1 = lane & 2;
-    float r = dpp_xor1(b0 ? x0 : x1);
-    if (b0) x0 = r; else x1 = r;
-    r = dpp_xor1(b0 ? x2 : x3);
-    if (b0) x2 = r; else x3 = r;
-    r = dpp_xor2(b1 ? x0 : x2);
-    if (b1) x0 = r; else x2 = r;
-    r = dpp_xor2(b1 ? x1 : x3);
-    if (b1) x1 = r; else x3 = r;
-}
-
 template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
 __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     using C = Cfg<D, DV, TB, MODE, DECAY>;
@@ -313,8 +311,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 for (int j = 0; j < 4; ++j) {
                     const int d = kb * 32 + 8 * j + 4 * h;
                     u32x2 pk;
-                    pk[0] = f32_to_bf16(sacc[s][4 * j + 0]) | (f32_to_bf16(sacc[s][4 * j + 1]) << 16);
-                    pk[1] = f32_to_bf16(sacc[s][4 * j + 2]) | (f32_to_bf16(sacc[s][4 * j + 3]) << 16);
+                    pk[0] = pack_bf16(sacc[s][4 * j + 0], sacc[s][4 * j + 1]);
+                    pk[1] = pack_bf16(sacc[s][4 * j + 2], sacc[s][4 * j + 3]);
                     *reinterpret_cast<u32x2 *>(smem + C::oST + nat_off<D>(nb * 32 + col, d >> 3) + (d & 7)) = pk;
                 }
             }
@@ -360,19 +358,19 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                         for (int n = 0; n < C::ODB; ++n) sn[n] = rdST(n, kn);
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(qa, sa[n], oacc[n]);
+                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(sa[n], qa, oacc[n]);
                         qa = qn;
 #pragma unroll
                         for (int n = 0; n < C::ODB; ++n) sa[n] = sn[n];
                     }
                     if constexpr (DECAY) {
+                        // every accumulator of this lane belongs to the row tb*32 + col
+                        const int i = tb * 32 + col;
+                        const float w = pw(DIR == Dir::Forward ? i + 1 : TB - i);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int i = tb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const float w = pw(DIR == Dir::Forward ? i + 1 : TB - i);
+                        for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
-                            for (int n = 0; n < C::ODB; ++n) oacc[n][r] *= w;
-                        }
+                            for (int r = 0; r < 16; ++r) oacc[n][r] *= w;
                     }
                 }
 
@@ -428,24 +426,44 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
                         for (int n = 0; n < C::ODB; ++n)
-                            oacc[n] = mfma(pf[x], DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), oacc[n]);
+                            oacc[n] = mfma(DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), pf[x], oacc[n]);
                 }
 
-                // store O: a quad transpose gives each lane 4 consecutive columns of one row; rows at
-                // or past T fall outside the buffer range and are dropped
+                // store O: the accumulators hold O^T, so each lane has 4 consecutive columns of its row
+                // tb*32 + col per group; rows at or past T fall outside the buffer range and are dropped
                 const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * p.DVT, (T - t0) * p.DVT * 2);
+                if constexpr (C::kStageO) {
+                    // through this wave's private LDS block: 8-byte writes of the O^T groups, then
+                    // 16-byte reads of whole rows, so every store instruction writes 8 full 128-byte rows
+                    constexpr int NC = C::OSW / 8;   // 16-byte chunks per staged row
+                    u16 *ob = smem + C::oOS + wave * 32 * C::OSW;
 #pragma unroll
-                for (int n = 0; n < C::ODB; ++n) {
+                    for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float x0 = oacc[n][4 * j], x1 = oacc[n][4 * j + 1], x2 = oacc[n][4 * j + 2],
-                              x3 = oacc[n][4 * j + 3];
-                        quad_transpose(x0, x1, x2, x3, lane);
-                        const int row = tb * 32 + 8 * j + 4 * h + (lane & 3);
-                        u32x2 pk;
-                        pk[0] = f32_to_bf16(x0) | (f32_to_bf16(x1) << 16);
-                        pk[1] = f32_to_bf16(x2) | (f32_to_bf16(x3) << 16);
-                        bstore8(ry, (row * p.DVT + (db0 + n) * 32 + (col & ~3)) * 2, pk);
+                        for (int j = 0; j < 4; ++j) {
+                            u32x2 pk;
+                            pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
+                            pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
+                            const int ch = (n * 32 + 8 * j) >> 3;
+                            *reinterpret_cast<u32x2 *>(ob + col * C::OSW + ((ch ^ (col & (NC - 1))) << 3) + 4 * h) = pk;
+                        }
+#pragma unroll
+                    for (int s2 = 0; s2 < 32 * NC / 64; ++s2) {
+                        const int q = lane + 64 * s2, row = q / NC, ch = q % NC;
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::OSW + ((ch ^ (row & (NC - 1))) << 3));
+                        bstore16(ry, ((tb * 32 + row) * p.DVT + db0 * 32 + ch * 8) * 2, v);
+                    }
+                } else {
+                    const int orow = (tb * 32 + col) * p.DVT;
+#pragma unroll
+                    for (int n = 0; n < C::ODB; ++n) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            u32x2 pk;
+                            pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
+                            pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
+                            bstore8(ry, (orow + (db0 + n) * 32 + 8 * j + 4 * h) * 2, pk);
+                        }
                     }
                 }
             }
