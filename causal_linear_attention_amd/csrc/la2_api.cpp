@@ -23,6 +23,7 @@ struct Plan {
     int TB;          // tile length the kernels run with
     int nseg;        // segments per chain
     int seg_tiles;   // tiles per segment
+    int narrow;      // bf16: run 128-wide value tensors as two 64-wide slices
     size_t ws_bytes; // workspace for the segment states
 };
 
@@ -34,7 +35,7 @@ bool block_ok(int dtype, int block) {
 }
 
 // Value-slice width a kernel launch uses for a value tensor of width `w`.
-int slice_width(int dtype, int w) { return dtype == LA2_BF16 ? w : 64; }
+int slice_width(int dtype, int w, int narrow) { return dtype == LA2_BF16 ? (narrow ? 64 : w) : 64; }
 
 int check_sizes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
@@ -54,13 +55,20 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     p.TB = dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
     const int64_t NT = (T + p.TB - 1) / p.TB;
     const int64_t chains = B * H;
-    const int64_t slices = dv / slice_width(dtype, (int)dv);
+    // Too few chains to fill the chip: when two 64-wide value slices per chain fill at least 3/4 of
+    // it, split the value width instead of T.  The two slices of a chain re-read the same q and k,
+    // which the kernel's XCD-aware order serves from one L2, while T segments cost an extra state
+    // pass over k and v.  A 64-wide slice still forms the whole score block, so it does about 0.6 of
+    // a 128-wide slice's work, and slices combined with segments lose to segments alone.
+    p.narrow = dtype == LA2_BF16 && dv == 128 && 2 * chains <= kComputeUnits && 8 * chains >= 3 * kComputeUnits;
+    if (const char *env = std::getenv("LA2_SLICE_WIDTH")) p.narrow = dtype == LA2_BF16 && std::strtol(env, nullptr, 10) == 64;
+    const int64_t slices = dv / slice_width(dtype, (int)dv, p.narrow);
     const int64_t work = chains * slices;
     int64_t seg_tiles = NT;
     if (const char *env = std::getenv("LA2_SEGMENT_TILES")) {
         const long v = std::strtol(env, nullptr, 10);
         if (v > 0) seg_tiles = v < NT ? v : NT;
-    } else if (work < kComputeUnits && NT > 1) {
+    } else if (!p.narrow && work < kComputeUnits && NT > 1) {
         int64_t nseg = kComputeUnits / work;
         if (nseg > NT) nseg = NT;
         seg_tiles = (NT + nseg - 1) / nseg;
@@ -98,13 +106,13 @@ la2::ScanArgs scan_args(const void *a, const void *b, const void *c, void *y, co
     args.nseg = pl.nseg;
     args.seg_tiles = pl.seg_tiles;
     args.chains = (int)chains;
-    args.nslice = W / slice_width(dtype, W);
+    args.nslice = W / slice_width(dtype, W, pl.narrow);
     return args;
 }
 
 hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, la2::Dir dir, la2::Mode mode,
                   hipStream_t s) {
-    const int DV = slice_width(dtype, args.DVT);
+    const int DV = slice_width(dtype, args.DVT, pl.narrow);
     return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, mode, s)
                              : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
 }

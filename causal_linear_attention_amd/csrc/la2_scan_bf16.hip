@@ -253,8 +253,13 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, col = lane & 31;
 
-    // work item
+    // work item; workgroups are dealt to the 8 XCDs round robin, so when the grid allows, the
+    // slices of one (chain, segment) get block ids that land on the same XCD and share its L2
     int item = blockIdx.x;
+    if (p.nslice > 1 && gridDim.x % (8 * p.nslice) == 0) {
+        const int xcd = item & 7, j = item >> 3;
+        item = ((j / p.nslice) * 8 + xcd) * p.nslice + j % p.nslice;
+    }
     const int slice = item % p.nslice;
     item /= p.nslice;
     const int seg = p.seg_first + item % p.seg_count;

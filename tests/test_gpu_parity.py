@@ -97,6 +97,25 @@ def test_forced_segments(seg_tiles, monkeypatch):
     check_full(x, 64)
 
 
+@pytest.mark.parametrize("B,H,T,seg_tiles", [(1, 8, 700, None), (1, 3, 300, None), (1, 2, 700, "2"), (1, 8, 520, "3")])
+@pytest.mark.parametrize("decay", ["heads", "none"])
+def test_narrow_value_slices(B, H, T, seg_tiles, decay, monkeypatch):
+    """128-wide values run as two 64-wide slices, with (8 chains) and without (3 chains) the
+    XCD-grouped block order, alone and combined with T segments."""
+    monkeypatch.setenv("LA2_SLICE_WIDTH", "64")
+    if seg_tiles:
+        monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    x = inputs.make_random(B, H, T, 128, 128, dtype="bf16", seed=23 + T, decay=decay)
+    check_full(x, 128)
+
+
+@pytest.mark.parametrize("B,H", [(4, 25), (8, 16)])
+def test_default_plan_narrow_slices(B, H):
+    """96 to 128 chains take the narrow-slice plan by default (8 x 16 chains: grouped block order)."""
+    x = inputs.make_random(B, H, 200, 128, 128, dtype="bf16", seed=B * H, decay="heads")
+    check_full(x, 128)
+
+
 @pytest.mark.parametrize("dtype,blocks", [("bf16", (64, 128, 256)), ("f32", (16, 32, 64))])
 def test_tile_size_invariance(dtype, blocks):
     x = inputs.make_random(1, 4, 640, 64, 64, dtype=dtype, seed=17, decay="heads")
