@@ -48,11 +48,16 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
 // RL = 128: chunk ^ (row ^ 4 (row & 3)) mod 16 spreads both 32 consecutive rows at one chunk
 // (fragment reads) and rows {r..r+3, r+8..r+11} at four chunks (transpose reads) over all banks.
 template <int RL>
-__device__ __forceinline__ int nat_off(int row, int chunk) {
+__device__ __forceinline__ int swz(int row) {
     if constexpr (RL == 128)
-        return row * 128 + ((chunk ^ ((row ^ ((row & 3) << 2)) & 15)) << 3);
+        return (row ^ ((row & 3) << 2)) & 15;
     else
-        return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+        return (row >> 1) & 7;
+}
+
+template <int RL>
+__device__ __forceinline__ int nat_off(int row, int chunk) {
+    return row * RL + ((chunk ^ swz<RL>(row)) << 3);
 }
 
 __device__ __forceinline__ bf16x8 lds_read(const u16 *s, int off) {
@@ -137,15 +142,21 @@ struct Cfg {
     static constexpr int NQ = (QCH + kThreads - 1) / kThreads;
     static constexpr int NK = (KCH + kThreads - 1) / kThreads;
     static constexpr int NV = (VCH + kThreads - 1) / kThreads;
-    // LDS carve-up (bf16 elements)
-    static constexpr int oQ = 0;
+    // LDS carve-up (bf16 elements).  A tile buffer holds Q (output mode), K and V; there are two
+    // of them, filled by direct global -> LDS loads one tile ahead, when they fit (kDMA), else one,
+    // filled from registers.
+    static constexpr int TILE = (kOut ? TB * D : 0) + TB * D + TB * DV;
+    static constexpr int oQ = 0;                             // offsets inside a tile buffer
     static constexpr int oK = oQ + (kOut ? TB * D : 0);
     static constexpr int oV = oK + TB * D;
-    static constexpr int oST = oV + TB * DV;
-    static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
     // per-wave staging of its 32 x ODB*32 output block, for full-row stores (no decay: LDS to spare)
     static constexpr bool kStageO = kOut && !DECAY;
     static constexpr int OSW = ODB * 32;                     // staged row width (elements)
+    static constexpr int kRest = (kOut ? DV * D : 0) + (DECAY ? TB * D : 0) + (kStageO ? kWaves * 32 * OSW : 0);
+    static constexpr bool kDMA = (2 * TILE + kRest) * 2 <= 160 * 1024;
+    static constexpr int NBUF = kDMA ? 2 : 1;
+    static constexpr int oST = NBUF * TILE;                  // S^T in bf16 (output mode)
+    static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
     static constexpr int oOS = oKW + (DECAY ? TB * D : 0);
     static constexpr int kLds = oOS + (kStageO ? kWaves * 32 * OSW : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
@@ -239,6 +250,50 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
     }
 }
 
+// Direct global -> LDS loads of the RL-wide rows [0, NR) of a tile (no registers involved).  Each
+// 16-byte lane load lands at the next 16 bytes of LDS, so lane l of load i fills LDS chunk
+// 64 i + l and fetches the global chunk that the XOR swizzle assigns there.  Rows past the
+// descriptor's range arrive as zeros.  Completion is tracked by this wave's vmcnt.
+template <int RL, int NR>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, u16 *dst, int gstride, int wave, int lane) {
+    constexpr int CPR = RL / 8, NL = NR * CPR / 64;
+    static_assert(NL % kWaves == 0, "whole loads per wave");
+#pragma unroll
+    for (int s = 0; s < NL / kWaves; ++s) {
+        const int i = wave + kWaves * s, c = 64 * i + lane, row = c / CPR, lc = (c % CPR) ^ swz<RL>(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 512 * i), 16,
+                                                 (row * gstride + lc * 8) * 2, 0, 0, 0);
+    }
+}
+
+// Issue the direct loads of the tile starting at position t0 into the tile buffer at `buf`.
+template <int D, int DV, int TB, Mode MODE>
+__device__ __forceinline__ void dma_tile(u16 *buf, const u16 *a, const u16 *b, const u16 *c, int64_t t0, int64_t T,
+                                         int DVT, int wave, int lane) {
+    using C = Cfg<D, DV, TB, MODE>;
+    if constexpr (C::kOut) dma_rows<D, TB>(make_rsrc(a + t0 * D, (T - t0) * D * 2), buf + C::oQ, D, wave, lane);
+    dma_rows<D, TB>(make_rsrc(b + t0 * D, (T - t0) * D * 2), buf + C::oK, D, wave, lane);
+    dma_rows<DV, TB>(make_rsrc(c + t0 * DVT, (T - t0) * DVT * 2), buf + C::oV, DVT, wave, lane);
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Decay: the state update's copy of the K tile, row j scaled by w_upd(j) and rounded once to bf16
+// (same swizzled layout, so a chunk keeps its offset).
+template <int D, int TB, Dir DIR>
+__device__ __forceinline__ void build_kw(const u16 *sk, u16 *skw, int tid, float l2) {
+#pragma unroll
+    for (int s = 0; s < TB * D / 8 / kThreads; ++s) {
+        const int c = tid + kThreads * s, row = c / (D / 8);
+        const float w = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - row : row) * l2);
+        u32x4 x = *reinterpret_cast<const u32x4 *>(sk + 8 * c);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            x[m] = f32_to_bf16(__uint_as_float(x[m] << 16) * w) | (f32_to_bf16(__uint_as_float(x[m] & 0xffff0000u) * w) << 16);
+        *reinterpret_cast<u32x4 *>(skw + 8 * c) = x;
+    }
+}
+
 // Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its
 // global loads, so the next tile's loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -325,16 +380,31 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     };
 
     Staged<D, DV, TB, MODE> st;
-    stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
-    stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+    if constexpr (C::kDMA) {
+        dma_tile<D, DV, TB, MODE>(smem, ga, gb, gc, tile_of(0) * TB, T, p.DVT, wave, lane);
+        wait_vm();
+        lds_barrier();
+        if constexpr (DECAY) build_kw<D, TB, DIR>(smem + C::oK, smem + C::oKW, tid, l2);
+    } else {
+        stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
+        stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+    }
     if (init_state) write_state_lds();
     lds_barrier();
 
-    const u16 *sQ = smem + C::oQ, *sK = smem + C::oK, *sV = smem + C::oV, *sST = smem + C::oST;
+    const u16 *sST = smem + C::oST;
     bool state_nonzero = init_state;
-    for (int it = 0; it < ntiles; ++it) {
+    int it = 0;
+    // One tile: `cur` is the tile buffer it reads, `nxt` the one the next tile's direct loads fill.
+    auto tile = [&](const u16 *cur, u16 *nxt) __attribute__((always_inline)) {
         const int64_t t0 = tile_of(it) * TB;
         const bool update = (MODE == Mode::StateOnly) || (it + 1 < ntiles);
+        const u16 *sQ = cur + C::oQ, *sK = cur + C::oK, *sV = cur + C::oV;
+        // the next tile's direct loads go out first and have this whole tile to land; its buffer was
+        // last read in the previous tile, which every wave has left
+        if constexpr (C::kDMA) {
+            if (it + 1 < ntiles) dma_tile<D, DV, TB, MODE>(nxt, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, wave, lane);
+        }
 
         if constexpr (C::kOut) {
             if (o_active) {
@@ -474,9 +544,11 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             }
         }
 
-        // The next tile's loads go out here, after the register-heavy intra-tile phase, and land in
-        // LDS after this tile's last barrier.
-        if (it + 1 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, tid);
+        // Without the second buffer, the next tile's loads go out here, after the register-heavy
+        // intra-tile phase, and land in LDS after this tile's last barrier.
+        if constexpr (!C::kDMA) {
+            if (it + 1 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, tid);
+        }
 
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
@@ -486,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
-                const u16 *sKU = smem + (DECAY ? C::oKW : C::oK);   // K as used by the update
+                const u16 *sKU = DECAY ? smem + C::oKW : sK;   // K as used by the update
                 auto rdKT = [&](int s, int x) {
                     return frag_tr<D, false>(sKU, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, lane);
                 };
@@ -520,10 +592,31 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             state_nonzero = true;
         }
 
-        lds_barrier();                       // every wave is done with this tile's LDS
-        if (update) write_state_lds();
-        if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+        if constexpr (C::kDMA) {
+            wait_vm();                       // this wave's loads of the next tile have landed
+            lds_barrier();                   // ... everyone's, and every wave is done with this tile
+            if (update) write_state_lds();
+            if constexpr (DECAY) {
+                if (it + 1 < ntiles) build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2);
+            }
+        } else {
+            lds_barrier();                   // every wave is done with this tile's LDS
+            if (update) write_state_lds();
+            if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+        }
         lds_barrier();
+    };
+    for (; it < ntiles; ++it) {
+        if constexpr (C::kDMA) {
+            // The two buffers are distinct and nothing else in a tile touches them, which the
+            // restrict qualifiers state; without that the compiler makes every LDS transpose read
+            // wait for the next tile's loads.
+            [&](const u16 *__restrict__ cur, u16 *__restrict__ nxt) __attribute__((always_inline)) {
+                tile(cur, nxt);
+            }(smem + (it & 1) * C::TILE, smem + ((it + 1) & 1) * C::TILE);
+        } else {
+            tile(smem, smem);
+        }
     }
 
     if constexpr (MODE == Mode::StateOnly) {
