@@ -50,9 +50,10 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int bloc
     return LA2_OK;
 }
 
-Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
+// `fused`: the plan of the fused bf16 dk/dv pass, which tiles by kDkdvTile and splits only T.
+Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype, bool fused = false) {
     Plan p{};
-    p.TB = dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
+    p.TB = fused ? la2::kDkdvTile : dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
     const int64_t NT = (T + p.TB - 1) / p.TB;
     const int64_t chains = B * H;
     // Too few chains to fill the chip: when two 64-wide value slices per chain fill at least 3/4 of
@@ -60,8 +61,9 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     // which the kernel's XCD-aware order serves from one L2, while T segments cost an extra state
     // pass over k and v.  A 64-wide slice still forms the whole score block, so it does about 0.6 of
     // a 128-wide slice's work, and slices combined with segments lose to segments alone.
-    p.narrow = dtype == LA2_BF16 && dv == 128 && 2 * chains <= kComputeUnits && 8 * chains >= 3 * kComputeUnits;
-    if (const char *env = std::getenv("LA2_SLICE_WIDTH")) p.narrow = dtype == LA2_BF16 && std::strtol(env, nullptr, 10) == 64;
+    p.narrow = !fused && dtype == LA2_BF16 && dv == 128 && 2 * chains <= kComputeUnits && 8 * chains >= 3 * kComputeUnits;
+    if (const char *env = std::getenv("LA2_SLICE_WIDTH"))
+        p.narrow = !fused && dtype == LA2_BF16 && std::strtol(env, nullptr, 10) == 64;
     const int64_t slices = dv / slice_width(dtype, (int)dv, p.narrow);
     const int64_t work = chains * slices;
     int64_t seg_tiles = NT;
@@ -77,6 +79,20 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     p.nseg = (int)((NT + seg_tiles - 1) / seg_tiles);
     p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nseg * d * dv * sizeof(float) : 0;
     return p;
+}
+
+// The backward computes dk and dv in one fused pass where a kernel exists for the shape (bf16,
+// d = d_v); LA2_SEPARATE_DKDV=1 selects the two separate reverse scans instead.
+bool fused_dkdv(int64_t d, int64_t dv, int dtype) {
+    if (const char *env = std::getenv("LA2_SEPARATE_DKDV"))
+        if (std::strtol(env, nullptr, 10) != 0) return false;
+    return dtype == LA2_BF16 && la2::dkdv_supported((int)d, (int)dv);
+}
+
+size_t backward_ws_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
+    const size_t a = make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
+    const size_t b = fused_dkdv(d, dv, dtype) ? make_plan(B, H, T, d, dv, block, dtype, true).ws_bytes : 0;
+    return a > b ? a : b;
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -168,9 +184,8 @@ const char *la2_status_string(int status) {
 
 size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                            int backward) {
-    (void)backward;   // forward and backward run scans of the same length and state size
     if (check_sizes(B, H, T, d, d_v, block, dtype) != LA2_OK) return (size_t)-1;
-    return make_plan(B, H, T, d, d_v, block, dtype).ws_bytes;
+    return backward ? backward_ws_bytes(B, H, T, d, d_v, block, dtype) : make_plan(B, H, T, d, d_v, block, dtype).ws_bytes;
 }
 
 int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B, int64_t H,
@@ -220,17 +235,18 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
     const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+    const bool fused = fused_dkdv(d, d_v, dtype);
+    const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype);
     const Range ins[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
                           range_of(decay, decay ? (size_t)H * 4 : 0)};
-    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv),
-                           range_of(workspace, pl.ws_bytes)};
+    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, ws_need)};
     for (int i = 0; i < 4; ++i) {
         for (int j = 0; j < 5; ++j)
             if (overlap(outs[i], ins[j])) return LA2_ERR_ALIAS;
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return LA2_ERR_ALIAS;
     }
-    if (pl.ws_bytes && (!workspace || workspace_bytes < pl.ws_bytes)) return LA2_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_need && (!workspace || workspace_bytes < ws_need)) return LA2_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chains = B * H;
     const int D = (int)d, DV = (int)d_v;
@@ -243,6 +259,28 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
     if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 0,
                           s)) != LA2_OK)
         return st;
+    if (fused) {
+        // dk_t = R_t v_t and dv_t = R_t^T k_t in one reverse pass, R_t = lam R_{t+1} + q_t do_t^T
+        const Plan fp = make_plan(B, H, T, d, d_v, block, dtype, true);
+        if (fp.nseg > 1 && (st = segment_states(q, dout, decay, chains, H, T, D, DV, fp, dtype, la2::Dir::Reverse,
+                                                workspace, s)) != LA2_OK)
+            return st;
+        la2::DkdvArgs a{};
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.dout = dout;
+        a.dk = dk;
+        a.dv = dv;
+        a.decay = decay;
+        a.states = fp.nseg > 1 ? static_cast<const float *>(workspace) : nullptr;
+        a.T = T;
+        a.H = (int)H;
+        a.nseg = fp.nseg;
+        a.seg_tiles = fp.seg_tiles;
+        a.chains = (int)chains;
+        return la2::launch_dkdv_bf16(a, D, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+    }
     // reverse state R_t = lam R_{t+1} + q_t do_t^T, [d, d_v], shared by the dv and dk scans
     if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace,
                                       s)) != LA2_OK)

@@ -47,4 +47,21 @@ hipError_t launch_segment_prefix(float *states, const float *decay, int chains, 
 bool bf16_supported(int D, int DV, int TB);
 bool f32_supported(int D, int DV, int TB);
 
+// Fused reverse pass of the bf16 backward: dk and dv of each (chain, segment) in one walk over its
+// tiles of kDkdvTile positions, from the reverse state R = sum lam^(s-t) q_s do_s^T (d = d_v).
+constexpr int kDkdvTile = 64;
+struct DkdvArgs {
+    const void *q, *k, *v, *dout;
+    void *dk, *dv;
+    const float *decay;    // [H] or nullptr (lam = 1)
+    const float *states;   // fp32 [chains, nseg, D, D] start states of R, or nullptr when not split
+    int64_t T;
+    int H;
+    int nseg;
+    int seg_tiles;
+    int chains;
+};
+bool dkdv_supported(int D, int DV);
+hipError_t launch_dkdv_bf16(const DkdvArgs &a, int D, hipStream_t s);
+
 }  // namespace la2

@@ -109,6 +109,26 @@ def test_narrow_value_slices(B, H, T, seg_tiles, decay, monkeypatch):
     check_full(x, 128)
 
 
+@pytest.mark.parametrize("d,T,decay,seg_tiles", [(128, 700, "heads", None), (64, 333, "none", None),
+                                                  (128, 520, "heads", "3")])
+def test_separate_dkdv_scans(d, T, decay, seg_tiles, monkeypatch):
+    """The two separate reverse scans that the fused dk/dv pass replaces for d = d_v."""
+    monkeypatch.setenv("LA2_SEPARATE_DKDV", "1")
+    if seg_tiles:
+        monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    x = inputs.make_random(1, 3, T, d, d, dtype="bf16", seed=31 + T, decay=decay)
+    check_full(x, 128)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 191])
+@pytest.mark.parametrize("seg_tiles", ["1", "2"])
+def test_fused_dkdv_segments(T, seg_tiles, monkeypatch):
+    """Fused dk/dv pass with every split of T into 64-position segments, ragged last tile."""
+    monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    x = inputs.make_random(2, 2, T, 128, 128, dtype="bf16", seed=41 + T, decay="heads")
+    check_full(x, 128)
+
+
 @pytest.mark.parametrize("B,H", [(4, 25), (8, 16)])
 def test_default_plan_narrow_slices(B, H):
     """96 to 128 chains take the narrow-slice plan by default (8 x 16 chains: grouped block order)."""
