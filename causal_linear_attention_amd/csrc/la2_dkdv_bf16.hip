@@ -241,13 +241,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
                 }
                 acc = mfma(ab, bb, acc);
             }
-            // mask lam^(j-i) for j >= i; only the diagonal block has masked entries
+            // mask lam^(j-i) for j >= i; only the diagonal block has masked entries.  The weights are
+            // recomputed per block (hiding log2 lam from loop-invariant hoisting): kept across the
+            // tile loop they would be spilled, and every reload waits on the next tile's loads.
+            // j - i of accumulator r is base + 8 (r / 4) + r % 4 (small integers, exact in fp32)
+            float base = (float)(u * 32 + 4 * h - brow);
+            asm volatile("" : "+v"(base));
             bf16x8 pf[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int diff = j - brow;
-                const float v = (u != tb || diff >= 0) ? (DECAY ? acc[r] * pw(diff) : acc[r]) : 0.0f;
+                const float diff = base + (float)(8 * (r >> 2) + (r & 3));
+                const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
+                const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
                 pf[r >> 3][r & 7] = (__bf16)v;
             }
 #pragma unroll

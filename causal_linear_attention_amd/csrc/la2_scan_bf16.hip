@@ -347,23 +347,21 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                         }
                         acc = mfma(kb, qb, acc);
                     }
-                    // causal decay mask: only the diagonal block has masked entries
+                    // causal decay mask: only the diagonal block has masked entries.  The distance of
+                    // accumulator r is base -/+ (8 (r / 4) + r % 4), small integers exact in fp32; the
+                    // base is hidden from loop-invariant hoisting, which would otherwise keep the
+                    // per-lane distances or weights across the tile loop in spilled registers (and
+                    // every spill reload waits on the next tile's loads).
+                    float base = (float)(DIR == Dir::Forward ? tcol - u * 32 - 4 * h : u * 32 + 4 * h - tcol);
+                    asm volatile("" : "+v"(base));
                     bf16x8 pf[2];
-                    if (u == tb) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
-                            const float v = diff >= 0 ? (DECAY ? acc[r] * pw(diff) : acc[r]) : 0.0f;
-                            pf[r >> 3][r & 7] = (__bf16)v;
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int tp = u * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const int diff = DIR == Dir::Forward ? tcol - tp : tp - tcol;
-                            pf[r >> 3][r & 7] = (__bf16)(DECAY ? acc[r] * pw(diff) : acc[r]);
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const float c = (float)(8 * (r >> 2) + (r & 3));
+                        const float diff = DIR == Dir::Forward ? base - c : base + c;
+                        const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
+                        const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
+                        pf[r >> 3][r & 7] = (__bf16)v;
                     }
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
