@@ -131,12 +131,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Decay: the state update's copy of a [TB][D] key-role tile, row j scaled by w_upd(j) (lam^(TB-1-j)
 // forward, lam^j reverse) and rounded once to bf16 (same swizzled layout, so a chunk keeps its offset).
+// `extra` adds lam^extra to every row (a tile's own decay factor when the tiles are not visited in
+// scan order).
 template <int D, int TB, Dir DIR>
-__device__ __forceinline__ void build_kw(const u16 *sk, u16 *skw, int tid, float l2) {
+__device__ __forceinline__ void build_kw(const u16 *sk, u16 *skw, int tid, float l2, int extra = 0) {
 #pragma unroll
     for (int s = 0; s < TB * D / 8 / kThreads; ++s) {
         const int c = tid + kThreads * s, row = c / (D / 8);
-        const float w = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - row : row) * l2);
+        const float w = __builtin_amdgcn_exp2f((float)((DIR == Dir::Forward ? TB - 1 - row : row) + extra) * l2);
         u32x4 x = *reinterpret_cast<const u32x4 *>(sk + 8 * c);
 #pragma unroll
         for (int m = 0; m < 4; ++m)

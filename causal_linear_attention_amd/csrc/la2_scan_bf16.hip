@@ -226,7 +226,14 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         }
     }
 
-    auto tile_of = [&](int it) -> int64_t { return DIR == Dir::Forward ? tile_lo + it : tile_hi - 1 - it; };
+    // A state-only pass only sums its segment's tile contributions, so it walks the tiles against the
+    // scan direction, each tile weighted by its own lam^(TB * it): it ends on the tiles the output
+    // pass reads first, which are then the most recently fetched ones in the memory-side cache.
+    constexpr bool kFlip = MODE == Mode::StateOnly;
+    static_assert(C::kDMA || !kFlip, "state-only passes use the direct loads");
+    auto tile_of = [&](int it) -> int64_t {
+        return (DIR == Dir::Forward) != kFlip ? tile_lo + it : tile_hi - 1 - it;
+    };
 
     // S^T (bf16) into LDS for the next tile's right product
     auto write_state_lds = [&]() {
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         dma_tile<D, DV, TB, MODE>(smem, ga, gb, gc, tile_of(0) * TB, T, p.DVT, wave, lane);
         wait_vm();
         lds_barrier();
-        if constexpr (DECAY) build_kw<D, TB, DIR>(smem + C::oK, smem + C::oKW, tid, l2);
+        if constexpr (DECAY) build_kw<D, TB, DIR>(smem + C::oK, smem + C::oKW, tid, l2, 0);
     } else {
         stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
         stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
             if (s_active) {
-                if constexpr (DECAY) {
+                if constexpr (DECAY && !kFlip) {
                     const float f = pw(TB);
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
@@ -463,7 +470,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             lds_barrier();                   // ... everyone's, and every wave is done with this tile
             if (update) write_state_lds();
             if constexpr (DECAY) {
-                if (it + 1 < ntiles) build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2);
+                if (it + 1 < ntiles)
+                    build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2, kFlip ? TB * (it + 1) : 0);
             }
         } else {
             lds_barrier();                   // every wave is done with this tile's LDS
