@@ -121,8 +121,9 @@ def main():
             la2.la2_forward(c["q"], c["k"], c["v"], c["decay"], c["o"], c["w"].block, c["ws"], stream)
             if ev:
                 ev[1].record(stream)
-            la2.la2_backward(c["q"], c["k"], c["v"], c["decay"], c["do"], c["dq"], c["dk"], c["dv"],
-                             c["w"].block, c["ws"], stream)
+            # the training step's backward: reuses the segment states la2_forward left in the workspace
+            la2.la2_backward_saved(c["q"], c["k"], c["v"], c["decay"], c["do"], c["dq"], c["dk"], c["dv"],
+                                   c["w"].block, c["ws"], stream)
             if ev:
                 ev[2].record(stream)
 
@@ -155,6 +156,10 @@ def main():
             "fwd_GBs": round(alg["fwd_bytes"] / (f * 1e-3) / 1e9, 1),
             "bwd_GBs": round(alg["bwd_bytes"] / (b * 1e-3) / 1e9, 1),
             "fwd_bwd_TFLOPs": round((alg["fwd_flops"] + alg["bwd_flops"]) / ((f + b) * 1e-3) / 1e12, 1),
+            # t_roof / t_measured, t_roof = max(algorithmic bytes / peak HBM, algorithmic flops / peak bf16)
+            "roofline_frac": round(max((alg["fwd_bytes"] + alg["bwd_bytes"]) / (PEAK_HBM_GBS * 1e9),
+                                       (alg["fwd_flops"] + alg["bwd_flops"]) / (PEAK_BF16_TFLOPS * 1e12))
+                                   / ((f + b) * 1e-3), 4),
         }
     tps = [v["tokens_per_s"] for v in sweep.values()]
 

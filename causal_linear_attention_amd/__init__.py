@@ -11,9 +11,11 @@ from .binding import (  # noqa: F401
     forward,
     la2_abi_version,
     la2_backward,
+    la2_backward_saved,
     la2_forward,
     la2_status_string,
     la2_workspace_bytes,
     lightning_attention,
     load_library,
+    workspace_for,
 )

@@ -16,7 +16,8 @@ LA2_F32 = 0
 LA2_BF16 = 1
 _DTYPES = {torch.float32: LA2_F32, torch.bfloat16: LA2_BF16}
 
-EXPORTS = ("la2_forward", "la2_backward", "la2_workspace_bytes", "la2_status_string", "la2_abi_version")
+EXPORTS = ("la2_forward", "la2_backward", "la2_backward_saved", "la2_workspace_bytes", "la2_status_string",
+           "la2_abi_version")
 
 _lib = None
 
@@ -40,6 +41,8 @@ def load_library(path=LIB_PATH):
     lib.la2_forward.restype = i32
     lib.la2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la2_backward.restype = i32
+    lib.la2_backward_saved.argtypes = lib.la2_backward.argtypes
+    lib.la2_backward_saved.restype = i32
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.la2_workspace_bytes.restype = sz
     lib.la2_status_string.argtypes = [i32]
@@ -110,17 +113,26 @@ def la2_forward(q, k, v, decay, o, block, workspace=None, stream=None):
         raise LA2Error(st, "la2_forward")
 
 
-def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None):
-    """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>."""
+def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
+    """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
+    la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
+    ``workspace``."""
     B, H, T, d = q.shape
     d_v = v.shape[-1]
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_backward(
+    lib = load_library()
+    fn = lib.la2_backward_saved if saved else lib.la2_backward
+    st = fn(
         _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(dout, "dout"),
         _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
         B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
     if st != 0:
-        raise LA2Error(st, "la2_backward")
+        raise LA2Error(st, "la2_backward_saved" if saved else "la2_backward")
+
+
+def la2_backward_saved(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None):
+    """la2_backward reusing the forward's segment states in ``workspace`` (see include/la2.h)."""
+    la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace, stream, saved=True)
 
 
 def _check_same(q, k, v, other=None):
@@ -147,13 +159,16 @@ def forward(q, k, v, decay=None, block=128, workspace=None):
     return o
 
 
-def backward(q, k, v, dout, decay=None, block=128, workspace=None):
-    """Allocate (dq, dk, dv) and run the backward pass."""
+def backward(q, k, v, dout, decay=None, block=128, workspace=None, saved=False):
+    """Allocate (dq, dk, dv) and run the backward pass (``saved``: reuse the forward's segment states,
+    which requires the workspace that forward() was given)."""
     _check_same(q, k, v, dout)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace of the forward call")
         workspace = workspace_for(q, v, block, True)
-    la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace)
+    la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace, saved=saved)
     return dq, dk, dv
 
 
@@ -163,14 +178,17 @@ class LA2Function(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, decay=None, block=128):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        # one workspace for both passes: the backward reuses the segment states the forward leaves
+        ws = workspace_for(q, v, block, True)
         ctx.save_for_backward(q, k, v, decay)
         ctx.block = block
-        return forward(q, k, v, decay, block)
+        ctx.ws = ws
+        return forward(q, k, v, decay, block, ws)
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, decay = ctx.saved_tensors
-        dq, dk, dv = backward(q, k, v, dout.contiguous(), decay, ctx.block)
+        dq, dk, dv = backward(q, k, v, dout.contiguous(), decay, ctx.block, ctx.ws, saved=ctx.ws is not None)
         return dq, dk, dv, None, None
 
 

@@ -56,14 +56,15 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     p.TB = fused ? la2::kDkdvTile : dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
     const int64_t NT = (T + p.TB - 1) / p.TB;
     const int64_t chains = B * H;
-    // Too few chains to fill the chip: when two 64-wide value slices per chain fill at least 3/4 of
-    // it, split the value width instead of T.  The two slices of a chain re-read the same q and k,
-    // which the kernel's XCD-aware order serves from one L2, while T segments cost an extra state
-    // pass over k and v.  A 64-wide slice still forms the whole score block, so it does about 0.6 of
-    // a 128-wide slice's work, and slices combined with segments lose to segments alone.
-    p.narrow = !fused && dtype == LA2_BF16 && dv == 128 && 2 * chains <= kComputeUnits && 8 * chains >= 3 * kComputeUnits;
+    // Too few chains to fill the chip: split T into segments (one extra state pass over k and v,
+    // whose result the backward reuses).  Running a 128-wide value as two 64-wide slices would
+    // avoid that pass (the kernel's XCD-aware order serves both slices' q and k from one L2), but
+    // each slice still forms the whole score block, about 0.6 of a full slice's work, and measured
+    // slower than segments once the backward reuses the forward's states; LA2_SLICE_WIDTH=64
+    // selects it.
+    p.narrow = false;
     if (const char *env = std::getenv("LA2_SLICE_WIDTH"))
-        p.narrow = !fused && dtype == LA2_BF16 && std::strtol(env, nullptr, 10) == 64;
+        p.narrow = !fused && dtype == LA2_BF16 && dv == 128 && std::strtol(env, nullptr, 10) == 64;
     const int64_t slices = dv / slice_width(dtype, (int)dv, p.narrow);
     const int64_t work = chains * slices;
     int64_t seg_tiles = NT;
@@ -89,10 +90,14 @@ bool fused_dkdv(int64_t d, int64_t dv, int dtype) {
     return dtype == LA2_BF16 && la2::dkdv_supported((int)d, (int)dv);
 }
 
-size_t backward_ws_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype) {
+// Backward workspace: [S segment states, exactly as la2_forward leaves them][R segment states].
+// Keeping the forward's S states in place lets la2_backward_saved skip recomputing them.
+size_t backward_ws_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype,
+                         size_t *s_bytes = nullptr) {
     const size_t a = make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
-    const size_t b = fused_dkdv(d, dv, dtype) ? make_plan(B, H, T, d, dv, block, dtype, true).ws_bytes : 0;
-    return a > b ? a : b;
+    const size_t b = fused_dkdv(d, dv, dtype) ? make_plan(B, H, T, d, dv, block, dtype, true).ws_bytes : a;
+    if (s_bytes) *s_bytes = a;
+    return a + b;
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -222,9 +227,14 @@ int la2_forward(const void *q, const void *k, const void *v, const float *decay,
                        0, s);
 }
 
-int la2_backward(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
-                 void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// reuse_s: the S segment states that la2_forward left at the start of the workspace are still there.
+int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
+                  void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream, bool reuse_s) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -236,7 +246,8 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
     const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
     const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
     const bool fused = fused_dkdv(d, d_v, dtype);
-    const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype);
+    size_t s_bytes = 0;
+    const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype, &s_bytes);
     const Range ins[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
                           range_of(decay, decay ? (size_t)H * 4 : 0)};
     const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, ws_need)};
@@ -252,18 +263,20 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
     const int D = (int)d, DV = (int)d_v;
     st = LA2_OK;
     const bool split = pl.nseg > 1;
-    // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T
-    if (split && (st = segment_states(v, k, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace,
-                                      s)) != LA2_OK)
+    void *ws_r = workspace ? static_cast<char *>(workspace) + s_bytes : nullptr;
+    // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T, so
+    // it reads the forward's S states ([d, d_v] per segment) transposed
+    if (split && !reuse_s &&
+        (st = segment_states(k, v, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Forward, workspace, s)) != LA2_OK)
         return st;
-    if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 0,
+    if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 1,
                           s)) != LA2_OK)
         return st;
     if (fused) {
         // dk_t = R_t v_t and dv_t = R_t^T k_t in one reverse pass, R_t = lam R_{t+1} + q_t do_t^T
         const Plan fp = make_plan(B, H, T, d, d_v, block, dtype, true);
         if (fp.nseg > 1 && (st = segment_states(q, dout, decay, chains, H, T, D, DV, fp, dtype, la2::Dir::Reverse,
-                                                workspace, s)) != LA2_OK)
+                                                ws_r, s)) != LA2_OK)
             return st;
         la2::DkdvArgs a{};
         a.q = q;
@@ -273,7 +286,7 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
         a.dk = dk;
         a.dv = dv;
         a.decay = decay;
-        a.states = fp.nseg > 1 ? static_cast<const float *>(workspace) : nullptr;
+        a.states = fp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
         a.T = T;
         a.H = (int)H;
         a.nseg = fp.nseg;
@@ -282,15 +295,33 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
         return la2::launch_dkdv_bf16(a, D, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
     }
     // reverse state R_t = lam R_{t+1} + q_t do_t^T, [d, d_v], shared by the dv and dk scans
-    if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace,
-                                      s)) != LA2_OK)
+    if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, s)) !=
+                     LA2_OK)
         return st;
     // dv_t = R_t^T k_t         = reverse scan with (k, q, do), state R
-    if ((st = output_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, workspace, 0,
-                          s)) != LA2_OK)
+    if ((st = output_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, 0, s)) !=
+        LA2_OK)
         return st;
     // dk_t = R_t v_t           = reverse scan with (v, do, q), state R^T: read R transposed
-    return output_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, workspace, 1, s);
+    return output_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, ws_r, 1, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int la2_backward(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
+                 void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
+                         stream, false);
+}
+
+int la2_backward_saved(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
+                       void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,
+                       int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
+                         stream, true);
 }
 
 }  // extern "C"

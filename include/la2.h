@@ -27,10 +27,13 @@
  * give unspecified results).
  *
  * Supported: d, d_v in {64, 128}; dtype LA2_BF16 with block in {64, 128, 256},
- * LA2_F32 with block in {16, 32, 64}.  A block of 256 is carried out as two
- * 128-position sub-tiles with the state handed over between them; the
- * decomposition gives the same result for any tile size (same page, section 2:
- * the split into intra- and inter-tile parts holds for every tile length).
+ * LA2_F32 with block in {16, 32, 64}.  `block` is the tile length asked for;
+ * a kernel may run shorter tiles with the state handed over between them,
+ * which gives the same result for any tile size (same page, section 2: the
+ * split into intra- and inter-tile parts holds for every tile length), up to
+ * rounding.  bf16 tiles are at most 128 positions (a block of 256 runs as two
+ * 128-position tiles), and the bf16 backward with d = d_v computes dK and dV
+ * in one fused reverse pass over 64-position tiles.
  *
  * Ownership.  The caller allocates and frees every buffer, including the
  * workspace (la2_workspace_bytes tells its size; it may be 0, in which case
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 1
+#define LA2_ABI_VERSION 2
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -75,7 +78,9 @@ enum la2_status {
  *   q, k: [B, H, T, d]; v, o: [B, H, T, d_v]; decay: [H] fp32 or NULL.
  *   block: tile length T_B; dtype: enum la2_dtype.
  *   workspace: device scratch of at least la2_workspace_bytes(..., 0) bytes,
- *   used for the per-segment states when a chain is split across workgroups. */
+ *   used for the per-segment states when a chain is split across workgroups.
+ *   On completion those bytes hold the state each segment starts from, which
+ *   la2_backward_saved can reuse. */
 int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o,
                 int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
@@ -88,8 +93,24 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
                  int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
                  void *stream);
 
-/* Workspace bytes needed by la2_forward (backward = 0) or la2_backward (backward = 1)
- * for these sizes; (size_t)-1 for arguments that la2_forward/la2_backward would reject. */
+/* Backward that reuses the segment start states of a preceding la2_forward (the
+ * usual training step: forward, then backward on the same q, k, v), instead of
+ * recomputing them from k and v.  Same arguments and results as la2_backward,
+ * with one more precondition: `workspace` is the pointer that the la2_forward
+ * call on the same q, k, v, decay, sizes, block and dtype received, and its
+ * first la2_workspace_bytes(..., 0) bytes are unchanged since that call (this
+ * call leaves them unchanged too, so it may be repeated).  The library cannot
+ * check this; with other contents dQ is wrong for chains split into segments.
+ * When no chain is split (la2_workspace_bytes(..., 0) == 0) it is la2_backward. */
+int la2_backward_saved(const void *q, const void *k, const void *v, const float *decay,
+                       const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                       int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by la2_forward (backward = 0) or la2_backward and
+ * la2_backward_saved (backward = 1) for these sizes; the backward size is never
+ * smaller, so one workspace of that size serves a forward + backward step.
+ * (size_t)-1 for arguments that la2_forward/la2_backward would reject. */
 size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,
                            int dtype, int backward);
 

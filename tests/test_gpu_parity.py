@@ -130,8 +130,9 @@ def test_fused_dkdv_segments(T, seg_tiles, monkeypatch):
 
 
 @pytest.mark.parametrize("B,H", [(4, 25), (8, 16)])
-def test_default_plan_narrow_slices(B, H):
-    """96 to 128 chains take the narrow-slice plan by default (8 x 16 chains: grouped block order)."""
+def test_narrow_slices_many_chains(B, H, monkeypatch):
+    """Narrow slices on 100 and 128 chains (8 x 16 chains: XCD-grouped block order)."""
+    monkeypatch.setenv("LA2_SLICE_WIDTH", "64")
     x = inputs.make_random(B, H, 200, 128, 128, dtype="bf16", seed=B * H, decay="heads")
     check_full(x, 128)
 
@@ -189,6 +190,34 @@ def test_autograd_matches_backward():
     o.backward(do)
     dq, dk, dv = la2.backward(q.detach(), k.detach(), v.detach(), do, decay, 64)
     assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+
+
+@pytest.mark.parametrize("dtype,d,block", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 64, 32)])
+def test_backward_saved_reuses_forward_states(dtype, d, block, monkeypatch):
+    """la2_backward_saved after la2_forward on split chains: twice in a row, bitwise equal to the
+    plain backward (which recomputes the same segment states), and within the bar of the oracle."""
+    monkeypatch.setenv("LA2_SEGMENT_TILES", "2")
+    x = inputs.make_random(1, 3, 700, d, d, dtype=dtype, seed=51, decay="heads")
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    decay = x["decay"].to(DEV)
+    ws = la2.workspace_for(q, v, block, True)
+    assert ws is not None
+    o = torch.empty_like(v)
+    la2.la2_forward(q, k, v, decay, o, block, ws)
+    runs = []
+    for _ in range(2):
+        g = tuple(torch.empty_like(t) for t in (q, k, v))
+        la2.la2_backward_saved(q, k, v, decay, do, *g, block, ws)
+        runs.append(g)
+    ref = la2.backward(q, k, v, do, decay, block)
+    torch.cuda.synchronize()
+    for g in runs:
+        for a, r in zip(g, ref):
+            assert torch.equal(a, r)
+    lam = lam_of(x)
+    want = oracle.backward(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam)
+    for a, r in zip(ref, want):
+        assert rel_err(f64(a), r) <= TOL[dtype]
 
 
 def test_stream_ordering_on_side_stream():
