@@ -26,10 +26,11 @@ METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roo
 
 # HBM bytes per launch of the forward output kernel at the 1K point, from rocprofv3 --pmc FETCH_SIZE
 # and WRITE_SIZE runs (one counter per run), each scaled by what the same counter reads for a plain
-# 1 GiB device copy (FETCH_SIZE x 2.0000, WRITE_SIZE x 1.0000).  Valid only for the kernel source they
-# were taken on; for any other source the roofline reports traffic as null.
-TRAFFIC_KERNEL_SHA256_16 = "7c05b347962bbd83"
-TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573084 * 1024, "write": 525900 * 1024}
+# 1 GiB device copy (FETCH_SIZE x 1.9999, WRITE_SIZE x 1.0000).  Valid only for the kernel source they
+# were taken on (sha256 of la2_scan_bf16.hip followed by la2_bf16_common.h); for any other source the
+# roofline reports traffic as null.
+TRAFFIC_KERNEL_SHA256_16 = "a22c682c82516bf6"
+TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573053 * 1024, "write": 524288 * 1024}
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--points", default="all", help="comma list of sweep lengths in K (e.g. 1,128) or 'all'")
+    ap.add_argument("--workload", default=None,
+                    help="time one named workload of inputs.WORKLOADS (e.g. tnl15b_layer, long128k_outliers) "
+                         "instead of the length sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
                     help="sequences of the 1K point the oracle runs for the CPU baseline")
@@ -90,7 +94,13 @@ def main():
 
     dev = torch.device("cuda:0")
     names = inputs.SWEEP_NAMES
-    if args.points != "all":
+    if args.workload:
+        if args.workload not in inputs.WORKLOADS or not inputs.WORKLOADS[args.workload].backward:
+            print(f"bench.py: unknown or forward-only workload {args.workload!r}", file=sys.stderr)
+            sys.exit(2)
+        names = [args.workload]
+        args.no_cpu_baseline = True
+    elif args.points != "all":
         want = {int(p) for p in args.points.split(",")}
         names = [n for n in names if inputs.WORKLOADS[n].T // 1024 in want]
 
@@ -168,8 +178,9 @@ def main():
     dom = next((i for i, c in enumerate(cases) if c["ws"] is None), None)
     roofline = None
     import hashlib
-    src = os.path.join(ROOT, "causal_linear_attention_amd", "csrc", "la2_scan_bf16.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "causal_linear_attention_amd", "csrc")
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                  for f in ("la2_scan_bf16.hip", "la2_bf16_common.h"))).hexdigest()[:16]
     traffic = (TRAFFIC_BYTES_PER_LAUNCH["fetch"] + TRAFFIC_BYTES_PER_LAUNCH["write"]
                if sha == TRAFFIC_KERNEL_SHA256_16 else None)
     if dom is not None:
@@ -209,13 +220,20 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {
+        "config": ({
             "workload": "fixed-token length sweep: 131072 tokens per batch at (B,T) in "
                         + ",".join(f"({c['w'].B},{c['w'].T})" for c in cases)
                         + "; H=16, d=d_v=128, T_B=128, no decay; one step = fwd+bwd over every batch",
             "tokens_per_step": tokens_per_step, "heads": 16, "d": 128, "d_v": 128, "block": 128,
             "parallelism": "none (1 GPU)",
-        },
+        } if not args.workload else {
+            "workload": f"{cases[0]['w'].name}: B={cases[0]['w'].B}, H={cases[0]['w'].H}, T={cases[0]['w'].T}, "
+                        f"d=d_v={cases[0]['w'].d}, T_B={cases[0]['w'].block}, "
+                        f"{'per-head decay' if cases[0]['w'].decay else 'no decay'}"
+                        f"{', 1% outlier rows x8' if cases[0]['w'].outlier_frac else ''}; one step = fwd+bwd",
+            "tokens_per_step": tokens_per_step, "heads": cases[0]["w"].H, "d": cases[0]["w"].d,
+            "d_v": cases[0]["w"].dv, "block": cases[0]["w"].block, "parallelism": "none (1 GPU)",
+        }),
         "sweep": sweep,
         "flatness": round(min(tps) / max(tps), 4) if tps else None,
         "roofline": roofline,

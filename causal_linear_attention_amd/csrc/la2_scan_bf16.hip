@@ -24,7 +24,9 @@
 // Operands that need 8 consecutive positions per lane (K^T, V) come from ds_read_b64_tr_b16: in
 // each group of 16 lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
 // i/4 + 4e, so lanes that address (row R0 + j/4, column C0 + 4 (j%4)) get column C0 + i, rows
-// R0..R0+3.  Each tile is staged global -> registers -> LDS during the second half of the previous one.
+// R0..R0+3.  Where two tile buffers fit in LDS the next tile goes global -> LDS directly, one whole
+// tile ahead; otherwise it is staged global -> registers -> LDS during the second half of the
+// current one.  Output tiles are staged per wave in LDS and stored as whole rows.
 #include "la2_bf16_common.h"
 
 namespace la2 {
