@@ -248,12 +248,28 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
             float base = (float)(u * 32 + 4 * h - brow);
             asm volatile("" : "+v"(base));
             bf16x8 pf[2];
+            if (DECAY && u != tb) {
+                // off the diagonal every distance is >= 1: lam^dist = lam^(base + 8m) * lam^e, one exp
+                // per group of 4 accumulators, both exponents >= 0 (lam^e rebuilt per block from a
+                // hidden copy of log2 lam rather than held across the tile loop)
+                float l2b = l2;
+                asm volatile("" : "+v"(l2b));
+                const float lam_e[4] = {1.0f, __builtin_amdgcn_exp2f(l2b), __builtin_amdgcn_exp2f(2.0f * l2b),
+                                        __builtin_amdgcn_exp2f(3.0f * l2b)};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float diff = base + (float)(8 * (r >> 2) + (r & 3));
-                const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
-                const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
-                pf[r >> 3][r & 7] = (__bf16)v;
+                for (int m = 0; m < 4; ++m) {
+                    const float pm = __builtin_amdgcn_exp2f((base + (float)(8 * m)) * l2);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pf[m >> 1][4 * (m & 1) + e] = (__bf16)(acc[4 * m + e] * (pm * lam_e[e]));
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float diff = base + (float)(8 * (r >> 2) + (r & 3));
+                    const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
+                    const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
+                    pf[r >> 3][r & 7] = (__bf16)v;
+                }
             }
 #pragma unroll
             for (int x = 0; x < 2; ++x)

@@ -59,20 +59,29 @@ struct Cfg {
     static constexpr int oQ = 0;                             // offsets inside a tile buffer
     static constexpr int oK = oQ + (kOut ? TB * D : 0);
     static constexpr int oV = oK + TB * D;
-    // per-wave staging of its 32 x ODB*32 output block, for full-row stores (no decay: LDS to spare)
-    static constexpr bool kStageO = kOut && !DECAY;
+    // per-wave staging of its 32 x ODB*32 output block, for full-row stores: in a region of its own
+    // where LDS allows (kStageO), else (decay) in the weighted K copy once the state update is done
+    // with it (kStageLate), O waiting in registers until then
     static constexpr int OSW = ODB * 32;                     // staged row width (elements)
-    static constexpr int kRest = (kOut ? DV * D : 0) + (DECAY ? TB * D : 0) + (kStageO ? kWaves * 32 * OSW : 0);
-    static constexpr bool kDMA = (2 * TILE + kRest) * 2 <= 160 * 1024;
+    static constexpr int OSZ = kOut ? kWaves * 32 * OSW : 0;
+    static constexpr int KWZ = DECAY ? TB * D : 0;           // weighted K copy
+    static constexpr bool fits(int nbuf, bool own_os) {
+        return (nbuf * TILE + (kOut ? DV * D : 0) + KWZ + (own_os ? OSZ : 0)) * 2 <= 160 * 1024;
+    }
+    static constexpr bool kLateOK = kOut && DECAY && OSZ <= KWZ;
+    static constexpr bool kDMA = fits(2, true) || (kLateOK && fits(2, false));
     static constexpr int NBUF = kDMA ? 2 : 1;
+    static constexpr bool kStageO = kOut && fits(NBUF, true);
+    static constexpr bool kStageLate = kOut && !kStageO;
     static constexpr int oST = NBUF * TILE;                  // S^T in bf16 (output mode)
     static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
-    static constexpr int oOS = oKW + (DECAY ? TB * D : 0);
-    static constexpr int kLds = oOS + (kStageO ? kWaves * 32 * OSW : 0);
+    static constexpr int oOS = oKW + KWZ;
+    static constexpr int kLds = oOS + (kStageO ? OSZ : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
     static_assert(ODB * WPT == NDB && NTB * WPT <= kWaves, "output blocks");
     static_assert(SPW * kWaves == NSB || (SPW == 1 && NSB <= kWaves), "state blocks");
     static_assert(kLds * 2 <= 160 * 1024, "LDS");
+    static_assert(!kStageLate || kLateOK, "late output staging fits the K copy");
 };
 
 // Row block and part (which ODB value blocks) of O owned by a wave.  Waves w and w + 4 share a
@@ -283,12 +292,38 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             if (it + 1 < ntiles) dma_tile<D, DV, TB, MODE>(nxt, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, wave, lane);
         }
 
+        // O^T accumulators of this wave's output block, and their store: each lane holds 4
+        // consecutive columns of its row tb*32 + col per group; rows at or past T fall outside the
+        // buffer range and are dropped.  Through a private LDS block at `ob`: 8-byte writes of the
+        // O^T groups, then 16-byte reads of whole rows, so every store instruction writes 8 full
+        // 128-byte rows.
+        f32x16 oacc[C::ODB];
+        auto store_o = [&](u16 *ob) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * p.DVT, (T - t0) * p.DVT * 2);
+            constexpr int NC = C::OSW / 8;   // 16-byte chunks per staged row
+#pragma unroll
+            for (int n = 0; n < C::ODB; ++n)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 pk;
+                    pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
+                    pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
+                    const int ch = (n * 32 + 8 * j) >> 3;
+                    *reinterpret_cast<u32x2 *>(ob + col * C::OSW + ((ch ^ (col & (NC - 1))) << 3) + 4 * h) = pk;
+                }
+#pragma unroll
+            for (int s2 = 0; s2 < 32 * NC / 64; ++s2) {
+                const int q = lane + 64 * s2, row = q / NC, ch = q % NC;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::OSW + ((ch ^ (row & (NC - 1))) << 3));
+                bstore16(ry, ((tb * 32 + row) * p.DVT + db0 * 32 + ch * 8) * 2, v);
+            }
+        };
+
         if constexpr (C::kOut) {
             if (o_active) {
                 const int qrow = tb * 32 + col;
                 auto rdQ = [&](int ks) { return lds_read(sQ, nat_off<D>(qrow, 2 * ks + h)); };
 
-                f32x16 oacc[C::ODB];
 #pragma unroll
                 for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
@@ -364,13 +399,34 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     float base = (float)(DIR == Dir::Forward ? tcol - u * 32 - 4 * h : u * 32 + 4 * h - tcol);
                     asm volatile("" : "+v"(base));
                     bf16x8 pf[2];
+                    if (DECAY && u != tb) {
+                        // off the diagonal every distance is >= 1: one exp per group of 4 accumulators,
+                        // lam^dist = lam^(smallest distance in the group) * lam^(offset from it), both
+                        // exponents >= 0, so neither factor can overflow (lam^e is rebuilt per block from
+                        // a hidden copy of log2 lam rather than held across the tile loop)
+                        float l2b = l2;
+                        asm volatile("" : "+v"(l2b));
+                        const float lam_e[4] = {1.0f, __builtin_amdgcn_exp2f(l2b), __builtin_amdgcn_exp2f(2.0f * l2b),
+                                                __builtin_amdgcn_exp2f(3.0f * l2b)};
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float c = (float)(8 * (r >> 2) + (r & 3));
-                        const float diff = DIR == Dir::Forward ? base - c : base + c;
-                        const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
-                        const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
-                        pf[r >> 3][r & 7] = (__bf16)v;
+                        for (int m = 0; m < 4; ++m) {
+                            const float pm = __builtin_amdgcn_exp2f(
+                                (DIR == Dir::Forward ? base - (float)(8 * m + 3) : base + (float)(8 * m)) * l2);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int r = 4 * m + e;
+                                pf[r >> 3][r & 7] = (__bf16)(acc[r] * (pm * lam_e[DIR == Dir::Forward ? 3 - e : e]));
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float c = (float)(8 * (r >> 2) + (r & 3));
+                            const float diff = DIR == Dir::Forward ? base - c : base + c;
+                            const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
+                            const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
+                            pf[r >> 3][r & 7] = (__bf16)v;
+                        }
                     }
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
@@ -379,43 +435,9 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                             oacc[n] = mfma(DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), pf[x], oacc[n]);
                 }
 
-                // store O: the accumulators hold O^T, so each lane has 4 consecutive columns of its row
-                // tb*32 + col per group; rows at or past T fall outside the buffer range and are dropped
-                const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * p.DVT, (T - t0) * p.DVT * 2);
-                if constexpr (C::kStageO) {
-                    // through this wave's private LDS block: 8-byte writes of the O^T groups, then
-                    // 16-byte reads of whole rows, so every store instruction writes 8 full 128-byte rows
-                    constexpr int NC = C::OSW / 8;   // 16-byte chunks per staged row
-                    u16 *ob = smem + C::oOS + wave * 32 * C::OSW;
-#pragma unroll
-                    for (int n = 0; n < C::ODB; ++n)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x2 pk;
-                            pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
-                            pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
-                            const int ch = (n * 32 + 8 * j) >> 3;
-                            *reinterpret_cast<u32x2 *>(ob + col * C::OSW + ((ch ^ (col & (NC - 1))) << 3) + 4 * h) = pk;
-                        }
-#pragma unroll
-                    for (int s2 = 0; s2 < 32 * NC / 64; ++s2) {
-                        const int q = lane + 64 * s2, row = q / NC, ch = q % NC;
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::OSW + ((ch ^ (row & (NC - 1))) << 3));
-                        bstore16(ry, ((tb * 32 + row) * p.DVT + db0 * 32 + ch * 8) * 2, v);
-                    }
-                } else {
-                    const int orow = (tb * 32 + col) * p.DVT;
-#pragma unroll
-                    for (int n = 0; n < C::ODB; ++n) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x2 pk;
-                            pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
-                            pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
-                            bstore8(ry, (orow + (db0 + n) * 32 + 8 * j + 4 * h) * 2, pk);
-                        }
-                    }
-                }
+                // with the LDS to spare, O goes out now; otherwise (decay: the weighted K copy fills
+                // LDS) it waits in registers until the state update has released that copy
+                if constexpr (C::kStageO) store_o(smem + C::oOS + wave * 32 * C::OSW);
             }
         }
 
@@ -434,11 +456,15 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
                 const u16 *sKU = DECAY ? smem + C::oKW : sK;   // K as used by the update
+                // with O held in registers across the update, its fragment addresses are rebuilt here
+                // from a hidden copy of the lane index rather than kept (and spilled) across the loop
+                int ln = lane;
+                if constexpr (C::kStageLate) asm volatile("" : "+v"(ln));
                 auto rdKT = [&](int s, int x) {
-                    return frag_tr<D, false>(sKU, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, lane);
+                    return frag_tr<D, false>(sKU, 16 * x, ((wave * C::SPW + s) / C::NDB) * 32, ln);
                 };
                 auto rdV = [&](int s, int x) {
-                    return frag_tr<DV, false>(sV, 16 * x, ((wave * C::SPW + s) % C::NDB) * 32, lane);
+                    return frag_tr<DV, false>(sV, 16 * x, ((wave * C::SPW + s) % C::NDB) * 32, ln);
                 };
                 bf16x8 ka[C::SPW], va[C::SPW];
 #pragma unroll
@@ -471,6 +497,10 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             wait_vm();                       // this wave's loads of the next tile have landed
             lds_barrier();                   // ... everyone's, and every wave is done with this tile
             if (update) write_state_lds();
+            if constexpr (C::kStageLate) {
+                if (o_active) store_o(smem + C::oKW + wave * 32 * C::OSW);
+                lds_barrier();               // every staged O is read back before the copy is rebuilt
+            }
             if constexpr (DECAY) {
                 if (it + 1 < ntiles)
                     build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2, kFlip ? TB * (it + 1) : 0);
@@ -478,6 +508,10 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         } else {
             lds_barrier();                   // every wave is done with this tile's LDS
             if (update) write_state_lds();
+            if constexpr (C::kStageLate) {
+                if (o_active) store_o(smem + C::oKW + wave * 32 * C::OSW);
+                lds_barrier();               // every staged O is read back before the copy is rebuilt
+            }
             if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
         }
         lds_barrier();
