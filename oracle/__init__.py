@@ -49,6 +49,8 @@ def _bind(lib):
     I = ctypes.c_int64
     lib.la2_oracle_forward.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.la2_oracle_forward.restype = None
+    lib.la2_oracle_forward_state.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+    lib.la2_oracle_forward_state.restype = None
     lib.la2_oracle_backward.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
     lib.la2_oracle_backward.restype = None
     lib.la2_oracle_forward_rows.argtypes = [I, I, I, ctypes.c_double, P, P, P, I,
@@ -97,6 +99,19 @@ class Oracle:
         lams = _chain_lams(lam, B, H)
         self.lib.la2_oracle_forward(B * H, T, d, dv, _ptr(lams), _ptr(q), _ptr(k), _ptr(v), _ptr(o))
         return o
+
+    def forward_state(self, q, k, v, lam=None, state_in=None):
+        """(o, final state) for [B, H, T, d] inputs starting from ``state_in`` ([B, H, d, dv], None = 0)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, T, d = q.shape
+        dv = v.shape[-1]
+        o = np.empty((B, H, T, dv), dtype=np.float64)
+        s_out = np.empty((B, H, d, dv), dtype=np.float64)
+        s_in = None if state_in is None else _f64(state_in).reshape(B, H, d, dv)
+        lams = _chain_lams(lam, B, H)
+        self.lib.la2_oracle_forward_state(B * H, T, d, dv, _ptr(lams), _ptr(q), _ptr(k), _ptr(v),
+                                          None if s_in is None else _ptr(s_in), _ptr(o), _ptr(s_out))
+        return o, s_out
 
     def backward(self, q, k, v, do, lam=None):
         """(dq, dk, dv) of <o, do> via the forward and reverse recurrences."""
@@ -152,6 +167,10 @@ def load(path=None):
 
 def forward(q, k, v, lam=None):
     return load().forward(q, k, v, lam)
+
+
+def forward_state(q, k, v, lam=None, state_in=None):
+    return load().forward_state(q, k, v, lam, state_in)
 
 
 def backward(q, k, v, do, lam=None):

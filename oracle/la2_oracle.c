@@ -47,9 +47,14 @@
 
 /* ---- whole-sequence recurrences --------------------------------------- */
 
-void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
-                        const double *lam, const double *q, const double *k,
-                        const double *v, double *o)
+/* The recurrence carried in from and out to a state, the summary of everything before the
+ * sequence (same page, section 2, "Memory footprint": the only state that persists across tiles
+ * is the d x dv matrix S).  s_in, s_out: [n_chains][d][dv] or NULL.  The sequence starts from
+ * S_{-1} = s_in (0 when NULL), so its first step is S_0 = lam * s_in + k_0 v_0^T, and S_{T-1} is
+ * written to s_out.  Splitting a sequence at any t and carrying S_{t-1} over gives the same o. */
+void la2_oracle_forward_state(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                              const double *lam, const double *q, const double *k,
+                              const double *v, const double *s_in, double *o, double *s_out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t c = 0; c < n_chains; ++c) {
@@ -59,6 +64,10 @@ void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
         double *oc = o + c * T * dv;
         const double l = lam[c];
         double *S = (double *)calloc((size_t)(d * dv), sizeof(double)); /* S[i][j], i < d, j < dv */
+        if (s_in)
+            for (int64_t i = 0; i < d; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = s_in[c * d * dv + i * dv + j];
         for (int64_t t = 0; t < T; ++t) {
             const double *kt = kc + t * d, *vt = vc + t * dv, *qt = qc + t * d;
             /* S_t = lam * S_{t-1} + k_t v_t^T */
@@ -73,8 +82,19 @@ void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
                 oc[t * dv + j] = acc;
             }
         }
+        if (s_out)
+            for (int64_t i = 0; i < d; ++i)
+                for (int64_t j = 0; j < dv; ++j)
+                    s_out[c * d * dv + i * dv + j] = S[i * dv + j];
         free(S);
     }
+}
+
+void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                        const double *lam, const double *q, const double *k,
+                        const double *v, double *o)
+{
+    la2_oracle_forward_state(n_chains, T, d, dv, lam, q, k, v, NULL, o, NULL);
 }
 
 void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,

@@ -227,6 +227,39 @@ def pin_rows(orc):
         _close(gv, tv.grad[0, h, rows].numpy(), 1e-12, "rows dv")
 
 
+def pin_state_closed_form(orc):
+    """With a carried-in state S_in the outputs and the final state have closed forms:
+    o_t = lam^(t+1) S_in^T q_t + (brute-force row t) and S_out = lam^T S_in + sum_s lam^(T-1-s) k_s v_s^T
+    (weights built with numpy powers, the sum with einsum)."""
+    B, H, T, d, dv = 2, 3, 23, 5, 4
+    q, k, v, _, lam = _setup(101, B=B, H=H, T=T, d=d, dv=dv)
+    s_in = _rand((B, H, d, dv), 107)
+    o, s_out = orc.forward_state(q, k, v, lam, s_in)
+    base = brute_forward(q, k, v, lam)
+    t = np.arange(T)
+    for h in range(H):
+        carry = (lam[h] ** (t + 1))[None, :, None] * np.einsum("bij,bti->btj", s_in[:, h], q[:, h])
+        _close(o[:, h], base[:, h] + carry, 1e-12, "o with state_in")
+        w = lam[h] ** (T - 1 - t)
+        want = lam[h] ** T * s_in[:, h] + np.einsum("t,bti,btj->bij", w, k[:, h], v[:, h])
+        _close(s_out[:, h], want, 1e-12, "final state")
+    # no state in: the final state of a single step is k v^T
+    o1, s1 = orc.forward_state(q[:, :, :1], k[:, :, :1], v[:, :, :1], lam, None)
+    _close(s1, np.einsum("bhi,bhj->bhij", k[:, :, 0], v[:, :, 0]), 1e-14, "one-step state")
+
+
+def pin_state_split_carry(orc):
+    """Cutting a sequence anywhere and carrying the state over reproduces the whole run: the state
+    is the complete summary of the past (page "Lightning Attention", section 2, Memory footprint)."""
+    q, k, v, _, lam = _setup(113, B=1, H=3, T=29, d=4, dv=6)
+    o_all, s_all = orc.forward_state(q, k, v, lam, None)
+    for cut in (0, 1, 7, 28, 29):
+        oa, sa = orc.forward_state(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], lam, None)
+        ob, sb = orc.forward_state(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], lam, sa)
+        _close(np.concatenate([oa, ob], axis=2), o_all, 1e-12, f"split at {cut}")
+        _close(sb, s_all, 1e-12, f"state after split at {cut}")
+
+
 ALL_PINS = [
     pin_golden_handworked,
     pin_bruteforce_forward,
@@ -240,4 +273,6 @@ ALL_PINS = [
     pin_backward_as_forward,
     pin_linearity_and_heads,
     pin_rows,
+    pin_state_closed_form,
+    pin_state_split_carry,
 ]

@@ -42,6 +42,12 @@ MUTANTS = [
     ("rows_dk_wrong_vector",
      "const double wk = p * dot(dout + s * dv, v + t * dv, dv);",
      "const double wk = p * dot(dout + t * dv, v + s * dv, dv);"),
+    ("state_in_transposed",
+     "S[i * dv + j] = s_in[c * d * dv + i * dv + j];",
+     "S[i * dv + j] = s_in[c * d * dv + j * d + i];"),
+    ("state_out_before_last_step",
+     "        if (s_out)\n            for (int64_t i = 0; i < d; ++i)",
+     "        if (s_out && T > 0) { for (int64_t i = 0; i < d * dv; ++i) S[i] -= kc[(T - 1) * d + i / dv] * vc[(T - 1) * dv + i % dv]; }\n        if (s_out)\n            for (int64_t i = 0; i < d; ++i)"),
     ("rows_skip_diagonal",
      "for (int64_t s = 0; s <= t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q",
      "for (int64_t s = 0; s < t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q"),
