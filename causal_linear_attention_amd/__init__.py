@@ -8,11 +8,15 @@ from .binding import (  # noqa: F401
     LA2Error,
     LA2Function,
     backward,
+    decode_step,
     forward,
+    forward_state,
     la2_abi_version,
     la2_backward,
     la2_backward_saved,
+    la2_decode_step,
     la2_forward,
+    la2_forward_state,
     la2_status_string,
     la2_workspace_bytes,
     lightning_attention,

@@ -16,8 +16,8 @@ LA2_F32 = 0
 LA2_BF16 = 1
 _DTYPES = {torch.float32: LA2_F32, torch.bfloat16: LA2_BF16}
 
-EXPORTS = ("la2_forward", "la2_backward", "la2_backward_saved", "la2_workspace_bytes", "la2_status_string",
-           "la2_abi_version")
+EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_backward", "la2_backward_saved",
+           "la2_workspace_bytes", "la2_status_string", "la2_abi_version")
 
 _lib = None
 
@@ -43,6 +43,10 @@ def load_library(path=LIB_PATH):
     lib.la2_backward.restype = i32
     lib.la2_backward_saved.argtypes = lib.la2_backward.argtypes
     lib.la2_backward_saved.restype = i32
+    lib.la2_forward_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la2_forward_state.restype = i32
+    lib.la2_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.la2_decode_step.restype = i32
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.la2_workspace_bytes.restype = sz
     lib.la2_status_string.argtypes = [i32]
@@ -113,6 +117,45 @@ def la2_forward(q, k, v, decay, o, block, workspace=None, stream=None):
         raise LA2Error(st, "la2_forward")
 
 
+def _state_ptr(t, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _dev_ptr(t, name)
+
+
+def la2_forward_state(q, k, v, decay, state_in, o, state_out, block, workspace=None, stream=None):
+    """Enqueue o = attention(q, k, v) from the carried-in fp32 state ``state_in`` ([B, H, d, d_v] or
+    None) and write the final state to ``state_out`` (same shape, may be ``state_in``, or None)."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None and tuple(t.shape) != (B, H, d, d_v):
+            raise ValueError(f"{name} must be [B, H, d, d_v] = {(B, H, d, d_v)}")
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_forward_state(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _state_ptr(state_in, "state_in"),
+        _dev_ptr(o, "o"), _state_ptr(state_out, "state_out"),
+        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_forward_state")
+
+
+def la2_decode_step(q, k, v, decay, o, state, stream=None):
+    """Enqueue one token per chain: state <- lam state + k v^T (in place), o = state^T q.
+    q, k: [B, H, d]; v, o: [B, H, d_v]; state: fp32 [B, H, d, d_v]."""
+    B, H, d = q.shape
+    d_v = v.shape[-1]
+    if tuple(state.shape) != (B, H, d, d_v):
+        raise ValueError(f"state must be [B, H, d, d_v] = {(B, H, d, d_v)}")
+    st = load_library().la2_decode_step(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
+        _state_ptr(state, "state"), B, H, d, d_v, dtype_code(q.dtype), _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_decode_step")
+
+
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
     la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
@@ -156,6 +199,28 @@ def forward(q, k, v, decay=None, block=128, workspace=None):
     if workspace is None:
         workspace = workspace_for(q, v, block, False)
     la2_forward(q, k, v, decay, o, block, workspace)
+    return o
+
+
+def forward_state(q, k, v, decay=None, block=128, state_in=None, workspace=None):
+    """Allocate o and the final state and run the forward from ``state_in`` (None = zero state);
+    returns (o, state_out)."""
+    _check_same(q, k, v)
+    B, H, T, d = q.shape
+    o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    state_out = torch.empty((B, H, d, v.shape[-1]), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, v, block, False)
+    la2_forward_state(q, k, v, decay, state_in, o, state_out, block, workspace)
+    return o, state_out
+
+
+def decode_step(q, k, v, state, decay=None):
+    """One token per chain from ``state`` (updated in place); q, k: [B, H, d], v: [B, H, d_v]; returns o."""
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must be [B, H, d] and v [B, H, d_v] of one dtype")
+    o = torch.empty_like(v)
+    la2_decode_step(q, k, v, decay, o, state)
     return o
 
 

@@ -140,8 +140,10 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
 
 // Segment start states of the scan with key role `b` (width D) and value role `c` (width W) in
 // direction `dir`, written to `ws` ([chains, nseg, D, W] fp32).  Only called for split chains.
+// `init` ([chains, D, W] or nullptr): the state the first segment starts from.
 int segment_states(const void *b, const void *c, const float *decay, int64_t chains, int64_t H, int64_t T, int D,
-                   int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s) {
+                   int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s,
+                   const float *init = nullptr) {
     la2::ScanArgs args = scan_args(nullptr, b, c, nullptr, decay, chains, H, T, W, pl, dtype);
     args.states = static_cast<float *>(ws);
     // deltas of the segments whose successor (forward) / predecessor (reverse) needs them
@@ -149,18 +151,22 @@ int segment_states(const void *b, const void *c, const float *decay, int64_t cha
     args.seg_count = pl.nseg - 1;
     if (launch(args, D, pl, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
     if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nseg, (int64_t)pl.seg_tiles * pl.TB,
-                                   (int64_t)D * W, dir, s) != hipSuccess)
+                                   (int64_t)D * W, dir, s, init) != hipSuccess)
         return LA2_ERR_HIP;
     return LA2_OK;
 }
 
 // Output pass y = attention(a, b, c) in direction `dir`, every segment starting from the states in
-// `ws` (transposed when states_t) or from zero when the chains are not split.
+// `ws` (transposed when states_t) or from zero when the chains are not split.  Forward only:
+// `state_in` ([chains, D, W]) is where an unsplit chain starts (a split chain's first segment reads
+// it from `ws`, where the prefix put it), and the final state goes to `state_out`.
 int output_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
                 int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, int states_t,
-                hipStream_t s) {
+                hipStream_t s, const float *state_in = nullptr, float *state_out = nullptr) {
     la2::ScanArgs args = scan_args(a, b, c, y, decay, chains, H, T, W, pl, dtype);
-    args.states = pl.nseg > 1 ? static_cast<float *>(ws) : nullptr;
+    args.states = pl.nseg > 1 ? static_cast<float *>(ws) : const_cast<float *>(state_in);
+    args.has_init = state_in != nullptr;
+    args.state_out = state_out;
     args.states_t = states_t;
     args.seg_first = 0;
     args.seg_count = pl.nseg;
@@ -193,38 +199,91 @@ size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d
     return backward ? backward_ws_bytes(B, H, T, d, d_v, block, dtype) : make_plan(B, H, T, d, d_v, block, dtype).ws_bytes;
 }
 
-int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B, int64_t H,
-                int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
-                void *stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void *q, const void *k, const void *v, const float *decay, const float *state_in, void *o,
+                 float *state_out, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                 void *workspace, size_t workspace_bytes, void *stream) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
     if (st != LA2_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (workspace && !aligned16(workspace)) ||
-        (reinterpret_cast<uintptr_t>(decay) & 3u))
+        !aligned16(state_in) || !aligned16(state_out) || (reinterpret_cast<uintptr_t>(decay) & 3u))
         return LA2_ERR_MISALIGNED;
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const size_t ns = (size_t)(B * H * d * d_v) * sizeof(float);
     const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
     const Range ro = range_of(o, nv);
+    const Range rdec = range_of(decay, decay ? (size_t)H * 4 : 0);
+    const Range rsi = range_of(state_in, state_in ? ns : 0), rso = range_of(state_out, state_out ? ns : 0);
     if (overlap(ro, range_of(q, nq)) || overlap(ro, range_of(k, nq)) || overlap(ro, range_of(v, nv)) ||
-        (decay && overlap(ro, range_of(decay, (size_t)H * 4))))
+        overlap(ro, rdec) || overlap(ro, rsi) || overlap(ro, rso))
+        return LA2_ERR_ALIAS;
+    // the final state may overwrite the initial one in place, but may not partly overlap it or any input
+    if (state_out && ((overlap(rso, rsi) && state_out != state_in) || overlap(rso, range_of(q, nq)) ||
+                      overlap(rso, range_of(k, nq)) || overlap(rso, range_of(v, nv)) || overlap(rso, rdec)))
         return LA2_ERR_ALIAS;
     if (pl.ws_bytes) {
         if (!workspace || workspace_bytes < pl.ws_bytes) return LA2_ERR_WORKSPACE_TOO_SMALL;
         const Range rw = range_of(workspace, pl.ws_bytes);
         if (overlap(rw, ro) || overlap(rw, range_of(q, nq)) || overlap(rw, range_of(k, nq)) ||
-            overlap(rw, range_of(v, nv)) || (decay && overlap(rw, range_of(decay, (size_t)H * 4))))
+            overlap(rw, range_of(v, nv)) || overlap(rw, rdec) || overlap(rw, rsi) || overlap(rw, rso))
             return LA2_ERR_ALIAS;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chains = B * H;
     if (pl.nseg > 1) {
-        st = segment_states(k, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s);
+        st = segment_states(k, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s,
+                            state_in);
         if (st != LA2_OK) return st;
     }
     return output_scan(q, k, v, o, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace,
-                       0, s);
+                       0, s, state_in, state_out);
+}
+
+}  // namespace
+
+extern "C" {
+
+int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B, int64_t H,
+                int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
+                void *stream) {
+    return forward_impl(q, k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block, dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+int la2_forward_state(const void *q, const void *k, const void *v, const float *decay, const float *state_in,
+                      void *o, float *state_out, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,
+                      int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_impl(q, k, v, decay, state_in, o, state_out, B, H, T, d, d_v, block, dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+int la2_decode_step(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
+                    int64_t B, int64_t H, int64_t d, int64_t d_v, int dtype, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o || !state) return LA2_ERR_NULL_POINTER;
+    const int st = check_sizes(B, H, 1, d, d_v, dtype == LA2_BF16 ? 128 : 64, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) ||
+        (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * d) * es, nv = (size_t)(B * H * d_v) * es;
+    const Range ro = range_of(o, nv), rs = range_of(state, (size_t)(B * H * d * d_v) * sizeof(float));
+    const Range rdec = range_of(decay, decay ? (size_t)H * 4 : 0);
+    const Range ins[4] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), rdec};
+    for (const Range &r : ins)
+        if (overlap(ro, r) || overlap(rs, r)) return LA2_ERR_ALIAS;
+    if (overlap(ro, rs)) return LA2_ERR_ALIAS;
+    return la2::launch_decode(q, k, v, decay, o, state, (int)(B * H), (int)H, (int)d, (int)d_v, dtype,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LA2_OK
+               : LA2_ERR_HIP;
 }
 
 }  // extern "C"

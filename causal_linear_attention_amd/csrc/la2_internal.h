@@ -19,6 +19,8 @@ struct ScanArgs {
     const float *decay;    // [H] or nullptr (lam = 1)
     float *states;         // fp32 [chains, nseg, D, DVT]: segment start states / segment deltas
     int states_t;          // 1: output launches read the start states transposed, [chains, nseg, DVT, D]
+    int has_init;          // output launches: segment 0 also starts from `states` (a carried-in state)
+    float *state_out;      // forward output launches: fp32 [chains, D, DVT] final state, or nullptr
     int64_t T;
     int H;
     int DVT;               // full value width (row stride of c and y)
@@ -39,9 +41,16 @@ hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, M
                             hipStream_t s);
 hipError_t launch_scan_f32(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
                            hipStream_t s);
-// Turns per-segment deltas into per-segment start states, in place.
+// Turns per-segment deltas into per-segment start states, in place; `init` ([chains, elems] or
+// nullptr) is the state the first segment starts from.
 hipError_t launch_segment_prefix(float *states, const float *decay, int chains, int H, int nseg,
-                                 int64_t seg_len, int64_t elems, Dir dir, hipStream_t s);
+                                 int64_t seg_len, int64_t elems, Dir dir, hipStream_t s,
+                                 const float *init = nullptr);
+
+// One token of the recurrence for every chain: state <- lam state + k v^T (fp32 [chains, D, DV], in
+// place), o = state^T q.  q, k: [chains, D]; v, o: [chains, DV]; bf16 (dtype 1) or fp32 (0).
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
+                         int chains, int H, int D, int DV, int dtype, hipStream_t s);
 
 // Which (D, DV, TB) the kernels are compiled for.
 bool bf16_supported(int D, int DV, int TB);

@@ -7,7 +7,7 @@
 // lizeman.github.io llm-arch-kb, section 2, "Memory footprint": the only persistent
 // state across tiles is the d x d_v matrix S), so the hand-over is one affine step
 // per segment:
-//   forward: S_in[0] = 0,        S_in[p+1] = lam^L S_in[p] + dS[p]
+//   forward: S_in[0] = init (0 if none),  S_in[p+1] = lam^L S_in[p] + dS[p]
 //   reverse: R_in[last] = 0,     R_in[p-1] = lam^L R_in[p] + dR[p]
 // L is the segment length in positions (every segment except the last is full, and
 // the last one's length only ever multiplies a zero state).
@@ -17,13 +17,14 @@ namespace la2 {
 namespace {
 
 __global__ __launch_bounds__(256) void segment_prefix_kernel(float *states, const float *decay, int H, int nseg,
-                                                             int64_t seg_len, int64_t elems, int reverse) {
+                                                             int64_t seg_len, int64_t elems, int reverse,
+                                                             const float *init) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int chain = blockIdx.y;
     if (e >= elems) return;
     const float f = decay ? exp2f((float)seg_len * log2f(decay[chain % H])) : 1.0f;
     float *base = states + (int64_t)chain * nseg * elems + e;
-    float run = 0.0f;
+    float run = init ? init[(int64_t)chain * elems + e] : 0.0f;
     if (!reverse) {
         for (int p = 0; p < nseg; ++p) {
             const float d = p < nseg - 1 ? base[(int64_t)p * elems] : 0.0f;
@@ -42,10 +43,10 @@ __global__ __launch_bounds__(256) void segment_prefix_kernel(float *states, cons
 }  // namespace
 
 hipError_t launch_segment_prefix(float *states, const float *decay, int chains, int H, int nseg, int64_t seg_len,
-                                 int64_t elems, Dir dir, hipStream_t s) {
+                                 int64_t elems, Dir dir, hipStream_t s, const float *init) {
     dim3 grid((unsigned)((elems + 255) / 256), (unsigned)chains);
     hipLaunchKernelGGL(segment_prefix_kernel, grid, dim3(256), 0, s, states, decay, H, nseg, seg_len, elems,
-                       dir == Dir::Reverse ? 1 : 0);
+                       dir == Dir::Reverse ? 1 : 0, init);
     return hipGetLastError();
 }
 

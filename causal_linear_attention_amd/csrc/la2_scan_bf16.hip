@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const bool s_active = wave * C::SPW < C::NSB;
 
     f32x16 sacc[C::SPW];
-    const bool init_state = C::kOut && gs != nullptr && (DIR == Dir::Forward ? seg > 0 : seg < p.nseg - 1);
+    const bool init_state =
+        C::kOut && gs != nullptr && (DIR == Dir::Forward ? (seg > 0 || p.has_init) : seg < p.nseg - 1);
 #pragma unroll
     for (int s = 0; s < C::SPW; ++s) {
         const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
@@ -538,6 +539,49 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 for (int r = 0; r < 16; ++r) {
                     const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                     gs[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
+                }
+            }
+        }
+    }
+
+    // Carried-out final state: the last tile's update, which the loop leaves out, over the tile's
+    // `leff` real positions, S = lam^leff S + sum_{j < leff} lam^(leff-1-j) k_j v_j^T (exact for a
+    // ragged last tile).  The last tile is still in LDS and nothing writes LDS any more.
+    if constexpr (C::kOut && DIR == Dir::Forward) {
+        if (p.state_out != nullptr && seg == p.nseg - 1 && s_active) {
+            const int last = ntiles - 1;
+            const u16 *cur = smem + (C::kDMA ? (last & 1) * C::TILE : 0);
+            const u16 *sK = cur + C::oK, *sV = cur + C::oV;
+            const int leff = (int)min((int64_t)TB, T - tile_of(last) * TB);
+            if constexpr (DECAY) {
+                const float f = pw(leff);
+#pragma unroll
+                for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
+            }
+#pragma unroll
+            for (int s = 0; s < C::SPW; ++s) {
+                const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+                for (int x = 0; x < TB / 16; ++x) {
+                    bf16x8 kf = frag_tr<D, false>(sK, 16 * x, kb * 32, lane);
+                    if constexpr (DECAY) {
+                        // rows j = 16x + 8h + e: weight lam^(leff-1-j), and 0 past the sequence end
+                        u32x4 u = __builtin_bit_cast(u32x4, kf);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            const int j = 16 * x + 8 * h + 2 * m;
+                            const float wl = j < leff ? __builtin_amdgcn_exp2f((float)(leff - 1 - j) * l2) : 0.0f;
+                            const float wh = j + 1 < leff ? __builtin_amdgcn_exp2f((float)(leff - 2 - j) * l2) : 0.0f;
+                            u[m] = pack_bf16(__uint_as_float(u[m] << 16) * wl, __uint_as_float(u[m] & 0xffff0000u) * wh);
+                        }
+                        kf = __builtin_bit_cast(bf16x8, u);
+                    }
+                    sacc[s] = mfma(kf, frag_tr<DV, false>(sV, 16 * x, nb * 32, lane), sacc[s]);
+                }
+                float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    so[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
                 }
             }
         }

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
     const float l2 = has_decay ? log2f(p.decay[chain % p.H]) : 0.0f;
     auto pw = [&](int n) -> float { return has_decay ? exp2f((float)n * l2) : 1.0f; };
 
-    const bool init_state = kOut && gs != nullptr && (DIR == Dir::Forward ? seg > 0 : seg < p.nseg - 1);
+    const bool init_state =
+        kOut && gs != nullptr && (DIR == Dir::Forward ? (seg > 0 || p.has_init) : seg < p.nseg - 1);
     for (int e = tid; e < D * DV; e += kThreads)
         sS[e] = init_state ? gs[p.states_t ? (int64_t)(e % DV) * D + e / DV : (int64_t)(e / DV) * p.DVT + e % DV] : 0.0f;
 
@@ -109,6 +110,23 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
     if constexpr (MODE == Mode::StateOnly) {
         __syncthreads();
         for (int e = tid; e < D * DV; e += kThreads) gs[(int64_t)(e / DV) * p.DVT + e % DV] = sS[e];
+    }
+
+    // Carried-out final state: the last tile's update, which the loop leaves out, over its `leff`
+    // real positions (exact for a ragged last tile); the last tile is still in LDS.
+    if constexpr (kOut && DIR == Dir::Forward) {
+        if (p.state_out != nullptr && seg == p.nseg - 1) {
+            __syncthreads();
+            const int leff = (int)min((int64_t)TB, T - (tile_hi - 1) * TB);
+            const float f = pw(leff);
+            float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
+            for (int e = tid; e < D * DV; e += kThreads) {
+                const int c = e / DV, n = e % DV;
+                float acc = sS[e] * f;
+                for (int j = 0; j < leff; ++j) acc = fmaf(sK[j * D + c] * pw(leff - 1 - j), sV[j * DV + n], acc);
+                so[(int64_t)c * p.DVT + n] = acc;
+            }
+        }
     }
 }
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 2
+#define LA2_ABI_VERSION 3
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -85,6 +85,38 @@ int la2_forward(const void *q, const void *k, const void *v, const float *decay,
                 int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Forward carried in from and out to a state: the same o, for a sequence whose
+ * prefix is summarized by state_in, and the state after its last position.
+ * The state is the fixed-size summary of everything before a position (page
+ * "Lightning Attention", section 2, "Memory footprint": the only persistent
+ * state across tiles is the d x d_v matrix S), so splitting a sequence
+ * anywhere and passing the state on gives the same outputs (chunked prefill,
+ * exact resume):
+ *     S_{-1} = state_in (0 when NULL),  S_t = lam S_{t-1} + k_t v_t^T,
+ *     o_t = S_t^T q_t,  state_out = S_{T-1}.
+ *   state_in, state_out: device fp32 [B, H, d, d_v], row-major (d rows), or
+ *   NULL (start from zero / do not write the final state).  state_out may be
+ *   the same pointer as state_in (updated in place) but may not otherwise
+ *   overlap it, an input, o or the workspace.  Other arguments and the
+ *   workspace as in la2_forward.  No backward is provided for a non-zero
+ *   state_in (la2_backward assumes the sequence starts from zero). */
+int la2_forward_state(const void *q, const void *k, const void *v, const float *decay,
+                      const float *state_in, void *o, float *state_out, int64_t B, int64_t H,
+                      int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* One generated token per chain (inference): state <- lam state + k v^T, then
+ * o = state^T q, with the cost of one step whatever the length of the prefix
+ * the state summarizes (Lightning Attention-2 abstract, arXiv 2401.04658:
+ * constant speed at any length).
+ *   q, k: [B, H, d]; v, o: [B, H, d_v] (one position, `dtype`); decay: [H] fp32
+ *   or NULL; state: device fp32 [B, H, d, d_v], read and overwritten in place.
+ *   o may not overlap an input or the state, nor the state an input.
+ *   No workspace; supported d, d_v in {64, 128}. */
+int la2_decode_step(const void *q, const void *k, const void *v, const float *decay, void *o,
+                    float *state, int64_t B, int64_t H, int64_t d, int64_t d_v, int dtype,
+                    void *stream);
+
 /* Backward: gradients of <o, dout> with respect to q, k and v.
  *   dout, dv: [B, H, T, d_v]; dq, dk: [B, H, T, d]; other arguments as in la2_forward.
  *   workspace: at least la2_workspace_bytes(..., 1) bytes. */
@@ -107,7 +139,7 @@ int la2_backward_saved(const void *q, const void *k, const void *v, const float 
                        int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
                        size_t workspace_bytes, void *stream);
 
-/* Workspace bytes needed by la2_forward (backward = 0) or la2_backward and
+/* Workspace bytes needed by la2_forward / la2_forward_state (backward = 0) or la2_backward and
  * la2_backward_saved (backward = 1) for these sizes; the backward size is never
  * smaller, so one workspace of that size serves a forward + backward step.
  * (size_t)-1 for arguments that la2_forward/la2_backward would reject. */

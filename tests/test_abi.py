@@ -102,6 +102,44 @@ def test_workspace(lib):
     assert lib.la2_workspace_bytes(1, 1, 64, 96, 64, 64, 1, 0) == ctypes.c_size_t(-1).value
 
 
+def fwds(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, s_in=P + 8 * MB, o=P + 3 * MB, s_out=P + 9 * MB, B=1, H=1,
+         T=64, d=64, dv=64, block=64, dtype=1, ws=None, wsb=0):
+    return lib.la2_forward_state(q, k, v, decay, s_in, o, s_out, B, H, T, d, dv, block, dtype, ws, wsb, None)
+
+
+def dec(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, state=P + 4 * MB, B=1, H=1, d=64, dv=64,
+        dtype=1):
+    return lib.la2_decode_step(q, k, v, decay, o, state, B, H, d, dv, dtype, None)
+
+
+def test_forward_state_validation(lib):
+    assert fwds(lib, q=None) == NULLP
+    assert fwds(lib, o=None) == NULLP
+    assert fwds(lib, T=0) == SHAPE
+    assert fwds(lib, d=96) == UNSUP
+    assert fwds(lib, s_in=P + 8 * MB + 4) == MISAL
+    assert fwds(lib, s_out=P + 9 * MB + 8) == MISAL
+    assert fwds(lib, s_out=P) == ALIAS                         # final state on top of q
+    assert fwds(lib, s_out=P + 3 * MB + 128) == ALIAS          # ... inside o
+    assert fwds(lib, s_out=P + 8 * MB + 64) == ALIAS           # partly over state_in
+    assert fwds(lib, s_in=P + 3 * MB) == ALIAS                 # o over state_in
+    assert fwds(lib, T=1024) == WS                             # split chain, no workspace
+    n = la2.la2_workspace_bytes(1, 1, 1024, 64, 64, 64, torch.bfloat16, False)
+    assert fwds(lib, T=1024, ws=P + 8 * MB, wsb=n) == ALIAS    # workspace over state_in
+
+
+def test_decode_step_validation(lib):
+    assert dec(lib, q=None) == NULLP
+    assert dec(lib, state=None) == NULLP
+    assert dec(lib, B=0) == SHAPE
+    assert dec(lib, d=32) == UNSUP
+    assert dec(lib, dtype=5) == UNSUP
+    assert dec(lib, state=P + 4 * MB + 4) == MISAL
+    assert dec(lib, o=P) == ALIAS                              # o over q
+    assert dec(lib, state=P + 2 * MB) == ALIAS                 # state over v
+    assert dec(lib, o=P + 4 * MB + 256) == ALIAS               # o inside the state
+
+
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):

@@ -1,0 +1,150 @@
+"""Carried states and one-token decode steps on the GPU, through the C ABI, against the oracle.
+
+The oracle's ``forward_state`` (pinned by the closed forms of the outputs and the final state and
+by split-and-carry invariance) is the reference.  Bars as for the plain passes: max|gpu - ref| /
+max|ref| <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs, on every output and on the final state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_amd as la2
+from causal_linear_attention_amd import inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref)
+    scale = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(np.asarray(got) - ref))) / (scale if scale > 0 else 1.0)
+
+
+def lam_of(x):
+    return None if x["decay"] is None else x["decay"].double().numpy()
+
+
+def seeded_state(B, H, d, dv, seed):
+    """A carried-in state: fp32 values both sides read exactly."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn((B, H, d, dv), generator=g) * 0.5).to(torch.float32)
+
+
+def to_dev(x):
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    decay = None if x["decay"] is None else x["decay"].to(DEV)
+    return q, k, v, decay
+
+
+CASES = [
+    # (B, H, T, d, dv, dtype, block, decay)
+    (1, 2, 777, 128, 128, "bf16", 128, "heads"),      # split chains, ragged last tile
+    (1, 2, 50, 128, 128, "bf16", 128, "heads"),       # one short tile
+    (2, 3, 700, 64, 128, "bf16", 64, "heads"),        # direct-to-LDS path
+    (1, 3, 333, 128, 64, "bf16", 256, "none"),
+    (16, 16, 200, 128, 128, "bf16", 128, "heads"),    # 256 chains: unsplit, state read at the start
+    (1, 2, 300, 64, 64, "f32", 32, "heads"),
+    (16, 16, 70, 64, 64, "f32", 64, "none"),          # fp32, unsplit
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}T{c[2]}d{c[3]}dv{c[4]}{c[5]}tb{c[6]}{c[7]}")
+def test_forward_state_matches_oracle(case):
+    B, H, T, d, dv, dtype, block, decay = case
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=61 + T, decay=decay, backward=False)
+    s_in = seeded_state(B, H, d, dv, 7 + T)
+    q, k, v, dec = to_dev(x)
+    o, s_out = la2.forward_state(q, k, v, dec, block, state_in=s_in.to(DEV))
+    ref_o, ref_s = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), f64(s_in))
+    torch.cuda.synchronize()
+    eo, es = rel_err(f64(o), ref_o), rel_err(f64(s_out), ref_s)
+    print(case, f"o {eo:.2e} state {es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    # without a carried-in state: the plain forward's o, and the final state from zero
+    o0, s0 = la2.forward_state(q, k, v, dec, block)
+    ref_o0, ref_s0 = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), None)
+    torch.cuda.synchronize()
+    assert rel_err(f64(o0), ref_o0) <= TOL[dtype] and rel_err(f64(s0), ref_s0) <= TOL[dtype]
+    assert torch.equal(o0, la2.forward(q, k, v, dec, block))
+
+
+@pytest.mark.parametrize("seg_tiles,slice_width", [("1", None), ("3", None), (None, "64"), ("2", "64")])
+def test_forward_state_plans(seg_tiles, slice_width, monkeypatch):
+    """Forced segment splits (prefix with a carried-in state) and 64-wide value slices."""
+    if seg_tiles:
+        monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    if slice_width:
+        monkeypatch.setenv("LA2_SLICE_WIDTH", slice_width)
+    x = inputs.make_random(2, 2, 600, 128, 128, dtype="bf16", seed=71, decay="heads", backward=False)
+    s_in = seeded_state(2, 2, 128, 128, 73)
+    q, k, v, dec = to_dev(x)
+    o, s_out = la2.forward_state(q, k, v, dec, 128, state_in=s_in.to(DEV))
+    ref_o, ref_s = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), f64(s_in))
+    torch.cuda.synchronize()
+    assert rel_err(f64(o), ref_o) <= 2e-2 and rel_err(f64(s_out), ref_s) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,d,dv,block", [("bf16", 128, 128, 128), ("bf16", 64, 128, 64), ("f32", 64, 64, 64)])
+def test_chunked_prefill_in_place(dtype, d, dv, block):
+    """A sequence run in uneven chunks, one state buffer updated in place, equals the whole run."""
+    B, H, T = 1, 4, 1000
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=83, decay="heads", backward=False)
+    q, k, v, dec = to_dev(x)
+    state = torch.zeros((B, H, d, dv), dtype=torch.float32, device=DEV)
+    outs, t = [], 0
+    for n in (300, 1, 450, 249):
+        sl = slice(t, t + n)
+        qc, kc, vc = (a[:, :, sl].contiguous() for a in (q, k, v))
+        oc = torch.empty_like(vc)
+        ws = la2.workspace_for(qc, vc, block, False)
+        la2.la2_forward_state(qc, kc, vc, dec, state, oc, state, block, ws)
+        outs.append(oc)
+        t += n
+    ref_o, ref_s = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), None)
+    torch.cuda.synchronize()
+    assert rel_err(f64(torch.cat(outs, dim=2)), ref_o) <= TOL[dtype]
+    assert rel_err(f64(state), ref_s) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,dv,decay", [("bf16", 128, 128, "heads"), ("bf16", 64, 128, "none"),
+                                              ("bf16", 128, 64, "heads"), ("f32", 64, 64, "heads"),
+                                              ("f32", 128, 128, "none")])
+def test_decode_steps_continue_a_prefill(dtype, d, dv, decay):
+    """Prefill T0 positions with la2_forward_state, then generate 6 positions with la2_decode_step;
+    outputs and final state against the oracle's whole-sequence run."""
+    B, H, T0, N = 2, 3, 257, 6
+    x = inputs.make_random(B, H, T0 + N, d, dv, dtype=dtype, seed=97 + d + dv, decay=decay, backward=False)
+    q, k, v, dec = to_dev(x)
+    block = 128 if dtype == "bf16" else 64
+    _, state = la2.forward_state(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                                 dec, block)
+    outs = []
+    for t in range(T0, T0 + N):
+        outs.append(la2.decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                                    state, dec))
+    ref_o, ref_s = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), None)
+    torch.cuda.synchronize()
+    got = torch.stack(outs, dim=2)
+    eo, es = rel_err(f64(got), ref_o[:, :, T0:]), rel_err(f64(state), ref_s)
+    print(dtype, d, dv, decay, f"o {eo:.2e} state {es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_step_from_zero_is_one_position():
+    """From a zero state a decode step is the one-position forward: o = (k . q) v."""
+    x = inputs.make_random(3, 5, 1, 128, 64, dtype="bf16", seed=5, decay="heads", backward=False)
+    q, k, v, dec = to_dev(x)
+    state = torch.zeros((3, 5, 128, 64), dtype=torch.float32, device=DEV)
+    o = la2.decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(), state, dec)
+    ref = oracle.forward(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x))[:, :, 0]
+    torch.cuda.synchronize()
+    assert rel_err(f64(o), ref) <= 2e-2
+    assert rel_err(f64(state), np.einsum("bhi,bhj->bhij", f64(x["k"])[:, :, 0], f64(x["v"])[:, :, 0])) <= 1e-6
