@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=64,
                     help="sequences of the 1K point the oracle runs for the CPU baseline")
+    ap.add_argument("--decode", action="store_true",
+                    help="time la2_decode_step (one new token per sequence from a carried state) instead")
+    ap.add_argument("--decode-batch", type=int, default=512,
+                    help="sequences per decode step (512 x 16 heads: 512 MiB of fp32 state, beyond the "
+                         "256 MiB memory-side cache)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -61,6 +66,59 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * src.element_size(), "copies": 5}))
+
+
+def decode_bench(args):
+    """One generated token per sequence: B sequences (default 512) x H = 16 heads, d = d_v = 128, bf16
+    q/k/v/o, fp32 state (the carried summary of each sequence's prefix), per-head decay.  Each step
+    reads and rewrites every state once, so it is HBM-bound: bytes per step = chains x (8 d d_v +
+    2 (2d + 2d_v)).  Below ~256 MiB of state (B <= 256) the states stay in the memory-side cache."""
+    import torch
+    import causal_linear_attention_amd as la2
+    from causal_linear_attention_amd import inputs
+    B, H, d, dv = args.decode_batch, 16, 128, 128
+    g = torch.Generator().manual_seed(5)
+    dev = torch.device("cuda:0")
+    steps_in = [[(torch.randn((B, H, n), generator=g) / math.sqrt(n)).to(torch.bfloat16).to(dev)
+                 for n in (d, d, dv)] for _ in range(4)]
+    decay = inputs.head_decays(H).to(dev)
+    state = (torch.randn((B, H, d, dv), generator=g) * 0.1).to(dev)
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v = steps_in[i % 4]
+        la2.la2_decode_step(q, k, v, decay, o, state, stream)
+
+    for i in range(max(args.warmup, 1) * 10):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(args.steps, 1) * 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / n
+    chains = B * H
+    bytes_step = chains * (8 * d * dv + 2 * (2 * d + 2 * dv))
+    achieved = bytes_step / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "decode tokens/sec (one new token per sequence from a carried state)", "value": round(B / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": max(args.warmup, 1) * 10,
+        "ms_per_step": round(ms, 5), "wall_ms_per_step": round(wall / n * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 q/k/v/o, f32 state", "data": "synthetic",
+        "config": {"workload": f"decode step: B={B} sequences, H={H}, d=d_v={d}, per-head decay, fp32 state",
+                   "chains": chains, "state_MiB": chains * d * dv * 4 >> 20,
+                   "cache_resident": chains * d * dv * 4 <= (256 << 20), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<bf16,D=128,DV=128>", "avg_launch_ms": round(ms, 5),
+                     "algorithmic_bytes_per_launch": bytes_step},
+    }), flush=True)
 
 
 def algorithmic(w):
@@ -81,6 +139,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode:
+        decode_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
