@@ -121,6 +121,17 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, u16 *dst, int
     }
 }
 
+// Lanes l and l + 32 (h = l / 32) hold the two 8-byte halves (h = 0 the first) of the 16-byte
+// chunks `a` and `b`.  Returns chunk `a` whole in lanes 0..31 and chunk `b` whole in lanes 32..63.
+// v_permlane32_swap(x, y) leaves, in lane l < 32, (x of lane l, x of lane l + 32) and, in lane
+// l >= 32, (y of lane l - 32, y of lane l): one swap per dword pairs up the halves.
+__device__ __forceinline__ u32x4 join_halves(const u32x2 &a, const u32x2 &b) {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+    const u32x4 w = {r0[0], r1[0], r0[1], r1[1]};
+    return w;
+}
+
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier for LDS hand-over only: waits for this wave's LDS operations, not for its

@@ -150,13 +150,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
 #pragma unroll
         for (int s = 0; s < C::SPW; ++s) {
             const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+            // the halves of chunks j = 2jp and 2jp + 1 (d = kb*32 + 8j + 4h + 0..3) are paired across h,
+            // so each lane writes one whole 16-byte chunk (no bank conflicts)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = kb * 32 + 8 * j + 4 * h;
-                u32x2 pk;
-                pk[0] = pack_bf16(sacc[s][4 * j + 0], sacc[s][4 * j + 1]);
-                pk[1] = pack_bf16(sacc[s][4 * j + 2], sacc[s][4 * j + 3]);
-                *reinterpret_cast<u32x2 *>(smem + C::oST + nat_off<D>(nb * 32 + col, d >> 3) + (d & 7)) = pk;
+            for (int jp = 0; jp < 2; ++jp) {
+                u32x2 a, b;
+                a[0] = pack_bf16(sacc[s][8 * jp + 0], sacc[s][8 * jp + 1]);
+                a[1] = pack_bf16(sacc[s][8 * jp + 2], sacc[s][8 * jp + 3]);
+                b[0] = pack_bf16(sacc[s][8 * jp + 4], sacc[s][8 * jp + 5]);
+                b[1] = pack_bf16(sacc[s][8 * jp + 6], sacc[s][8 * jp + 7]);
+                lds_write(smem + C::oST, nat_off<D>(nb * 32 + col, kb * 4 + 2 * jp + h), join_halves(a, b));
             }
         }
     };
@@ -282,20 +285,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * D, (T - t0) * D * 2);
         constexpr int NC = C::OSW / 8;
         u16 *ob = smem + C::oOS + wave * 32 * C::OSW;
+        // 16 lanes writing one chunk of 16 consecutive rows (or reading whole rows) hit 16 bank groups
+        auto oswz = [&](int row) { return (row / (16 / NC)) & (NC - 1); };
 #pragma unroll
         for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x2 pk;
-                pk[0] = pack_bf16(oacc[n][4 * j], oacc[n][4 * j + 1]);
-                pk[1] = pack_bf16(oacc[n][4 * j + 2], oacc[n][4 * j + 3]);
-                const int ch = (n * 32 + 8 * j) >> 3;
-                *reinterpret_cast<u32x2 *>(ob + col * C::OSW + ((ch ^ (col & (NC - 1))) << 3) + 4 * h) = pk;
+            for (int jp = 0; jp < 2; ++jp) {
+                u32x2 a, b;
+                a[0] = pack_bf16(oacc[n][8 * jp + 0], oacc[n][8 * jp + 1]);
+                a[1] = pack_bf16(oacc[n][8 * jp + 2], oacc[n][8 * jp + 3]);
+                b[0] = pack_bf16(oacc[n][8 * jp + 4], oacc[n][8 * jp + 5]);
+                b[1] = pack_bf16(oacc[n][8 * jp + 6], oacc[n][8 * jp + 7]);
+                const int ch = 4 * n + 2 * jp + h;
+                lds_write(ob, col * C::OSW + ((ch ^ oswz(col)) << 3), join_halves(a, b));
             }
 #pragma unroll
         for (int s2 = 0; s2 < 32 * NC / 64; ++s2) {
             const int qd = lane + 64 * s2, row = qd / NC, ch = qd % NC;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::OSW + ((ch ^ (row & (NC - 1))) << 3));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::OSW + ((ch ^ oswz(row)) << 3));
             bstore16(ry, ((tb * 32 + row) * D + db0 * 32 + ch * 8) * 2, v);
         }
     };
