@@ -45,7 +45,7 @@ def parse():
                     help="time one named workload of inputs.WORKLOADS (e.g. tnl15b_layer, long128k_outliers) "
                          "instead of the length sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=64,
+    ap.add_argument("--cpu-sample-seqs", type=int, default=128,
                     help="sequences of the 1K point the oracle runs for the CPU baseline")
     ap.add_argument("--decode", action="store_true",
                     help="time la2_decode_step (one new token per sequence from a carried state) instead")
