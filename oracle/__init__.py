@@ -12,7 +12,9 @@ Two independent formulations live here, both in fp64:
   prefix-sum recurrence, with identity feature map and no denominator), and its
   chain-rule backward with the reverse sweep R_t = lam R_{t+1} + q_t do_t^T.
   ``forward_rows`` / ``backward_rows`` evaluate single rows from the closed
-  sums, for spot checks of very long sequences.
+  sums, for spot checks of very long sequences.  ``forward_normalized`` is
+  the same section's whole output, phi(q)^T S / phi(q)^T z with the
+  denominator sum z_t = lam z_{t-1} + phi(k_t) and phi = identity or elu + 1.
 * ``tiled_forward`` / ``tiled_backward`` (numpy, this file): the same page's
   section 2 derivation in its own order -- Step 1 split of each output row
   into an intra-tile and an inter-tile part, Step 2 the masked left product
@@ -51,6 +53,8 @@ def _bind(lib):
     lib.la2_oracle_forward.restype = None
     lib.la2_oracle_forward_state.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     lib.la2_oracle_forward_state.restype = None
+    lib.la2_oracle_forward_normalized.argtypes = [I, I, I, I, P, P, P, P, ctypes.c_int, P]
+    lib.la2_oracle_forward_normalized.restype = None
     lib.la2_oracle_backward.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
     lib.la2_oracle_backward.restype = None
     lib.la2_oracle_forward_rows.argtypes = [I, I, I, ctypes.c_double, P, P, P, I,
@@ -113,6 +117,18 @@ class Oracle:
                                           None if s_in is None else _ptr(s_in), _ptr(o), _ptr(s_out))
         return o, s_out
 
+    def forward_normalized(self, q, k, v, lam=None, feature_map="elu1"):
+        """Normalized output phi(q)^T S / phi(q)^T z with phi = identity or elu + 1."""
+        fmap = {"identity": 0, "elu1": 1}[feature_map]
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, T, d = q.shape
+        dv = v.shape[-1]
+        o = np.empty((B, H, T, dv), dtype=np.float64)
+        lams = _chain_lams(lam, B, H)
+        self.lib.la2_oracle_forward_normalized(B * H, T, d, dv, _ptr(lams), _ptr(q), _ptr(k), _ptr(v), fmap,
+                                               _ptr(o))
+        return o
+
     def backward(self, q, k, v, do, lam=None):
         """(dq, dk, dv) of <o, do> via the forward and reverse recurrences."""
         q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -171,6 +187,10 @@ def forward(q, k, v, lam=None):
 
 def forward_state(q, k, v, lam=None, state_in=None):
     return load().forward_state(q, k, v, lam, state_in)
+
+
+def forward_normalized(q, k, v, lam=None, feature_map="elu1"):
+    return load().forward_normalized(q, k, v, lam, feature_map)
 
 
 def backward(q, k, v, do, lam=None):

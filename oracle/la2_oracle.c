@@ -23,6 +23,10 @@
  *   R_t  = lam * R_{t+1} + q_t do_t^T,  R_{T+1} = 0  (reverse sweep)
  *   dk_t = R_t v_t,   dv_t = R_t^T k_t
  *
+ * la2_oracle_forward_normalized is the full output of the same section 1, numerator
+ * over denominator, with a feature map phi (identity, or elu + 1) and the decay
+ * applied to the denominator's prefix sum z_t = lam z_{t-1} + phi(k_t) as to S.
+ *
  * The *_rows entry points evaluate the same quantities one output row at a
  * time from the closed sums
  *   o_t  = sum_{s<=t} lam^{t-s} (q_t . k_s) v_s
@@ -95,6 +99,61 @@ void la2_oracle_forward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
                         const double *v, double *o)
 {
     la2_oracle_forward_state(n_chains, T, d, dv, lam, q, k, v, NULL, o, NULL);
+}
+
+/* ---- normalized form with a feature map ------------------------------- */
+
+/* The feature map phi applied elementwise: 0 = identity (the default configuration named on the
+ * "Lightning Attention" page, section 2), 1 = elu(x) + 1 (x + 1 for x > 0, e^x otherwise), a
+ * strictly positive map as in the linear-transformer lineage that page builds on (section 1). */
+static double feature(double x, int fmap)
+{
+    if (fmap == 1)
+        return x > 0.0 ? x + 1.0 : exp(x);
+    return x;
+}
+
+/* Normalized output of the same page, section 1 (numerator over denominator, both prefix sums of
+ * phi(k)), with the decay applied to both recurrences:
+ *   S_t = lam S_{t-1} + phi(k_t) v_t^T,   z_t = lam z_{t-1} + phi(k_t),
+ *   o_t = (S_t^T phi(q_t)) / (z_t . phi(q_t)).
+ * No epsilon: with a strictly positive phi the denominator is positive. */
+void la2_oracle_forward_normalized(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                                   const double *lam, const double *q, const double *k,
+                                   const double *v, int fmap, double *o)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_chains; ++c) {
+        const double l = lam[c];
+        double *S = (double *)calloc((size_t)(d * dv), sizeof(double));
+        double *z = (double *)calloc((size_t)d, sizeof(double));
+        double *pq = (double *)malloc((size_t)d * sizeof(double));
+        double *pk = (double *)malloc((size_t)d * sizeof(double));
+        for (int64_t t = 0; t < T; ++t) {
+            const double *qt = q + (c * T + t) * d, *kt = k + (c * T + t) * d, *vt = v + (c * T + t) * dv;
+            for (int64_t i = 0; i < d; ++i) {
+                pq[i] = feature(qt[i], fmap);
+                pk[i] = feature(kt[i], fmap);
+            }
+            double den = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                z[i] = l * z[i] + pk[i];
+                den += z[i] * pq[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = l * S[i * dv + j] + pk[i] * vt[j];
+            }
+            for (int64_t j = 0; j < dv; ++j) {
+                double num = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    num += S[i * dv + j] * pq[i];
+                o[(c * T + t) * dv + j] = num / den;
+            }
+        }
+        free(S);
+        free(z);
+        free(pq);
+        free(pk);
+    }
 }
 
 void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,

@@ -260,6 +260,47 @@ def pin_state_split_carry(orc):
         _close(sb, s_all, 1e-12, f"state after split at {cut}")
 
 
+def _elu1(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def pin_normalized_bruteforce(orc):
+    """Normalized form == ((Psi Phi^T (.) D) V) / ((Psi Phi^T (.) D) 1) row by row, Psi = phi(Q),
+    Phi = phi(K) (the page's section 1 ratio written as one masked product; numpy)."""
+    q, k, v, _, lam = _setup(131, B=2, H=3, T=31, d=5, dv=4)
+    for fmap, phi in (("elu1", _elu1), ("identity", lambda x: x)):
+        qq, kk = (q, k) if fmap == "elu1" else (np.abs(q) + 0.5, np.abs(k) + 0.5)   # positive denominators
+        got = orc.forward_normalized(qq, kk, v, lam, fmap)
+        for b in range(2):
+            for h in range(3):
+                A = (phi(qq[b, h]) @ phi(kk[b, h]).T) * _decay_matrix(31, lam[h])
+                _close(got[b, h], (A @ v[b, h]) / A.sum(axis=1, keepdims=True), 1e-12, f"normalized {fmap}")
+
+
+def pin_normalized_invariants(orc):
+    """With v = 1 every output is exactly 1 (a weighted average of ones); in general each output
+    lies within the range of the values seen so far (positive weights summing to 1)."""
+    q, k, v, _, lam = _setup(137, B=1, H=3, T=40, d=6, dv=5)
+    ones = np.ones_like(v)
+    _close(orc.forward_normalized(q, k, ones, lam, "elu1"), ones, 1e-13, "weights sum to one")
+    o = orc.forward_normalized(q, k, v, lam, "elu1")
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12), "outputs outside the running value range"
+    # the map itself: phi(x) = x + 1 above 0, e^x at or below 0.  One position, one key: with
+    # k = 0 the denominator is phi(0) . phi(q) and the output is v whatever phi is, so the map is
+    # read off the two-position case instead: o_1 = (a v_0 + b v_1) / (a + b) with a = phi(k_0) phi(q_1)
+    # and b = phi(k_1) phi(q_1) for d = 1, no decay.
+    for k0, k1 in ((2.5, -1.0), (-0.5, 0.0), (0.25, 3.0)):
+        qq = np.array([0.3, 0.7]).reshape(1, 1, 2, 1)
+        kk = np.array([k0, k1]).reshape(1, 1, 2, 1)
+        vv = np.array([1.0, 0.0]).reshape(1, 1, 2, 1)
+        a, b_ = _elu1(np.array(k0)), _elu1(np.array(k1))
+        got = orc.forward_normalized(qq, kk, vv, None, "elu1")[0, 0, 1, 0]
+        _close(got, a / (a + b_), 1e-14, "elu + 1 feature values")
+    _close(_elu1(np.array([2.5, -1.0, 0.0])), [3.5, np.exp(-1.0), 1.0], 1e-15, "elu + 1 values")
+
+
 ALL_PINS = [
     pin_golden_handworked,
     pin_bruteforce_forward,
@@ -275,4 +316,6 @@ ALL_PINS = [
     pin_rows,
     pin_state_closed_form,
     pin_state_split_carry,
+    pin_normalized_bruteforce,
+    pin_normalized_invariants,
 ]

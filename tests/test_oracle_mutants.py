@@ -48,6 +48,15 @@ MUTANTS = [
     ("state_out_before_last_step",
      "        if (s_out)\n            for (int64_t i = 0; i < d; ++i)",
      "        if (s_out && T > 0) { for (int64_t i = 0; i < d * dv; ++i) S[i] -= kc[(T - 1) * d + i / dv] * vc[(T - 1) * dv + i % dv]; }\n        if (s_out)\n            for (int64_t i = 0; i < d; ++i)"),
+    ("normalized_denominator_no_decay",
+     "z[i] = l * z[i] + pk[i];",
+     "z[i] = z[i] + pk[i];"),
+    ("normalized_feature_branch_swapped",
+     "return x > 0.0 ? x + 1.0 : exp(x);",
+     "return x > 0.0 ? exp(x) : x + 1.0;"),
+    ("normalized_query_feature_skipped",
+     "pq[i] = feature(qt[i], fmap);",
+     "pq[i] = qt[i];"),
     ("rows_skip_diagonal",
      "for (int64_t s = 0; s <= t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q",
      "for (int64_t s = 0; s < t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q"),
