@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--decode-batch", type=int, default=512,
                     help="sequences per decode step (512 x 16 heads: 512 MiB of fp32 state, beyond the "
                          "256 MiB memory-side cache)")
+    ap.add_argument("--normalized", action="store_true",
+                    help="time la2_forward_normalized (numerator over denominator, phi = elu + 1) on the 1K "
+                         "point of the sweep instead, with the plain forward timed beside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -121,6 +124,59 @@ def decode_bench(args):
     }), flush=True)
 
 
+def normalized_bench(args):
+    """The normalized forward o_t = phi(q_t)^T S_t / phi(q_t)^T z_t with phi = elu + 1 on the 1K point
+    of the length sweep (B = 128, H = 16, T = 1024, d = d_v = 128, bf16, no decay).  Its algorithmic
+    bytes are those of the plain forward (read q, k, v; write o): 4 d e per token-head; the library
+    takes three passes (denominator writing phi(q), phi(k); numerator scan; division), so the extra
+    traffic shows as a lower roofline fraction."""
+    import torch
+    import causal_linear_attention_amd as la2
+    from causal_linear_attention_amd import inputs
+    w = inputs.WORKLOADS["sweep131k_t1k"]
+    x = inputs.make(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    decay = None if x["decay"] is None else x["decay"].to(dev)
+    o = torch.empty_like(v)
+    ws_n = la2.normalized_workspace_for(q, v, "elu1", w.block)
+    ws_f = la2.workspace_for(q, v, w.block, False)
+    stream = torch.cuda.current_stream()
+    n = max(args.steps, 1) * 10
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1) * 3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_n = timed(lambda: la2.la2_forward_normalized(q, k, v, decay, o, "elu1", w.block, ws_n, stream))
+    ms_f = timed(lambda: la2.la2_forward(q, k, v, decay, o, w.block, ws_f, stream))
+    th = w.B * w.H * w.T
+    byts = th * 4 * w.d * 2
+    achieved = byts / (ms_n * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "normalized forward tokens/sec (phi = elu + 1, numerator / denominator)",
+        "value": round(w.B * w.T / (ms_n * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": max(args.warmup, 1) * 3, "ms_per_step": round(ms_n, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B}, H={w.H}, T={w.T}, d=d_v={w.d}, T_B={w.block}, no decay",
+                   "parallelism": "none (1 GPU)"},
+        "plain_forward_ms": round(ms_f, 5),
+        "plain_forward_tokens_per_s": round(w.B * w.T / (ms_f * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "la2_forward_normalized (denominator + numerator scan + division launches)",
+                     "avg_launch_ms": round(ms_n, 5), "algorithmic_bytes_per_launch": byts},
+    }), flush=True)
+
+
 def algorithmic(w):
     """Algorithmic bytes and flops of one forward and one backward over workload w (per call)."""
     th = w.B * w.H * w.T                      # token-heads
@@ -142,6 +198,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.normalized:
+        normalized_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

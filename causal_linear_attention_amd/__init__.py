@@ -10,16 +10,20 @@ from .binding import (  # noqa: F401
     backward,
     decode_step,
     forward,
+    forward_normalized,
     forward_state,
     la2_abi_version,
     la2_backward,
     la2_backward_saved,
     la2_decode_step,
     la2_forward,
+    la2_forward_normalized,
     la2_forward_state,
+    la2_normalized_workspace_bytes,
     la2_status_string,
     la2_workspace_bytes,
     lightning_attention,
     load_library,
+    normalized_workspace_for,
     workspace_for,
 )

@@ -16,8 +16,13 @@ LA2_F32 = 0
 LA2_BF16 = 1
 _DTYPES = {torch.float32: LA2_F32, torch.bfloat16: LA2_BF16}
 
-EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_backward", "la2_backward_saved",
-           "la2_workspace_bytes", "la2_status_string", "la2_abi_version")
+LA2_PHI_IDENTITY = 0
+LA2_PHI_ELU1 = 1
+_FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
+
+EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_backward",
+           "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
+           "la2_abi_version")
 
 _lib = None
 
@@ -47,6 +52,10 @@ def load_library(path=LIB_PATH):
     lib.la2_forward_state.restype = i32
     lib.la2_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la2_decode_step.restype = i32
+    lib.la2_forward_normalized.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]
+    lib.la2_forward_normalized.restype = i32
+    lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.la2_normalized_workspace_bytes.restype = sz
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.la2_workspace_bytes.restype = sz
     lib.la2_status_string.argtypes = [i32]
@@ -78,6 +87,23 @@ def la2_workspace_bytes(B, H, T, d, d_v, block, dtype, backward):
     n = load_library().la2_workspace_bytes(B, H, T, d, d_v, block, code, 1 if backward else 0)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported sizes for la2_workspace_bytes")
+    return n
+
+
+def feature_map_code(feature_map):
+    if isinstance(feature_map, int):
+        return feature_map
+    try:
+        return _FMAPS[feature_map]
+    except KeyError:
+        raise ValueError(f"unknown feature map {feature_map!r}; use 'identity' or 'elu1'") from None
+
+
+def la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map, block, dtype):
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    n = load_library().la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map_code(feature_map), block, code)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported arguments for la2_normalized_workspace_bytes")
     return n
 
 
@@ -156,6 +182,19 @@ def la2_decode_step(q, k, v, decay, o, state, stream=None):
         raise LA2Error(st, "la2_decode_step")
 
 
+def la2_forward_normalized(q, k, v, decay, o, feature_map, block, workspace=None, stream=None):
+    """Enqueue the normalized output o = phi(q)^T S / phi(q)^T z (feature_map 'identity' or 'elu1')."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_forward_normalized(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
+        B, H, T, d, d_v, feature_map_code(feature_map), int(block), dtype_code(q.dtype),
+        _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_forward_normalized")
+
+
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
     la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
@@ -213,6 +252,22 @@ def forward_state(q, k, v, decay=None, block=128, state_in=None, workspace=None)
         workspace = workspace_for(q, v, block, False)
     la2_forward_state(q, k, v, decay, state_in, o, state_out, block, workspace)
     return o, state_out
+
+
+def normalized_workspace_for(q, v, feature_map, block):
+    B, H, T, d = q.shape
+    n = la2_normalized_workspace_bytes(B, H, T, d, v.shape[-1], feature_map, block, q.dtype)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def forward_normalized(q, k, v, decay=None, block=128, feature_map="elu1", workspace=None):
+    """Allocate o (and the workspace if none is given) and run the normalized forward."""
+    _check_same(q, k, v)
+    o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = normalized_workspace_for(q, v, feature_map, block)
+    la2_forward_normalized(q, k, v, decay, o, feature_map, block, workspace)
+    return o
 
 
 def decode_step(q, k, v, state, decay=None):

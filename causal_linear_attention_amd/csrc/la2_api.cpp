@@ -290,6 +290,127 @@ int la2_decode_step(const void *q, const void *k, const void *v, const float *de
 
 namespace {
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Segments of the denominator pass: enough (chain, segment) workgroups to give every compute unit
+// about 8, each segment at least 256 positions and a multiple of the kernel's 64-position chunk.
+// LA2_NORM_SEGMENT forces the segment length (positions).
+struct DenPlan {
+    int64_t seg_len;
+    int nseg;
+};
+
+DenPlan den_plan(int64_t chains, int64_t T) {
+    int64_t nseg = 1;
+    if (chains < 8 * kComputeUnits) {
+        nseg = (8 * kComputeUnits + chains - 1) / chains;
+        const int64_t most = (T + 255) / 256;
+        if (nseg > most) nseg = most;
+    }
+    int64_t seg_len = (T + nseg - 1) / nseg;
+    if (const char *env = std::getenv("LA2_NORM_SEGMENT")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) seg_len = v;
+    }
+    seg_len = (seg_len + 63) / 64 * 64;
+    return DenPlan{seg_len, (int)((T + seg_len - 1) / seg_len)};
+}
+
+// Workspace of the normalized forward: [phi(q)][phi(k)] (elu + 1 only), [den, fp32 per position],
+// [segment sums of phi(k)] (split chains only), [the numerator scan's own workspace]; every part
+// 256-byte aligned.
+struct NormLayout {
+    size_t phi;        // bytes of each of phi(q), phi(k)
+    size_t den_off;
+    size_t z_off, z_bytes;
+    size_t scan_off, scan_bytes;
+    size_t total;
+    DenPlan dp;
+};
+
+NormLayout norm_layout(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int fmap, int block, int dtype) {
+    NormLayout L{};
+    const int64_t chains = B * H;
+    L.phi = fmap ? align256((size_t)(chains * T * d) * elem_size(dtype)) : 0;
+    L.dp = den_plan(chains, T);
+    L.den_off = 2 * L.phi;
+    L.z_off = L.den_off + align256((size_t)(chains * T) * sizeof(float));
+    L.z_bytes = L.dp.nseg > 1 ? align256((size_t)chains * (L.dp.nseg - 1) * d * sizeof(float)) : 0;
+    L.scan_off = L.z_off + L.z_bytes;
+    L.scan_bytes = make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
+    L.total = L.scan_off + L.scan_bytes;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la2_normalized_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int feature_map,
+                                      int block, int dtype) {
+    if (check_sizes(B, H, T, d, d_v, block, dtype) != LA2_OK || (feature_map != 0 && feature_map != 1))
+        return (size_t)-1;
+    return norm_layout(B, H, T, d, d_v, feature_map, block, dtype).total;
+}
+
+int la2_forward_normalized(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B,
+                           int64_t H, int64_t T, int64_t d, int64_t d_v, int feature_map, int block, int dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (feature_map != LA2_PHI_IDENTITY && feature_map != LA2_PHI_ELU1) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
+    int st = check_sizes(B, H, T, d, d_v, block, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (workspace && !aligned16(workspace)) ||
+        (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const NormLayout L = norm_layout(B, H, T, d, d_v, feature_map, block, dtype);
+    const Range ins[4] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                          range_of(decay, decay ? (size_t)H * 4 : 0)};
+    const Range ro = range_of(o, nv);
+    for (const Range &r : ins)
+        if (overlap(ro, r)) return LA2_ERR_ALIAS;
+    if (L.total) {
+        if (!workspace || workspace_bytes < L.total) return LA2_ERR_WORKSPACE_TOO_SMALL;
+        const Range rw = range_of(workspace, L.total);
+        if (overlap(rw, ro)) return LA2_ERR_ALIAS;
+        for (const Range &r : ins)
+            if (overlap(rw, r)) return LA2_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const int64_t chains = B * H;
+    // 1. denominator den_t = phi(q_t) . z_t (fp32), and phi(q), phi(k) for the numerator
+    la2::DenArgs a{};
+    a.q = q;
+    a.k = k;
+    a.pq = L.phi ? ws : nullptr;
+    a.pk = L.phi ? ws + L.phi : nullptr;
+    a.den = reinterpret_cast<float *>(ws + L.den_off);
+    a.decay = decay;
+    a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.z_off) : nullptr;
+    a.T = T;
+    a.seg_len = L.dp.seg_len;
+    a.H = (int)H;
+    a.nseg = L.dp.nseg;
+    a.chains = (int)chains;
+    if (a.nseg > 1 && la2::launch_denominator(a, (int)d, dtype, feature_map, false, s) != hipSuccess)
+        return LA2_ERR_HIP;
+    if (la2::launch_denominator(a, (int)d, dtype, feature_map, true, s) != hipSuccess) return LA2_ERR_HIP;
+    // 2. numerator: the plain scan on phi(q), phi(k)
+    st = forward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block,
+                      dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream);
+    if (st != LA2_OK) return st;
+    // 3. o_t /= den_t
+    return la2::launch_divide(o, a.den, chains * T, (int)d_v, dtype, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
 // reuse_s: the S segment states that la2_forward left at the start of the workspace are still there.
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,

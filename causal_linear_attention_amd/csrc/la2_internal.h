@@ -52,6 +52,25 @@ hipError_t launch_segment_prefix(float *states, const float *decay, int chains, 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
                          int chains, int H, int D, int DV, int dtype, hipStream_t s);
 
+// Normalized output (feature map phi: 0 identity, 1 elu + 1).  launch_denominator with
+// norm = false writes each segment's decayed sum of phi(k) (all segments but the last); with
+// norm = true it writes den_t = phi(q_t) . z_t for every position, and phi(q), phi(k) when pq and pk
+// are given (elu + 1), which the numerator scan then reads.  launch_divide divides o by den.
+struct DenArgs {
+    const void *q, *k;     // [chains, T, D], phi applied inside
+    void *pq, *pk;         // [chains, T, D] phi(q), phi(k) out, or nullptr
+    float *den;            // fp32 [chains, T] out
+    const float *decay;    // [H] or nullptr (lam = 1)
+    float *zseg;           // fp32 [chains, nseg - 1, D]
+    int64_t T;
+    int64_t seg_len;       // positions per segment, a multiple of 64
+    int H;
+    int nseg;
+    int chains;
+};
+hipError_t launch_denominator(const DenArgs &a, int D, int dtype, int fmap, bool norm, hipStream_t s);
+hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s);
+
 // Which (D, DV, TB) the kernels are compiled for.
 bool bf16_supported(int D, int DV, int TB);
 bool f32_supported(int D, int DV, int TB);

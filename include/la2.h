@@ -59,9 +59,15 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 3
+#define LA2_ABI_VERSION 4
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
+
+/* Feature maps of the normalized forward (la2_forward_normalized). */
+enum la2_feature_map {
+    LA2_PHI_IDENTITY = 0,   /* phi(x) = x */
+    LA2_PHI_ELU1 = 1        /* phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise (strictly positive) */
+};
 
 enum la2_status {
     LA2_OK = 0,
@@ -116,6 +122,33 @@ int la2_forward_state(const void *q, const void *k, const void *v, const float *
 int la2_decode_step(const void *q, const void *k, const void *v, const float *decay, void *o,
                     float *state, int64_t B, int64_t H, int64_t d, int64_t d_v, int dtype,
                     void *stream);
+
+/* Normalized forward: the whole output of page "Lightning Attention", section 1,
+ * numerator over denominator, with a feature map applied to q and k and the
+ * decay applied to both prefix sums:
+ *     S_t = lam S_{t-1} + phi(k_t) v_t^T,   z_t = lam z_{t-1} + phi(k_t),
+ *     o_t = S_t^T phi(q_t) / (z_t . phi(q_t)).
+ *   feature_map: enum la2_feature_map.  With LA2_PHI_ELU1 every weight is
+ *   positive, so o_t is a weighted average of v_0..v_t; with
+ *   LA2_PHI_IDENTITY (the pages' default map) the denominator can vanish or
+ *   change sign and is not guarded (a zero gives inf or NaN, as the formula
+ *   does).  The numerator runs through the same tiled scan as la2_forward
+ *   (on phi(q), phi(k) rounded to `dtype`) and is stored in o; the
+ *   denominator is accumulated in fp32 from phi in fp32, and o is then
+ *   divided by it in fp32 and rounded to `dtype` again.
+ *   Other arguments as in la2_forward; workspace: at least
+ *   la2_normalized_workspace_bytes(...) bytes (phi(q) and phi(k) for
+ *   LA2_PHI_ELU1, one fp32 denominator per position, per-segment sums and
+ *   the numerator's own workspace; never 0).  No backward is provided. */
+int la2_forward_normalized(const void *q, const void *k, const void *v, const float *decay, void *o,
+                           int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int feature_map,
+                           int block, int dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Workspace bytes needed by la2_forward_normalized for these arguments;
+ * (size_t)-1 for arguments it would reject. */
+size_t la2_normalized_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
+                                      int feature_map, int block, int dtype);
 
 /* Backward: gradients of <o, dout> with respect to q, k and v.
  *   dout, dv: [B, H, T, d_v]; dq, dk: [B, H, T, d]; other arguments as in la2_forward.

@@ -140,6 +140,34 @@ def test_decode_step_validation(lib):
     assert dec(lib, o=P + 4 * MB + 256) == ALIAS               # o inside the state
 
 
+def nrm(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, B=1, H=1, T=64, d=64, dv=64, fmap=1, block=64,
+        dtype=1, ws=None, wsb=0):
+    return lib.la2_forward_normalized(q, k, v, decay, o, B, H, T, d, dv, fmap, block, dtype, ws, wsb, None)
+
+
+def test_forward_normalized_validation(lib):
+    assert nrm(lib, q=None) == NULLP
+    assert nrm(lib, o=None) == NULLP
+    assert nrm(lib, fmap=2) == UNSUP
+    assert nrm(lib, T=0) == SHAPE
+    assert nrm(lib, dv=32) == UNSUP
+    assert nrm(lib, v=P + 2 * MB + 8) == MISAL
+    assert nrm(lib, o=P + MB + 64) == ALIAS                    # o inside k
+    assert nrm(lib) == WS                                      # elu + 1 needs phi(q), phi(k) in the workspace
+    n = la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.bfloat16)
+    assert n == 2 * 64 * 64 * 2 + 256                          # phi(q), phi(k) (bf16) and 64 fp32 denominators
+    assert nrm(lib, ws=P + 4 * MB, wsb=n - 1) == WS
+    assert nrm(lib, ws=P + 2 * MB, wsb=n) == ALIAS             # workspace over v
+    assert nrm(lib, ws=P + 3 * MB - 256, wsb=n) == ALIAS       # workspace runs into o
+    # identity map on a short sequence: only the denominators
+    assert la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "identity", 64, torch.bfloat16) == 256
+    # few chains, long sequences: per-segment sums of phi(k) and the numerator's segment states
+    big = la2.la2_normalized_workspace_bytes(1, 2, 1 << 16, 128, 128, "identity", 128, torch.bfloat16)
+    assert big >= la2.la2_workspace_bytes(1, 2, 1 << 16, 128, 128, 128, torch.bfloat16, False) + 2 * 128 * 4
+    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1) == ctypes.c_size_t(-1).value
+    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 96, 64, 1, 64, 1) == ctypes.c_size_t(-1).value
+
+
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):

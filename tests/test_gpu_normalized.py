@@ -1,0 +1,110 @@
+"""Normalized forward (numerator over denominator, feature map phi) on the GPU, through the C ABI,
+against the oracle's ``forward_normalized`` (pinned by the masked-product ratio, weights that sum
+to one, the running value range and the map's values).
+
+Bars as for the plain forward: max|gpu - ref| / max|ref| <= 1e-5 for fp32 inputs, <= 2e-2 for
+bf16 inputs.  With phi = elu + 1 every weight is positive, so the denominator is well away from 0;
+the identity map is tested on inputs made positive (|x| + 0.1), where the same holds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_amd as la2
+from causal_linear_attention_amd import inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref)
+    scale = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(np.asarray(got) - ref))) / (scale if scale > 0 else 1.0)
+
+
+def lam_of(x):
+    return None if x["decay"] is None else x["decay"].double().numpy()
+
+
+def positive(t):
+    """|x| + 0.1, rounded to the tensor's own dtype (both sides read the rounded values)."""
+    return (t.float().abs() + 0.1).to(t.dtype)
+
+
+def run_case(B, H, T, d, dv, dtype, block, decay, fmap, seed):
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=seed, decay=decay, backward=False)
+    if fmap == "identity":
+        x["q"], x["k"] = positive(x["q"]), positive(x["k"])
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    dec = None if x["decay"] is None else x["decay"].to(DEV)
+    o = la2.forward_normalized(q, k, v, dec, block, fmap)
+    ref = oracle.forward_normalized(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), fmap)
+    torch.cuda.synchronize()
+    err = rel_err(f64(o), ref)
+    print((B, H, T, d, dv, dtype, block, decay, fmap), f"{err:.2e}", flush=True)
+    assert np.isfinite(f64(o)).all()
+    assert err <= TOL[dtype], err
+    return o
+
+
+CASES = [
+    # (B, H, T, d, dv, dtype, block, decay, fmap)
+    (2, 3, 333, 128, 128, "bf16", 128, "heads", "elu1"),    # split numerator and denominator, ragged tail
+    (1, 2, 1000, 64, 128, "bf16", 64, "heads", "elu1"),
+    (16, 16, 200, 128, 64, "bf16", 128, "none", "elu1"),   # 256 chains: nothing split
+    (1, 3, 777, 64, 64, "f32", 32, "heads", "elu1"),
+    (2, 2, 300, 128, 128, "f32", 64, "none", "identity"),
+    (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
+    (3, 1, 1, 64, 64, "bf16", 64, "heads", "elu1"),        # one position: o = v
+    (2, 2, 65, 128, 64, "f32", 16, 0.5, "elu1"),           # strong decay
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c))
+def test_normalized_matches_oracle(case):
+    run_case(*case, seed=101 + case[2])
+
+
+@pytest.mark.parametrize("seg", ["64", "128", "320"])
+def test_normalized_forced_segments(seg, monkeypatch):
+    """Denominator segments of a forced length: the segment sums chained across up to 16 segments."""
+    monkeypatch.setenv("LA2_NORM_SEGMENT", seg)
+    run_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=7)
+    run_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=8)
+
+
+def test_normalized_ones_values_give_ones():
+    """v = 1 everywhere: every output is exactly a weighted average of ones."""
+    x = inputs.make_random(2, 4, 700, 128, 128, dtype="bf16", seed=3, decay="heads", backward=False)
+    q, k = x["q"].to(DEV), x["k"].to(DEV)
+    v = torch.ones((2, 4, 700, 128), dtype=torch.bfloat16, device=DEV)
+    o = la2.forward_normalized(q, k, v, x["decay"].to(DEV), 128, "elu1")
+    torch.cuda.synchronize()
+    assert float((o.float() - 1.0).abs().max()) <= 2e-2
+
+
+def test_normalized_full_size_sampled():
+    """The 1K-position length-sweep workload (128 x 16 chains, d = d_v = 128, bf16) with elu + 1,
+    at full size in one launch; the oracle on sampled whole chains."""
+    x = inputs.make("sweep131k_t1k")
+    w = x["workload"]
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    dec = None if x["decay"] is None else x["decay"].to(DEV)
+    o = la2.forward_normalized(q, k, v, dec, w.block, "elu1")
+    torch.cuda.synchronize()
+    lam = lam_of(x)
+    for b, h in [(0, 0), (w.B - 1, 15), (w.B // 2, 7)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        lh = None if lam is None else lam[h:h + 1]
+        ref = oracle.forward_normalized(*(f64(x[n][sl]) for n in ("q", "k", "v")), lh, "elu1")
+        err = rel_err(f64(o[sl]), ref)
+        print("chain", b, h, f"{err:.2e}", flush=True)
+        assert err <= TOL["bf16"]
