@@ -55,6 +55,12 @@ def parse():
     ap.add_argument("--normalized", action="store_true",
                     help="time la2_forward_normalized (numerator over denominator, phi = elu + 1) on the 1K "
                          "point of the sweep instead, with the plain forward timed beside it")
+    ap.add_argument("--compare", action="store_true",
+                    help="comparison curves over T at a fixed token count: the tiled scan, the token-serial "
+                         "recurrence kernel and torch's causal softmax attention (flash / memory-efficient "
+                         "backends only), H = 12, d = 128, bf16")
+    ap.add_argument("--compare-points", default="0.25,0.5,1,2,4,8,16,32,64,128",
+                    help="sequence lengths in K for --compare")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -177,6 +183,91 @@ def normalized_bench(args):
     }), flush=True)
 
 
+def compare_bench(args):
+    """Wall clock of three ways to attend causally over the same tokens, at 131,072 tokens per batch
+    (B = 128K / T), H = 12 heads, d = d_v = 128, bf16, seeded N(0, 1/d) inputs, no decay -- the shape
+    of the pages' comparison of the tiled scan with a FlashAttention kernel and with the serial
+    recurrence, on this GPU:
+      lightning: la2_forward (+ la2_backward_saved), T_B = 128;
+      serial:    la2_forward_serial, the recurrence one position after another (forward only);
+      softmax:   torch.nn.functional.scaled_dot_product_attention(is_causal=True) on the flash or
+                 memory-efficient backend (the math backend is never allowed), forward and
+                 forward + backward through autograd.
+    Each timing is the median of 3 calls after 1 warm-up, HIP events on the current stream."""
+    import torch
+    import causal_linear_attention_amd as la2
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    dev = torch.device("cuda:0")
+    H, d, tokens = 12, 128, 131072
+    stream = torch.cuda.current_stream()
+
+    def t_ms(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return sorted(out)[len(out) // 2]
+
+    backend = None
+    curves = []
+    for tk in [float(x) for x in args.compare_points.split(",")]:
+        T = int(tk * 1024)
+        B = tokens // T
+        g = torch.Generator().manual_seed(17 + T)
+        q, k, v, do = [(torch.randn((B, H, T, d), generator=g) / (math.sqrt(d) if i < 3 else 1.0)).to(torch.bfloat16)
+                       .to(dev) for i in range(4)]
+        row = {"T": T, "B": B}
+        o = torch.empty_like(v)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = la2.workspace_for(q, v, 128, True)
+        row["lightning_fwd_ms"] = round(t_ms(lambda: la2.la2_forward(q, k, v, None, o, 128, ws)), 4)
+        row["lightning_fwd_bwd_ms"] = round(t_ms(lambda: (la2.la2_forward(q, k, v, None, o, 128, ws),
+                                                          la2.la2_backward_saved(q, k, v, None, do, dq, dk, dv, 128,
+                                                                                 ws))), 4)
+        row["serial_fwd_ms"] = round(t_ms(lambda: la2.la2_forward_serial(q, k, v, None, o)), 4)
+        print(f"[compare] T={T} lightning and serial timed", file=sys.stderr, flush=True)
+        qg, kg, vg = (t.detach().clone().requires_grad_(True) for t in (q, k, v))
+        for cand in ([SDPBackend.FLASH_ATTENTION], [SDPBackend.EFFICIENT_ATTENTION]) if backend is None else [backend]:
+            try:
+                with sdpa_kernel(cand):
+                    row["softmax_fwd_ms"] = round(t_ms(lambda: torch.nn.functional.scaled_dot_product_attention(
+                        q, k, v, is_causal=True)), 4)
+
+                    def fb():
+                        out = torch.nn.functional.scaled_dot_product_attention(qg, kg, vg, is_causal=True)
+                        out.backward(do)
+                    row["softmax_fwd_bwd_ms"] = round(t_ms(fb), 4)
+                backend = cand
+                break
+            except RuntimeError as e:
+                row["softmax_error"] = str(e).splitlines()[0][:200]
+        if backend is not None:
+            row.pop("softmax_error", None)
+        for key in ("lightning_fwd_bwd_ms", "softmax_fwd_bwd_ms", "serial_fwd_ms", "lightning_fwd_ms", "softmax_fwd_ms"):
+            if key in row:
+                row[key.replace("_ms", "_tokens_per_s")] = round(B * T / (row[key] * 1e-3), 1)
+        curves.append(row)
+        print(f"[compare] T={T} done", file=sys.stderr, flush=True)
+        del q, k, v, do, o, dq, dk, dv, ws, qg, kg, vg
+        torch.cuda.empty_cache()
+    last = curves[-1]
+    print(json.dumps({
+        "metric": "fwd+bwd tokens/sec vs T: tiled lightning scan vs causal softmax attention vs token-serial recurrence",
+        "value": last.get("lightning_fwd_bwd_tokens_per_s"), "unit": "tokens/s", "n_gpus": 1,
+        "steps": 3, "warmup": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "comparison: 131072 tokens per batch, H=12, d=d_v=128, no decay, T_B=128",
+                   "softmax_backend": None if backend is None else str(backend[0]), "parallelism": "none (1 GPU)"},
+        "curves": curves,
+    }), flush=True)
+
+
 def algorithmic(w):
     """Algorithmic bytes and flops of one forward and one backward over workload w (per call)."""
     th = w.B * w.H * w.T                      # token-heads
@@ -201,6 +292,9 @@ def main():
         return
     if args.normalized:
         normalized_bench(args)
+        return
+    if args.compare:
+        compare_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

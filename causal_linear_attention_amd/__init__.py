@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     decode_step,
     forward,
     forward_normalized,
+    forward_serial,
     forward_state,
     la2_abi_version,
     la2_backward,
@@ -18,6 +19,7 @@ from .binding import (  # noqa: F401
     la2_decode_step,
     la2_forward,
     la2_forward_normalized,
+    la2_forward_serial,
     la2_forward_state,
     la2_normalized_workspace_bytes,
     la2_status_string,

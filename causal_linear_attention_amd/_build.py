@@ -19,7 +19,7 @@ LIB = os.path.join(LIBDIR, "libla2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["la2_scan_bf16.hip", "la2_dkdv_bf16.hip", "la2_scan_f32.hip", "la2_prefix.hip", "la2_decode.hip", "la2_norm.hip",
-           "la2_api.cpp"]
+           "la2_serial.hip", "la2_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

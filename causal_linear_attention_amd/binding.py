@@ -20,7 +20,8 @@ LA2_PHI_IDENTITY = 0
 LA2_PHI_ELU1 = 1
 _FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
 
-EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_backward",
+EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
+           "la2_backward",
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
 
@@ -54,6 +55,8 @@ def load_library(path=LIB_PATH):
     lib.la2_decode_step.restype = i32
     lib.la2_forward_normalized.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]
     lib.la2_forward_normalized.restype = i32
+    lib.la2_forward_serial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.la2_forward_serial.restype = i32
     lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.la2_normalized_workspace_bytes.restype = sz
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
@@ -195,6 +198,17 @@ def la2_forward_normalized(q, k, v, decay, o, feature_map, block, workspace=None
         raise LA2Error(st, "la2_forward_normalized")
 
 
+def la2_forward_serial(q, k, v, decay, o, stream=None):
+    """Enqueue o = attention(q, k, v) computed one position after another (comparison kernel)."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    st = load_library().la2_forward_serial(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
+        B, H, T, d, d_v, dtype_code(q.dtype), _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_forward_serial")
+
+
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
     la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
@@ -267,6 +281,14 @@ def forward_normalized(q, k, v, decay=None, block=128, feature_map="elu1", works
     if workspace is None:
         workspace = normalized_workspace_for(q, v, feature_map, block)
     la2_forward_normalized(q, k, v, decay, o, feature_map, block, workspace)
+    return o
+
+
+def forward_serial(q, k, v, decay=None):
+    """Allocate o and run the token-serial recurrence."""
+    _check_same(q, k, v)
+    o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    la2_forward_serial(q, k, v, decay, o)
     return o
 
 

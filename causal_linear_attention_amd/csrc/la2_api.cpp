@@ -286,6 +286,27 @@ int la2_decode_step(const void *q, const void *k, const void *v, const float *de
                : LA2_ERR_HIP;
 }
 
+int la2_forward_serial(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B, int64_t H,
+                       int64_t T, int64_t d, int64_t d_v, int dtype, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
+    const int st = check_sizes(B, H, T, d, d_v, dtype == LA2_BF16 ? 128 : 64, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const Range ro = range_of(o, nv);
+    const Range ins[4] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                          range_of(decay, decay ? (size_t)H * 4 : 0)};
+    for (const Range &r : ins)
+        if (overlap(ro, r)) return LA2_ERR_ALIAS;
+    return la2::launch_serial(q, k, v, decay, o, (int)(B * H), (int)H, T, (int)d, (int)d_v, dtype,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+               ? LA2_OK
+               : LA2_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

@@ -71,6 +71,11 @@ struct DenArgs {
 hipError_t launch_denominator(const DenArgs &a, int D, int dtype, int fmap, bool norm, hipStream_t s);
 hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s);
 
+// The recurrence run token by token (comparison with the tiled scan): o for every chain, state in
+// registers from zero.  q, k: [chains, T, D]; v, o: [chains, T, DV]; bf16 (dtype 1) or fp32 (0).
+hipError_t launch_serial(const void *q, const void *k, const void *v, const float *decay, void *o, int chains, int H,
+                         int64_t T, int D, int DV, int dtype, hipStream_t s);
+
 // Which (D, DV, TB) the kernels are compiled for.
 bool bf16_supported(int D, int DV, int TB);
 bool f32_supported(int D, int DV, int TB);

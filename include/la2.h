@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 4
+#define LA2_ABI_VERSION 5
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -149,6 +149,18 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
  * (size_t)-1 for arguments it would reject. */
 size_t la2_normalized_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
                                       int feature_map, int block, int dtype);
+
+/* The same o as la2_forward, computed the way the recurrence is written: one
+ * position after another (page "Lightning Attention", section 1, where the
+ * serial loop's rank-1 updates are what the tiling of section 2 removes).
+ * Provided to compare the two on the same GPU, not for use on the hot path:
+ * each position costs 2 d d_v vector FMAs and a chain is one workgroup per
+ * 64 value columns, so the work runs in parallel only across chains.
+ *   Arguments as in la2_forward, without block and workspace; fp32 state.
+ *   Supported: d, d_v in {64, 128}, LA2_BF16 or LA2_F32. */
+int la2_forward_serial(const void *q, const void *k, const void *v, const float *decay, void *o,
+                       int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int dtype,
+                       void *stream);
 
 /* Backward: gradients of <o, dout> with respect to q, k and v.
  *   dout, dv: [B, H, T, d_v]; dq, dk: [B, H, T, d]; other arguments as in la2_forward.

@@ -168,6 +168,21 @@ def test_forward_normalized_validation(lib):
     assert lib.la2_normalized_workspace_bytes(1, 1, 64, 96, 64, 1, 64, 1) == ctypes.c_size_t(-1).value
 
 
+def ser(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, B=1, H=1, T=64, d=64, dv=64, dtype=1):
+    return lib.la2_forward_serial(q, k, v, decay, o, B, H, T, d, dv, dtype, None)
+
+
+def test_forward_serial_validation(lib):
+    assert ser(lib, v=None) == NULLP
+    assert ser(lib, H=0) == SHAPE
+    assert ser(lib, d=32) == UNSUP
+    assert ser(lib, dtype=7) == UNSUP
+    assert ser(lib, o=P + 3 * MB + 2) == MISAL
+    assert ser(lib, decay=P + 5 * MB + 2) == MISAL
+    assert ser(lib, o=P + 2 * MB + 512) == ALIAS               # o inside v
+    assert ser(lib, decay=P + 3 * MB + 64) == ALIAS            # o over the decays
+
+
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
