@@ -38,8 +38,11 @@ PEAK_BF16_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 5 for the length sweep, 50 for one --workload)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps before the timed ones (default 10 for the length sweep, 50 "
+                         "for one --workload: the GPU needs some tens of ms of work before its clocks settle)")
     ap.add_argument("--points", default="all", help="comma list of sweep lengths in K (e.g. 1,128) or 'all'")
     ap.add_argument("--workload", default=None,
                     help="time one named workload of inputs.WORKLOADS (e.g. tnl15b_layer, long128k_outliers) "
@@ -63,7 +66,13 @@ def parse():
                     help="sequence lengths in K for --compare")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    single = args.workload is not None
+    if args.steps is None:
+        args.steps = 50 if single else 5
+    if args.warmup is None:
+        args.warmup = 50 if single else 10
+    return args
 
 
 def copy_calibration():

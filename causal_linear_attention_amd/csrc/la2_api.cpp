@@ -23,9 +23,38 @@ struct Plan {
     int TB;          // tile length the kernels run with
     int nseg;        // segments per chain
     int seg_tiles;   // tiles per segment
+    int sub;         // state-pass sub-segments per segment (sub divides seg_tiles)
+    int nsub;        // state entries per chain (sub-segments of seg_tiles / sub tiles)
     int narrow;      // bf16: run 128-wide value tensors as two 64-wide slices
     size_t ws_bytes; // workspace for the segment states
 };
+
+// Sub-segments of the state-only pass.  It has (nseg - 1) segments per chain to sum, one workgroup
+// each, and one workgroup fills a CU, so with few chains it can leave CUs idle (128 chains split
+// in two: half the chip).  Cutting each segment into `sub` pieces (at least 32 tiles each, so the
+// extra fp32 state written per piece stays small next to the tiles it sums) gives more workgroups;
+// sub is chosen to fill whole rounds of the 256 CUs best, and only when that gains 10%.
+// LA2_STATE_SUB forces it (any divisor of seg_tiles).
+int choose_sub(int64_t work, int nseg, int seg_tiles) {
+    if (nseg < 2) return 1;
+    if (const char *env = std::getenv("LA2_STATE_SUB")) {
+        const long v = std::strtol(env, nullptr, 10);
+        return v > 0 && seg_tiles % v == 0 ? (int)v : 1;
+    }
+    const int64_t base = work * (nseg - 1);
+    auto fill = [&](int r) {
+        const int64_t w = base * r, rounds = (w + kComputeUnits - 1) / kComputeUnits;
+        return (double)w / (double)(rounds * kComputeUnits);
+    };
+    int best = 1;
+    double bf = fill(1);
+    for (int r = 2; seg_tiles / r >= 32; ++r)
+        if (seg_tiles % r == 0 && fill(r) > bf + 0.1) {
+            best = r;
+            bf = fill(r);
+        }
+    return best;
+}
 
 int elem_size(int dtype) { return dtype == LA2_BF16 ? 2 : 4; }
 
@@ -78,7 +107,10 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     }
     p.seg_tiles = (int)seg_tiles;
     p.nseg = (int)((NT + seg_tiles - 1) / seg_tiles);
-    p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nseg * d * dv * sizeof(float) : 0;
+    p.sub = choose_sub(work, p.nseg, p.seg_tiles);
+    const int64_t sub_tiles = seg_tiles / p.sub;
+    p.nsub = p.nseg > 1 ? (int)((NT + sub_tiles - 1) / sub_tiles) : 1;
+    p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nsub * d * dv * sizeof(float) : 0;
     return p;
 }
 
@@ -128,6 +160,8 @@ la2::ScanArgs scan_args(const void *a, const void *b, const void *c, void *y, co
     args.seg_tiles = pl.seg_tiles;
     args.chains = (int)chains;
     args.nslice = W / slice_width(dtype, W, pl.narrow);
+    args.sub = pl.sub;
+    args.nsub = pl.nsub;
     return args;
 }
 
@@ -144,13 +178,18 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
 int segment_states(const void *b, const void *c, const float *decay, int64_t chains, int64_t H, int64_t T, int D,
                    int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s,
                    const float *init = nullptr) {
-    la2::ScanArgs args = scan_args(nullptr, b, c, nullptr, decay, chains, H, T, W, pl, dtype);
+    // the state pass runs the sub-segments: every state entry is one segment of its own
+    Plan sp = pl;
+    sp.seg_tiles = pl.seg_tiles / pl.sub;
+    sp.nseg = pl.nsub;
+    sp.sub = 1;
+    la2::ScanArgs args = scan_args(nullptr, b, c, nullptr, decay, chains, H, T, W, sp, dtype);
     args.states = static_cast<float *>(ws);
-    // deltas of the segments whose successor (forward) / predecessor (reverse) needs them
-    args.seg_first = dir == la2::Dir::Forward ? 0 : 1;
-    args.seg_count = pl.nseg - 1;
-    if (launch(args, D, pl, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
-    if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nseg, (int64_t)pl.seg_tiles * pl.TB,
+    // deltas of the sub-segments that some later (forward) / earlier (reverse) output segment needs
+    args.seg_first = dir == la2::Dir::Forward ? 0 : pl.sub;
+    args.seg_count = dir == la2::Dir::Forward ? (pl.nseg - 1) * pl.sub : pl.nsub - pl.sub;
+    if (launch(args, D, sp, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
+    if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nsub, (int64_t)sp.seg_tiles * pl.TB,
                                    (int64_t)D * W, dir, s, init) != hipSuccess)
         return LA2_ERR_HIP;
     return LA2_OK;
@@ -493,6 +532,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         a.nseg = fp.nseg;
         a.seg_tiles = fp.seg_tiles;
         a.chains = (int)chains;
+        a.sub = fp.sub;
+        a.nsub = fp.nsub;
         return la2::launch_dkdv_bf16(a, D, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
     }
     // reverse state R_t = lam R_{t+1} + q_t do_t^T, [d, d_v], shared by the dv and dk scans

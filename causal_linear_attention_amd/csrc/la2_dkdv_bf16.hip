@@ -119,7 +119,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
     const u16 *gq = static_cast<const u16 *>(p.q) + base, *gk = static_cast<const u16 *>(p.k) + base;
     const u16 *gv = static_cast<const u16 *>(p.v) + base, *go = static_cast<const u16 *>(p.dout) + base;
     u16 *gdk = static_cast<u16 *>(p.dk) + base, *gdv = static_cast<u16 *>(p.dv) + base;
-    const float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * D : nullptr;
+    const float *gs =
+        p.states ? p.states + ((int64_t)chain * p.nsub + state_index(seg, p.sub, p.nsub, true)) * D * D : nullptr;
 
     const float l2 = DECAY ? log2f(p.decay[chain % p.H]) : 0.0f;
     auto pw = [&](int n) -> float { return DECAY ? __builtin_amdgcn_exp2f((float)n * l2) : 1.0f; };

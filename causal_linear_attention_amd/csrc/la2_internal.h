@@ -17,8 +17,8 @@ struct ScanArgs {
     const void *c;
     void *y;               // output [chains, T, DVT] (unused in state-only launches)
     const float *decay;    // [H] or nullptr (lam = 1)
-    float *states;         // fp32 [chains, nseg, D, DVT]: segment start states / segment deltas
-    int states_t;          // 1: output launches read the start states transposed, [chains, nseg, DVT, D]
+    float *states;         // fp32 [chains, nsub, D, DVT]: segment start states / segment deltas
+    int states_t;          // 1: output launches read the start states transposed, [chains, nsub, DVT, D]
     int has_init;          // output launches: segment 0 also starts from `states` (a carried-in state)
     float *state_out;      // forward output launches: fp32 [chains, D, DVT] final state, or nullptr
     int64_t T;
@@ -30,7 +30,20 @@ struct ScanArgs {
     int seg_count;         // segments per chain handled by this launch
     int nslice;            // value slices per chain (DVT / slice width)
     int chains;            // B * H
+    // `states` holds nsub entries per chain, `sub` per segment of this launch (state-only launches
+    // may run finer segments than the output launch that reads them); output segment s starts from
+    // entry state_index(s)
+    int sub;
+    int nsub;
 };
+
+// Entry of the states array a segment starts from: its first sub-segment in the forward direction,
+// its last one in the reverse direction.
+__host__ __device__ inline int state_index(int seg, int sub, int nsub, bool reverse) {
+    if (!reverse) return seg * sub;
+    const int i = seg * sub + sub - 1;
+    return i < nsub - 1 ? i : nsub - 1;
+}
 
 // Kernel families.
 enum class Dir { Forward, Reverse };
@@ -87,12 +100,14 @@ struct DkdvArgs {
     const void *q, *k, *v, *dout;
     void *dk, *dv;
     const float *decay;    // [H] or nullptr (lam = 1)
-    const float *states;   // fp32 [chains, nseg, D, D] start states of R, or nullptr when not split
+    const float *states;   // fp32 [chains, nsub, D, D] start states of R, or nullptr when not split
     int64_t T;
     int H;
     int nseg;
     int seg_tiles;
     int chains;
+    int sub;               // entries of `states` per segment (see ScanArgs)
+    int nsub;
 };
 bool dkdv_supported(int D, int DV);
 hipError_t launch_dkdv_bf16(const DkdvArgs &a, int D, hipStream_t s);

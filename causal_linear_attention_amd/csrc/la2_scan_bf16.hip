@@ -210,7 +210,8 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const u16 *gb = static_cast<const u16 *>(p.b) + (int64_t)chain * T * D;
     const u16 *gc = static_cast<const u16 *>(p.c) + (int64_t)chain * T * p.DVT + dv0;
     u16 *gy = C::kOut ? static_cast<u16 *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
-    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
+    const int sidx = state_index(seg, p.sub, p.nsub, DIR == Dir::Reverse);
+    float *gs = p.states ? p.states + ((int64_t)chain * p.nsub + sidx) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
                          : nullptr;
 
     // lam^n = 2^(n log2 lam) with the hardware exp2 (n >= 0 only, so no overflow; tiny powers flush to 0)

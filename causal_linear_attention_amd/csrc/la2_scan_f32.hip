@@ -42,7 +42,8 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
     const float *gb = static_cast<const float *>(p.b) + (int64_t)chain * T * D;
     const float *gc = static_cast<const float *>(p.c) + (int64_t)chain * T * p.DVT + dv0;
     float *gy = kOut ? static_cast<float *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
-    float *gs = p.states ? p.states + ((int64_t)chain * p.nseg + seg) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
+    const int sidx = state_index(seg, p.sub, p.nsub, DIR == Dir::Reverse);
+    float *gs = p.states ? p.states + ((int64_t)chain * p.nsub + sidx) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
                          : nullptr;
 
     const bool has_decay = p.decay != nullptr;

@@ -97,6 +97,34 @@ def test_forced_segments(seg_tiles, monkeypatch):
     check_full(x, 64)
 
 
+@pytest.mark.parametrize("T,d,dtype,block,seg_tiles,sub", [
+    (700, 128, "bf16", 64, "4", "2"),     # 11 tiles: 3 segments of 2 state pieces, last piece 1 tile
+    (700, 128, "bf16", 64, "4", "4"),     # pieces of one tile
+    (1000, 128, "bf16", 128, "4", "4"),   # 128-position tiles (the fused dk/dv pass keeps 64)
+    (520, 64, "bf16", 64, "4", "2"),      # last segment one piece of one tile
+    (300, 64, "f32", 32, "4", "2"),
+])
+def test_state_sub_segments(T, d, dtype, block, seg_tiles, sub, monkeypatch):
+    """State-only passes over finer pieces than the output segments (start states read from the
+    first piece forward, the last piece reverse), forward + backward against the oracle, and the
+    saved-state backward bitwise equal to the recomputing one."""
+    monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    monkeypatch.setenv("LA2_STATE_SUB", sub)
+    x = inputs.make_random(1, 3, T, d, d, dtype=dtype, seed=61 + T, decay="heads")
+    check_full(x, block)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    decay = x["decay"].to(DEV)
+    ws = la2.workspace_for(q, v, block, True)
+    o = torch.empty_like(v)
+    la2.la2_forward(q, k, v, decay, o, block, ws)
+    g = tuple(torch.empty_like(t) for t in (q, k, v))
+    la2.la2_backward_saved(q, k, v, decay, do, *g, block, ws)
+    ref = la2.backward(q, k, v, do, decay, block)
+    torch.cuda.synchronize()
+    for a, r in zip(g, ref):
+        assert torch.equal(a, r)
+
+
 @pytest.mark.parametrize("B,H,T,seg_tiles", [(1, 8, 700, None), (1, 3, 300, None), (1, 2, 700, "2"), (1, 8, 520, "3")])
 @pytest.mark.parametrize("decay", ["heads", "none"])
 def test_narrow_value_slices(B, H, T, seg_tiles, decay, monkeypatch):

@@ -76,11 +76,15 @@ def test_forward_state_matches_oracle(case):
     assert torch.equal(o0, la2.forward(q, k, v, dec, block))
 
 
-@pytest.mark.parametrize("seg_tiles,slice_width", [("1", None), ("3", None), (None, "64"), ("2", "64")])
-def test_forward_state_plans(seg_tiles, slice_width, monkeypatch):
-    """Forced segment splits (prefix with a carried-in state) and 64-wide value slices."""
+@pytest.mark.parametrize("seg_tiles,slice_width,sub", [("1", None, None), ("3", None, None), (None, "64", None),
+                                                       ("2", "64", None), ("4", None, "2")])
+def test_forward_state_plans(seg_tiles, slice_width, sub, monkeypatch):
+    """Forced segment splits (prefix with a carried-in state), state pieces finer than the segments
+    and 64-wide value slices."""
     if seg_tiles:
         monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
+    if sub:
+        monkeypatch.setenv("LA2_STATE_SUB", sub)
     if slice_width:
         monkeypatch.setenv("LA2_SLICE_WIDTH", slice_width)
     x = inputs.make_random(2, 2, 600, 128, 128, dtype="bf16", seed=71, decay="heads", backward=False)
