@@ -33,6 +33,7 @@ TRAFFIC_KERNEL_SHA256_16 = "a22c682c82516bf6"
 TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573053 * 1024, "write": 524288 * 1024}
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
 
 
 def parse():
@@ -124,6 +125,23 @@ def decode_bench(args):
     chains = B * H
     bytes_step = chains * (8 * d * dv + 2 * (2 * d + 2 * dv))
     achieved = bytes_step / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's state-carrying forward, one position at a time from the same kind of state: 128
+        # sequences, 16 positions (the state handed from each call to the next)
+        import oracle
+        nb, nsteps = min(128, B), 16
+        s_cur = state[:nb].double().cpu().numpy()
+        lam = decay.double().cpu().numpy()
+        ins = [[t[:nb].double().cpu().numpy()[:, :, None, :] for t in steps_in[i % 4]] for i in range(nsteps)]
+        ta = time.perf_counter()
+        for q, k, v in ins:
+            _, s_cur = oracle.forward_state(q, k, v, lam, s_cur)
+        tc = time.perf_counter() - ta
+        cpu = {"value": round(nb * nsteps / tc, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"{nsteps} positions of {nb} sequences x {H} heads, each from the "
+                                           f"fp32 state the previous one left, fp64, {tc:.2f} s",
+               "host": host_info()}
     print(json.dumps({
         "metric": "decode tokens/sec (one new token per sequence from a carried state)", "value": round(B / (ms * 1e-3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": max(args.warmup, 1) * 10,
@@ -136,6 +154,7 @@ def decode_bench(args):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "decode_kernel<bf16,D=128,DV=128>", "avg_launch_ms": round(ms, 5),
                      "algorithmic_bytes_per_launch": bytes_step},
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -176,6 +195,16 @@ def normalized_bench(args):
     th = w.B * w.H * w.T
     byts = th * 4 * w.d * 2
     achieved = byts / (ms_n * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = 32
+        ta = time.perf_counter()
+        oracle.forward_normalized(*(x[n][:nb].double().numpy() for n in ("q", "k", "v")), None, "elu1")
+        tc = time.perf_counter() - ta
+        cpu = {"value": round(nb * w.T / tc, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"{nb} sequences x {w.H} heads x {w.T} tokens, fp64, {tc:.1f} s",
+               "host": host_info()}
     print(json.dumps({
         "metric": "normalized forward tokens/sec (phi = elu + 1, numerator / denominator)",
         "value": round(w.B * w.T / (ms_n * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n,
@@ -189,6 +218,7 @@ def normalized_bench(args):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "la2_forward_normalized (denominator + numerator scan + division launches)",
                      "avg_launch_ms": round(ms_n, 5), "algorithmic_bytes_per_launch": byts},
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
@@ -288,7 +318,56 @@ def algorithmic(w):
         "bwd_bytes": th * 7 * d * e,          # read q, k, v, do; write dq, dk, dv
         "fwd_flops": th * (4 * tb * d + 4 * d * d),
         "bwd_flops": th * (10 * tb * d + 10 * d * d),
+        # the same products over the causal triangle only (diagonal included), which is the work
+        # the kernels actually do inside a tile
+        "fwd_flops_causal": th * (2 * d * (tb + 1) + 4 * d * d),
+        "bwd_flops_causal": th * (5 * d * (tb + 1) + 10 * d * d),
     }
+
+
+def host_info():
+    model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                 "unknown CPU")
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
+def oracle_rate(x, nb, nh, backward, threads=None):
+    """Token-heads per second of the C oracle (fp64 token recurrence) on the first nb sequences and nh
+    heads of workload inputs x, forward (+ backward)."""
+    import oracle
+    sub = lambda t: t[:nb, :nh].double().numpy()
+    q, k, v = (sub(x[n]) for n in ("q", "k", "v"))
+    lam = None if x["decay"] is None else x["decay"][:nh].double().numpy()
+    before = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    used = oracle.num_threads()
+    try:
+        ta = time.perf_counter()
+        oracle.forward(q, k, v, lam)
+        if backward:
+            oracle.backward(q, k, v, sub(x["do"]), lam)
+        tc = time.perf_counter() - ta
+    finally:
+        oracle.set_num_threads(before)
+    return nb * nh * x["workload"].T / tc, tc, used
+
+
+def cpu_baseline(x, nb, nh, backward, one_thread=None):
+    """The oracle as it stands on a bounded sample of workload x, all host threads, reported as tokens/s over
+    all H heads; `one_thread` = (nb, nh) of a smaller sample timed on one thread."""
+    w = x["workload"]
+    rate, tc, used = oracle_rate(x, nb, nh, backward)
+    what = "forward + backward" if backward else "forward"
+    out = {"value": round(rate / w.H, 1), "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"{nb} sequence(s) x {nh} of {w.H} heads x {w.T} tokens of {w.name}, {what}, fp64 token "
+                     f"recurrence, {tc:.1f} s",
+           "host": host_info()}
+    if one_thread:
+        r1, t1, _ = oracle_rate(x, one_thread[0], one_thread[1], backward, threads=1)
+        out["one_thread"] = {"value": round(r1 / w.H, 1), "unit": "tokens/s",
+                             "sample": f"{one_thread[0]} sequence(s) x {one_thread[1]} heads, {t1:.1f} s"}
+    return out
 
 
 def main():
@@ -318,11 +397,10 @@ def main():
     dev = torch.device("cuda:0")
     names = inputs.SWEEP_NAMES
     if args.workload:
-        if args.workload not in inputs.WORKLOADS or not inputs.WORKLOADS[args.workload].backward:
-            print(f"bench.py: unknown or forward-only workload {args.workload!r}", file=sys.stderr)
+        if args.workload not in inputs.WORKLOADS:
+            print(f"bench.py: unknown workload {args.workload!r}", file=sys.stderr)
             sys.exit(2)
         names = [args.workload]
-        args.no_cpu_baseline = True
     elif args.points != "all":
         want = {int(p) for p in args.points.split(",")}
         names = [n for n in names if inputs.WORKLOADS[n].T // 1024 in want]
@@ -332,14 +410,15 @@ def main():
     for n in names:
         x = inputs.make(n)
         w = x["workload"]
-        q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
+        q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
+        do = x["do"].to(dev) if w.backward else None
         decay = None if x["decay"] is None else x["decay"].to(dev)
         ws_n = max(la2.la2_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.block, q.dtype, b) for b in (0, 1))
         ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
         o = torch.empty_like(v)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if w.backward else (None,) * 3
         cases.append(dict(w=w, q=q, k=k, v=v, do=do, decay=decay, ws=ws, o=o, dq=dq, dk=dk, dv=dv,
-                          host=x if (w.T == 1024 and not args.no_cpu_baseline) else None))
+                          host=x if ((w.T == 1024 or args.workload) and not args.no_cpu_baseline) else None))
         print(f"[bench] {w.name}: B={w.B} T={w.T} workspace={ws_n} B", file=sys.stderr, flush=True)
         del x
     torch.cuda.synchronize()
@@ -355,8 +434,9 @@ def main():
             if ev:
                 ev[1].record(stream)
             # the training step's backward: reuses the segment states la2_forward left in the workspace
-            la2.la2_backward_saved(c["q"], c["k"], c["v"], c["decay"], c["do"], c["dq"], c["dk"], c["dv"],
-                                   c["w"].block, c["ws"], stream)
+            if c["w"].backward:
+                la2.la2_backward_saved(c["q"], c["k"], c["v"], c["decay"], c["do"], c["dq"], c["dk"], c["dv"],
+                                       c["w"].block, c["ws"], stream)
             if ev:
                 ev[2].record(stream)
 
@@ -383,17 +463,27 @@ def main():
     for c, f, b in zip(cases, fwd_ms, bwd_ms):
         w = c["w"]
         alg = algorithmic(w)
+        if not w.backward:
+            b = 0.0
+            for key in ("bwd_bytes", "bwd_flops", "bwd_flops_causal"):
+                alg[key] = 0
+        t = (f + b) * 1e-3
+        byts, flops = alg["fwd_bytes"] + alg["bwd_bytes"], alg["fwd_flops"] + alg["bwd_flops"]
+        peak_flops = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS) * 1e12
         sweep[f"T={w.T}"] = {
-            "B": w.B, "fwd_ms": round(f, 4), "bwd_ms": round(b, 4),
-            "tokens_per_s": round(w.tokens / ((f + b) * 1e-3), 1),
+            "B": w.B, "fwd_ms": round(f, 4), "bwd_ms": round(b, 4) if w.backward else None,
+            "tokens_per_s": round(w.tokens / t, 1),
             "fwd_GBs": round(alg["fwd_bytes"] / (f * 1e-3) / 1e9, 1),
-            "bwd_GBs": round(alg["bwd_bytes"] / (b * 1e-3) / 1e9, 1),
-            "fwd_bwd_TFLOPs": round((alg["fwd_flops"] + alg["bwd_flops"]) / ((f + b) * 1e-3) / 1e12, 1),
-            # t_roof / t_measured, t_roof = max(algorithmic bytes / peak HBM, algorithmic flops / peak bf16)
-            "roofline_frac": round(max((alg["fwd_bytes"] + alg["bwd_bytes"]) / (PEAK_HBM_GBS * 1e9),
-                                       (alg["fwd_flops"] + alg["bwd_flops"]) / (PEAK_BF16_TFLOPS * 1e12))
-                                   / ((f + b) * 1e-3), 4),
+            "bwd_GBs": round(alg["bwd_bytes"] / (b * 1e-3) / 1e9, 1) if w.backward else None,
+            "fwd_bwd_TFLOPs": round(flops / t / 1e12, 1),
+            "fwd_bwd_TFLOPs_causal": round((alg["fwd_flops_causal"] + alg["bwd_flops_causal"]) / t / 1e12, 1),
+            "hbm_frac": round(byts / t / (PEAK_HBM_GBS * 1e9), 4),
+            "mfma_frac": round(flops / t / peak_flops, 4),
+            # t_roof / t_measured, t_roof = max(algorithmic bytes / peak HBM, algorithmic flops / peak MFMA)
+            "roofline_frac": round(max(byts / (PEAK_HBM_GBS * 1e9), flops / peak_flops) / t, 4),
         }
+        if byts <= (256 << 20):
+            sweep[f"T={w.T}"]["cache_resident"] = True   # inputs and outputs fit the 256 MiB memory-side cache
     tps = [v["tokens_per_s"] for v in sweep.values()]
 
     # Dominant kernel: the forward-direction output scan; at the 1K point la2_forward is exactly one
@@ -413,7 +503,8 @@ def main():
         roofline = {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "scan_bf16_kernel<D=128,DV=128,TB=128,Forward,Output>",
+            "kernel": f"scan_{'bf16' if w.dtype == 'bf16' else 'f32'}_kernel<D={w.d},DV={w.dv},"
+                      f"TB={min(w.block, 128) if w.dtype == 'bf16' else w.block},Forward,Output>",
             "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
             "avg_launch_ms": round(fwd_ms[dom], 4),
             "algorithmic_bytes_per_launch": alg["fwd_bytes"],
@@ -424,25 +515,23 @@ def main():
     cpu = None
     hostc = next((c for c in cases if c["host"] is not None), None)
     if hostc is not None:
-        import oracle
         x = hostc["host"]
-        nseq = min(args.cpu_sample_seqs, x["workload"].B)
-        sl = lambda t: t[:nseq].double().numpy()
-        q, k, v, do = (sl(x[n]) for n in ("q", "k", "v", "do"))
-        ta = time.perf_counter()
-        oracle.forward(q, k, v, None)
-        oracle.backward(q, k, v, do, None)
-        tc = time.perf_counter() - ta
-        cpu = {"value": round(nseq * x["workload"].T / tc, 1), "unit": "tokens/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{nseq} sequences x 1024 tokens x 16 heads of the T=1K batch, forward + backward, "
-                         f"fp64 token recurrence, {tc:.1f} s"}
+        w = x["workload"]
+        if not args.workload:
+            # the 1K point: up to --cpu-sample-seqs sequences, all heads
+            cpu = cpu_baseline(x, min(args.cpu_sample_seqs, w.B), w.H, True, one_thread=(4, w.H))
+        elif w.T * w.B * w.H <= (1 << 20):
+            cpu = cpu_baseline(x, w.B, w.H, w.backward, one_thread=(1, min(w.H, 4)))
+        else:
+            # long sequences: a few heads of the first sequence
+            cpu = cpu_baseline(x, 1, min(w.H, 8), w.backward)
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC if all(c["w"].backward for c in cases) else "forward tokens/sec on 1 MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if any(c["w"].dtype == "f32" for c in cases) else "bf16", "data": "synthetic",
         "config": ({
             "workload": "fixed-token length sweep: 131072 tokens per batch at (B,T) in "
                         + ",".join(f"({c['w'].B},{c['w'].T})" for c in cases)
@@ -453,7 +542,8 @@ def main():
             "workload": f"{cases[0]['w'].name}: B={cases[0]['w'].B}, H={cases[0]['w'].H}, T={cases[0]['w'].T}, "
                         f"d=d_v={cases[0]['w'].d}, T_B={cases[0]['w'].block}, "
                         f"{'per-head decay' if cases[0]['w'].decay else 'no decay'}"
-                        f"{', 1% outlier rows x8' if cases[0]['w'].outlier_frac else ''}; one step = fwd+bwd",
+                        f"{', 1% outlier rows x8' if cases[0]['w'].outlier_frac else ''}; one step = "
+                        f"{'fwd+bwd' if cases[0]['w'].backward else 'fwd'}",
             "tokens_per_step": tokens_per_step, "heads": cases[0]["w"].H, "d": cases[0]["w"].d,
             "d_v": cases[0]["w"].dv, "block": cases[0]["w"].block, "parallelism": "none (1 GPU)",
         }),

@@ -65,6 +65,8 @@ def _bind(lib):
     lib.la2_oracle_backward_rows.restype = None
     lib.la2_oracle_num_threads.argtypes = []
     lib.la2_oracle_num_threads.restype = ctypes.c_int
+    lib.la2_oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.la2_oracle_set_num_threads.restype = None
     return lib
 
 
@@ -86,6 +88,11 @@ def _chain_lams(lam, B, H):
 def num_threads(lib=None):
     """OpenMP threads the C oracle runs with."""
     return (lib or _load()).la2_oracle_num_threads()
+
+
+def set_num_threads(n, lib=None):
+    """Threads for the following C oracle calls (for timing; the results do not depend on it)."""
+    (lib or _load()).la2_oracle_set_num_threads(int(n))
 
 
 class Oracle:

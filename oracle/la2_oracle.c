@@ -286,3 +286,14 @@ int la2_oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following oracle calls (timing only; results do not depend on it). */
+void la2_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
