@@ -15,6 +15,8 @@ Two independent formulations live here, both in fp64:
   sums, for spot checks of very long sequences.  ``forward_normalized`` is
   the same section's whole output, phi(q)^T S / phi(q)^T z with the
   denominator sum z_t = lam z_{t-1} + phi(k_t) and phi = identity or elu + 1.
+  ``backward_state`` is the backward of ``forward_state``: gradients of
+  <o, do> + <state_out, dstate_out> including the one of the carried-in state.
 * ``tiled_forward`` / ``tiled_backward`` (numpy, this file): the same page's
   section 2 derivation in its own order -- Step 1 split of each output row
   into an intra-tile and an inter-tile part, Step 2 the masked left product
@@ -53,6 +55,8 @@ def _bind(lib):
     lib.la2_oracle_forward.restype = None
     lib.la2_oracle_forward_state.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     lib.la2_oracle_forward_state.restype = None
+    lib.la2_oracle_backward_state.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+    lib.la2_oracle_backward_state.restype = None
     lib.la2_oracle_forward_normalized.argtypes = [I, I, I, I, P, P, P, P, ctypes.c_int, P]
     lib.la2_oracle_forward_normalized.restype = None
     lib.la2_oracle_backward.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
@@ -123,6 +127,23 @@ class Oracle:
         self.lib.la2_oracle_forward_state(B * H, T, d, dv, _ptr(lams), _ptr(q), _ptr(k), _ptr(v),
                                           None if s_in is None else _ptr(s_in), _ptr(o), _ptr(s_out))
         return o, s_out
+
+    def backward_state(self, q, k, v, do, lam=None, state_in=None, dstate_out=None):
+        """(dq, dk, dv, dstate_in) of <o, do> + <state_out, dstate_out> for the forward from state_in."""
+        q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+        B, H, T, d = q.shape
+        dv_ = v.shape[-1]
+        dq, dk = np.empty_like(q), np.empty_like(k)
+        dvo = np.empty_like(v)
+        ds_in = np.empty((B, H, d, dv_), dtype=np.float64)
+        lams = _chain_lams(lam, B, H)
+        s_in = None if state_in is None else _f64(state_in)
+        ds_out = None if dstate_out is None else _f64(dstate_out)
+        self.lib.la2_oracle_backward_state(B * H, T, d, dv_, _ptr(lams), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                           None if s_in is None else _ptr(s_in),
+                                           None if ds_out is None else _ptr(ds_out),
+                                           _ptr(dq), _ptr(dk), _ptr(dvo), _ptr(ds_in))
+        return dq, dk, dvo, ds_in
 
     def forward_normalized(self, q, k, v, lam=None, feature_map="elu1"):
         """Normalized output phi(q)^T S / phi(q)^T z with phi = identity or elu + 1."""
@@ -198,6 +219,10 @@ def forward_state(q, k, v, lam=None, state_in=None):
 
 def forward_normalized(q, k, v, lam=None, feature_map="elu1"):
     return load().forward_normalized(q, k, v, lam, feature_map)
+
+
+def backward_state(q, k, v, do, lam=None, state_in=None, dstate_out=None):
+    return load().backward_state(q, k, v, do, lam, state_in, dstate_out)
 
 
 def backward(q, k, v, do, lam=None):

@@ -23,6 +23,10 @@
  *   R_t  = lam * R_{t+1} + q_t do_t^T,  R_{T+1} = 0  (reverse sweep)
  *   dk_t = R_t v_t,   dv_t = R_t^T k_t
  *
+ * la2_oracle_backward_state is the backward of la2_oracle_forward_state: the gradients of
+ * <o, do> + <state_out, ds_out>, the carried-in state's among them (ds_in = lam R_0), so that a
+ * sequence trained in chunks gets the same gradients as trained whole.
+ *
  * la2_oracle_forward_normalized is the full output of the same section 1, numerator
  * over denominator, with a feature map phi (identity, or elu + 1) and the decay
  * applied to the denominator's prefix sum z_t = lam z_{t-1} + phi(k_t) as to S.
@@ -156,10 +160,18 @@ void la2_oracle_forward_normalized(int64_t n_chains, int64_t T, int64_t d, int64
     }
 }
 
-void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
-                         const double *lam, const double *q, const double *k,
-                         const double *v, const double *dout, double *dq,
-                         double *dk, double *dvo)
+/* Backward of the forward carried in from s_in and out to state_out = S_{T-1} (fp64 [d, dv] per
+ * chain, as la2_oracle_forward_state), for the loss <o, dout> + <state_out, ds_out>.  By the chain
+ * rule through the recurrence:
+ *   dq_t = S_t do_t                       (the forward sweep from S_{-1} = s_in)
+ *   R_{T-1} = q_{T-1} do_{T-1}^T + ds_out,   R_t = lam R_{t+1} + q_t do_t^T
+ *   dk_t = R_t v_t,   dv_t = R_t^T k_t,   ds_in = lam R_0
+ * s_in, ds_out: NULL for zero; ds_in: NULL when not wanted. */
+void la2_oracle_backward_state(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                               const double *lam, const double *q, const double *k,
+                               const double *v, const double *dout, const double *s_in,
+                               const double *ds_out, double *dq, double *dk, double *dvo,
+                               double *ds_in)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t c = 0; c < n_chains; ++c) {
@@ -172,6 +184,9 @@ void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
         double *dvc = dvo + c * T * dv;
         const double l = lam[c];
         double *S = (double *)calloc((size_t)(d * dv), sizeof(double));
+        if (s_in)
+            for (int64_t e = 0; e < d * dv; ++e)
+                S[e] = s_in[c * d * dv + e];
         /* forward sweep: dq_t = S_t do_t */
         for (int64_t t = 0; t < T; ++t) {
             const double *kt = kc + t * d, *vt = vc + t * dv, *gt = gc + t * dv;
@@ -185,7 +200,8 @@ void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
                 dqc[t * d + i] = acc;
             }
         }
-        /* reverse sweep: R_t = lam R_{t+1} + q_t do_t^T; dk_t = R_t v_t; dv_t = R_t^T k_t */
+        /* reverse sweep: R_t = lam R_{t+1} + q_t do_t^T (+ ds_out at the last position);
+         * dk_t = R_t v_t; dv_t = R_t^T k_t */
         double *R = S;
         memset(R, 0, sizeof(double) * (size_t)(d * dv));
         for (int64_t t = T - 1; t >= 0; --t) {
@@ -194,6 +210,9 @@ void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
             for (int64_t i = 0; i < d; ++i)
                 for (int64_t j = 0; j < dv; ++j)
                     R[i * dv + j] = l * R[i * dv + j] + qt[i] * gt[j];
+            if (ds_out && t == T - 1)
+                for (int64_t e = 0; e < d * dv; ++e)
+                    R[e] += ds_out[c * d * dv + e];
             for (int64_t i = 0; i < d; ++i) {
                 double acc = 0.0;
                 for (int64_t j = 0; j < dv; ++j)
@@ -207,8 +226,20 @@ void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
                 dvc[t * dv + j] = acc;
             }
         }
+        /* ds_in: S_t depends on s_in through lam^(t+1) */
+        if (ds_in)
+            for (int64_t e = 0; e < d * dv; ++e)
+                ds_in[c * d * dv + e] = l * R[e];
         free(S);
     }
+}
+
+void la2_oracle_backward(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                         const double *lam, const double *q, const double *k,
+                         const double *v, const double *dout, double *dq,
+                         double *dk, double *dvo)
+{
+    la2_oracle_backward_state(n_chains, T, d, dv, lam, q, k, v, dout, NULL, NULL, dq, dk, dvo, NULL);
 }
 
 /* ---- single rows from the closed sums (one chain) ---------------------- */

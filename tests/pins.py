@@ -301,6 +301,64 @@ def pin_normalized_invariants(orc):
     _close(_elu1(np.array([2.5, -1.0, 0.0])), [3.5, np.exp(-1.0), 1.0], 1e-15, "elu + 1 values")
 
 
+def pin_backward_state_finite_differences(orc):
+    """backward_state == central differences of L = <o, do> + <state_out, G> with respect to q, k, v
+    and the carried-in state (forward_state gives o and state_out; fp64, step 1e-6)."""
+    q, k, v, do, lam = _setup(151, B=1, H=2, T=6, d=3, dv=2)
+    s_in = _rand((1, 2, 3, 2), 157)
+    G = _rand((1, 2, 3, 2), 163)
+
+    def loss(q_, k_, v_, s_):
+        o, s_out = orc.forward_state(q_, k_, v_, lam, s_)
+        return float(np.sum(o * do) + np.sum(s_out * G))
+
+    dq, dk, dv, ds = orc.backward_state(q, k, v, do, lam, s_in, G)
+    h = 1e-6
+    for name, arr, got in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("state_in", s_in, ds)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += h
+            a2[idx] -= h
+            args1 = [q, k, v, s_in]
+            args2 = [q, k, v, s_in]
+            pos = ("q", "k", "v", "state_in").index(name)
+            args1[pos], args2[pos] = a1, a2
+            num[idx] = (loss(*args1) - loss(*args2)) / (2 * h)
+        _close(got, num, 1e-7, f"backward_state d{name}")
+
+
+def pin_backward_state_chunks(orc):
+    """Training in chunks: the backward of a sequence cut at t (second chunk from the state the first
+    one left, its d(state_in) fed to the first chunk as d(state_out)) equals the whole backward, and
+    with no carried states it is the plain backward with d(state_in) = sum_t lam^(t+1) q_t do_t^T."""
+    q, k, v, do, lam = _setup(167, B=2, H=3, T=23, d=4, dv=3)
+    s0 = _rand((2, 3, 4, 3), 171)
+    G = _rand((2, 3, 4, 3), 173)
+    whole = orc.backward_state(q, k, v, do, lam, s0, G)
+    for t in (0, 1, 9, 22, 23):
+        a, b = slice(0, t), slice(t, 23)
+        _, s_mid = orc.forward_state(q[:, :, a], k[:, :, a], v[:, :, a], lam, s0) if t else (None, s0)
+        if t < 23:
+            g2 = orc.backward_state(q[:, :, b], k[:, :, b], v[:, :, b], do[:, :, b], lam, s_mid, G)
+            ds_mid = g2[3]
+        else:
+            g2, ds_mid = None, G
+        if t:
+            g1 = orc.backward_state(q[:, :, a], k[:, :, a], v[:, :, a], do[:, :, a], lam, s0, ds_mid)
+        for i, what in enumerate(("dq", "dk", "dv")):
+            parts = ([g1[i]] if t else []) + ([g2[i]] if g2 is not None else [])
+            _close(np.concatenate(parts, axis=2), whole[i], 1e-12, f"chunked {what} at {t}")
+        _close(g1[3] if t else ds_mid, whole[3], 1e-12, f"chunked d(state_in) at {t}")
+    plain = orc.backward(q, k, v, do, lam)
+    zero = orc.backward_state(q, k, v, do, lam, None, None)
+    for a_, b_ in zip(zero[:3], plain):
+        _close(a_, b_, 1e-14, "no carried states")
+    w = lam[None, :, None] ** (np.arange(23)[None, None, :] + 1)
+    _close(zero[3], np.einsum("bht,bhti,bhtj->bhij", np.broadcast_to(w, (2, 3, 23)), q, do), 1e-12,
+           "d(state_in) closed form")
+
+
 ALL_PINS = [
     pin_golden_handworked,
     pin_bruteforce_forward,
@@ -318,4 +376,6 @@ ALL_PINS = [
     pin_state_split_carry,
     pin_normalized_bruteforce,
     pin_normalized_invariants,
+    pin_backward_state_finite_differences,
+    pin_backward_state_chunks,
 ]

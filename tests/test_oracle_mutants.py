@@ -57,6 +57,15 @@ MUTANTS = [
     ("normalized_query_feature_skipped",
      "pq[i] = feature(qt[i], fmap);",
      "pq[i] = qt[i];"),
+    ("dstate_in_missing_decay",
+     "ds_in[c * d * dv + e] = l * R[e];",
+     "ds_in[c * d * dv + e] = R[e];"),
+    ("dstate_out_ignored",
+     "                    R[e] += ds_out[c * d * dv + e];",
+     "                    R[e] += 0.0 * ds_out[c * d * dv + e];"),
+    ("backward_ignores_state_in",
+     "            for (int64_t e = 0; e < d * dv; ++e)\n                S[e] = s_in[c * d * dv + e];",
+     "            for (int64_t e = 0; e < d * dv; ++e)\n                S[e] = 0.0 * s_in[c * d * dv + e];"),
     ("rows_skip_diagonal",
      "for (int64_t s = 0; s <= t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q",
      "for (int64_t s = 0; s < t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q"),
