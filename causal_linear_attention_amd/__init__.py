@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     LA2Error,
     LA2Function,
     backward,
+    backward_state,
     decode_step,
     forward,
     forward_normalized,
@@ -16,6 +17,7 @@ from .binding import (  # noqa: F401
     la2_abi_version,
     la2_backward,
     la2_backward_saved,
+    la2_backward_state,
     la2_decode_step,
     la2_forward,
     la2_forward_normalized,

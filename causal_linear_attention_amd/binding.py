@@ -21,7 +21,7 @@ LA2_PHI_ELU1 = 1
 _FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
 
 EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
-           "la2_backward",
+           "la2_backward", "la2_backward_state",
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
 
@@ -55,6 +55,9 @@ def load_library(path=LIB_PATH):
     lib.la2_decode_step.restype = i32
     lib.la2_forward_normalized.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]
     lib.la2_forward_normalized.restype = i32
+    lib.la2_backward_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32,
+                                       vp, sz, vp]
+    lib.la2_backward_state.restype = i32
     lib.la2_forward_serial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.la2_forward_serial.restype = i32
     lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
@@ -226,6 +229,25 @@ def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream
         raise LA2Error(st, "la2_backward_saved" if saved else "la2_backward")
 
 
+def la2_backward_state(q, k, v, decay, state_in, dout, dstate_out, dq, dk, dv, dstate_in, block, workspace=None,
+                       stream=None):
+    """Enqueue the backward of la2_forward_state: (dq, dk, dv) and d(state_in) (fp32 [B, H, d, d_v] or
+    None) of <o, dout> + <state_out, dstate_out> (state_in, dstate_out: fp32 [B, H, d, d_v] or None)."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("state_in", state_in), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        if t is not None and tuple(t.shape) != (B, H, d, d_v):
+            raise ValueError(f"{name} must be [B, H, d, d_v] = {(B, H, d, d_v)}")
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_backward_state(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _state_ptr(state_in, "state_in"),
+        _dev_ptr(dout, "dout"), _state_ptr(dstate_out, "dstate_out"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
+        _dev_ptr(dv, "dv"), _state_ptr(dstate_in, "dstate_in"),
+        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_backward_state")
+
+
 def la2_backward_saved(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None):
     """la2_backward reusing the forward's segment states in ``workspace`` (see include/la2.h)."""
     la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace, stream, saved=True)
@@ -290,6 +312,18 @@ def forward_serial(q, k, v, decay=None):
     o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     la2_forward_serial(q, k, v, decay, o)
     return o
+
+
+def backward_state(q, k, v, dout, decay=None, block=128, state_in=None, dstate_out=None, workspace=None):
+    """Allocate (dq, dk, dv, dstate_in) and run the backward of forward_state."""
+    _check_same(q, k, v, dout)
+    B, H, T, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dstate_in = torch.empty((B, H, d, v.shape[-1]), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, v, block, True)
+    la2_backward_state(q, k, v, decay, state_in, dout, dstate_out, dq, dk, dv, dstate_in, block, workspace)
+    return dq, dk, dv, dstate_in
 
 
 def decode_step(q, k, v, state, decay=None):

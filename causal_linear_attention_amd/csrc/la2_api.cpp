@@ -189,16 +189,20 @@ int segment_states(const void *b, const void *c, const float *decay, int64_t cha
     args.seg_first = dir == la2::Dir::Forward ? 0 : pl.sub;
     args.seg_count = dir == la2::Dir::Forward ? (pl.nseg - 1) * pl.sub : pl.nsub - pl.sub;
     if (launch(args, D, sp, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
+    // a reverse init sits at the chain's last position: the last piece's length - 1 before its start
+    const int64_t init_len = T - 1 - (int64_t)(pl.nsub - 1) * sp.seg_tiles * pl.TB;
     if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nsub, (int64_t)sp.seg_tiles * pl.TB,
-                                   (int64_t)D * W, dir, s, init) != hipSuccess)
+                                   (int64_t)D * W, dir, s, init, init_len) != hipSuccess)
         return LA2_ERR_HIP;
     return LA2_OK;
 }
 
 // Output pass y = attention(a, b, c) in direction `dir`, every segment starting from the states in
-// `ws` (transposed when states_t) or from zero when the chains are not split.  Forward only:
-// `state_in` ([chains, D, W]) is where an unsplit chain starts (a split chain's first segment reads
-// it from `ws`, where the prefix put it), and the final state goes to `state_out`.
+// `ws` (transposed when states_t) or from zero when the chains are not split.  `state_in`
+// ([chains, D, W], read transposed when states_t) is where an unsplit chain starts (a split chain's
+// first segment in scan order reads it from `ws`, where the prefix put it): forward, a carried-in
+// state; reverse, the gradient of a carried-out state.  `state_out` receives the forward's final
+// state, or in reverse lam times the state at position 0.
 int output_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
                 int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, int states_t,
                 hipStream_t s, const float *state_in = nullptr, float *state_out = nullptr) {
@@ -474,27 +478,32 @@ namespace {
 // reuse_s: the S segment states that la2_forward left at the start of the workspace are still there.
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
-                  void *workspace, size_t workspace_bytes, void *stream, bool reuse_s) {
+                  void *workspace, size_t workspace_bytes, void *stream, bool reuse_s, const float *state_in = nullptr,
+                  const float *dstate_out = nullptr, float *dstate_in = nullptr) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
     if (st != LA2_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dv) || (workspace && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(decay) & 3u))
+        !aligned16(dv) || (workspace && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(decay) & 3u) ||
+        !aligned16(state_in) || !aligned16(dstate_out) || !aligned16(dstate_in))
         return LA2_ERR_MISALIGNED;
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const size_t ns = (size_t)(B * H * d * d_v) * sizeof(float);
     const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
     const bool fused = fused_dkdv(d, d_v, dtype);
     size_t s_bytes = 0;
     const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype, &s_bytes);
-    const Range ins[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
-                          range_of(decay, decay ? (size_t)H * 4 : 0)};
-    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, ws_need)};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 5; ++j)
+    const Range ins[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
+                          range_of(decay, decay ? (size_t)H * 4 : 0), range_of(state_in, state_in ? ns : 0),
+                          range_of(dstate_out, dstate_out ? ns : 0)};
+    const Range outs[5] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, ws_need),
+                           range_of(dstate_in, dstate_in ? ns : 0)};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 7; ++j)
             if (overlap(outs[i], ins[j])) return LA2_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
+        for (int j = i + 1; j < 5; ++j)
             if (overlap(outs[i], outs[j])) return LA2_ERR_ALIAS;
     }
     if (ws_need && (!workspace || workspace_bytes < ws_need)) return LA2_ERR_WORKSPACE_TOO_SMALL;
@@ -507,16 +516,17 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T, so
     // it reads the forward's S states ([d, d_v] per segment) transposed
     if (split && !reuse_s &&
-        (st = segment_states(k, v, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Forward, workspace, s)) != LA2_OK)
+        (st = segment_states(k, v, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Forward, workspace, s,
+                             state_in)) != LA2_OK)
         return st;
     if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 1,
-                          s)) != LA2_OK)
+                          s, state_in)) != LA2_OK)
         return st;
     if (fused) {
         // dk_t = R_t v_t and dv_t = R_t^T k_t in one reverse pass, R_t = lam R_{t+1} + q_t do_t^T
         const Plan fp = make_plan(B, H, T, d, d_v, block, dtype, true);
         if (fp.nseg > 1 && (st = segment_states(q, dout, decay, chains, H, T, D, DV, fp, dtype, la2::Dir::Reverse,
-                                                ws_r, s)) != LA2_OK)
+                                                ws_r, s, dstate_out)) != LA2_OK)
             return st;
         la2::DkdvArgs a{};
         a.q = q;
@@ -526,7 +536,9 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         a.dk = dk;
         a.dv = dv;
         a.decay = decay;
-        a.states = fp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
+        a.states = fp.nseg > 1 ? static_cast<const float *>(ws_r) : dstate_out;
+        a.has_init = dstate_out != nullptr;
+        a.state_out = dstate_in;
         a.T = T;
         a.H = (int)H;
         a.nseg = fp.nseg;
@@ -537,15 +549,16 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         return la2::launch_dkdv_bf16(a, D, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
     }
     // reverse state R_t = lam R_{t+1} + q_t do_t^T, [d, d_v], shared by the dv and dk scans
-    if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, s)) !=
-                     LA2_OK)
+    if (split && (st = segment_states(q, dout, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, s,
+                                      dstate_out)) != LA2_OK)
         return st;
-    // dv_t = R_t^T k_t         = reverse scan with (k, q, do), state R
-    if ((st = output_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, 0, s)) !=
-        LA2_OK)
+    // dv_t = R_t^T k_t         = reverse scan with (k, q, do), state R; it also gives lam R_0
+    if ((st = output_scan(k, q, dout, dv, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Reverse, ws_r, 0, s,
+                          dstate_out, dstate_in)) != LA2_OK)
         return st;
     // dk_t = R_t v_t           = reverse scan with (v, do, q), state R^T: read R transposed
-    return output_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, ws_r, 1, s);
+    return output_scan(v, dout, q, dk, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Reverse, ws_r, 1, s,
+                       dstate_out);
 }
 
 }  // namespace
@@ -564,6 +577,14 @@ int la2_backward_saved(const void *q, const void *k, const void *v, const float 
                        int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
                          stream, true);
+}
+
+int la2_backward_state(const void *q, const void *k, const void *v, const float *decay, const float *state_in,
+                       const void *dout, const float *dstate_out, void *dq, void *dk, void *dv, float *dstate_in,
+                       int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
+                         stream, false, state_in, dstate_out, dstate_in);
 }
 
 }  // extern "C"

@@ -134,7 +134,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
 
     // R blocks (d rows kb, d_v columns nb), fp32; segment start state when the chain is split
     f32x16 sacc[C::SPW];
-    const bool init_state = gs != nullptr && seg < p.nseg - 1;
+    const bool init_state = gs != nullptr && (seg < p.nseg - 1 || p.has_init);
+    // a carried-in R (gradient of a carried-out forward state) is attached at the chain's last
+    // position: on the chain's last tile, the first processed here, rows are weighted lam^(leff-1-i)
+    // and it is carried on with lam^(leff-1), leff the tile's real length
+    const bool end_init = p.has_init && seg == p.nseg - 1;
+    const int leff_end = (int)min((int64_t)TB, T - (NT - 1) * TB);
 #pragma unroll
     for (int s = 0; s < C::SPW; ++s) {
         const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
     // One wave's output block for the tile at t0.  DK selects the gradient: the rows of the
     // tile's "query" role (B operand of the scores, rows tb) are K for dV and V for dK, the
     // "key" role (rows u) Q for dV and dO for dK, and the "value" role dO for dV and Q for dK.
-    auto out_block = [&](auto dk_tag, int64_t t0) __attribute__((always_inline)) {
+    auto out_block = [&](auto dk_tag, int64_t t0, bool first_end) __attribute__((always_inline)) {
         constexpr bool DK = decltype(dk_tag)::value;
         const u16 *sB = DK ? sV : sK;
         const u16 *sA = DK ? sO : sQ;
@@ -220,7 +225,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
                 for (int n = 0; n < C::ODB; ++n) sa[n] = sn[n];
             }
             if constexpr (DECAY) {
-                const float w = pw(TB - brow);
+                const int ew = first_end ? leff_end - 1 - brow : TB - brow;
+                const float w = ew >= 0 ? pw(ew) : 0.0f;
 #pragma unroll
                 for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
@@ -312,10 +318,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
         const int64_t t0 = tile_of(it) * TB;
         const bool update = it + 1 < ntiles;
 
+        const bool first_end = end_init && it == 0;
         if (is_dk)
-            out_block(std::true_type{}, t0);
+            out_block(std::true_type{}, t0, first_end);
         else
-            out_block(std::false_type{}, t0);
+            out_block(std::false_type{}, t0, first_end);
 
         // the next tile's loads go out after the register-heavy output phase
         if (update) fstage_load<D>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
@@ -324,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
         if (update) {
             if (s_active) {
                 if constexpr (DECAY) {
-                    const float f = pw(TB);
+                    const float f = first_end ? pw(leff_end - 1) : pw(TB);
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
@@ -368,6 +375,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
             fstage_store<D, DECAY>(st, smem, tid, l2);
         }
         lds_barrier();
+    }
+
+    // Gradient of a carried-in forward state: lam R_0, R_0 = lam^TB R + (w_upd Q)^T dO over tile 0
+    // (the update the loop leaves out; the tile is still in LDS, rows past T are zero).
+    if (p.state_out != nullptr && seg == 0 && s_active) {
+        if constexpr (DECAY) {
+            const float f = end_init && ntiles == 1 ? pw(leff_end - 1) : pw(TB);
+#pragma unroll
+            for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
+        }
+        const u16 *sQU = DECAY ? smem + C::oQW : sQ;
+#pragma unroll
+        for (int s = 0; s < C::SPW; ++s) {
+            const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+            for (int x = 0; x < TB / 16; ++x)
+                sacc[s] = mfma(frag_tr<D, false>(sQU, 16 * x, kb * 32, lane), frag_tr<D, false>(sO, 16 * x, nb * 32, lane),
+                               sacc[s]);
+            const float scale = pw(1);
+            float *so = p.state_out + (int64_t)chain * D * D;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                so[(int64_t)d * D + nb * 32 + col] = sacc[s][r] * scale;
+            }
+        }
     }
 }
 

@@ -19,8 +19,11 @@ struct ScanArgs {
     const float *decay;    // [H] or nullptr (lam = 1)
     float *states;         // fp32 [chains, nsub, D, DVT]: segment start states / segment deltas
     int states_t;          // 1: output launches read the start states transposed, [chains, nsub, DVT, D]
-    int has_init;          // output launches: segment 0 also starts from `states` (a carried-in state)
-    float *state_out;      // forward output launches: fp32 [chains, D, DVT] final state, or nullptr
+    int has_init;          // output launches: the first segment in scan order also starts from `states`
+                           // (forward: a carried-in state; reverse: the gradient of a carried-out
+                           // state, attached at the chain's last position)
+    float *state_out;      // output launches: fp32 [chains, D, DVT], forward: the final state; reverse:
+                           // lam times the state at position 0 (gradient of a carried-in state)
     int64_t T;
     int H;
     int DVT;               // full value width (row stride of c and y)
@@ -55,10 +58,12 @@ hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, M
 hipError_t launch_scan_f32(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
                            hipStream_t s);
 // Turns per-segment deltas into per-segment start states, in place; `init` ([chains, elems] or
-// nullptr) is the state the first segment starts from.
+// nullptr) is the state the first segment in scan order starts from (reverse: the gradient of a
+// carried-out state, attached at the chain's last position, which the first step weights with
+// lam^init_len, init_len = the last segment's length - 1).
 hipError_t launch_segment_prefix(float *states, const float *decay, int chains, int H, int nseg,
                                  int64_t seg_len, int64_t elems, Dir dir, hipStream_t s,
-                                 const float *init = nullptr);
+                                 const float *init = nullptr, int64_t init_len = 0);
 
 // One token of the recurrence for every chain: state <- lam state + k v^T (fp32 [chains, D, DV], in
 // place), o = state^T q.  q, k: [chains, D]; v, o: [chains, DV]; bf16 (dtype 1) or fp32 (0).
@@ -108,6 +113,9 @@ struct DkdvArgs {
     int chains;
     int sub;               // entries of `states` per segment (see ScanArgs)
     int nsub;
+    int has_init;          // the last segment also starts from `states`: a gradient of the carried-out
+                           // state, attached at the chain's last position
+    float *state_out;      // fp32 [chains, D, D]: lam R_0 (gradient of a carried-in state), or nullptr
 };
 bool dkdv_supported(int D, int DV);
 hipError_t launch_dkdv_bf16(const DkdvArgs &a, int D, hipStream_t s);

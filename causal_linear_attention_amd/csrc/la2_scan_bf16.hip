@@ -226,8 +226,14 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const bool s_active = wave * C::SPW < C::NSB;
 
     f32x16 sacc[C::SPW];
-    const bool init_state =
-        C::kOut && gs != nullptr && (DIR == Dir::Forward ? (seg > 0 || p.has_init) : seg < p.nseg - 1);
+    const bool init_state = C::kOut && gs != nullptr &&
+                            (DIR == Dir::Forward ? (seg > 0 || p.has_init) : (seg < p.nseg - 1 || p.has_init));
+    // A reverse output pass with a carried-in state (the gradient of a carried-out forward state)
+    // has it attached at the chain's last position: on the chain's last tile, the first this
+    // workgroup processes, its rows are weighted lam^(leff-1-i) and it is carried on with
+    // lam^(leff-1), leff the tile's real length.
+    const bool end_init = DIR == Dir::Reverse && C::kOut && p.has_init && seg == p.nseg - 1;
+    const int leff_end = (int)min((int64_t)TB, T - (NT - 1) * TB);
 #pragma unroll
     for (int s = 0; s < C::SPW; ++s) {
         const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
@@ -368,7 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                     if constexpr (DECAY) {
                         // every accumulator of this lane belongs to the row tb*32 + col
                         const int i = tb * 32 + col;
-                        const float w = pw(DIR == Dir::Forward ? i + 1 : TB - i);
+                        int e = DIR == Dir::Forward ? i + 1 : TB - i;
+                        if (DIR == Dir::Reverse && end_init && it == 0) e = leff_end - 1 - i;
+                        const float w = e >= 0 ? pw(e) : 0.0f;
 #pragma unroll
                         for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         if (update) {
             if (s_active) {
                 if constexpr (DECAY && !kFlip) {
-                    const float f = pw(TB);
+                    const float f = (DIR == Dir::Reverse && end_init && it == 0) ? pw(leff_end - 1) : pw(TB);
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
                 }
@@ -558,17 +566,22 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         }
     }
 
-    // Carried-out final state: the last tile's update, which the loop leaves out, over the tile's
+    // Carried-out state, from the workgroup that processes the chain's last tile in scan order.
+    // Forward: the final state, i.e. the last tile's update (which the loop leaves out) over its
     // `leff` real positions, S = lam^leff S + sum_{j < leff} lam^(leff-1-j) k_j v_j^T (exact for a
-    // ragged last tile).  The last tile is still in LDS and nothing writes LDS any more.
-    if constexpr (C::kOut && DIR == Dir::Forward) {
-        if (p.state_out != nullptr && seg == p.nseg - 1 && s_active) {
+    // ragged last tile).  Reverse: lam times the state at position 0, R = lam^TB R + sum_j lam^j
+    // b_j c_j^T over tile 0 (rows past T are zero) -- the gradient of a carried-in forward state.
+    // The last tile is still in LDS and nothing writes LDS any more; its weights are applied to the
+    // fragments in registers (the weighted copy may hold staged outputs by now).
+    if constexpr (C::kOut) {
+        const bool want = p.state_out != nullptr && s_active && (DIR == Dir::Forward ? seg == p.nseg - 1 : seg == 0);
+        if (want) {
             const int last = ntiles - 1;
             const u16 *cur = smem + (C::kDMA ? (last & 1) * C::TILE : 0);
             const u16 *sK = cur + C::oK, *sV = cur + C::oV;
             const int leff = (int)min((int64_t)TB, T - tile_of(last) * TB);
             if constexpr (DECAY) {
-                const float f = pw(leff);
+                const float f = DIR == Dir::Forward ? pw(leff) : (end_init && ntiles == 1 ? pw(leff_end - 1) : pw(TB));
 #pragma unroll
                 for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
             }
@@ -578,24 +591,32 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 for (int x = 0; x < TB / 16; ++x) {
                     bf16x8 kf = frag_tr<D, false>(sK, 16 * x, kb * 32, lane);
                     if constexpr (DECAY) {
-                        // rows j = 16x + 8h + e: weight lam^(leff-1-j), and 0 past the sequence end
+                        // rows j = 16x + 8h + e: forward lam^(leff-1-j) and 0 past the sequence end,
+                        // reverse lam^j
                         u32x4 u = __builtin_bit_cast(u32x4, kf);
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
                             const int j = 16 * x + 8 * h + 2 * m;
-                            const float wl = j < leff ? __builtin_amdgcn_exp2f((float)(leff - 1 - j) * l2) : 0.0f;
-                            const float wh = j + 1 < leff ? __builtin_amdgcn_exp2f((float)(leff - 2 - j) * l2) : 0.0f;
+                            float wl, wh;
+                            if constexpr (DIR == Dir::Forward) {
+                                wl = j < leff ? __builtin_amdgcn_exp2f((float)(leff - 1 - j) * l2) : 0.0f;
+                                wh = j + 1 < leff ? __builtin_amdgcn_exp2f((float)(leff - 2 - j) * l2) : 0.0f;
+                            } else {
+                                wl = __builtin_amdgcn_exp2f((float)j * l2);
+                                wh = __builtin_amdgcn_exp2f((float)(j + 1) * l2);
+                            }
                             u[m] = pack_bf16(__uint_as_float(u[m] << 16) * wl, __uint_as_float(u[m] & 0xffff0000u) * wh);
                         }
                         kf = __builtin_bit_cast(bf16x8, u);
                     }
                     sacc[s] = mfma(kf, frag_tr<DV, false>(sV, 16 * x, nb * 32, lane), sacc[s]);
                 }
+                const float scale = DIR == Dir::Reverse ? pw(1) : 1.0f;
                 float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    so[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
+                    so[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r] * scale;
                 }
             }
         }

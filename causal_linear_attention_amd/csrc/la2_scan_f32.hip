@@ -50,8 +50,12 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
     const float l2 = has_decay ? log2f(p.decay[chain % p.H]) : 0.0f;
     auto pw = [&](int n) -> float { return has_decay ? exp2f((float)n * l2) : 1.0f; };
 
-    const bool init_state =
-        kOut && gs != nullptr && (DIR == Dir::Forward ? (seg > 0 || p.has_init) : seg < p.nseg - 1);
+    const bool init_state = kOut && gs != nullptr &&
+                            (DIR == Dir::Forward ? (seg > 0 || p.has_init) : (seg < p.nseg - 1 || p.has_init));
+    // reverse with a carried-in state: attached at the chain's last position (weights lam^(leff-1-i)
+    // and carry lam^(leff-1) on the chain's last tile, the first this workgroup processes)
+    const bool end_init = DIR == Dir::Reverse && kOut && p.has_init && seg == p.nseg - 1;
+    const int leff_end = (int)min((int64_t)TB, T - (NT - 1) * TB);
     for (int e = tid; e < D * DV; e += kThreads)
         sS[e] = init_state ? gs[p.states_t ? (int64_t)(e % DV) * D + e / DV : (int64_t)(e / DV) * p.DVT + e % DV] : 0.0f;
 
@@ -89,7 +93,9 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
                 const int i = e / DV, n = e % DV;
                 float inter = 0.0f;
                 for (int c = 0; c < D; ++c) inter = fmaf(sQ[i * D + c], sS[c * DV + n], inter);
-                float acc = inter * pw(DIR == Dir::Forward ? i + 1 : TB - i);
+                int ew = DIR == Dir::Forward ? i + 1 : TB - i;
+                if (end_init && it == 0) ew = leff_end - 1 - i;
+                float acc = ew >= 0 ? inter * pw(ew) : 0.0f;
                 for (int j = 0; j < TB; ++j) acc = fmaf(sP[i * TB + j], sV[j * DV + n], acc);
                 const int64_t t = t0 + i;
                 if (t < T) gy[t * p.DVT + n] = acc;
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
         }
         // Step 4 state update
         if (update) {
-            const float f = pw(TB);
+            const float f = (end_init && it == 0) ? pw(leff_end - 1) : pw(TB);
             for (int e = tid; e < D * DV; e += kThreads) {
                 const int c = e / DV, n = e % DV;
                 float acc = sS[e] * f;
@@ -113,19 +119,23 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
         for (int e = tid; e < D * DV; e += kThreads) gs[(int64_t)(e / DV) * p.DVT + e % DV] = sS[e];
     }
 
-    // Carried-out final state: the last tile's update, which the loop leaves out, over its `leff`
-    // real positions (exact for a ragged last tile); the last tile is still in LDS.
-    if constexpr (kOut && DIR == Dir::Forward) {
-        if (p.state_out != nullptr && seg == p.nseg - 1) {
+    // Carried-out state, from the workgroup that processes the chain's last tile in scan order
+    // (the tile is still in LDS).  Forward: the final state, the last tile's update over its `leff`
+    // real positions.  Reverse: lam times the state at position 0, the update over tile 0 (rows
+    // past T are zero) -- the gradient of a carried-in forward state.
+    if constexpr (kOut) {
+        if (p.state_out != nullptr && (DIR == Dir::Forward ? seg == p.nseg - 1 : seg == 0)) {
             __syncthreads();
-            const int leff = (int)min((int64_t)TB, T - (tile_hi - 1) * TB);
-            const float f = pw(leff);
+            const int leff = (int)min((int64_t)TB, T - (DIR == Dir::Forward ? tile_hi - 1 : tile_lo) * TB);
+            const float f = DIR == Dir::Forward ? pw(leff) : (end_init && ntiles == 1 ? pw(leff_end - 1) : pw(TB));
+            const float scale = DIR == Dir::Forward ? 1.0f : pw(1);
             float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
             for (int e = tid; e < D * DV; e += kThreads) {
                 const int c = e / DV, n = e % DV;
                 float acc = sS[e] * f;
-                for (int j = 0; j < leff; ++j) acc = fmaf(sK[j * D + c] * pw(leff - 1 - j), sV[j * DV + n], acc);
-                so[(int64_t)c * p.DVT + n] = acc;
+                for (int j = 0; j < leff; ++j)
+                    acc = fmaf(sK[j * D + c] * pw(DIR == Dir::Forward ? leff - 1 - j : j), sV[j * DV + n], acc);
+                so[(int64_t)c * p.DVT + n] = acc * scale;
             }
         }
     }

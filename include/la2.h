@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 5
+#define LA2_ABI_VERSION 6
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -104,8 +104,7 @@ int la2_forward(const void *q, const void *k, const void *v, const float *decay,
  *   NULL (start from zero / do not write the final state).  state_out may be
  *   the same pointer as state_in (updated in place) but may not otherwise
  *   overlap it, an input, o or the workspace.  Other arguments and the
- *   workspace as in la2_forward.  No backward is provided for a non-zero
- *   state_in (la2_backward assumes the sequence starts from zero). */
+ *   workspace as in la2_forward.  Its backward is la2_backward_state. */
 int la2_forward_state(const void *q, const void *k, const void *v, const float *decay,
                       const float *state_in, void *o, float *state_out, int64_t B, int64_t H,
                       int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
@@ -184,8 +183,26 @@ int la2_backward_saved(const void *q, const void *k, const void *v, const float 
                        int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,
                        size_t workspace_bytes, void *stream);
 
-/* Workspace bytes needed by la2_forward / la2_forward_state (backward = 0) or la2_backward and
- * la2_backward_saved (backward = 1) for these sizes; the backward size is never
+/* Backward of la2_forward_state: the gradients of <o, dout> + <state_out, dstate_out> with
+ * respect to q, k, v and the carried-in state, so that a sequence trained in chunks, each chunk's
+ * forward carried in from the state the previous one left and its d(state_in) passed back as the
+ * previous chunk's dstate_out, gets the gradients of the whole sequence.  By the chain rule
+ * through S_t = lam S_{t-1} + k_t v_t^T (S_{-1} = state_in):
+ *     dq_t = S_t do_t;   R_{T-1} = q_{T-1} do_{T-1}^T + dstate_out,
+ *     R_t = lam R_{t+1} + q_t do_t^T;   dk_t = R_t v_t;   dv_t = R_t^T k_t;
+ *     dstate_in = lam R_0.
+ *   state_in, dstate_out: device fp32 [B, H, d, d_v] or NULL (zero); dstate_in: device fp32
+ *   [B, H, d, d_v] or NULL (not written).  dstate_in may not overlap anything else; the inputs may
+ *   overlap each other.  Other arguments and the workspace (la2_workspace_bytes(..., 1)) as in
+ *   la2_backward; with both states NULL it computes what la2_backward does. */
+int la2_backward_state(const void *q, const void *k, const void *v, const float *decay,
+                       const float *state_in, const void *dout, const float *dstate_out, void *dq,
+                       void *dk, void *dv, float *dstate_in, int64_t B, int64_t H, int64_t T,
+                       int64_t d, int64_t d_v, int block, int dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by la2_forward / la2_forward_state (backward = 0) or la2_backward,
+ * la2_backward_saved and la2_backward_state (backward = 1) for these sizes; the backward size is never
  * smaller, so one workspace of that size serves a forward + backward step.
  * (size_t)-1 for arguments that la2_forward/la2_backward would reject. */
 size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,

@@ -183,6 +183,29 @@ def test_forward_serial_validation(lib):
     assert ser(lib, decay=P + 3 * MB + 64) == ALIAS            # o over the decays
 
 
+def bst(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, s_in=P + 8 * MB, do=P + 3 * MB, ds_out=P + 9 * MB,
+        dq=P + 4 * MB, dk=P + 5 * MB, dv_=P + 6 * MB, ds_in=P + 10 * MB, B=1, H=1, T=64, d=64, dv=64, block=64,
+        dtype=1, ws=None, wsb=0):
+    return lib.la2_backward_state(q, k, v, decay, s_in, do, ds_out, dq, dk, dv_, ds_in, B, H, T, d, dv, block,
+                                  dtype, ws, wsb, None)
+
+
+def test_backward_state_validation(lib):
+    assert bst(lib, q=None) == NULLP
+    assert bst(lib, dq=None) == NULLP
+    assert bst(lib, T=0) == SHAPE
+    assert bst(lib, d=96) == UNSUP
+    assert bst(lib, s_in=P + 8 * MB + 4) == MISAL
+    assert bst(lib, ds_in=P + 10 * MB + 8) == MISAL
+    assert bst(lib, ds_in=P + 3 * MB) == ALIAS                # d(state_in) over dout
+    assert bst(lib, ds_in=P + 9 * MB + 64) == ALIAS           # ... inside dstate_out
+    assert bst(lib, ds_in=P + 4 * MB + 256) == ALIAS          # ... inside dq
+    assert bst(lib, dq=P + 8 * MB) == ALIAS                   # dq over state_in
+    assert bst(lib, T=1024) == WS                             # split chain, no workspace
+    n = la2.la2_workspace_bytes(1, 1, 1024, 64, 64, 64, torch.bfloat16, True)
+    assert bst(lib, T=1024, ws=P + 9 * MB, wsb=n) == ALIAS    # workspace over dstate_out
+
+
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):

@@ -152,3 +152,89 @@ def test_decode_step_from_zero_is_one_position():
     torch.cuda.synchronize()
     assert rel_err(f64(o), ref) <= 2e-2
     assert rel_err(f64(state), np.einsum("bhi,bhj->bhij", f64(x["k"])[:, :, 0], f64(x["v"])[:, :, 0])) <= 1e-6
+
+
+# ---- backward from carried states ----------------------------------------------------------------
+
+BCASES = [
+    # (B, H, T, d, dv, dtype, block, decay)
+    (1, 2, 777, 128, 128, "bf16", 128, "heads"),      # fused dk/dv, split chains, ragged last tile
+    (2, 3, 700, 64, 128, "bf16", 64, "heads"),        # separate reverse scans (d != d_v), split
+    (16, 16, 200, 128, 128, "bf16", 128, "heads"),    # 256 chains: unsplit, states read directly
+    (1, 3, 333, 128, 64, "bf16", 128, "none"),
+    (2, 2, 64, 128, 128, "bf16", 64, "heads"),        # one fused tile: the only tile carries the gradient
+    (1, 1, 50, 64, 64, "bf16", 64, "heads"),          # one ragged tile
+    (1, 2, 300, 64, 64, "f32", 32, "heads"),
+    (16, 16, 70, 64, 64, "f32", 64, "heads"),         # fp32, unsplit
+]
+
+
+def check_backward_state(B, H, T, d, dv, dtype, block, decay, seed, with_in=True, with_out=True):
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=seed, decay=decay, backward=True)
+    q, k, v, dec = to_dev(x)
+    do = x["do"].to(DEV)
+    s_in = seeded_state(B, H, d, dv, seed + 1) if with_in else None
+    g_out = seeded_state(B, H, d, dv, seed + 2) if with_out else None
+    dq, dk, dv_, ds_in = la2.backward_state(q, k, v, do, dec, block,
+                                            None if s_in is None else s_in.to(DEV),
+                                            None if g_out is None else g_out.to(DEV))
+    ref = oracle.backward_state(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x),
+                                None if s_in is None else f64(s_in), None if g_out is None else f64(g_out))
+    torch.cuda.synchronize()
+    errs = [rel_err(f64(g), r) for g, r in zip((dq, dk, dv_, ds_in), ref)]
+    print((B, H, T, d, dv, dtype, block, decay, with_in, with_out), " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("case", BCASES, ids=lambda c: f"B{c[0]}H{c[1]}T{c[2]}d{c[3]}dv{c[4]}{c[5]}tb{c[6]}{c[7]}")
+def test_backward_state_matches_oracle(case):
+    check_backward_state(*case, seed=301 + case[2])
+
+
+@pytest.mark.parametrize("with_in,with_out", [(True, False), (False, True), (False, False)])
+def test_backward_state_partial(with_in, with_out):
+    check_backward_state(1, 3, 500, 128, 128, "bf16", 128, "heads", 17, with_in, with_out)
+    check_backward_state(1, 3, 500, 64, 128, "bf16", 64, "heads", 19, with_in, with_out)
+
+
+@pytest.mark.parametrize("env", [{"LA2_SEGMENT_TILES": "2"}, {"LA2_SEGMENT_TILES": "4", "LA2_STATE_SUB": "2"},
+                                 {"LA2_SEPARATE_DKDV": "1", "LA2_SEGMENT_TILES": "3"},
+                                 {"LA2_SLICE_WIDTH": "64", "LA2_SEGMENT_TILES": "2"}],
+                         ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
+def test_backward_state_plans(env, monkeypatch):
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    check_backward_state(1, 2, 777, 128, 128, "bf16", 128, "heads", 23)
+    check_backward_state(1, 2, 601, 64, 64, "f32", 32, "heads", 29)
+
+
+@pytest.mark.parametrize("dtype,d,block", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 64, 32)])
+def test_chunked_training(dtype, d, block):
+    """One sequence trained in uneven chunks: forwards carried through the states, backwards in
+    reverse order with each chunk's d(state_in) passed to the previous chunk as d(state_out); the
+    chunk gradients together equal the oracle's whole-sequence ones."""
+    B, H, T = 1, 4, 1000
+    x = inputs.make_random(B, H, T, d, d, dtype=dtype, seed=83, decay="heads", backward=True)
+    q, k, v, dec = to_dev(x)
+    do = x["do"].to(DEV)
+    G = seeded_state(B, H, d, d, 89)
+    cuts = [0, 300, 301, 751, 1000]
+    states = [None]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = slice(a, b)
+        _, s_next = la2.forward_state(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(),
+                                      dec, block, state_in=states[-1])
+        states.append(s_next)
+    grads, g_out = [], G.to(DEV)
+    for c in range(len(cuts) - 2, -1, -1):
+        sl = slice(cuts[c], cuts[c + 1])
+        dq, dk, dv_, g_out = la2.backward_state(*(t[:, :, sl].contiguous() for t in (q, k, v, do)), dec, block,
+                                                states[c], g_out)
+        grads.append((dq, dk, dv_))
+    grads.reverse()
+    ref = oracle.backward_state(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), None, f64(G))
+    torch.cuda.synchronize()
+    for i in range(3):
+        got = torch.cat([g[i] for g in grads], dim=2)
+        assert rel_err(f64(got), ref[i]) <= TOL[dtype], i
+    assert rel_err(f64(g_out), ref[3]) <= TOL[dtype]
