@@ -7,6 +7,7 @@ without it.
 from .binding import (  # noqa: F401
     LA2Error,
     LA2Function,
+    LA2StateFunction,
     backward,
     backward_state,
     decode_step,
@@ -27,6 +28,7 @@ from .binding import (  # noqa: F401
     la2_status_string,
     la2_workspace_bytes,
     lightning_attention,
+    lightning_attention_state,
     load_library,
     normalized_workspace_for,
     workspace_for,

@@ -371,3 +371,33 @@ class LA2Function(torch.autograd.Function):
 def lightning_attention(q, k, v, decay=None, block=128):
     """o = attention(q, k, v) with autograd support."""
     return LA2Function.apply(q, k, v, decay, block)
+
+
+class LA2StateFunction(torch.autograd.Function):
+    """autograd bridge of the state-carrying forward (la2_forward_state / la2_backward_state):
+    (o, state_out) from (q, k, v, state_in), differentiable in q, k, v and state_in, so a long
+    sequence can be trained in chunks, each chunk started from the state the previous one left."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, state_in, decay=None, block=128):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        s_in = None if state_in is None else state_in.contiguous()
+        o, state_out = forward_state(q, k, v, decay, block, s_in)
+        ctx.save_for_backward(q, k, v, s_in, decay)
+        ctx.block = block
+        return o, state_out
+
+    @staticmethod
+    def backward(ctx, dout, dstate_out):
+        q, k, v, s_in, decay = ctx.saved_tensors
+        if dout is None:
+            dout = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+        dq, dk, dv, dstate_in = backward_state(q, k, v, dout.contiguous(), decay, ctx.block, s_in,
+                                               None if dstate_out is None else dstate_out.contiguous())
+        return dq, dk, dv, (dstate_in if s_in is not None else None), None, None
+
+
+def lightning_attention_state(q, k, v, state_in=None, decay=None, block=128):
+    """(o, state_out) = attention(q, k, v) carried in from state_in (fp32 [B, H, d, d_v] or None),
+    with autograd support through q, k, v and state_in."""
+    return LA2StateFunction.apply(q, k, v, state_in, decay, block)

@@ -238,3 +238,32 @@ def test_chunked_training(dtype, d, block):
         got = torch.cat([g[i] for g in grads], dim=2)
         assert rel_err(f64(got), ref[i]) <= TOL[dtype], i
     assert rel_err(f64(g_out), ref[3]) <= TOL[dtype]
+
+
+def test_autograd_chunked_training_matches_whole():
+    """lightning_attention_state in PyTorch autograd: a loss over a sequence run in two chunks (the
+    second from the first's state, through which gradients flow) gives the whole run's gradients."""
+    x = inputs.make_random(1, 3, 600, 128, 128, dtype="bf16", seed=97, decay="heads", backward=True)
+    dec = x["decay"].to(DEV)
+    do = x["do"].to(DEV)
+    G = seeded_state(1, 3, 128, 128, 98).to(DEV)
+
+    def grads(cut):
+        q, k, v = (x[n].to(DEV).requires_grad_(True) for n in ("q", "k", "v"))
+        if cut is None:
+            o, s = la2.lightning_attention_state(q, k, v, None, dec, 128)
+        else:
+            sl1, sl2 = slice(0, cut), slice(cut, 600)
+            o1, s1 = la2.lightning_attention_state(q[:, :, sl1], k[:, :, sl1], v[:, :, sl1], None, dec, 128)
+            o2, s = la2.lightning_attention_state(q[:, :, sl2], k[:, :, sl2], v[:, :, sl2], s1, dec, 128)
+            o = torch.cat([o1, o2], dim=2)
+        loss = (o.float() * do.float()).sum() + (s * G).sum()
+        loss.backward()
+        return q.grad, k.grad, v.grad
+
+    whole = grads(None)
+    chunked = grads(257)
+    torch.cuda.synchronize()
+    ref = oracle.backward_state(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), None, f64(G))
+    for a, b, r in zip(whole, chunked, ref):
+        assert rel_err(f64(a), r) <= 2e-2 and rel_err(f64(b), r) <= 2e-2
