@@ -14,7 +14,8 @@ Two independent formulations live here, both in fp64:
   ``forward_rows`` / ``backward_rows`` evaluate single rows from the closed
   sums, for spot checks of very long sequences.  ``forward_normalized`` is
   the same section's whole output, phi(q)^T S / phi(q)^T z with the
-  denominator sum z_t = lam z_{t-1} + phi(k_t) and phi = identity or elu + 1.
+  denominator sum z_t = lam z_{t-1} + phi(k_t) and phi = identity or elu + 1;
+  ``backward_normalized`` its backward.
   ``backward_state`` is the backward of ``forward_state``: gradients of
   <o, do> + <state_out, dstate_out> including the one of the carried-in state.
 * ``tiled_forward`` / ``tiled_backward`` (numpy, this file): the same page's
@@ -57,6 +58,8 @@ def _bind(lib):
     lib.la2_oracle_forward_state.restype = None
     lib.la2_oracle_backward_state.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
     lib.la2_oracle_backward_state.restype = None
+    lib.la2_oracle_backward_normalized.argtypes = [I, I, I, I, P, P, P, P, P, ctypes.c_int, P, P, P]
+    lib.la2_oracle_backward_normalized.restype = None
     lib.la2_oracle_forward_normalized.argtypes = [I, I, I, I, P, P, P, P, ctypes.c_int, P]
     lib.la2_oracle_forward_normalized.restype = None
     lib.la2_oracle_backward.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
@@ -127,6 +130,17 @@ class Oracle:
         self.lib.la2_oracle_forward_state(B * H, T, d, dv, _ptr(lams), _ptr(q), _ptr(k), _ptr(v),
                                           None if s_in is None else _ptr(s_in), _ptr(o), _ptr(s_out))
         return o, s_out
+
+    def backward_normalized(self, q, k, v, do, lam=None, feature_map="elu1"):
+        """(dq, dk, dv) of <o, do> for the normalized output."""
+        fmap = {"identity": 0, "elu1": 1}[feature_map]
+        q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+        B, H, T, d = q.shape
+        dq, dk, dvo = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        lams = _chain_lams(lam, B, H)
+        self.lib.la2_oracle_backward_normalized(B * H, T, d, v.shape[-1], _ptr(lams), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(do), fmap, _ptr(dq), _ptr(dk), _ptr(dvo))
+        return dq, dk, dvo
 
     def backward_state(self, q, k, v, do, lam=None, state_in=None, dstate_out=None):
         """(dq, dk, dv, dstate_in) of <o, do> + <state_out, dstate_out> for the forward from state_in."""
@@ -223,6 +237,10 @@ def forward_normalized(q, k, v, lam=None, feature_map="elu1"):
 
 def backward_state(q, k, v, do, lam=None, state_in=None, dstate_out=None):
     return load().backward_state(q, k, v, do, lam, state_in, dstate_out)
+
+
+def backward_normalized(q, k, v, do, lam=None, feature_map="elu1"):
+    return load().backward_normalized(q, k, v, do, lam, feature_map)
 
 
 def backward(q, k, v, do, lam=None):

@@ -29,7 +29,8 @@
  *
  * la2_oracle_forward_normalized is the full output of the same section 1, numerator
  * over denominator, with a feature map phi (identity, or elu + 1) and the decay
- * applied to the denominator's prefix sum z_t = lam z_{t-1} + phi(k_t) as to S.
+ * applied to the denominator's prefix sum z_t = lam z_{t-1} + phi(k_t) as to S;
+ * la2_oracle_backward_normalized is its backward, by the chain rule through the ratio.
  *
  * The *_rows entry points evaluate the same quantities one output row at a
  * time from the closed sums
@@ -167,6 +168,100 @@ void la2_oracle_forward_normalized(int64_t n_chains, int64_t T, int64_t d, int64
  *   R_{T-1} = q_{T-1} do_{T-1}^T + ds_out,   R_t = lam R_{t+1} + q_t do_t^T
  *   dk_t = R_t v_t,   dv_t = R_t^T k_t,   ds_in = lam R_0
  * s_in, ds_out: NULL for zero; ds_in: NULL when not wanted. */
+/* Derivative of the feature map: 1 for the identity, 1 above 0 and e^x at or below for elu + 1. */
+static double feature_deriv(double x, int fmap)
+{
+    if (fmap == 1)
+        return x > 0.0 ? 1.0 : exp(x);
+    return 1.0;
+}
+
+/* Backward of la2_oracle_forward_normalized for the loss <o, dout>, by the chain rule through
+ * o_t = n_t / den_t, n_t = S_t^T pq_t, den_t = z_t . pq_t (pq = phi(q), pk = phi(k)):
+ *   dn_t = do_t / den_t,   dden_t = -(do_t . o_t) / den_t
+ *   d pq_t = S_t dn_t + dden_t z_t
+ *   R_t = lam R_{t+1} + pq_t dn_t^T,   y_t = lam y_{t+1} + dden_t pq_t     (reverse sweep)
+ *   d pk_t = R_t v_t + y_t,   dv_t = R_t^T pk_t
+ *   dq = d pq (.) phi'(q),   dk = d pk (.) phi'(k). */
+void la2_oracle_backward_normalized(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
+                                    const double *lam, const double *q, const double *k,
+                                    const double *v, const double *dout, int fmap, double *dq,
+                                    double *dk, double *dvo)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < n_chains; ++c) {
+        const double l = lam[c];
+        const double *qc = q + c * T * d, *kc = k + c * T * d, *vc = v + c * T * dv, *gc = dout + c * T * dv;
+        double *dqc = dq + c * T * d, *dkc = dk + c * T * d, *dvc = dvo + c * T * dv;
+        double *S = (double *)calloc((size_t)(d * dv), sizeof(double));
+        double *z = (double *)calloc((size_t)d, sizeof(double));
+        double *pq = (double *)malloc((size_t)(T * d) * sizeof(double));
+        double *pk = (double *)malloc((size_t)(T * d) * sizeof(double));
+        double *dn = (double *)malloc((size_t)(T * dv) * sizeof(double));
+        double *dden = (double *)malloc((size_t)T * sizeof(double));
+        for (int64_t e = 0; e < T * d; ++e) {
+            pq[e] = feature(qc[e], fmap);
+            pk[e] = feature(kc[e], fmap);
+        }
+        /* forward sweep: S_t, z_t, the output, then d pq_t */
+        for (int64_t t = 0; t < T; ++t) {
+            const double *pqt = pq + t * d, *pkt = pk + t * d, *vt = vc + t * dv, *gt = gc + t * dv;
+            double den = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                z[i] = l * z[i] + pkt[i];
+                den += z[i] * pqt[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    S[i * dv + j] = l * S[i * dv + j] + pkt[i] * vt[j];
+            }
+            double go = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+                double num = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    num += S[i * dv + j] * pqt[i];
+                go += gt[j] * (num / den);
+                dn[t * dv + j] = gt[j] / den;
+            }
+            dden[t] = -go / den;
+            for (int64_t i = 0; i < d; ++i) {
+                double acc = dden[t] * z[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += S[i * dv + j] * dn[t * dv + j];
+                dqc[t * d + i] = acc * feature_deriv(qc[t * d + i], fmap);
+            }
+        }
+        /* reverse sweep: R_t, y_t, then d pk_t and dv_t */
+        double *R = S, *y = z;
+        memset(R, 0, sizeof(double) * (size_t)(d * dv));
+        memset(y, 0, sizeof(double) * (size_t)d);
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const double *pqt = pq + t * d, *pkt = pk + t * d, *vt = vc + t * dv;
+            for (int64_t i = 0; i < d; ++i) {
+                y[i] = l * y[i] + dden[t] * pqt[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    R[i * dv + j] = l * R[i * dv + j] + pqt[i] * dn[t * dv + j];
+            }
+            for (int64_t i = 0; i < d; ++i) {
+                double acc = y[i];
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += vt[j] * R[i * dv + j];
+                dkc[t * d + i] = acc * feature_deriv(kc[t * d + i], fmap);
+            }
+            for (int64_t j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < d; ++i)
+                    acc += R[i * dv + j] * pkt[i];
+                dvc[t * dv + j] = acc;
+            }
+        }
+        free(S);
+        free(z);
+        free(pq);
+        free(pk);
+        free(dn);
+        free(dden);
+    }
+}
+
 void la2_oracle_backward_state(int64_t n_chains, int64_t T, int64_t d, int64_t dv,
                                const double *lam, const double *q, const double *k,
                                const double *v, const double *dout, const double *s_in,

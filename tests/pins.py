@@ -359,6 +359,42 @@ def pin_backward_state_chunks(orc):
            "d(state_in) closed form")
 
 
+def pin_backward_normalized(orc):
+    """backward_normalized == central differences of <o, do> (elu + 1, and the identity on positive
+    inputs) and == torch autograd (float64) through the masked-product ratio with the map applied."""
+    import torch
+    q, k, v, do, lam = _setup(181, B=1, H=2, T=6, d=3, dv=2)
+    for fmap in ("elu1", "identity"):
+        qq, kk = (q, k) if fmap == "elu1" else (np.abs(q) + 0.5, np.abs(k) + 0.5)
+        dq, dk, dv = orc.backward_normalized(qq, kk, v, do, lam, fmap)
+
+        def loss(q_, k_, v_):
+            return float(np.sum(orc.forward_normalized(q_, k_, v_, lam, fmap) * do))
+
+        h = 1e-6
+        for name, arr, got in (("q", qq, dq), ("k", kk, dk), ("v", v, dv)):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                a1, a2 = arr.copy(), arr.copy()
+                a1[idx] += h
+                a2[idx] -= h
+                args1, args2 = [qq, kk, v], [qq, kk, v]
+                pos = ("q", "k", "v").index(name)
+                args1[pos], args2[pos] = a1, a2
+                num[idx] = (loss(*args1) - loss(*args2)) / (2 * h)
+            _close(got, num, 1e-7, f"backward_normalized {fmap} d{name}")
+        tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (qq, kk, v))
+        phi = (lambda x: torch.where(x > 0, x + 1.0, torch.exp(torch.clamp(x, max=0.0)))) if fmap == "elu1" else (lambda x: x)
+        outs = []
+        for hh in range(2):
+            D = torch.tensor(_decay_matrix(6, lam[hh]))
+            A = (phi(tq[0, hh]) @ phi(tk[0, hh]).T) * D
+            outs.append((A @ tv[0, hh]) / A.sum(dim=1, keepdim=True))
+        (torch.stack(outs)[None] * torch.tensor(do)).sum().backward()
+        for name, got, ref in (("q", dq, tq.grad), ("k", dk, tk.grad), ("v", dv, tv.grad)):
+            _close(got, ref.numpy(), 1e-12, f"backward_normalized {fmap} d{name} vs autograd")
+
+
 ALL_PINS = [
     pin_golden_handworked,
     pin_bruteforce_forward,
@@ -378,4 +414,5 @@ ALL_PINS = [
     pin_normalized_invariants,
     pin_backward_state_finite_differences,
     pin_backward_state_chunks,
+    pin_backward_normalized,
 ]

@@ -66,6 +66,15 @@ MUTANTS = [
     ("backward_ignores_state_in",
      "            for (int64_t e = 0; e < d * dv; ++e)\n                S[e] = s_in[c * d * dv + e];",
      "            for (int64_t e = 0; e < d * dv; ++e)\n                S[e] = 0.0 * s_in[c * d * dv + e];"),
+    ("normalized_backward_dden_sign",
+     "dden[t] = -go / den;",
+     "dden[t] = go / den;"),
+    ("normalized_backward_no_feature_deriv",
+     "dkc[t * d + i] = acc * feature_deriv(kc[t * d + i], fmap);",
+     "dkc[t * d + i] = acc;"),
+    ("normalized_backward_y_undecayed",
+     "y[i] = l * y[i] + dden[t] * pqt[i];",
+     "y[i] = y[i] + dden[t] * pqt[i];"),
     ("rows_skip_diagonal",
      "for (int64_t s = 0; s <= t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q",
      "for (int64_t s = 0; s < t; ++s) {\n            const double w = pow(lam, (double)(t - s)) * dot(q"),
