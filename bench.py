@@ -195,6 +195,13 @@ def normalized_bench(args):
 
     ms_n = timed(lambda: la2.la2_forward_normalized(q, k, v, decay, o, "elu1", w.block, ws_n, stream))
     ms_f = timed(lambda: la2.la2_forward(q, k, v, decay, o, w.block, ws_f, stream))
+    # the backward of the same normalized forward (o from it)
+    do = x["do"].to(dev)
+    la2.la2_forward_normalized(q, k, v, decay, o, "elu1", w.block, ws_n, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_b = la2.normalized_workspace_for(q, v, "elu1", w.block, True)
+    ms_b = timed(lambda: la2.la2_backward_normalized(q, k, v, decay, o, do, dq, dk, dv, "elu1", w.block, ws_b,
+                                                     stream))
     th = w.B * w.H * w.T
     byts = th * 4 * w.d * 2
     achieved = byts / (ms_n * 1e-3) / 1e9
@@ -217,6 +224,9 @@ def normalized_bench(args):
                    "parallelism": "none (1 GPU)"},
         "plain_forward_ms": round(ms_f, 5),
         "plain_forward_tokens_per_s": round(w.B * w.T / (ms_f * 1e-3), 1),
+        "backward_ms": round(ms_b, 5),
+        "fwd_bwd_tokens_per_s": round(w.B * w.T / ((ms_n + ms_b) * 1e-3), 1),
+        "backward_hbm_frac": round(th * 7 * w.d * 2 / (ms_b * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "la2_forward_normalized (denominator + numerator scan + division launches)",

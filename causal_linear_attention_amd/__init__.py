@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     LA2Function,
     LA2StateFunction,
     backward,
+    backward_normalized,
     backward_state,
     decode_step,
     forward,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     forward_state,
     la2_abi_version,
     la2_backward,
+    la2_backward_normalized,
     la2_backward_saved,
     la2_backward_state,
     la2_decode_step,

@@ -21,7 +21,7 @@ LA2_PHI_ELU1 = 1
 _FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
 
 EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
-           "la2_backward", "la2_backward_state",
+           "la2_backward", "la2_backward_state", "la2_backward_normalized",
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
 
@@ -60,7 +60,10 @@ def load_library(path=LIB_PATH):
     lib.la2_backward_state.restype = i32
     lib.la2_forward_serial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.la2_forward_serial.restype = i32
-    lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.la2_backward_normalized.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32,
+                                            i32, vp, sz, vp]
+    lib.la2_backward_normalized.restype = i32
+    lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32]
     lib.la2_normalized_workspace_bytes.restype = sz
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
     lib.la2_workspace_bytes.restype = sz
@@ -105,9 +108,10 @@ def feature_map_code(feature_map):
         raise ValueError(f"unknown feature map {feature_map!r}; use 'identity' or 'elu1'") from None
 
 
-def la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map, block, dtype):
+def la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map, block, dtype, backward=False):
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
-    n = load_library().la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map_code(feature_map), block, code)
+    n = load_library().la2_normalized_workspace_bytes(B, H, T, d, d_v, feature_map_code(feature_map), block, code,
+                                                      1 if backward else 0)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("unsupported arguments for la2_normalized_workspace_bytes")
     return n
@@ -212,6 +216,20 @@ def la2_forward_serial(q, k, v, decay, o, stream=None):
         raise LA2Error(st, "la2_forward_serial")
 
 
+def la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace=None, stream=None):
+    """Enqueue (dq, dk, dv) = gradients of <o, dout> for the normalized forward that returned o."""
+    B, H, T, d = q.shape
+    d_v = v.shape[-1]
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().la2_backward_normalized(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
+        _dev_ptr(dout, "dout"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
+        B, H, T, d, d_v, feature_map_code(feature_map), int(block), dtype_code(q.dtype),
+        _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_backward_normalized")
+
+
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
     la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
@@ -290,9 +308,9 @@ def forward_state(q, k, v, decay=None, block=128, state_in=None, workspace=None)
     return o, state_out
 
 
-def normalized_workspace_for(q, v, feature_map, block):
+def normalized_workspace_for(q, v, feature_map, block, backward=False):
     B, H, T, d = q.shape
-    n = la2_normalized_workspace_bytes(B, H, T, d, v.shape[-1], feature_map, block, q.dtype)
+    n = la2_normalized_workspace_bytes(B, H, T, d, v.shape[-1], feature_map, block, q.dtype, backward)
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 
@@ -324,6 +342,16 @@ def backward_state(q, k, v, dout, decay=None, block=128, state_in=None, dstate_o
         workspace = workspace_for(q, v, block, True)
     la2_backward_state(q, k, v, decay, state_in, dout, dstate_out, dq, dk, dv, dstate_in, block, workspace)
     return dq, dk, dv, dstate_in
+
+
+def backward_normalized(q, k, v, o, dout, decay=None, block=128, feature_map="elu1", workspace=None):
+    """Allocate (dq, dk, dv) and run the normalized backward (o: the normalized forward's output)."""
+    _check_same(q, k, v, dout)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = normalized_workspace_for(q, v, feature_map, block, True)
+    la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace)
+    return dq, dk, dv
 
 
 def decode_step(q, k, v, state, decay=None):

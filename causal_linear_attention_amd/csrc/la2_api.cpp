@@ -381,40 +381,66 @@ DenPlan den_plan(int64_t chains, int64_t T) {
 }
 
 // Workspace of the normalized forward: [phi(q)][phi(k)] (elu + 1 only), [den, fp32 per position],
-// [segment sums of phi(k)] (split chains only), [the numerator scan's own workspace]; every part
-// 256-byte aligned.
+// [segment sums of the denominator's vector scans] (split chains only), [the numerator scan's own
+// workspace]; the backward adds [dden, fp32 per position][dn, the numerator's output gradient] and
+// takes the numerator backward's workspace.  Every part 256-byte aligned.
 struct NormLayout {
     size_t phi;        // bytes of each of phi(q), phi(k)
-    size_t den_off;
+    size_t den_off, dden_off, dn_off;
     size_t z_off, z_bytes;
     size_t scan_off, scan_bytes;
     size_t total;
     DenPlan dp;
 };
 
-NormLayout norm_layout(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int fmap, int block, int dtype) {
+NormLayout norm_layout(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int fmap, int block, int dtype,
+                       bool backward = false) {
     NormLayout L{};
     const int64_t chains = B * H;
+    const size_t rows_f32 = align256((size_t)(chains * T) * sizeof(float));
     L.phi = fmap ? align256((size_t)(chains * T * d) * elem_size(dtype)) : 0;
     L.dp = den_plan(chains, T);
     L.den_off = 2 * L.phi;
-    L.z_off = L.den_off + align256((size_t)(chains * T) * sizeof(float));
-    L.z_bytes = L.dp.nseg > 1 ? align256((size_t)chains * (L.dp.nseg - 1) * d * sizeof(float)) : 0;
+    L.dden_off = L.den_off + rows_f32;
+    L.dn_off = L.dden_off + (backward ? rows_f32 : 0);
+    L.z_off = L.dn_off + (backward ? align256((size_t)(chains * T * dv) * elem_size(dtype)) : 0);
+    L.z_bytes = L.dp.nseg > 1 ? align256((size_t)chains * L.dp.nseg * d * sizeof(float)) : 0;
     L.scan_off = L.z_off + L.z_bytes;
-    L.scan_bytes = make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
+    L.scan_bytes = backward ? backward_ws_bytes(B, H, T, d, dv, block, dtype) : make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
     L.total = L.scan_off + L.scan_bytes;
     return L;
 }
+
+la2::DenArgs den_args(const void *q, const void *k, const float *decay, char *ws, const NormLayout &L, int64_t H,
+                      int64_t T, int64_t chains) {
+    la2::DenArgs a{};
+    a.q = q;
+    a.k = k;
+    a.pq = L.phi ? ws : nullptr;
+    a.pk = L.phi ? ws + L.phi : nullptr;
+    a.den = reinterpret_cast<float *>(ws + L.den_off);
+    a.decay = decay;
+    a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.z_off) : nullptr;
+    a.T = T;
+    a.seg_len = L.dp.seg_len;
+    a.H = (int)H;
+    a.nseg = L.dp.nseg;
+    a.chains = (int)chains;
+    return a;
+}
+
+// Scan modes of launch_vscan (la2_norm.hip).
+constexpr int kVZSeg = 0, kVDen = 1, kVDQ = 2, kVYSeg = 3, kVDK = 4;
 
 }  // namespace
 
 extern "C" {
 
 size_t la2_normalized_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int feature_map,
-                                      int block, int dtype) {
+                                      int block, int dtype, int backward) {
     if (check_sizes(B, H, T, d, d_v, block, dtype) != LA2_OK || (feature_map != 0 && feature_map != 1))
         return (size_t)-1;
-    return norm_layout(B, H, T, d, d_v, feature_map, block, dtype).total;
+    return norm_layout(B, H, T, d, d_v, feature_map, block, dtype, backward != 0).total;
 }
 
 int la2_forward_normalized(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B,
@@ -447,22 +473,9 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
     char *ws = static_cast<char *>(workspace);
     const int64_t chains = B * H;
     // 1. denominator den_t = phi(q_t) . z_t (fp32), and phi(q), phi(k) for the numerator
-    la2::DenArgs a{};
-    a.q = q;
-    a.k = k;
-    a.pq = L.phi ? ws : nullptr;
-    a.pk = L.phi ? ws + L.phi : nullptr;
-    a.den = reinterpret_cast<float *>(ws + L.den_off);
-    a.decay = decay;
-    a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.z_off) : nullptr;
-    a.T = T;
-    a.seg_len = L.dp.seg_len;
-    a.H = (int)H;
-    a.nseg = L.dp.nseg;
-    a.chains = (int)chains;
-    if (a.nseg > 1 && la2::launch_denominator(a, (int)d, dtype, feature_map, false, s) != hipSuccess)
-        return LA2_ERR_HIP;
-    if (la2::launch_denominator(a, (int)d, dtype, feature_map, true, s) != hipSuccess) return LA2_ERR_HIP;
+    const la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
+    if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess) return LA2_ERR_HIP;
+    if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
     // 2. numerator: the plain scan on phi(q), phi(k)
     st = forward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block,
                       dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream);
@@ -585,6 +598,63 @@ int la2_backward_state(const void *q, const void *k, const void *v, const float 
                        size_t workspace_bytes, void *stream) {
     return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
                          stream, false, state_in, dstate_out, dstate_in);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int la2_backward_normalized(const void *q, const void *k, const void *v, const float *decay, const void *o,
+                            const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d,
+                            int64_t d_v, int feature_map, int block, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (feature_map != LA2_PHI_IDENTITY && feature_map != LA2_PHI_ELU1) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
+    int st = check_sizes(B, H, T, d, d_v, block, dtype);
+    if (st != LA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || (workspace && !aligned16(workspace)) ||
+        (reinterpret_cast<uintptr_t>(decay) & 3u))
+        return LA2_ERR_MISALIGNED;
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
+    const NormLayout L = norm_layout(B, H, T, d, d_v, feature_map, block, dtype, true);
+    if (!workspace || workspace_bytes < L.total) return LA2_ERR_WORKSPACE_TOO_SMALL;
+    const Range ins[6] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(o, nv), range_of(dout, nv),
+                          range_of(decay, decay ? (size_t)H * 4 : 0)};
+    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, L.total)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return LA2_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return LA2_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    const int64_t chains = B * H;
+    la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
+    float *dden = reinterpret_cast<float *>(ws + L.dden_off);
+    void *dn = ws + L.dn_off;
+    // 1. the forward's denominator, phi(q), phi(k) (recomputed)
+    if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess) return LA2_ERR_HIP;
+    if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
+    // 2. dn = do / den, dden = -(do . o) / den
+    if (la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)
+        return LA2_ERR_HIP;
+    // 3. the numerator's gradients: the plain backward on (phi(q), phi(k), v) with output gradient dn;
+    //    dv is final, dq and dk hold the gradients with respect to phi(q), phi(k) so far
+    st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, dq, dk, dv, B, H, T, d, d_v, block, dtype,
+                       L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, false);
+    if (st != LA2_OK) return st;
+    // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place),
+    //    dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative
+    a.dden = dden;
+    a.g = dq;
+    if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDQ, s) != hipSuccess) return LA2_ERR_HIP;
+    a.g = dk;
+    if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVYSeg, s) != hipSuccess) return LA2_ERR_HIP;
+    return la2::launch_vscan(a, (int)d, dtype, feature_map, kVDK, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
 }
 
 }  // extern "C"

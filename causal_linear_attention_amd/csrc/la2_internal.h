@@ -70,24 +70,30 @@ hipError_t launch_segment_prefix(float *states, const float *decay, int chains, 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
                          int chains, int H, int D, int DV, int dtype, hipStream_t s);
 
-// Normalized output (feature map phi: 0 identity, 1 elu + 1).  launch_denominator with
-// norm = false writes each segment's decayed sum of phi(k) (all segments but the last); with
-// norm = true it writes den_t = phi(q_t) . z_t for every position, and phi(q), phi(k) when pq and pk
-// are given (elu + 1), which the numerator scan then reads.  launch_divide divides o by den.
+// Normalized output (feature map phi: 0 identity, 1 elu + 1) and its backward.  launch_vscan runs
+// the decayed d-vector scans of the denominator (modes in la2_norm.hip: 0 forward segment sums of
+// phi(k), 1 den_t = phi(q_t) . z_t with phi(q), phi(k) written where pq / pk are given, 2 the
+// denominator's part of dq, 3 reverse segment sums of dden_t phi(q_t), 4 the denominator's part of
+// dk), launch_divide divides o by den, launch_grad_rows forms dn = do / den and
+// dden = -(do . o) / den.
 struct DenArgs {
     const void *q, *k;     // [chains, T, D], phi applied inside
-    void *pq, *pk;         // [chains, T, D] phi(q), phi(k) out, or nullptr
-    float *den;            // fp32 [chains, T] out
+    void *pq, *pk;         // [chains, T, D] phi(q), phi(k) out (mode 1), or nullptr
+    float *den;            // fp32 [chains, T]: out (mode 1)
+    const float *dden;     // fp32 [chains, T]: in (modes 2-4)
+    void *g;               // [chains, T, D]: dq (mode 2) or dk (mode 4), updated in place
     const float *decay;    // [H] or nullptr (lam = 1)
-    float *zseg;           // fp32 [chains, nseg - 1, D]
+    float *zseg;           // fp32 [chains, nseg, D]: per-segment sums
     int64_t T;
     int64_t seg_len;       // positions per segment, a multiple of 64
     int H;
     int nseg;
     int chains;
 };
-hipError_t launch_denominator(const DenArgs &a, int D, int dtype, int fmap, bool norm, hipStream_t s);
+hipError_t launch_vscan(const DenArgs &a, int D, int dtype, int fmap, int mode, hipStream_t s);
 hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s);
+hipError_t launch_grad_rows(const void *o, const void *dout, const float *den, void *dn, float *dden, int64_t rows,
+                            int DV, int dtype, hipStream_t s);
 
 // The recurrence run token by token (comparison with the tiled scan): o for every chain, state in
 // registers from zero.  q, k: [chains, T, D]; v, o: [chains, T, DV]; bf16 (dtype 1) or fp32 (0).

@@ -68,11 +68,28 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
     reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
-// NORM: write den_t of every position of segment `seg` (and phi(q), phi(k) where asked for).
-// !NORM: write the segment's own decayed sum of phi(k) (z at its last position, starting from
-// zero) to zseg.
-template <typename E, int D, int FMAP, bool NORM>
-__global__ __launch_bounds__(kThreadsN) void denom_kernel(DenArgs p) {
+template <int FMAP>
+__device__ __forceinline__ float phi_deriv(float x) {
+    if constexpr (FMAP == 1)
+        return x > 0.0f ? 1.0f : expf(x);
+    else
+        return 1.0f;
+}
+
+// Modes of the d-vector scan.  Forward ones run the decayed prefix sum z_t = lam z_{t-1} + x_t of
+// x_t = phi(k_t); reverse ones the suffix sum y_t = lam y_{t+1} + x_t of x_t = dden_t phi(q_t).
+enum : int {
+    kZSeg = 0,   // forward: each segment's own sum (z at its last position from zero), segments 0..nseg-2
+    kDen = 1,    // forward: den_t = phi(q_t) . z_t (and phi(q), phi(k) where asked for)
+    kDQ = 2,     // forward: dq_t = (dq_t + dden_t z_t) (.) phi'(q_t), in place
+    kYSeg = 3,   // reverse: each segment's own sum referred to its first position, segments 1..nseg-1
+    kDK = 4      // reverse: dk_t = (dk_t + y_t) (.) phi'(k_t), in place
+};
+
+template <typename E, int D, int FMAP, int MODE>
+__global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
+    constexpr bool REV = MODE == kYSeg || MODE == kDK;
+    constexpr bool SUMS = MODE == kZSeg || MODE == kYSeg;
     constexpr int CPR = D / 8;                  // threads per row (8 dims each)
     constexpr int G = kThreadsN / CPR;          // position groups
     constexpr int PPG = kChunkN / G;            // positions per group per chunk
@@ -81,106 +98,170 @@ __global__ __launch_bounds__(kThreadsN) void denom_kernel(DenArgs p) {
     __shared__ float zc[2][D];
 
     const int tid = threadIdx.x, c8 = tid % CPR, g = tid / CPR;
-    const int nseg_here = NORM ? p.nseg : p.nseg - 1;
-    const int chain = blockIdx.x / nseg_here, seg = blockIdx.x % nseg_here;
+    const int nseg_here = SUMS ? p.nseg - 1 : p.nseg;
+    const int chain = blockIdx.x / nseg_here;
+    const int seg = blockIdx.x % nseg_here + (MODE == kYSeg ? 1 : 0);
     const float l2 = p.decay ? log2f(p.decay[chain % p.H]) : 0.0f;
     const float lam = exp2f(l2);
     const float lamG = exp2f((float)PPG * l2);
     const int64_t s0 = (int64_t)seg * p.seg_len;
     const int64_t s1 = min(p.T, s0 + p.seg_len);
-    const E *kc = static_cast<const E *>(p.k) + (int64_t)chain * p.T * D + c8 * 8;
-    const E *qc = static_cast<const E *>(p.q) + (int64_t)chain * p.T * D + c8 * 8;
-    const bool keep_phi = FMAP != 0 && p.pq != nullptr;
-    E *pqc = keep_phi ? static_cast<E *>(p.pq) + (int64_t)chain * p.T * D + c8 * 8 : nullptr;
-    E *pkc = keep_phi ? static_cast<E *>(p.pk) + (int64_t)chain * p.T * D + c8 * 8 : nullptr;
-    float *denc = p.den + (int64_t)chain * p.T;
+    const int64_t len = s1 - s0;
+    // Step r of the walk is position s0 + r (forward) or s1 - 1 - (r - pad) (reverse).  A reverse walk
+    // puts the ragged chunk first, as leading zeros (pad of them), so the sum at its last step carries
+    // exact exponents; only the last segment is ragged, and nothing is carried into it.
+    const int64_t pad = REV ? (kChunkN - len % kChunkN) % kChunkN : 0;
+    const int64_t steps = len + pad;
+    auto pos = [&](int64_t r) -> int64_t { return REV ? s1 - 1 - (r - pad) : s0 + r; };
+    auto real = [&](int64_t r) -> bool { return REV ? r >= pad : r < len; };
 
-    // z before the segment: Horner over the earlier segments' sums, z <- lam^seg_len z + dz_j
+    const int64_t row0 = (int64_t)chain * p.T;
+    const E *kc = static_cast<const E *>(p.k) + row0 * D + c8 * 8;
+    const E *qc = static_cast<const E *>(p.q) + row0 * D + c8 * 8;
+    const bool keep_phi = MODE == kDen && FMAP != 0 && p.pq != nullptr;
+    E *pqc = keep_phi ? static_cast<E *>(p.pq) + row0 * D + c8 * 8 : nullptr;
+    E *pkc = keep_phi ? static_cast<E *>(p.pk) + row0 * D + c8 * 8 : nullptr;
+    E *gc = (MODE == kDQ || MODE == kDK) ? static_cast<E *>(p.g) + row0 * D + c8 * 8 : nullptr;
+    const float *ddc = (MODE == kDQ || REV) ? p.dden + row0 : nullptr;
+
+    // what is carried into the segment: Horner over the other segments' sums in walk order,
+    // z <- lam^seg_len z + sum_j
     if (tid < D) {
         float z = 0.0f;
-        if (NORM && seg > 0) {
+        if constexpr (!SUMS) {
             const float lamS = exp2f((float)p.seg_len * l2);
-            const float *zs = p.zseg + (int64_t)chain * (p.nseg - 1) * D + tid;
-            for (int j = 0; j < seg; ++j) z = fmaf(z, lamS, zs[(int64_t)j * D]);
+            const float *zs = p.zseg + (int64_t)chain * p.nseg * D + tid;
+            if constexpr (REV) {
+                for (int j = p.nseg - 1; j > seg; --j) z = fmaf(z, lamS, zs[(int64_t)j * D]);
+            } else {
+                for (int j = 0; j < seg; ++j) z = fmaf(z, lamS, zs[(int64_t)j * D]);
+            }
         }
         zc[0][tid] = z;
     }
     __syncthreads();
 
     int buf = 0;
-    for (int64_t c0 = s0; c0 < s1; c0 += kChunkN) {
-        float kk[PPG][8];
-        float qq[NORM ? PPG : 1][8];
+    for (int64_t c0 = 0; c0 < steps; c0 += kChunkN) {
+        float xx[PPG][8];
+        float qq[MODE == kDen ? PPG : 1][8];
 #pragma unroll
         for (int i = 0; i < PPG; ++i) {
-            const int64_t s = c0 + g * PPG + i;
-            if (s < s1) {
-                load8(kc + s * D, kk[i]);
-                if constexpr (NORM) load8(qc + s * D, qq[i]);
+            const int64_t r = c0 + g * PPG + i;
+            if (real(r)) {
+                const int64_t t = pos(r);
+                if constexpr (REV) {
+                    load8(qc + t * D, xx[i]);
+                    const float dd = ddc[t];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    kk[i][m] = phi<FMAP>(kk[i][m]);
-                    if constexpr (NORM) qq[i][m] = phi<FMAP>(qq[i][m]);
-                }
-                if constexpr (NORM && FMAP != 0) {
-                    if (keep_phi) {
-                        store8(pqc + s * D, qq[i]);
-                        store8(pkc + s * D, kk[i]);
+                    for (int m = 0; m < 8; ++m) xx[i][m] = dd * phi<FMAP>(xx[i][m]);
+                } else {
+                    load8(kc + t * D, xx[i]);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) xx[i][m] = phi<FMAP>(xx[i][m]);
+                    if constexpr (MODE == kDen) {
+                        load8(qc + t * D, qq[i]);
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) qq[i][m] = phi<FMAP>(qq[i][m]);
+                        if (keep_phi) {
+                            store8(pqc + t * D, qq[i]);
+                            store8(pkc + t * D, xx[i]);
+                        }
                     }
                 }
             } else {
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    kk[i][m] = 0.0f;
-                    if constexpr (NORM) qq[i][m] = 0.0f;
+                    xx[i][m] = 0.0f;
+                    if constexpr (MODE == kDen) qq[i][m] = 0.0f;
                 }
             }
         }
-        // this run's decayed sum, z at its last position when starting from zero
+        // this run's decayed sum, the running sum at its last step when starting from zero
         float loc[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) loc[m] = kk[0][m];
+        for (int m = 0; m < 8; ++m) loc[m] = xx[0][m];
 #pragma unroll
         for (int i = 1; i < PPG; ++i)
 #pragma unroll
-            for (int m = 0; m < 8; ++m) loc[m] = fmaf(loc[m], lam, kk[i][m]);
+            for (int m = 0; m < 8; ++m) loc[m] = fmaf(loc[m], lam, xx[i][m]);
 #pragma unroll
         for (int m = 0; m < 8; ++m) part[g][c8 * 8 + m] = loc[m];
         __syncthreads();
-        // z entering this run: the chunk's carry, then the earlier runs of the chunk
+        // the sum entering this run: the chunk's carry, then the earlier runs of the chunk
         float z[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) z[m] = zc[buf][c8 * 8 + m];
         for (int j = 0; j < g; ++j)
 #pragma unroll
             for (int m = 0; m < 8; ++m) z[m] = fmaf(z[m], lamG, part[j][c8 * 8 + m]);
-        if constexpr (NORM) {
-#pragma unroll
-            for (int i = 0; i < PPG; ++i) {
-                float pd = 0.0f;
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    z[m] = fmaf(z[m], lam, kk[i][m]);
-                    pd = fmaf(z[m], qq[i][m], pd);
-                }
-#pragma unroll
-                for (int w = 1; w < CPR; w <<= 1) pd += __shfl_xor(pd, w, CPR);
-                const int64_t s = c0 + g * PPG + i;
-                if (s < s1 && c8 == 0) denc[s] = pd;
-            }
-        } else {
+        if constexpr (SUMS) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) z[m] = fmaf(z[m], lamG, loc[m]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PPG; ++i) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) z[m] = fmaf(z[m], lam, xx[i][m]);
+                const int64_t r = c0 + g * PPG + i;
+                if constexpr (MODE == kDen) {
+                    float pd = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) pd = fmaf(z[m], qq[i][m], pd);
+#pragma unroll
+                    for (int w = 1; w < CPR; w <<= 1) pd += __shfl_xor(pd, w, CPR);
+                    if (real(r) && c8 == 0) p.den[row0 + pos(r)] = pd;
+                } else if (real(r)) {
+                    const int64_t t = pos(r);
+                    float gr[8], xr[8];
+                    load8(gc + t * D, gr);
+                    load8((MODE == kDQ ? qc : kc) + t * D, xr);
+                    const float dd = MODE == kDQ ? ddc[t] : 1.0f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) gr[m] = fmaf(dd, z[m], gr[m]) * phi_deriv<FMAP>(xr[m]);
+                    store8(gc + t * D, gr);
+                }
+            }
         }
-        // the last run's z is the next chunk's carry (only read when this chunk was full)
+        // the last run's sum is the next chunk's carry (read only after a full chunk)
         if (g == G - 1)
 #pragma unroll
             for (int m = 0; m < 8; ++m) zc[buf ^ 1][c8 * 8 + m] = z[m];
         __syncthreads();
         buf ^= 1;
     }
-    if constexpr (!NORM) {
-        if (tid < D) p.zseg[((int64_t)chain * (p.nseg - 1) + seg) * D + tid] = zc[buf][tid];
+    if constexpr (SUMS) {
+        if (tid < D) p.zseg[((int64_t)chain * p.nseg + seg) * D + tid] = zc[buf][tid];
+    }
+}
+
+// Per row of the normalized output's backward: dn = do / den (the numerator's output gradient, in
+// the output dtype) and dden = -(do . o) / den (fp32).  D/8 consecutive lanes own a row.
+template <typename E, int DV>
+__global__ __launch_bounds__(kThreadsN) void grad_rows_kernel(const E *o, const E *dout, const float *den, E *dn,
+                                                              float *dden, int64_t rows) {
+    constexpr int CPR = DV / 8, RPB = kThreadsN / CPR;
+    const int c8 = threadIdx.x % CPR;
+    for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR; row - threadIdx.x / CPR < rows;
+         row += (int64_t)gridDim.x * RPB) {
+        const bool ok = row < rows;
+        float ov[8], gv[8];
+        float dot = 0.0f, dr = 1.0f;
+        if (ok) {
+            load8(o + row * DV + c8 * 8, ov);
+            load8(dout + row * DV + c8 * 8, gv);
+            dr = den[row];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) dot = fmaf(gv[m], ov[m], dot);
+        }
+#pragma unroll
+        for (int w = 1; w < CPR; w <<= 1) dot += __shfl_xor(dot, w, CPR);
+        if (ok) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) gv[m] = gv[m] / dr;
+            store8(dn + row * DV + c8 * 8, gv);
+            if (c8 == 0) dden[row] = -dot / dr;
+        }
     }
 }
 
@@ -215,18 +296,22 @@ __global__ __launch_bounds__(kThreadsN) void divide_kernel(E *o, const float *de
 }
 
 template <typename E, int D, int FMAP>
-hipError_t launch_den(const DenArgs &a, bool norm, hipStream_t s) {
-    const unsigned grid = (unsigned)a.chains * (unsigned)(norm ? a.nseg : a.nseg - 1);
-    if (norm)
-        hipLaunchKernelGGL((denom_kernel<E, D, FMAP, true>), dim3(grid), dim3(kThreadsN), 0, s, a);
-    else
-        hipLaunchKernelGGL((denom_kernel<E, D, FMAP, false>), dim3(grid), dim3(kThreadsN), 0, s, a);
+hipError_t launch_vs(const DenArgs &a, int mode, hipStream_t s) {
+    const bool sums = mode == kZSeg || mode == kYSeg;
+    const unsigned grid = (unsigned)a.chains * (unsigned)(sums ? a.nseg - 1 : a.nseg);
+    switch (mode) {
+        case kZSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kZSeg>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kDen: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDen>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kDQ: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQ>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kYSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kYSeg>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        default: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDK>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
 template <typename E, int FMAP>
-hipError_t launch_den_e(const DenArgs &a, int D, bool norm, hipStream_t s) {
-    return D == 64 ? launch_den<E, 64, FMAP>(a, norm, s) : launch_den<E, 128, FMAP>(a, norm, s);
+hipError_t launch_vs_e(const DenArgs &a, int D, int mode, hipStream_t s) {
+    return D == 64 ? launch_vs<E, 64, FMAP>(a, mode, s) : launch_vs<E, 128, FMAP>(a, mode, s);
 }
 
 template <typename E>
@@ -242,13 +327,38 @@ hipError_t launch_div_e(void *o, const float *den, int64_t rows, int DV, hipStre
 
 }  // namespace
 
-hipError_t launch_denominator(const DenArgs &a, int D, int dtype, int fmap, bool norm, hipStream_t s) {
-    if (!(D == 64 || D == 128) || a.chains <= 0 || a.nseg < (norm ? 1 : 2) || a.seg_len % kChunkN != 0 ||
-        (fmap != 0 && fmap != 1))
+hipError_t launch_vscan(const DenArgs &a, int D, int dtype, int fmap, int mode, hipStream_t s) {
+    const bool sums = mode == kZSeg || mode == kYSeg;
+    if (!(D == 64 || D == 128) || a.chains <= 0 || a.nseg < (sums ? 2 : 1) || a.seg_len % kChunkN != 0 ||
+        (fmap != 0 && fmap != 1) || mode < kZSeg || mode > kDK)
         return hipErrorInvalidValue;
     if (dtype == 1)
-        return fmap ? launch_den_e<__bf16, 1>(a, D, norm, s) : launch_den_e<__bf16, 0>(a, D, norm, s);
-    return fmap ? launch_den_e<float, 1>(a, D, norm, s) : launch_den_e<float, 0>(a, D, norm, s);
+        return fmap ? launch_vs_e<__bf16, 1>(a, D, mode, s) : launch_vs_e<__bf16, 0>(a, D, mode, s);
+    return fmap ? launch_vs_e<float, 1>(a, D, mode, s) : launch_vs_e<float, 0>(a, D, mode, s);
+}
+
+hipError_t launch_grad_rows(const void *o, const void *dout, const float *den, void *dn, float *dden, int64_t rows,
+                            int DV, int dtype, hipStream_t s) {
+    if (!(DV == 64 || DV == 128) || rows <= 0) return hipErrorInvalidValue;
+    const int64_t rpb = kThreadsN / (DV / 8);
+    const int64_t want = (rows + rpb - 1) / rpb;
+    const unsigned grid = (unsigned)(want < 16384 ? want : 16384);
+    if (dtype == 1) {
+        if (DV == 64)
+            hipLaunchKernelGGL((grad_rows_kernel<__bf16, 64>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<const __bf16 *>(o),
+                               static_cast<const __bf16 *>(dout), den, static_cast<__bf16 *>(dn), dden, rows);
+        else
+            hipLaunchKernelGGL((grad_rows_kernel<__bf16, 128>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<const __bf16 *>(o),
+                               static_cast<const __bf16 *>(dout), den, static_cast<__bf16 *>(dn), dden, rows);
+    } else {
+        if (DV == 64)
+            hipLaunchKernelGGL((grad_rows_kernel<float, 64>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<const float *>(o),
+                               static_cast<const float *>(dout), den, static_cast<float *>(dn), dden, rows);
+        else
+            hipLaunchKernelGGL((grad_rows_kernel<float, 128>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<const float *>(o),
+                               static_cast<const float *>(dout), den, static_cast<float *>(dn), dden, rows);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s) {

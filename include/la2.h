@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 6
+#define LA2_ABI_VERSION 7
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -136,18 +136,38 @@ int la2_decode_step(const void *q, const void *k, const void *v, const float *de
  *   denominator is accumulated in fp32 from phi in fp32, and o is then
  *   divided by it in fp32 and rounded to `dtype` again.
  *   Other arguments as in la2_forward; workspace: at least
- *   la2_normalized_workspace_bytes(...) bytes (phi(q) and phi(k) for
+ *   la2_normalized_workspace_bytes(..., 0) bytes (phi(q) and phi(k) for
  *   LA2_PHI_ELU1, one fp32 denominator per position, per-segment sums and
- *   the numerator's own workspace; never 0).  No backward is provided. */
+ *   the numerator's own workspace; never 0).  Its backward is
+ *   la2_backward_normalized. */
 int la2_forward_normalized(const void *q, const void *k, const void *v, const float *decay, void *o,
                            int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int feature_map,
                            int block, int dtype, void *workspace, size_t workspace_bytes,
                            void *stream);
 
-/* Workspace bytes needed by la2_forward_normalized for these arguments;
- * (size_t)-1 for arguments it would reject. */
+/* Backward of la2_forward_normalized: gradients of <o, dout> with respect to
+ * q, k and v, by the chain rule through the ratio (pq = phi(q), pk = phi(k)):
+ *     dn_t = do_t / den_t,   dden_t = -(do_t . o_t) / den_t,
+ *     d pq_t = S_t dn_t + dden_t z_t,
+ *     d pk_t = R_t v_t + sum_{s >= t} lam^(s-t) dden_s pq_s,   dv_t = R_t^T pk_t,
+ *     dq = d pq (.) phi'(q),   dk = d pk (.) phi'(k),
+ * R the reverse state of the numerator with output gradient dn.
+ *   o: the output la2_forward_normalized returned for these inputs (read).
+ *   The denominator and phi(q), phi(k) are recomputed; the numerator's part
+ *   runs through the same passes as la2_backward.  Other arguments as in
+ *   la2_forward_normalized; workspace: at least
+ *   la2_normalized_workspace_bytes(..., 1) bytes. */
+int la2_backward_normalized(const void *q, const void *k, const void *v, const float *decay,
+                            const void *o, const void *dout, void *dq, void *dk, void *dv,
+                            int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
+                            int feature_map, int block, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace bytes needed by la2_forward_normalized (backward = 0) or
+ * la2_backward_normalized (backward = 1) for these arguments; (size_t)-1 for
+ * arguments they would reject. */
 size_t la2_normalized_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
-                                      int feature_map, int block, int dtype);
+                                      int feature_map, int block, int dtype, int backward);
 
 /* The same o as la2_forward, computed the way the recurrence is written: one
  * position after another (page "Lightning Attention", section 1, where the

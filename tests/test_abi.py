@@ -164,8 +164,10 @@ def test_forward_normalized_validation(lib):
     # few chains, long sequences: per-segment sums of phi(k) and the numerator's segment states
     big = la2.la2_normalized_workspace_bytes(1, 2, 1 << 16, 128, 128, "identity", 128, torch.bfloat16)
     assert big >= la2.la2_workspace_bytes(1, 2, 1 << 16, 128, 128, 128, torch.bfloat16, False) + 2 * 128 * 4
-    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1) == ctypes.c_size_t(-1).value
-    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 96, 64, 1, 64, 1) == ctypes.c_size_t(-1).value
+    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1, 0) == ctypes.c_size_t(-1).value
+    assert lib.la2_normalized_workspace_bytes(1, 1, 64, 96, 64, 1, 64, 1, 0) == ctypes.c_size_t(-1).value
+    # the backward adds dden (fp32 per position) and dn (one output-sized gradient)
+    assert la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.bfloat16, True) == n + 256 + 64 * 64 * 2
 
 
 def ser(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, B=1, H=1, T=64, d=64, dv=64, dtype=1):
@@ -204,6 +206,25 @@ def test_backward_state_validation(lib):
     assert bst(lib, T=1024) == WS                             # split chain, no workspace
     n = la2.la2_workspace_bytes(1, 1, 1024, 64, 64, 64, torch.bfloat16, True)
     assert bst(lib, T=1024, ws=P + 9 * MB, wsb=n) == ALIAS    # workspace over dstate_out
+
+
+def bnr(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, do=P + 4 * MB, dq=P + 5 * MB, dk=P + 6 * MB,
+        dv_=P + 7 * MB, B=1, H=1, T=64, d=64, dv=64, fmap=1, block=64, dtype=1, ws=P + 8 * MB, wsb=1 << 24):
+    return lib.la2_backward_normalized(q, k, v, decay, o, do, dq, dk, dv_, B, H, T, d, dv, fmap, block, dtype, ws,
+                                       wsb, None)
+
+
+def test_backward_normalized_validation(lib):
+    assert bnr(lib, o=None) == NULLP
+    assert bnr(lib, dv_=None) == NULLP
+    assert bnr(lib, fmap=5) == UNSUP
+    assert bnr(lib, T=0) == SHAPE
+    assert bnr(lib, do=P + 4 * MB + 2) == MISAL
+    assert bnr(lib, ws=None, wsb=0) == WS
+    assert bnr(lib, wsb=100) == WS
+    assert bnr(lib, dq=P + 3 * MB) == ALIAS                  # dq over o
+    assert bnr(lib, dk=P + 5 * MB + 64) == ALIAS             # dk inside dq
+    assert bnr(lib, ws=P + 7 * MB) == ALIAS                  # workspace over dv
 
 
 def test_binding_refuses_cpu_tensors():

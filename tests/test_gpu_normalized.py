@@ -108,3 +108,76 @@ def test_normalized_full_size_sampled():
         err = rel_err(f64(o[sl]), ref)
         print("chain", b, h, f"{err:.2e}", flush=True)
         assert err <= TOL["bf16"]
+
+
+# ---- backward ----------------------------------------------------------------------------------
+#
+# The bar for dq and dk in bf16.  They are d pq = S dn + dden z and d pk = R v + y (times phi'), and
+# for the gradient of a ratio the two terms largely cancel: the exact dq of a one-position sequence
+# is 0 while each term is O(1).  On the bf16 path each term carries bf16 roundings of its own size
+# (phi(q), phi(k), dn and the MFMA operand S in bf16, dq stored in bf16 before the second term is
+# added), so the error is bounded relative to the terms, not to their difference.  The bar is
+# therefore max|gpu - ref| <= 2e-2 x max(max|ref|, max|numerator term|), the numerator term being the
+# plain backward of (phi(q), phi(k), v) for the output gradient dn = do / den (oracle, fp64).  dv has
+# no such cancellation and keeps 2e-2 x max|ref|; fp32 keeps 1e-5 x max|ref| throughout.
+
+
+def numerator_terms(x, fmap):
+    """(d pq, d pk) of the numerator alone: the oracle's plain backward on phi(q), phi(k), v with the
+    normalized output's gradient dn = do / den (fp64)."""
+    q, k, v, do = (f64(x[n]) for n in ("q", "k", "v", "do"))
+    phi = (lambda a: np.where(a > 0, a + 1.0, np.exp(np.minimum(a, 0.0)))) if fmap == "elu1" else (lambda a: a)
+    pq, pk = phi(q), phi(k)
+    lam = lam_of(x)
+    ones = np.ones_like(v[..., :1])
+    den = oracle.forward(pq, pk, np.repeat(ones, 64, axis=-1), lam)[..., :1]   # z_t . phi(q_t)
+    dq_n, dk_n, _ = oracle.backward(pq, pk, v, do / den, lam)
+    return dq_n, dk_n
+
+BN_CASES = [
+    # (B, H, T, d, dv, dtype, block, decay, fmap)
+    (2, 3, 333, 128, 128, "bf16", 128, "heads", "elu1"),    # split numerator and denominator, ragged tail
+    (1, 2, 1000, 64, 128, "bf16", 64, "heads", "elu1"),     # d != d_v: separate reverse scans
+    (16, 16, 200, 128, 64, "bf16", 128, "none", "elu1"),   # 256 chains: nothing split
+    (1, 3, 777, 64, 64, "f32", 32, "heads", "elu1"),
+    (2, 2, 300, 128, 128, "f32", 64, "none", "identity"),
+    (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
+    (3, 1, 1, 64, 64, "bf16", 64, "heads", "elu1"),        # one position
+    (2, 2, 65, 128, 64, "f32", 16, 0.5, "elu1"),           # strong decay
+]
+
+
+def run_backward_case(B, H, T, d, dv, dtype, block, decay, fmap, seed):
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=seed, decay=decay, backward=True)
+    if fmap == "identity":
+        x["q"], x["k"] = positive(x["q"]), positive(x["k"])
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    dec = None if x["decay"] is None else x["decay"].to(DEV)
+    o = la2.forward_normalized(q, k, v, dec, block, fmap)
+    dq, dk, dv_ = la2.backward_normalized(q, k, v, o, do, dec, block, fmap)
+    ref = oracle.backward_normalized(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), fmap)
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        terms = numerator_terms(x, fmap)
+        errs = [float(np.max(np.abs(f64(g) - r))) / max(float(np.max(np.abs(r))), float(np.max(np.abs(t))))
+                for g, r, t in zip((dq, dk), ref[:2], terms)] + [rel_err(f64(dv_), ref[2])]
+    else:
+        errs = [rel_err(f64(g), r) for g, r in zip((dq, dk, dv_), ref)]
+    print((B, H, T, d, dv, dtype, block, decay, fmap), " ".join(f"{e:.2e}" for e in errs), flush=True)
+    for g in (dq, dk, dv_):
+        assert np.isfinite(f64(g)).all()
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("case", BN_CASES, ids=lambda c: "-".join(str(v) for v in c))
+def test_backward_normalized_matches_oracle(case):
+    run_backward_case(*case, seed=401 + case[2])
+
+
+@pytest.mark.parametrize("seg", ["64", "128", "320"])
+def test_backward_normalized_forced_segments(seg, monkeypatch):
+    """Denominator scans over forced segments: forward and reverse carries across up to 16 segments,
+    the reverse walk over a ragged last segment."""
+    monkeypatch.setenv("LA2_NORM_SEGMENT", seg)
+    run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
+    run_backward_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=12)
