@@ -398,7 +398,7 @@ def main():
         compare_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this library runs on one GPU only (asked for --gpus {args.gpus}); "
               "chains shard across GPUs with no communication, but no multi-GPU path is built.",
               file=sys.stderr)
         sys.exit(2)
