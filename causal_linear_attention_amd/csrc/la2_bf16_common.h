@@ -73,8 +73,11 @@ __device__ __forceinline__ bf16x8 frag_tr(const u16 *s, int k0, int n0, int lane
 
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0 and stores past
 // the end are dropped by the hardware range check, which is what handles a ragged last tile.
+// Every caller addresses at most one tile past `base`, so a range longer than 1 GiB is cut to
+// 1 GiB: the 32-bit record count must not wrap on chains of more than 2^31 bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int n = bytes <= 0 ? 0 : (int)bytes;
+    constexpr int64_t kCap = (int64_t)1 << 30;
+    const int n = bytes <= 0 ? 0 : (int)(bytes < kCap ? bytes : kCap);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 

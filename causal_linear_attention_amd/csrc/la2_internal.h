@@ -57,6 +57,9 @@ hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, M
                             hipStream_t s);
 hipError_t launch_scan_f32(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
                            hipStream_t s);
+// State-only pass of bf16 split chains (its own 64-position tiles, several in flight); `a` gives
+// the segments in tiles of TB positions, TB a multiple of 64.
+hipError_t launch_state_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, hipStream_t s);
 // Turns per-segment deltas into per-segment start states, in place; `init` ([chains, elems] or
 // nullptr) is the state the first segment in scan order starts from (reverse: the gradient of a
 // carried-out state, attached at the chain's last position, which the first step weights with
