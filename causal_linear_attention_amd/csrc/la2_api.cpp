@@ -169,7 +169,7 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
                   hipStream_t s) {
     const int DV = slice_width(dtype, args.DVT, pl.narrow);
     if (dtype == LA2_BF16 && mode == la2::Mode::StateOnly) return la2::launch_state_bf16(args, D, DV, pl.TB, dir, s);
-    return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, mode, s)
+    return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, s)
                              : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
 }
 

@@ -53,8 +53,8 @@ enum class Dir { Forward, Reverse };
 enum class Mode { Output, StateOnly };
 
 // Launchers (return hipGetLastError() after the launch).
-hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
-                            hipStream_t s);
+// Output pass of the bf16 tile scan (state-only passes: launch_state_bf16).
+hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, hipStream_t s);
 hipError_t launch_scan_f32(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode,
                            hipStream_t s);
 // State-only pass of bf16 split chains (its own 64-position tiles, several in flight); `a` gives

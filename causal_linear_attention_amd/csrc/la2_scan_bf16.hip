@@ -34,9 +34,8 @@ namespace {
 
 using namespace dev;
 
-template <int D, int DV, int TB, Mode MODE, bool DECAY = false>
+template <int D, int DV, int TB, bool DECAY = false>
 struct Cfg {
-    static constexpr bool kOut = MODE == Mode::Output;
     static constexpr int NTB = TB / 32;          // 32-row blocks of the tile
     static constexpr int NDB = DV / 32;          // 32-column blocks of the value slice
     static constexpr int NKB = D / 32;           // 32-row blocks of the state
@@ -46,35 +45,35 @@ struct Cfg {
     static constexpr int SPW = NSB > kWaves ? NSB / kWaves : 1;   // state blocks per wave
     static constexpr int KS = D / 16;            // contraction steps over d
     // global -> register staging, 16-byte chunks of the natural tiles
-    static constexpr int QCH = kOut ? TB * D / 8 : 0;
+    static constexpr int QCH = TB * D / 8;
     static constexpr int KCH = TB * D / 8;
     static constexpr int VCH = TB * DV / 8;
     static constexpr int NQ = (QCH + kThreads - 1) / kThreads;
     static constexpr int NK = (KCH + kThreads - 1) / kThreads;
     static constexpr int NV = (VCH + kThreads - 1) / kThreads;
-    // LDS carve-up (bf16 elements).  A tile buffer holds Q (output mode), K and V; there are two
-    // of them, filled by direct global -> LDS loads one tile ahead, when they fit (kDMA), else one,
-    // filled from registers.
-    static constexpr int TILE = (kOut ? TB * D : 0) + TB * D + TB * DV;
+    // LDS carve-up (bf16 elements).  A tile buffer holds Q, K and V; there are two of them, filled
+    // by direct global -> LDS loads one tile ahead, when they fit (kDMA), else one, filled from
+    // registers.
+    static constexpr int TILE = TB * D + TB * D + TB * DV;
     static constexpr int oQ = 0;                             // offsets inside a tile buffer
-    static constexpr int oK = oQ + (kOut ? TB * D : 0);
+    static constexpr int oK = oQ + TB * D;
     static constexpr int oV = oK + TB * D;
     // per-wave staging of its 32 x ODB*32 output block, for full-row stores: in a region of its own
     // where LDS allows (kStageO), else (decay) in the weighted K copy once the state update is done
     // with it (kStageLate), O waiting in registers until then
     static constexpr int OSW = ODB * 32;                     // staged row width (elements)
-    static constexpr int OSZ = kOut ? kWaves * 32 * OSW : 0;
+    static constexpr int OSZ = kWaves * 32 * OSW;
     static constexpr int KWZ = DECAY ? TB * D : 0;           // weighted K copy
     static constexpr bool fits(int nbuf, bool own_os) {
-        return (nbuf * TILE + (kOut ? DV * D : 0) + KWZ + (own_os ? OSZ : 0)) * 2 <= 160 * 1024;
+        return (nbuf * TILE + DV * D + KWZ + (own_os ? OSZ : 0)) * 2 <= 160 * 1024;
     }
-    static constexpr bool kLateOK = kOut && DECAY && OSZ <= KWZ;
+    static constexpr bool kLateOK = DECAY && OSZ <= KWZ;
     static constexpr bool kDMA = fits(2, true) || (kLateOK && fits(2, false));
     static constexpr int NBUF = kDMA ? 2 : 1;
-    static constexpr bool kStageO = kOut && fits(NBUF, true);
-    static constexpr bool kStageLate = kOut && !kStageO;
-    static constexpr int oST = NBUF * TILE;                  // S^T in bf16 (output mode)
-    static constexpr int oKW = oST + (kOut ? DV * D : 0);   // K rows weighted by w_upd (decay only)
+    static constexpr bool kStageO = fits(NBUF, true);
+    static constexpr bool kStageLate = !kStageO;
+    static constexpr int oST = NBUF * TILE;                  // S^T in bf16
+    static constexpr int oKW = oST + DV * D;                 // K rows weighted by w_upd (decay only)
     static constexpr int oOS = oKW + KWZ;
     static constexpr int kLds = oOS + (kStageO ? OSZ : 0);
     static_assert(NTB == 2 || NTB == 4, "tile of 64 or 128 positions");
@@ -100,21 +99,21 @@ __device__ __forceinline__ void wave_rows(int wave, int &tb, int &part) {
     }
 }
 
-template <int D, int DV, int TB, Mode MODE>
+template <int D, int DV, int TB>
 struct Staged {
-    using C = Cfg<D, DV, TB, MODE>;
-    u32x4 q[C::NQ > 0 ? C::NQ : 1];
+    using C = Cfg<D, DV, TB>;
+    u32x4 q[C::NQ];
     u32x4 k[C::NK];
     u32x4 v[C::NV];
 };
 
 // Issue the global loads of the tile starting at position t0 into registers (16-byte chunks of
 // the natural row-major tiles).  Nothing waits for them here; rows at or past T read as zero.
-template <int D, int DV, int TB, Mode MODE>
-__device__ __forceinline__ void stage_load(Staged<D, DV, TB, MODE> &r, const u16 *a, const u16 *b,
-                                           const u16 *c, int64_t t0, int64_t T, int DVT, int tid) {
-    using C = Cfg<D, DV, TB, MODE>;
-    if constexpr (C::NQ > 0) {
+template <int D, int DV, int TB>
+__device__ __forceinline__ void stage_load(Staged<D, DV, TB> &r, const u16 *a, const u16 *b, const u16 *c,
+                                           int64_t t0, int64_t T, int DVT, int tid) {
+    using C = Cfg<D, DV, TB>;
+    {
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + t0 * D, (T - t0) * D * 2);
 #pragma unroll
         for (int s = 0; s < C::NQ; ++s) {
@@ -136,9 +135,9 @@ __device__ __forceinline__ void stage_load(Staged<D, DV, TB, MODE> &r, const u16
     }
 }
 
-template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
-__device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u16 *smem, int tid, float l2) {
-    using C = Cfg<D, DV, TB, MODE, DECAY>;
+template <int D, int DV, int TB, Dir DIR, bool DECAY>
+__device__ __forceinline__ void stage_store(const Staged<D, DV, TB> &r, u16 *smem, int tid, float l2) {
+    using C = Cfg<D, DV, TB, DECAY>;
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
         const int cid = tid + s * kThreads;
@@ -149,7 +148,7 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
         const int cid = tid + s * kThreads;
         if (cid < C::KCH) {
             const int row = cid / (D / 8), off = nat_off<D>(row, cid % (D / 8));
-            if constexpr (C::kOut || !DECAY) lds_write(smem + C::oK, off, r.k[s]);
+            lds_write(smem + C::oK, off, r.k[s]);
             if constexpr (DECAY) {
                 // the state update's copy of K: row j scaled by w_upd(j), rounded once to bf16
                 const float w = __builtin_amdgcn_exp2f((float)(DIR == Dir::Forward ? TB - 1 - row : row) * l2);
@@ -170,18 +169,18 @@ __device__ __forceinline__ void stage_store(const Staged<D, DV, TB, MODE> &r, u1
 }
 
 // Issue the direct loads of the tile starting at position t0 into the tile buffer at `buf`.
-template <int D, int DV, int TB, Mode MODE>
+template <int D, int DV, int TB>
 __device__ __forceinline__ void dma_tile(u16 *buf, const u16 *a, const u16 *b, const u16 *c, int64_t t0, int64_t T,
                                          int DVT, int wave, int lane) {
-    using C = Cfg<D, DV, TB, MODE>;
-    if constexpr (C::kOut) dma_rows<D, TB>(make_rsrc(a + t0 * D, (T - t0) * D * 2), buf + C::oQ, D, wave, lane);
+    using C = Cfg<D, DV, TB>;
+    dma_rows<D, TB>(make_rsrc(a + t0 * D, (T - t0) * D * 2), buf + C::oQ, D, wave, lane);
     dma_rows<D, TB>(make_rsrc(b + t0 * D, (T - t0) * D * 2), buf + C::oK, D, wave, lane);
     dma_rows<DV, TB>(make_rsrc(c + t0 * DVT, (T - t0) * DVT * 2), buf + C::oV, DVT, wave, lane);
 }
 
-template <int D, int DV, int TB, Dir DIR, Mode MODE, bool DECAY>
+template <int D, int DV, int TB, Dir DIR, bool DECAY>
 __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
-    using C = Cfg<D, DV, TB, MODE, DECAY>;
+    using C = Cfg<D, DV, TB, DECAY>;
     __shared__ __attribute__((aligned(16))) u16 smem[C::kLds];
 
     const int tid = threadIdx.x;
@@ -209,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const u16 *ga = static_cast<const u16 *>(p.a) + (int64_t)chain * T * D;
     const u16 *gb = static_cast<const u16 *>(p.b) + (int64_t)chain * T * D;
     const u16 *gc = static_cast<const u16 *>(p.c) + (int64_t)chain * T * p.DVT + dv0;
-    u16 *gy = C::kOut ? static_cast<u16 *>(p.y) + (int64_t)chain * T * p.DVT + dv0 : nullptr;
+    u16 *gy = static_cast<u16 *>(p.y) + (int64_t)chain * T * p.DVT + dv0;
     const int sidx = state_index(seg, p.sub, p.nsub, DIR == Dir::Reverse);
     float *gs = p.states ? p.states + ((int64_t)chain * p.nsub + sidx) * D * p.DVT + (p.states_t ? (int64_t)dv0 * D : dv0)
                          : nullptr;
@@ -226,13 +225,13 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     const bool s_active = wave * C::SPW < C::NSB;
 
     f32x16 sacc[C::SPW];
-    const bool init_state = C::kOut && gs != nullptr &&
+    const bool init_state = gs != nullptr &&
                             (DIR == Dir::Forward ? (seg > 0 || p.has_init) : (seg < p.nseg - 1 || p.has_init));
     // A reverse output pass with a carried-in state (the gradient of a carried-out forward state)
     // has it attached at the chain's last position: on the chain's last tile, the first this
     // workgroup processes, its rows are weighted lam^(leff-1-i) and it is carried on with
     // lam^(leff-1), leff the tile's real length.
-    const bool end_init = DIR == Dir::Reverse && C::kOut && p.has_init && seg == p.nseg - 1;
+    const bool end_init = DIR == Dir::Reverse && p.has_init && seg == p.nseg - 1;
     const int leff_end = (int)min((int64_t)TB, T - (NT - 1) * TB);
 #pragma unroll
     for (int s = 0; s < C::SPW; ++s) {
@@ -245,48 +244,39 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         }
     }
 
-    // A state-only pass only sums its segment's tile contributions, so it walks the tiles against the
-    // scan direction, each tile weighted by its own lam^(TB * it): it ends on the tiles the output
-    // pass reads first, which are then the most recently fetched ones in the memory-side cache.
-    constexpr bool kFlip = MODE == Mode::StateOnly;
-    static_assert(C::kDMA || !kFlip, "state-only passes use the direct loads");
-    auto tile_of = [&](int it) -> int64_t {
-        return (DIR == Dir::Forward) != kFlip ? tile_lo + it : tile_hi - 1 - it;
-    };
+    auto tile_of = [&](int it) -> int64_t { return DIR == Dir::Forward ? tile_lo + it : tile_hi - 1 - it; };
 
     // S^T (bf16) into LDS for the next tile's right product
     auto write_state_lds = [&]() {
-        if constexpr (C::kOut) {
-            if (!s_active) return;
+        if (!s_active) return;
 #pragma unroll
-            for (int s = 0; s < C::SPW; ++s) {
-                const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-                // lane (col, h) holds d = kb*32 + 8j + 4h + 0..3 of row nb*32 + col: pair up the two
-                // halves of chunks j and j + 1 across h, so every lane writes one whole 16-byte chunk
-                // (8-byte writes of one half would leave half the banks idle: 2-way conflicts)
+        for (int s = 0; s < C::SPW; ++s) {
+            const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+            // lane (col, h) holds d = kb*32 + 8j + 4h + 0..3 of row nb*32 + col: pair up the two
+            // halves of chunks j and j + 1 across h, so every lane writes one whole 16-byte chunk
+            // (8-byte writes of one half would leave half the banks idle: 2-way conflicts)
 #pragma unroll
-                for (int jp = 0; jp < 2; ++jp) {
-                    u32x2 a, b;
-                    a[0] = pack_bf16(sacc[s][8 * jp + 0], sacc[s][8 * jp + 1]);
-                    a[1] = pack_bf16(sacc[s][8 * jp + 2], sacc[s][8 * jp + 3]);
-                    b[0] = pack_bf16(sacc[s][8 * jp + 4], sacc[s][8 * jp + 5]);
-                    b[1] = pack_bf16(sacc[s][8 * jp + 6], sacc[s][8 * jp + 7]);
-                    const u32x4 w = join_halves(a, b);
-                    lds_write(smem + C::oST, nat_off<D>(nb * 32 + col, kb * 4 + 2 * jp + h), w);
-                }
+            for (int jp = 0; jp < 2; ++jp) {
+                u32x2 a, b;
+                a[0] = pack_bf16(sacc[s][8 * jp + 0], sacc[s][8 * jp + 1]);
+                a[1] = pack_bf16(sacc[s][8 * jp + 2], sacc[s][8 * jp + 3]);
+                b[0] = pack_bf16(sacc[s][8 * jp + 4], sacc[s][8 * jp + 5]);
+                b[1] = pack_bf16(sacc[s][8 * jp + 6], sacc[s][8 * jp + 7]);
+                const u32x4 w = join_halves(a, b);
+                lds_write(smem + C::oST, nat_off<D>(nb * 32 + col, kb * 4 + 2 * jp + h), w);
             }
         }
     };
 
-    Staged<D, DV, TB, MODE> st;
+    Staged<D, DV, TB> st;
     if constexpr (C::kDMA) {
-        dma_tile<D, DV, TB, MODE>(smem, ga, gb, gc, tile_of(0) * TB, T, p.DVT, wave, lane);
+        dma_tile<D, DV, TB>(smem, ga, gb, gc, tile_of(0) * TB, T, p.DVT, wave, lane);
         wait_vm();
         lds_barrier();
         if constexpr (DECAY) build_kw<D, TB, DIR>(smem + C::oK, smem + C::oKW, tid, l2, 0);
     } else {
-        stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
-        stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+        stage_load<D, DV, TB>(st, ga, gb, gc, tile_of(0) * TB, T, p.DVT, tid);
+        stage_store<D, DV, TB, DIR, DECAY>(st, smem, tid, l2);
     }
     if (init_state) write_state_lds();
     lds_barrier();
@@ -297,12 +287,12 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     // One tile: `cur` is the tile buffer it reads, `nxt` the one the next tile's direct loads fill.
     auto tile = [&](const u16 *cur, u16 *nxt) __attribute__((always_inline)) {
         const int64_t t0 = tile_of(it) * TB;
-        const bool update = (MODE == Mode::StateOnly) || (it + 1 < ntiles);
+        const bool update = it + 1 < ntiles;
         const u16 *sQ = cur + C::oQ, *sK = cur + C::oK, *sV = cur + C::oV;
         // the next tile's direct loads go out first and have this whole tile to land; its buffer was
         // last read in the previous tile, which every wave has left
         if constexpr (C::kDMA) {
-            if (it + 1 < ntiles) dma_tile<D, DV, TB, MODE>(nxt, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, wave, lane);
+            if (it + 1 < ntiles) dma_tile<D, DV, TB>(nxt, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, wave, lane);
         }
 
         // O^T accumulators of this wave's output block, and their store: each lane holds 4
@@ -340,140 +330,138 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             }
         };
 
-        if constexpr (C::kOut) {
-            if (o_active) {
-                const int qrow = tb * 32 + col;
-                auto rdQ = [&](int ks) { return lds_read(sQ, nat_off<D>(qrow, 2 * ks + h)); };
+        if (o_active) {
+            const int qrow = tb * 32 + col;
+            auto rdQ = [&](int ks) { return lds_read(sQ, nat_off<D>(qrow, 2 * ks + h)); };
 
 #pragma unroll
-                for (int n = 0; n < C::ODB; ++n)
+            for (int n = 0; n < C::ODB; ++n)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
 
-                // Step 3: inter-tile right product, rows weighted by w_inter
-                if (state_nonzero) {
-                    auto rdST = [&](int n, int ks) {
-                        return lds_read(sST, nat_off<D>((db0 + n) * 32 + col, 2 * ks + h));
-                    };
-                    bf16x8 qa = rdQ(0), sa[C::ODB];
+            // Step 3: inter-tile right product, rows weighted by w_inter
+            if (state_nonzero) {
+                auto rdST = [&](int n, int ks) {
+                    return lds_read(sST, nat_off<D>((db0 + n) * 32 + col, 2 * ks + h));
+                };
+                bf16x8 qa = rdQ(0), sa[C::ODB];
 #pragma unroll
-                    for (int n = 0; n < C::ODB; ++n) sa[n] = rdST(n, 0);
+                for (int n = 0; n < C::ODB; ++n) sa[n] = rdST(n, 0);
 #pragma unroll 2
-                    for (int ks = 0; ks < C::KS; ++ks) {
-                        const int kn = ks + 1 < C::KS ? ks + 1 : ks;
-                        const bf16x8 qn = rdQ(kn);
-                        bf16x8 sn[C::ODB];
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    const int kn = ks + 1 < C::KS ? ks + 1 : ks;
+                    const bf16x8 qn = rdQ(kn);
+                    bf16x8 sn[C::ODB];
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) sn[n] = rdST(n, kn);
+                    for (int n = 0; n < C::ODB; ++n) sn[n] = rdST(n, kn);
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(sa[n], qa, oacc[n]);
-                        qa = qn;
+                    for (int n = 0; n < C::ODB; ++n) oacc[n] = mfma(sa[n], qa, oacc[n]);
+                    qa = qn;
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n) sa[n] = sn[n];
-                    }
-                    if constexpr (DECAY) {
-                        // every accumulator of this lane belongs to the row tb*32 + col
-                        const int i = tb * 32 + col;
-                        int e = DIR == Dir::Forward ? i + 1 : TB - i;
-                        if (DIR == Dir::Reverse && end_init && it == 0) e = leff_end - 1 - i;
-                        const float w = e >= 0 ? pw(e) : 0.0f;
-#pragma unroll
-                        for (int n = 0; n < C::ODB; ++n)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) oacc[n][r] *= w;
-                    }
+                    for (int n = 0; n < C::ODB; ++n) sa[n] = sn[n];
                 }
+                if constexpr (DECAY) {
+                    // every accumulator of this lane belongs to the row tb*32 + col
+                    const int i = tb * 32 + col;
+                    int e = DIR == Dir::Forward ? i + 1 : TB - i;
+                    if (DIR == Dir::Reverse && end_init && it == 0) e = leff_end - 1 - i;
+                    const float w = e >= 0 ? pw(e) : 0.0f;
+#pragma unroll
+                    for (int n = 0; n < C::ODB; ++n)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[n][r] *= w;
+                }
+            }
 
-                // Step 2: intra-tile masked left product, one 32x32 block of A^T at a time
-                const int ulo = DIR == Dir::Forward ? 0 : tb;
-                const int uhi = DIR == Dir::Forward ? tb : C::NTB - 1;
-                const int tcol = tb * 32 + col;
-                for (int u = ulo; u <= uhi; ++u) {
-                    asm volatile("" ::: "memory");   // keep each block's LDS reads inside its iteration
-                    // V fragments of this block, in P's row order; in the forward direction they are read
-                    // before the A^T chain, which hides their latency
-                    bf16x8 vf[2][C::ODB];
-                    auto rdVF = [&](int x, int n) { return frag_tr<DV, true>(sV, u * 32 + 16 * x, (db0 + n) * 32, lane); };
-                    if constexpr (DIR == Dir::Forward) {
-#pragma unroll
-                        for (int x = 0; x < 2; ++x)
-#pragma unroll
-                            for (int n = 0; n < C::ODB; ++n) vf[x][n] = rdVF(x, n);
-                    }
-                    f32x16 acc;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-                    bf16x8 ka = lds_read(sK, nat_off<D>(u * 32 + col, h)), qa = rdQ(0);
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ks += 2) {
-                        const bf16x8 kb = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 1) + h)), qb = rdQ(ks + 1);
-                        acc = mfma(ka, qa, acc);
-                        if (ks + 2 < C::KS) {
-                            ka = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 2) + h));
-                            qa = rdQ(ks + 2);
-                        }
-                        acc = mfma(kb, qb, acc);
-                    }
-                    // causal decay mask: only the diagonal block has masked entries.  The distance of
-                    // accumulator r is base -/+ (8 (r / 4) + r % 4), small integers exact in fp32; the
-                    // base is hidden from loop-invariant hoisting, which would otherwise keep the
-                    // per-lane distances or weights across the tile loop in spilled registers (and
-                    // every spill reload waits on the next tile's loads).
-                    float base = (float)(DIR == Dir::Forward ? tcol - u * 32 - 4 * h : u * 32 + 4 * h - tcol);
-                    asm volatile("" : "+v"(base));
-                    bf16x8 pf[2];
-                    if (DECAY && u != tb) {
-                        // off the diagonal every distance is >= 1: one exp per group of 4 accumulators,
-                        // lam^dist = lam^(smallest distance in the group) * lam^(offset from it), both
-                        // exponents >= 0, so neither factor can overflow (lam^e is rebuilt per block from
-                        // a hidden copy of log2 lam rather than held across the tile loop)
-                        float l2b = l2;
-                        asm volatile("" : "+v"(l2b));
-                        const float lam_e[4] = {1.0f, __builtin_amdgcn_exp2f(l2b), __builtin_amdgcn_exp2f(2.0f * l2b),
-                                                __builtin_amdgcn_exp2f(3.0f * l2b)};
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const float pm = __builtin_amdgcn_exp2f(
-                                (DIR == Dir::Forward ? base - (float)(8 * m + 3) : base + (float)(8 * m)) * l2);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int r = 4 * m + e;
-                                pf[r >> 3][r & 7] = (__bf16)(acc[r] * (pm * lam_e[DIR == Dir::Forward ? 3 - e : e]));
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float c = (float)(8 * (r >> 2) + (r & 3));
-                            const float diff = DIR == Dir::Forward ? base - c : base + c;
-                            const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
-                            const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
-                            pf[r >> 3][r & 7] = (__bf16)v;
-                        }
-                    }
+            // Step 2: intra-tile masked left product, one 32x32 block of A^T at a time
+            const int ulo = DIR == Dir::Forward ? 0 : tb;
+            const int uhi = DIR == Dir::Forward ? tb : C::NTB - 1;
+            const int tcol = tb * 32 + col;
+            for (int u = ulo; u <= uhi; ++u) {
+                asm volatile("" ::: "memory");   // keep each block's LDS reads inside its iteration
+                // V fragments of this block, in P's row order; in the forward direction they are read
+                // before the A^T chain, which hides their latency
+                bf16x8 vf[2][C::ODB];
+                auto rdVF = [&](int x, int n) { return frag_tr<DV, true>(sV, u * 32 + 16 * x, (db0 + n) * 32, lane); };
+                if constexpr (DIR == Dir::Forward) {
 #pragma unroll
                     for (int x = 0; x < 2; ++x)
 #pragma unroll
-                        for (int n = 0; n < C::ODB; ++n)
-                            oacc[n] = mfma(DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), pf[x], oacc[n]);
+                        for (int n = 0; n < C::ODB; ++n) vf[x][n] = rdVF(x, n);
                 }
-
-                // with the LDS to spare, O goes out now; otherwise (decay: the weighted K copy fills
-                // LDS) it waits in registers until the state update has released that copy
-                if constexpr (C::kStageO) store_o(smem + C::oOS + wave * 32 * C::OSW);
+                f32x16 acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+                bf16x8 ka = lds_read(sK, nat_off<D>(u * 32 + col, h)), qa = rdQ(0);
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ks += 2) {
+                    const bf16x8 kb = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 1) + h)), qb = rdQ(ks + 1);
+                    acc = mfma(ka, qa, acc);
+                    if (ks + 2 < C::KS) {
+                        ka = lds_read(sK, nat_off<D>(u * 32 + col, 2 * (ks + 2) + h));
+                        qa = rdQ(ks + 2);
+                    }
+                    acc = mfma(kb, qb, acc);
+                }
+                // causal decay mask: only the diagonal block has masked entries.  The distance of
+                // accumulator r is base -/+ (8 (r / 4) + r % 4), small integers exact in fp32; the
+                // base is hidden from loop-invariant hoisting, which would otherwise keep the
+                // per-lane distances or weights across the tile loop in spilled registers (and
+                // every spill reload waits on the next tile's loads).
+                float base = (float)(DIR == Dir::Forward ? tcol - u * 32 - 4 * h : u * 32 + 4 * h - tcol);
+                asm volatile("" : "+v"(base));
+                bf16x8 pf[2];
+                if (DECAY && u != tb) {
+                    // off the diagonal every distance is >= 1: one exp per group of 4 accumulators,
+                    // lam^dist = lam^(smallest distance in the group) * lam^(offset from it), both
+                    // exponents >= 0, so neither factor can overflow (lam^e is rebuilt per block from
+                    // a hidden copy of log2 lam rather than held across the tile loop)
+                    float l2b = l2;
+                    asm volatile("" : "+v"(l2b));
+                    const float lam_e[4] = {1.0f, __builtin_amdgcn_exp2f(l2b), __builtin_amdgcn_exp2f(2.0f * l2b),
+                                            __builtin_amdgcn_exp2f(3.0f * l2b)};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float pm = __builtin_amdgcn_exp2f(
+                            (DIR == Dir::Forward ? base - (float)(8 * m + 3) : base + (float)(8 * m)) * l2);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * m + e;
+                            pf[r >> 3][r & 7] = (__bf16)(acc[r] * (pm * lam_e[DIR == Dir::Forward ? 3 - e : e]));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float c = (float)(8 * (r >> 2) + (r & 3));
+                        const float diff = DIR == Dir::Forward ? base - c : base + c;
+                        const float w = DECAY ? __builtin_amdgcn_exp2f(diff * l2) : 1.0f;
+                        const float v = diff >= 0.0f ? (DECAY ? acc[r] * w : acc[r]) : 0.0f;
+                        pf[r >> 3][r & 7] = (__bf16)v;
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int n = 0; n < C::ODB; ++n)
+                        oacc[n] = mfma(DIR == Dir::Forward ? vf[x][n] : rdVF(x, n), pf[x], oacc[n]);
             }
+
+            // with the LDS to spare, O goes out now; otherwise (decay: the weighted K copy fills
+            // LDS) it waits in registers until the state update has released that copy
+            if constexpr (C::kStageO) store_o(smem + C::oOS + wave * 32 * C::OSW);
         }
 
         // Without the second buffer, the next tile's loads go out here, after the register-heavy
         // intra-tile phase, and land in LDS after this tile's last barrier.
         if constexpr (!C::kDMA) {
-            if (it + 1 < ntiles) stage_load<D, DV, TB, MODE>(st, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, tid);
+            if (it + 1 < ntiles) stage_load<D, DV, TB>(st, ga, gb, gc, tile_of(it + 1) * TB, T, p.DVT, tid);
         }
 
         // Step 4: state update S = lam^TB S + (w_upd K)^T V, fp32 accumulators
         if (update) {
             if (s_active) {
-                if constexpr (DECAY && !kFlip) {
+                if constexpr (DECAY) {
                     const float f = (DIR == Dir::Reverse && end_init && it == 0) ? pw(leff_end - 1) : pw(TB);
 #pragma unroll
                     for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
@@ -526,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
             }
             if constexpr (DECAY) {
                 if (it + 1 < ntiles)
-                    build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2, kFlip ? TB * (it + 1) : 0);
+                    build_kw<D, TB, DIR>(nxt + C::oK, smem + C::oKW, tid, l2);
             }
         } else {
             lds_barrier();                   // every wave is done with this tile's LDS
@@ -535,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
                 if (o_active) store_o(smem + C::oKW + wave * 32 * C::OSW);
                 lds_barrier();               // every staged O is read back before the copy is rebuilt
             }
-            if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, MODE, DECAY>(st, smem, tid, l2);
+            if (it + 1 < ntiles) stage_store<D, DV, TB, DIR, DECAY>(st, smem, tid, l2);
         }
         lds_barrier();
     };
@@ -552,20 +540,6 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         }
     }
 
-    if constexpr (MODE == Mode::StateOnly) {
-        if (s_active) {
-#pragma unroll
-            for (int s = 0; s < C::SPW; ++s) {
-                const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    gs[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r];
-                }
-            }
-        }
-    }
-
     // Carried-out state, from the workgroup that processes the chain's last tile in scan order.
     // Forward: the final state, i.e. the last tile's update (which the loop leaves out) over its
     // `leff` real positions, S = lam^leff S + sum_{j < leff} lam^(leff-1-j) k_j v_j^T (exact for a
@@ -573,80 +547,69 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     // b_j c_j^T over tile 0 (rows past T are zero) -- the gradient of a carried-in forward state.
     // The last tile is still in LDS and nothing writes LDS any more; its weights are applied to the
     // fragments in registers (the weighted copy may hold staged outputs by now).
-    if constexpr (C::kOut) {
-        const bool want = p.state_out != nullptr && s_active && (DIR == Dir::Forward ? seg == p.nseg - 1 : seg == 0);
-        if (want) {
-            const int last = ntiles - 1;
-            const u16 *cur = smem + (C::kDMA ? (last & 1) * C::TILE : 0);
-            const u16 *sK = cur + C::oK, *sV = cur + C::oV;
-            const int leff = (int)min((int64_t)TB, T - tile_of(last) * TB);
-            if constexpr (DECAY) {
-                const float f = DIR == Dir::Forward ? pw(leff) : (end_init && ntiles == 1 ? pw(leff_end - 1) : pw(TB));
+    const bool want = p.state_out != nullptr && s_active && (DIR == Dir::Forward ? seg == p.nseg - 1 : seg == 0);
+    if (want) {
+        const int last = ntiles - 1;
+        const u16 *cur = smem + (C::kDMA ? (last & 1) * C::TILE : 0);
+        const u16 *sK = cur + C::oK, *sV = cur + C::oV;
+        const int leff = (int)min((int64_t)TB, T - tile_of(last) * TB);
+        if constexpr (DECAY) {
+            const float f = DIR == Dir::Forward ? pw(leff) : (end_init && ntiles == 1 ? pw(leff_end - 1) : pw(TB));
 #pragma unroll
-                for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
-            }
+            for (int s = 0; s < C::SPW; ++s) sacc[s] *= f;
+        }
 #pragma unroll
-            for (int s = 0; s < C::SPW; ++s) {
-                const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
-                for (int x = 0; x < TB / 16; ++x) {
-                    bf16x8 kf = frag_tr<D, false>(sK, 16 * x, kb * 32, lane);
-                    if constexpr (DECAY) {
-                        // rows j = 16x + 8h + e: forward lam^(leff-1-j) and 0 past the sequence end,
-                        // reverse lam^j
-                        u32x4 u = __builtin_bit_cast(u32x4, kf);
+        for (int s = 0; s < C::SPW; ++s) {
+            const int sb = wave * C::SPW + s, kb = sb / C::NDB, nb = sb % C::NDB;
+            for (int x = 0; x < TB / 16; ++x) {
+                bf16x8 kf = frag_tr<D, false>(sK, 16 * x, kb * 32, lane);
+                if constexpr (DECAY) {
+                    // rows j = 16x + 8h + e: forward lam^(leff-1-j) and 0 past the sequence end,
+                    // reverse lam^j
+                    u32x4 u = __builtin_bit_cast(u32x4, kf);
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const int j = 16 * x + 8 * h + 2 * m;
-                            float wl, wh;
-                            if constexpr (DIR == Dir::Forward) {
-                                wl = j < leff ? __builtin_amdgcn_exp2f((float)(leff - 1 - j) * l2) : 0.0f;
-                                wh = j + 1 < leff ? __builtin_amdgcn_exp2f((float)(leff - 2 - j) * l2) : 0.0f;
-                            } else {
-                                wl = __builtin_amdgcn_exp2f((float)j * l2);
-                                wh = __builtin_amdgcn_exp2f((float)(j + 1) * l2);
-                            }
-                            u[m] = pack_bf16(__uint_as_float(u[m] << 16) * wl, __uint_as_float(u[m] & 0xffff0000u) * wh);
+                    for (int m = 0; m < 4; ++m) {
+                        const int j = 16 * x + 8 * h + 2 * m;
+                        float wl, wh;
+                        if constexpr (DIR == Dir::Forward) {
+                            wl = j < leff ? __builtin_amdgcn_exp2f((float)(leff - 1 - j) * l2) : 0.0f;
+                            wh = j + 1 < leff ? __builtin_amdgcn_exp2f((float)(leff - 2 - j) * l2) : 0.0f;
+                        } else {
+                            wl = __builtin_amdgcn_exp2f((float)j * l2);
+                            wh = __builtin_amdgcn_exp2f((float)(j + 1) * l2);
                         }
-                        kf = __builtin_bit_cast(bf16x8, u);
+                        u[m] = pack_bf16(__uint_as_float(u[m] << 16) * wl, __uint_as_float(u[m] & 0xffff0000u) * wh);
                     }
-                    sacc[s] = mfma(kf, frag_tr<DV, false>(sV, 16 * x, nb * 32, lane), sacc[s]);
+                    kf = __builtin_bit_cast(bf16x8, u);
                 }
-                const float scale = DIR == Dir::Reverse ? pw(1) : 1.0f;
-                float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
+                sacc[s] = mfma(kf, frag_tr<DV, false>(sV, 16 * x, nb * 32, lane), sacc[s]);
+            }
+            const float scale = DIR == Dir::Reverse ? pw(1) : 1.0f;
+            float *so = p.state_out + (int64_t)chain * D * p.DVT + dv0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    so[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r] * scale;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                so[(int64_t)d * p.DVT + nb * 32 + col] = sacc[s][r] * scale;
             }
         }
     }
 }
 
-template <int D, int DV, int TB, Dir DIR, Mode MODE>
+template <int D, int DV, int TB, Dir DIR>
 hipError_t launch_one(const ScanArgs &a, hipStream_t s) {
     const int64_t items = (int64_t)a.chains * a.seg_count * a.nslice;
     if (a.decay)
-        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, MODE, true>), dim3((unsigned)items), dim3(kThreads), 0,
-                           s, a);
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, true>), dim3((unsigned)items), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, MODE, false>), dim3((unsigned)items), dim3(kThreads),
-                           0, s, a);
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, false>), dim3((unsigned)items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <int D, int DV, int TB>
-hipError_t launch_dm(const ScanArgs &a, Dir dir, Mode mode, hipStream_t s) {
-    if (dir == Dir::Forward)
-        return mode == Mode::Output ? launch_one<D, DV, TB, Dir::Forward, Mode::Output>(a, s)
-                                    : launch_one<D, DV, TB, Dir::Forward, Mode::StateOnly>(a, s);
-    return mode == Mode::Output ? launch_one<D, DV, TB, Dir::Reverse, Mode::Output>(a, s)
-                                : launch_one<D, DV, TB, Dir::Reverse, Mode::StateOnly>(a, s);
-}
-
 template <int D, int DV>
-hipError_t launch_tb(const ScanArgs &a, int TB, Dir dir, Mode mode, hipStream_t s) {
-    return TB == 64 ? launch_dm<D, DV, 64>(a, dir, mode, s) : launch_dm<D, DV, 128>(a, dir, mode, s);
+hipError_t launch_tb(const ScanArgs &a, int TB, Dir dir, hipStream_t s) {
+    if (dir == Dir::Forward)
+        return TB == 64 ? launch_one<D, DV, 64, Dir::Forward>(a, s) : launch_one<D, DV, 128, Dir::Forward>(a, s);
+    return TB == 64 ? launch_one<D, DV, 64, Dir::Reverse>(a, s) : launch_one<D, DV, 128, Dir::Reverse>(a, s);
 }
 
 }  // namespace
@@ -655,10 +618,10 @@ bool bf16_supported(int D, int DV, int TB) {
     return (D == 64 || D == 128) && (DV == 64 || DV == 128) && (TB == 64 || TB == 128);
 }
 
-hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, Mode mode, hipStream_t s) {
+hipError_t launch_scan_bf16(const ScanArgs &a, int D, int DV, int TB, Dir dir, hipStream_t s) {
     if (!bf16_supported(D, DV, TB)) return hipErrorInvalidValue;
-    if (D == 64) return DV == 64 ? launch_tb<64, 64>(a, TB, dir, mode, s) : launch_tb<64, 128>(a, TB, dir, mode, s);
-    return DV == 64 ? launch_tb<128, 64>(a, TB, dir, mode, s) : launch_tb<128, 128>(a, TB, dir, mode, s);
+    if (D == 64) return DV == 64 ? launch_tb<64, 64>(a, TB, dir, s) : launch_tb<64, 128>(a, TB, dir, s);
+    return DV == 64 ? launch_tb<128, 64>(a, TB, dir, s) : launch_tb<128, 128>(a, TB, dir, s);
 }
 
 }  // namespace la2
