@@ -18,6 +18,8 @@
 namespace la2 {
 namespace {
 
+constexpr int kBatch = 8;
+
 __global__ __launch_bounds__(256) void segment_prefix_kernel(float *states, const float *decay, int H, int nseg,
                                                              int64_t seg_len, int64_t elems, int reverse,
                                                              const float *init, int64_t init_len) {
@@ -28,18 +30,35 @@ __global__ __launch_bounds__(256) void segment_prefix_kernel(float *states, cons
     const float f = decay ? exp2f((float)seg_len * l2) : 1.0f;
     float *base = states + (int64_t)chain * nseg * elems + e;
     float run = init ? init[(int64_t)chain * elems + e] : 0.0f;
+    // The deltas are read kBatch at a time before any of them is overwritten, so their loads are in
+    // flight together rather than one segment's latency after another.
     if (!reverse) {
-        for (int p = 0; p < nseg; ++p) {
-            const float d = p < nseg - 1 ? base[(int64_t)p * elems] : 0.0f;
-            base[(int64_t)p * elems] = run;
-            run = fmaf(f, run, d);
+        for (int p0 = 0; p0 < nseg; p0 += kBatch) {
+            float d[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) d[i] = p0 + i < nseg - 1 ? base[(int64_t)(p0 + i) * elems] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (p0 + i < nseg) {
+                    base[(int64_t)(p0 + i) * elems] = run;
+                    run = fmaf(f, run, d[i]);
+                }
+            }
         }
     } else {
         const float f0 = init && decay ? exp2f((float)init_len * l2) : f;
-        for (int p = nseg - 1; p >= 0; --p) {
-            const float d = p > 0 ? base[(int64_t)p * elems] : 0.0f;
-            base[(int64_t)p * elems] = run;
-            run = fmaf(p == nseg - 1 ? f0 : f, run, d);
+        for (int p0 = nseg - 1; p0 >= 0; p0 -= kBatch) {
+            float d[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) d[i] = p0 - i > 0 ? base[(int64_t)(p0 - i) * elems] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int p = p0 - i;
+                if (p >= 0) {
+                    base[(int64_t)p * elems] = run;
+                    run = fmaf(p == nseg - 1 ? f0 : f, run, d[i]);
+                }
+            }
         }
     }
 }
