@@ -229,7 +229,7 @@ def normalized_bench(args):
         "backward_hbm_frac": round(th * 7 * w.d * 2 / (ms_b * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "la2_forward_normalized (denominator + numerator scan + division launches)",
+                     "kernel": "la2_forward_normalized (denominator scan + numerator scan dividing in its output pass)",
                      "avg_launch_ms": round(ms_n, 5), "algorithmic_bytes_per_launch": byts},
         "cpu_baseline": cpu,
     }), flush=True)

@@ -206,8 +206,10 @@ int segment_states(const void *b, const void *c, const float *decay, int64_t cha
 // state, or in reverse lam times the state at position 0.
 int output_scan(const void *a, const void *b, const void *c, void *y, const float *decay, int64_t chains, int64_t H,
                 int64_t T, int D, int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, int states_t,
-                hipStream_t s, const float *state_in = nullptr, float *state_out = nullptr) {
+                hipStream_t s, const float *state_in = nullptr, float *state_out = nullptr,
+                const float *den = nullptr) {
     la2::ScanArgs args = scan_args(a, b, c, y, decay, chains, H, T, W, pl, dtype);
+    args.den = den;
     args.states = pl.nseg > 1 ? static_cast<float *>(ws) : const_cast<float *>(state_in);
     args.has_init = state_in != nullptr;
     args.state_out = state_out;
@@ -247,9 +249,10 @@ size_t la2_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t d
 
 namespace {
 
+// `den` (fp32 [B, H, T] or nullptr): o_t is divided by den_t before it is stored (the normalized form).
 int forward_impl(const void *q, const void *k, const void *v, const float *decay, const float *state_in, void *o,
                  float *state_out, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 void *workspace, size_t workspace_bytes, void *stream, const float *den = nullptr) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -286,7 +289,7 @@ int forward_impl(const void *q, const void *k, const void *v, const float *decay
         if (st != LA2_OK) return st;
     }
     return output_scan(q, k, v, o, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace,
-                       0, s, state_in, state_out);
+                       0, s, state_in, state_out, den);
 }
 
 }  // namespace
@@ -477,12 +480,10 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
     const la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
     if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess) return LA2_ERR_HIP;
     if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
-    // 2. numerator: the plain scan on phi(q), phi(k)
-    st = forward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block,
-                      dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream);
-    if (st != LA2_OK) return st;
-    // 3. o_t /= den_t
-    return la2::launch_divide(o, a.den, chains * T, (int)d_v, dtype, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+    // 2. numerator: the plain scan on phi(q), phi(k), each output row divided by its den_t before it is
+    //    stored (in fp32, so o is rounded once)
+    return forward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block,
+                        dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, a.den);
 }
 
 }  // extern "C"

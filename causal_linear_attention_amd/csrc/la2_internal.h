@@ -38,6 +38,8 @@ struct ScanArgs {
     // entry state_index(s)
     int sub;
     int nsub;
+    const float *den;      // forward output launches: fp32 [chains, T], y_t is divided by den_t before it
+                           // is stored (the normalized form), or nullptr
 };
 
 // Entry of the states array a segment starts from: its first sub-segment in the forward direction,
@@ -77,8 +79,8 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
 // the decayed d-vector scans of the denominator (modes in la2_norm.hip: 0 forward segment sums of
 // phi(k), 1 den_t = phi(q_t) . z_t with phi(q), phi(k) written where pq / pk are given, 2 the
 // denominator's part of dq, 3 reverse segment sums of dden_t phi(q_t), 4 the denominator's part of
-// dk), launch_divide divides o by den, launch_grad_rows forms dn = do / den and
-// dden = -(do . o) / den.
+// dk; the division by den is done by the numerator's output launch, ScanArgs::den),
+// launch_grad_rows forms dn = do / den and dden = -(do . o) / den.
 struct DenArgs {
     const void *q, *k;     // [chains, T, D], phi applied inside
     void *pq, *pk;         // [chains, T, D] phi(q), phi(k) out (mode 1), or nullptr
@@ -94,7 +96,6 @@ struct DenArgs {
     int chains;
 };
 hipError_t launch_vscan(const DenArgs &a, int D, int dtype, int fmap, int mode, hipStream_t s);
-hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s);
 hipError_t launch_grad_rows(const void *o, const void *dout, const float *den, void *dn, float *dden, int64_t rows,
                             int DV, int dtype, hipStream_t s);
 

@@ -7,7 +7,8 @@
 // The numerator is the plain tile scan run on phi(q), phi(k).  The denominator is a d-vector scan:
 // 2 d flops per position against 2 d elements read, so it is a pure HBM stream done on the vector
 // ALUs.  It runs first, reading q and k once: it writes phi(q) and phi(k) for the numerator scan
-// (elu + 1 only) and den_t in fp32; after the numerator scan one elementwise pass divides o.
+// (elu + 1 only) and den_t in fp32; the numerator scan's output pass divides each row by its den_t
+// before it stores it.
 //
 // Denominator kernel layout: one workgroup of 256 threads per (chain, segment) walks the segment in
 // chunks of 64 positions.  Thread (c8, g) owns 8 consecutive feature dims (c8 of D/8) and a run of
@@ -265,36 +266,6 @@ __global__ __launch_bounds__(kThreadsN) void grad_rows_kernel(const E *o, const 
     }
 }
 
-// o[r, :] /= den[r] over `rows` rows of DV elements.  Each thread takes 4 groups of 8 elements per
-// step, 256 threads apart, and issues all their loads before the first division.
-constexpr int kDivUnroll = 4;
-
-template <typename E, int DV>
-__global__ __launch_bounds__(kThreadsN) void divide_kernel(E *o, const float *den, int64_t rows) {
-    constexpr int G8 = DV / 8;
-    const int64_t n = rows * G8, stride = (int64_t)gridDim.x * kThreadsN * kDivUnroll;
-    for (int64_t i0 = (int64_t)blockIdx.x * kThreadsN * kDivUnroll + threadIdx.x; i0 < n; i0 += stride) {
-        float x[kDivUnroll][8], d[kDivUnroll];
-#pragma unroll
-        for (int u = 0; u < kDivUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kThreadsN;
-            if (i < n) {
-                load8(o + i * 8, x[u]);
-                d[u] = den[i / G8];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kDivUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kThreadsN;
-            if (i < n) {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) x[u][m] = x[u][m] / d[u];
-                store8(o + i * 8, x[u]);
-            }
-        }
-    }
-}
-
 template <typename E, int D, int FMAP>
 hipError_t launch_vs(const DenArgs &a, int mode, hipStream_t s) {
     const bool sums = mode == kZSeg || mode == kYSeg;
@@ -312,17 +283,6 @@ hipError_t launch_vs(const DenArgs &a, int mode, hipStream_t s) {
 template <typename E, int FMAP>
 hipError_t launch_vs_e(const DenArgs &a, int D, int mode, hipStream_t s) {
     return D == 64 ? launch_vs<E, 64, FMAP>(a, mode, s) : launch_vs<E, 128, FMAP>(a, mode, s);
-}
-
-template <typename E>
-hipError_t launch_div_e(void *o, const float *den, int64_t rows, int DV, hipStream_t s) {
-    const int64_t want = (rows * (DV / 8) + kThreadsN * kDivUnroll - 1) / (kThreadsN * kDivUnroll);
-    const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
-    if (DV == 64)
-        hipLaunchKernelGGL((divide_kernel<E, 64>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<E *>(o), den, rows);
-    else
-        hipLaunchKernelGGL((divide_kernel<E, 128>), dim3(grid), dim3(kThreadsN), 0, s, static_cast<E *>(o), den, rows);
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -359,11 +319,6 @@ hipError_t launch_grad_rows(const void *o, const void *dout, const float *den, v
                                static_cast<const float *>(dout), den, static_cast<float *>(dn), dden, rows);
     }
     return hipGetLastError();
-}
-
-hipError_t launch_divide(void *o, const float *den, int64_t rows, int DV, int dtype, hipStream_t s) {
-    if (!(DV == 64 || DV == 128) || rows <= 0) return hipErrorInvalidValue;
-    return dtype == 1 ? launch_div_e<__bf16>(o, den, rows, DV, s) : launch_div_e<float>(o, den, rows, DV, s);
 }
 
 }  // namespace la2

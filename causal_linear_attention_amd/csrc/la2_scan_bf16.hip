@@ -178,7 +178,7 @@ __device__ __forceinline__ void dma_tile(u16 *buf, const u16 *a, const u16 *b, c
     dma_rows<DV, TB>(make_rsrc(c + t0 * DVT, (T - t0) * DVT * 2), buf + C::oV, DVT, wave, lane);
 }
 
-template <int D, int DV, int TB, Dir DIR, bool DECAY>
+template <int D, int DV, int TB, Dir DIR, bool DECAY, bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     using C = Cfg<D, DV, TB, DECAY>;
     __shared__ __attribute__((aligned(16))) u16 smem[C::kLds];
@@ -301,8 +301,20 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
         // O^T groups, then 16-byte reads of whole rows, so every store instruction writes 8 full
         // 128-byte rows.
         f32x16 oacc[C::ODB];
+        // normalized form: the denominator of this lane's row, fetched now so that its load has the
+        // tile to land (rows past T divide by 1 and are not stored)
+        float den = 1.0f;
+        if constexpr (NORM) {
+            const int64_t t = t0 + tb * 32 + col;
+            if (t < T) den = p.den[(int64_t)chain * T + t];
+        }
         auto store_o = [&](u16 *ob) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * p.DVT, (T - t0) * p.DVT * 2);
+            if constexpr (NORM) {
+                const float rd = 1.0f / den;
+#pragma unroll
+                for (int n = 0; n < C::ODB; ++n) oacc[n] *= rd;
+            }
             constexpr int NC = C::OSW / 8;   // 16-byte chunks per staged row
             // chunk swizzle: 16 lanes writing one chunk of 16 consecutive rows (or reading whole rows)
             // touch 16 different bank groups
@@ -595,14 +607,26 @@ __global__ __launch_bounds__(kThreads, 1) void scan_bf16_kernel(ScanArgs p) {
     }
 }
 
-template <int D, int DV, int TB, Dir DIR>
-hipError_t launch_one(const ScanArgs &a, hipStream_t s) {
+template <int D, int DV, int TB, Dir DIR, bool NORM>
+hipError_t launch_norm(const ScanArgs &a, hipStream_t s) {
     const int64_t items = (int64_t)a.chains * a.seg_count * a.nslice;
     if (a.decay)
-        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, true>), dim3((unsigned)items), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, true, NORM>), dim3((unsigned)items), dim3(kThreads), 0, s,
+                           a);
     else
-        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, false>), dim3((unsigned)items), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((scan_bf16_kernel<D, DV, TB, DIR, false, NORM>), dim3((unsigned)items), dim3(kThreads), 0,
+                           s, a);
     return hipGetLastError();
+}
+
+template <int D, int DV, int TB, Dir DIR>
+hipError_t launch_one(const ScanArgs &a, hipStream_t s) {
+    if constexpr (DIR == Dir::Forward) {
+        if (a.den) return launch_norm<D, DV, TB, DIR, true>(a, s);
+    } else {
+        if (a.den) return hipErrorInvalidValue;
+    }
+    return launch_norm<D, DV, TB, DIR, false>(a, s);
 }
 
 template <int D, int DV>

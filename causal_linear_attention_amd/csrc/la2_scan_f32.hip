@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void scan_f32_kernel(ScanArgs p) {
                 float acc = ew >= 0 ? inter * pw(ew) : 0.0f;
                 for (int j = 0; j < TB; ++j) acc = fmaf(sP[i * TB + j], sV[j * DV + n], acc);
                 const int64_t t = t0 + i;
-                if (t < T) gy[t * p.DVT + n] = acc;
+                if (t < T) gy[t * p.DVT + n] = p.den ? acc / p.den[(int64_t)chain * T + t] : acc;
             }
             __syncthreads();   // sS reads done before the update
         }
