@@ -131,10 +131,10 @@ int la2_decode_step(const void *q, const void *k, const void *v, const float *de
  *   positive, so o_t is a weighted average of v_0..v_t; with
  *   LA2_PHI_IDENTITY (the pages' default map) the denominator can vanish or
  *   change sign and is not guarded (a zero gives inf or NaN, as the formula
- *   does).  The numerator runs through the same tiled scan as la2_forward
- *   (on phi(q), phi(k) rounded to `dtype`) and is stored in o; the
- *   denominator is accumulated in fp32 from phi in fp32, and o is then
- *   divided by it in fp32 and rounded to `dtype` again.
+ *   does).  The denominator is accumulated first, in fp32 from phi in fp32;
+ *   the numerator then runs through the same tiled scan as la2_forward (on
+ *   phi(q), phi(k) rounded to `dtype`), each output row divided by its
+ *   denominator in fp32 and rounded to `dtype` once when it is stored.
  *   Other arguments as in la2_forward; workspace: at least
  *   la2_normalized_workspace_bytes(..., 0) bytes (phi(q) and phi(k) for
  *   LA2_PHI_ELU1, one fp32 denominator per position, per-segment sums and
