@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     la2_abi_version,
     la2_backward,
     la2_backward_normalized,
+    la2_backward_normalized_saved,
     la2_backward_saved,
     la2_backward_state,
     la2_decode_step,

@@ -21,7 +21,7 @@ LA2_PHI_ELU1 = 1
 _FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
 
 EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
-           "la2_backward", "la2_backward_state", "la2_backward_normalized",
+           "la2_backward", "la2_backward_state", "la2_backward_normalized", "la2_backward_normalized_saved",
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
 
@@ -63,6 +63,8 @@ def load_library(path=LIB_PATH):
     lib.la2_backward_normalized.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32,
                                             i32, vp, sz, vp]
     lib.la2_backward_normalized.restype = i32
+    lib.la2_backward_normalized_saved.argtypes = lib.la2_backward_normalized.argtypes
+    lib.la2_backward_normalized_saved.restype = i32
     lib.la2_normalized_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32]
     lib.la2_normalized_workspace_bytes.restype = sz
     lib.la2_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32]
@@ -216,18 +218,30 @@ def la2_forward_serial(q, k, v, decay, o, stream=None):
         raise LA2Error(st, "la2_forward_serial")
 
 
-def la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace=None, stream=None):
-    """Enqueue (dq, dk, dv) = gradients of <o, dout> for the normalized forward that returned o."""
+def la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace=None, stream=None,
+                            saved=False):
+    """Enqueue (dq, dk, dv) = gradients of <o, dout> for the normalized forward that returned o.
+    ``saved``: call la2_backward_normalized_saved, reusing what la2_forward_normalized on the same
+    inputs left in ``workspace`` (which must then be the backward-sized workspace it was given)."""
     B, H, T, d = q.shape
     d_v = v.shape[-1]
     ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_backward_normalized(
+    lib = load_library()
+    fn = lib.la2_backward_normalized_saved if saved else lib.la2_backward_normalized
+    st = fn(
         _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
         _dev_ptr(dout, "dout"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
         B, H, T, d, d_v, feature_map_code(feature_map), int(block), dtype_code(q.dtype),
         _dev_ptr(workspace, "workspace"), ws, _stream(stream))
     if st != 0:
-        raise LA2Error(st, "la2_backward_normalized")
+        raise LA2Error(st, "la2_backward_normalized_saved" if saved else "la2_backward_normalized")
+
+
+def la2_backward_normalized_saved(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace=None,
+                                  stream=None):
+    """la2_backward_normalized reusing the forward's denominators, phi(q), phi(k) and segment states
+    in ``workspace`` (see include/la2.h)."""
+    la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace, stream, saved=True)
 
 
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
@@ -344,13 +358,16 @@ def backward_state(q, k, v, dout, decay=None, block=128, state_in=None, dstate_o
     return dq, dk, dv, dstate_in
 
 
-def backward_normalized(q, k, v, o, dout, decay=None, block=128, feature_map="elu1", workspace=None):
-    """Allocate (dq, dk, dv) and run the normalized backward (o: the normalized forward's output)."""
+def backward_normalized(q, k, v, o, dout, decay=None, block=128, feature_map="elu1", workspace=None, saved=False):
+    """Allocate (dq, dk, dv) and run the normalized backward (o: the normalized forward's output;
+    ``saved``: ``workspace`` is the backward-sized one the forward on the same inputs was given)."""
     _check_same(q, k, v, dout)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace the normalized forward filled")
         workspace = normalized_workspace_for(q, v, feature_map, block, True)
-    la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace)
+    la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, block, workspace, saved=saved)
     return dq, dk, dv
 
 

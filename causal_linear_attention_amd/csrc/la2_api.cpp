@@ -386,12 +386,15 @@ DenPlan den_plan(int64_t chains, int64_t T) {
 
 // Workspace of the normalized forward: [phi(q)][phi(k)] (elu + 1 only), [den, fp32 per position],
 // [segment sums of the denominator's vector scans] (split chains only), [the numerator scan's own
-// workspace]; the backward adds [dden, fp32 per position][dn, the numerator's output gradient] and
-// takes the numerator backward's workspace.  Every part 256-byte aligned.
+// workspace]; the backward takes the numerator backward's workspace in the same place (its first
+// part holds the states exactly as the numerator forward leaves them) and adds [dden, fp32 per
+// position][dn, the numerator's output gradient][the reverse segment sums of its dk part] after it,
+// so everything the forward wrote sits where the backward reads it and nothing overwrites it
+// (la2_backward_normalized_saved may run again on the same workspace).  Every part 256-byte aligned.
 struct NormLayout {
     size_t phi;        // bytes of each of phi(q), phi(k)
     size_t den_off, dden_off, dn_off;
-    size_t z_off, z_bytes;
+    size_t z_off, z_bytes, y_off;
     size_t scan_off, scan_bytes;
     size_t total;
     DenPlan dp;
@@ -405,13 +408,15 @@ NormLayout norm_layout(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, i
     L.phi = fmap ? align256((size_t)(chains * T * d) * elem_size(dtype)) : 0;
     L.dp = den_plan(chains, T);
     L.den_off = 2 * L.phi;
-    L.dden_off = L.den_off + rows_f32;
-    L.dn_off = L.dden_off + (backward ? rows_f32 : 0);
-    L.z_off = L.dn_off + (backward ? align256((size_t)(chains * T * dv) * elem_size(dtype)) : 0);
+    L.z_off = L.den_off + rows_f32;
     L.z_bytes = L.dp.nseg > 1 ? align256((size_t)chains * L.dp.nseg * d * sizeof(float)) : 0;
     L.scan_off = L.z_off + L.z_bytes;
-    L.scan_bytes = backward ? backward_ws_bytes(B, H, T, d, dv, block, dtype) : make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
-    L.total = L.scan_off + L.scan_bytes;
+    L.scan_bytes = align256(backward ? backward_ws_bytes(B, H, T, d, dv, block, dtype)
+                                     : make_plan(B, H, T, d, dv, block, dtype).ws_bytes);
+    L.dden_off = L.scan_off + L.scan_bytes;
+    L.dn_off = L.dden_off + (backward ? rows_f32 : 0);
+    L.y_off = L.dn_off + (backward ? align256((size_t)(chains * T * dv) * elem_size(dtype)) : 0);
+    L.total = L.y_off + (backward ? L.z_bytes : 0);
     return L;
 }
 
@@ -604,12 +609,14 @@ int la2_backward_state(const void *q, const void *k, const void *v, const float 
 
 }  // extern "C"
 
-extern "C" {
+namespace {
 
-int la2_backward_normalized(const void *q, const void *k, const void *v, const float *decay, const void *o,
-                            const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d,
-                            int64_t d_v, int feature_map, int block, int dtype, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+// saved: phi(q), phi(k), the denominators, their segment sums and the numerator's segment states are
+// still in the workspace from la2_forward_normalized on the same inputs.
+int backward_normalized_impl(const void *q, const void *k, const void *v, const float *decay, const void *o,
+                             const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T,
+                             int64_t d, int64_t d_v, int feature_map, int block, int dtype, void *workspace,
+                             size_t workspace_bytes, void *stream, bool saved) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (feature_map != LA2_PHI_IDENTITY && feature_map != LA2_PHI_ELU1) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
@@ -638,16 +645,19 @@ int la2_backward_normalized(const void *q, const void *k, const void *v, const f
     la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
     float *dden = reinterpret_cast<float *>(ws + L.dden_off);
     void *dn = ws + L.dn_off;
-    // 1. the forward's denominator, phi(q), phi(k) (recomputed)
-    if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess) return LA2_ERR_HIP;
-    if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
+    // 1. the forward's denominator, phi(q), phi(k) (recomputed unless the forward left them)
+    if (!saved) {
+        if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess)
+            return LA2_ERR_HIP;
+        if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
+    }
     // 2. dn = do / den, dden = -(do . o) / den
     if (la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)
         return LA2_ERR_HIP;
     // 3. the numerator's gradients: the plain backward on (phi(q), phi(k), v) with output gradient dn;
     //    dv is final, dq and dk hold the gradients with respect to phi(q), phi(k) so far
     st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, dq, dk, dv, B, H, T, d, d_v, block, dtype,
-                       L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, false);
+                       L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, saved);
     if (st != LA2_OK) return st;
     // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place),
     //    dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative
@@ -655,8 +665,29 @@ int la2_backward_normalized(const void *q, const void *k, const void *v, const f
     a.g = dq;
     if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDQ, s) != hipSuccess) return LA2_ERR_HIP;
     a.g = dk;
+    a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.y_off) : nullptr;   // the forward's z sums stay
     if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVYSeg, s) != hipSuccess) return LA2_ERR_HIP;
     return la2::launch_vscan(a, (int)d, dtype, feature_map, kVDK, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la2_backward_normalized(const void *q, const void *k, const void *v, const float *decay, const void *o,
+                            const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d,
+                            int64_t d_v, int feature_map, int block, int dtype, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return backward_normalized_impl(q, k, v, decay, o, dout, dq, dk, dv, B, H, T, d, d_v, feature_map, block, dtype,
+                                    workspace, workspace_bytes, stream, false);
+}
+
+int la2_backward_normalized_saved(const void *q, const void *k, const void *v, const float *decay, const void *o,
+                                  const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t T,
+                                  int64_t d, int64_t d_v, int feature_map, int block, int dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return backward_normalized_impl(q, k, v, decay, o, dout, dq, dk, dv, B, H, T, d, d_v, feature_map, block, dtype,
+                                    workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

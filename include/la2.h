@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 7
+#define LA2_ABI_VERSION 8
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -162,6 +162,20 @@ int la2_backward_normalized(const void *q, const void *k, const void *v, const f
                             int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
                             int feature_map, int block, int dtype, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* la2_backward_normalized for the training step: the workspace must be the one
+ * that la2_forward_normalized was just given for the same q, k, v, decay,
+ * feature map, block and dtype (at least la2_normalized_workspace_bytes(..., 1)
+ * bytes, since the backward needs the larger size), unchanged since.  phi(q),
+ * phi(k), the denominators, their segment sums and the numerator's segment
+ * states are then read from it instead of recomputed; the result is the same
+ * as la2_backward_normalized's.  With a workspace the forward did not fill,
+ * the gradients are garbage (there is no way to detect it). */
+int la2_backward_normalized_saved(const void *q, const void *k, const void *v, const float *decay,
+                                  const void *o, const void *dout, void *dq, void *dk, void *dv,
+                                  int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v,
+                                  int feature_map, int block, int dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Workspace bytes needed by la2_forward_normalized (backward = 0) or
  * la2_backward_normalized (backward = 1) for these arguments; (size_t)-1 for

@@ -1,6 +1,7 @@
 """C-ABI library on the CPU: it loads, exports what include/la2.h declares, and
 rejects bad arguments before anything is enqueued (no GPU needed)."""
 import ctypes
+import functools
 import os
 import re
 
@@ -209,12 +210,15 @@ def test_backward_state_validation(lib):
 
 
 def bnr(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, do=P + 4 * MB, dq=P + 5 * MB, dk=P + 6 * MB,
-        dv_=P + 7 * MB, B=1, H=1, T=64, d=64, dv=64, fmap=1, block=64, dtype=1, ws=P + 8 * MB, wsb=1 << 24):
-    return lib.la2_backward_normalized(q, k, v, decay, o, do, dq, dk, dv_, B, H, T, d, dv, fmap, block, dtype, ws,
-                                       wsb, None)
+        dv_=P + 7 * MB, B=1, H=1, T=64, d=64, dv=64, fmap=1, block=64, dtype=1, ws=P + 8 * MB, wsb=1 << 24,
+        saved=False):
+    fn = lib.la2_backward_normalized_saved if saved else lib.la2_backward_normalized
+    return fn(q, k, v, decay, o, do, dq, dk, dv_, B, H, T, d, dv, fmap, block, dtype, ws, wsb, None)
 
 
-def test_backward_normalized_validation(lib):
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_normalized_validation(lib, saved):
+    bnr = functools.partial(globals()["bnr"], saved=saved)
     assert bnr(lib, o=None) == NULLP
     assert bnr(lib, dv_=None) == NULLP
     assert bnr(lib, fmap=5) == UNSUP

@@ -181,3 +181,45 @@ def test_backward_normalized_forced_segments(seg, monkeypatch):
     monkeypatch.setenv("LA2_NORM_SEGMENT", seg)
     run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
     run_backward_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=12)
+
+
+# ---- backward reusing the forward's workspace ----------------------------------------------------
+
+SAVED_CASES = [
+    # (B, H, T, d, dv, dtype, block, decay, fmap)
+    (2, 3, 333, 128, 128, "bf16", 128, "heads", "elu1"),    # split numerator and denominator, ragged tail
+    (16, 16, 200, 128, 64, "bf16", 128, "none", "elu1"),   # 256 chains: nothing split
+    (1, 3, 777, 64, 64, "f32", 32, "heads", "elu1"),
+    (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
+]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=lambda c: "-".join(str(v) for v in c))
+def test_backward_normalized_saved(case):
+    """la2_backward_normalized_saved after la2_forward_normalized on the backward-sized workspace:
+    bitwise the gradients of la2_backward_normalized (which recomputes the denominators, phi and
+    the numerator's segment states the saved call reads), twice in a row on the same workspace
+    (nothing the forward left there is overwritten), and within the oracle's bar."""
+    B, H, T, d, dv, dtype, block, decay, fmap = case
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=601 + T, decay=decay, backward=True)
+    if fmap == "identity":
+        x["q"], x["k"] = positive(x["q"]), positive(x["k"])
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    dec = None if x["decay"] is None else x["decay"].to(DEV)
+    ws = la2.normalized_workspace_for(q, v, fmap, block, backward=True)
+    o = la2.forward_normalized(q, k, v, dec, block, fmap, workspace=ws)
+    ref = la2.backward_normalized(q, k, v, o, do, dec, block, fmap)
+    for rep in range(2):
+        got = la2.backward_normalized(q, k, v, o, do, dec, block, fmap, workspace=ws, saved=True)
+        torch.cuda.synchronize()
+        for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(g, r), (rep, name)
+    oref = oracle.backward_normalized(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), fmap)
+    if dtype == "bf16":
+        terms = numerator_terms(x, fmap)
+        errs = [float(np.max(np.abs(f64(g) - r))) / max(float(np.max(np.abs(r))), float(np.max(np.abs(t))))
+                for g, r, t in zip(got[:2], oref[:2], terms)] + [rel_err(f64(got[2]), oref[2])]
+    else:
+        errs = [rel_err(f64(g), r) for g, r in zip(got, oref)]
+    print(case, " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= TOL[dtype], errs
