@@ -11,6 +11,7 @@ import os
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2.so")
+LA2_ABI_VERSION = 8   # the include/la2.h version these signatures follow
 
 LA2_F32 = 0
 LA2_BF16 = 1
@@ -73,6 +74,9 @@ def load_library(path=LIB_PATH):
     lib.la2_status_string.restype = ctypes.c_char_p
     lib.la2_abi_version.argtypes = []
     lib.la2_abi_version.restype = i32
+    if lib.la2_abi_version() != LA2_ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.la2_abi_version()}, this binding expects "
+                           f"{LA2_ABI_VERSION}; rebuild it with __graft_entry__.build()")
     if path == LIB_PATH:
         _lib = lib
     return lib

@@ -38,6 +38,7 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     ver = int(re.search(r"#define LA2_ABI_VERSION (\d+)", HEADER).group(1))
     assert la2.la2_abi_version() == ver
+    assert binding.LA2_ABI_VERSION == ver
     for code in range(8):
         s = la2.la2_status_string(code)
         assert s and s != "unknown status"
