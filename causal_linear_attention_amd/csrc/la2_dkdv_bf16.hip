@@ -319,13 +319,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
         const bool update = it + 1 < ntiles;
 
         const bool first_end = end_init && it == 0;
+        // the next tile's loads go out first and have the whole tile to land (32 VGPRs of staging fit
+        // beside the output block's registers: no spills, measured ~1% faster than issuing them after it)
+        if (update) fstage_load<D>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
         if (is_dk)
             out_block(std::true_type{}, t0, first_end);
         else
             out_block(std::false_type{}, t0, first_end);
 
-        // the next tile's loads go out after the register-heavy output phase
-        if (update) fstage_load<D>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
 
         // R = lam^TB R + (w_upd Q)^T dO
         if (update) {
