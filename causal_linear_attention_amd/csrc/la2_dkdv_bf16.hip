@@ -58,7 +58,8 @@ struct FStaged {
 };
 
 // Global loads of the four tiles starting at t0 into registers; rows at or past T read as zero.
-template <int D>
+// PART: 0 all four, 1 Q and dO only, 2 K and V only.
+template <int D, int PART = 0>
 __device__ __forceinline__ void fstage_load(FStaged<D> &r, const u16 *q, const u16 *k, const u16 *v, const u16 *o,
                                             int64_t t0, int64_t T, int tid) {
     const int64_t bytes = (T - t0) * D * 2;
@@ -67,10 +68,10 @@ __device__ __forceinline__ void fstage_load(FStaged<D> &r, const u16 *q, const u
 #pragma unroll
     for (int s = 0; s < FStaged<D>::NCH; ++s) {
         const int cid = tid + s * kThreads, off = ((cid / (D / 8)) * D + (cid % (D / 8)) * 8) * 2;
-        r.q[s] = bload(rq, off);
-        r.k[s] = bload(rk, off);
-        r.v[s] = bload(rv, off);
-        r.o[s] = bload(ro, off);
+        if constexpr (PART != 2) r.q[s] = bload(rq, off);
+        if constexpr (PART != 1) r.k[s] = bload(rk, off);
+        if constexpr (PART != 1) r.v[s] = bload(rv, off);
+        if constexpr (PART != 2) r.o[s] = bload(ro, off);
     }
 }
 
@@ -320,14 +321,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(DkdvArgs p) {
 
         const bool first_end = end_init && it == 0;
         // the next tile's loads go out first and have the whole tile to land (32 VGPRs of staging fit
-        // beside the output block's registers: no spills, measured ~1% faster than issuing them after it)
-        if (update) fstage_load<D>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
+        // beside the output block's registers: no spills, measured ~1% faster than issuing them after
+        // it); with decay, only K and V go out here and Q and dO after the output blocks (~1% faster
+        // on the decay workloads)
+        if (update) fstage_load<D, DECAY ? 2 : 0>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
         if (is_dk)
             out_block(std::true_type{}, t0, first_end);
         else
             out_block(std::false_type{}, t0, first_end);
 
 
+        if constexpr (DECAY) {
+            if (update) fstage_load<D, 1>(st, gq, gk, gv, go, tile_of(it + 1) * TB, T, tid);
+        }
         // R = lam^TB R + (w_upd Q)^T dO
         if (update) {
             if (s_active) {
