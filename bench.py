@@ -532,8 +532,9 @@ def main():
         roofline = {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": f"scan_{'bf16' if w.dtype == 'bf16' else 'f32'}_kernel<D={w.d},DV={w.dv},"
-                      f"TB={min(w.block, 128) if w.dtype == 'bf16' else w.block},Forward,Output>",
+            "kernel": (f"scan_bf16_kernel<D={w.d},DV={w.dv},TB={min(w.block, 128)},Forward,"
+                       f"decay={'true' if w.decay else 'false'}> (forward output scan)" if w.dtype == "bf16" else
+                       f"scan_f32_kernel<D={w.d},DV=64,TB={w.block},Forward,Output>"),
             "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
             "avg_launch_ms": round(dom_ms, 4),
             "algorithmic_bytes_per_launch": alg["fwd_bytes"],
