@@ -21,12 +21,17 @@
 //   sK  [TB][D]   K tile      (A^T A operand: plain reads; state-update A operand K^T: transpose reads)
 //   sV  [TB][DV]  V tile      (P V and state-update B operand V: transpose reads)
 //   sST [DV][D]   S^T in bf16 (Q S B operand)
+//   sKW [TB][D]   K rows weighted by w_upd (decay only: the state update's A operand)
+//   sOS           per-wave output staging (where LDS allows; with decay at TB = 128, sKW once the
+//                 state update is done with it)
 // Operands that need 8 consecutive positions per lane (K^T, V) come from ds_read_b64_tr_b16: in
 // each group of 16 lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
 // i/4 + 4e, so lanes that address (row R0 + j/4, column C0 + 4 (j%4)) get column C0 + i, rows
 // R0..R0+3.  Where two tile buffers fit in LDS the next tile goes global -> LDS directly, one whole
-// tile ahead; otherwise it is staged global -> registers -> LDS during the second half of the
-// current one.  Output tiles are staged per wave in LDS and stored as whole rows.
+// tile ahead; otherwise it is staged global -> registers -> LDS, its loads issued during the
+// current tile (without decay the query-role tile at its top, the others after the intra-tile
+// phase).  Output tiles are staged per wave in LDS and stored as whole rows; with the normalized
+// form each output row is divided by its denominator first.
 #include "la2_bf16_common.h"
 
 namespace la2 {
