@@ -251,7 +251,9 @@ def compare_bench(args):
       softmax:   torch.nn.functional.scaled_dot_product_attention(is_causal=True) on the flash or
                  memory-efficient backend (the math backend is never allowed), forward and
                  forward + backward through autograd.
-    Each timing is the median of 3 calls after 1 warm-up, HIP events on the current stream."""
+    Each timing is the median of 3 measurements, each of back-to-back calls covering about 20 ms
+    (at least one call), after at least 3 warm-up calls and 50 ms of work; HIP events on the current
+    stream."""
     import torch
     import causal_linear_attention_amd as la2
     from torch.nn.attention import SDPBackend, sdpa_kernel
@@ -260,16 +262,24 @@ def compare_bench(args):
     stream = torch.cuda.current_stream()
 
     def t_ms(fn, reps=3):
-        fn()
-        torch.cuda.synchronize()
+        # warm-up: at least 3 calls and about 50 ms of GPU work, so that the clocks have settled;
+        # then `reps` measurements of back-to-back calls (about 20 ms of work each, at least one
+        # call), median of the per-call times
+        t0, n = time.perf_counter(), 0
+        while n < 3 or time.perf_counter() - t0 < 0.05:
+            fn()
+            torch.cuda.synchronize()
+            n += 1
+        calls = max(1, int(0.02 / max((time.perf_counter() - t0) / n, 1e-6)))
         out = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            fn()
+            for _ in range(calls):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            out.append(e0.elapsed_time(e1))
+            out.append(e0.elapsed_time(e1) / calls)
         return sorted(out)[len(out) // 2]
 
     backend = None
@@ -318,7 +328,7 @@ def compare_bench(args):
     print(json.dumps({
         "metric": "fwd+bwd tokens/sec vs T: tiled lightning scan vs causal softmax attention vs token-serial recurrence",
         "value": last.get("lightning_fwd_bwd_tokens_per_s"), "unit": "tokens/s", "n_gpus": 1,
-        "steps": 3, "warmup": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "steps": 3, "warmup": 3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "comparison: 131072 tokens per batch, H=12, d=d_v=128, no decay, T_B=128",
                    "softmax_backend": None if backend is None else str(backend[0]), "parallelism": "none (1 GPU)"},
