@@ -32,8 +32,8 @@ METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roo
 # 1 GiB device copy (FETCH_SIZE x 1.9999, WRITE_SIZE x 1.0000).  Valid only for the kernel source they
 # were taken on (sha256 of la2_scan_bf16.hip followed by la2_bf16_common.h); for any other source the
 # roofline reports traffic as null.
-TRAFFIC_KERNEL_SHA256_16 = "ad69baee44285b16"
-TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573093 * 1024, "write": 524288 * 1024}
+TRAFFIC_KERNEL_SHA256_16 = "e57aa0bdbebc71dc"
+TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573061 * 1024, "write": 524288 * 1024}
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3

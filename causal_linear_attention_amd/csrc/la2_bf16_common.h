@@ -71,6 +71,11 @@ __device__ __forceinline__ bf16x8 frag_tr(const u16 *s, int k0, int n0, int lane
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// Cache policy of the tile streams: every tile is read (or written) once per launch, so the loads
+// and stores carry the nontemporal hint (nt, bit 1 of the cache-policy operand), which keeps
+// them from displacing reusable lines in L2 and the memory-side cache.
+constexpr int kStreamCpol = 2;
+
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0 and stores past
 // the end are dropped by the hardware range check, which is what handles a ragged last tile.
 // Every caller addresses at most one tile past `base`, so a range longer than 1 GiB is cut to
@@ -82,17 +87,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kStreamCpol));
 }
 
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x4 &v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
-                                           byte_off, 0, 0);
+                                           byte_off, 0, kStreamCpol);
 }
 
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x2 &v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r,
-                                          byte_off, 0, 0);
+                                          byte_off, 0, kStreamCpol);
 }
 
 __device__ __forceinline__ unsigned int f32_to_bf16(float f) {
@@ -120,7 +125,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, u16 *dst, int
     for (int s = 0; s < NL / kWaves; ++s) {
         const int i = wave + kWaves * s, c = 64 * i + lane, row = c / CPR, lc = (c % CPR) ^ swz<RL>(row);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 512 * i), 16,
-                                                 (row * gstride + lc * 8) * 2, 0, 0, 0);
+                                                 (row * gstride + lc * 8) * 2, 0, 0, kStreamCpol);
     }
 }
 
