@@ -34,8 +34,13 @@ __device__ __forceinline__ float phi(float x) {
         return x;
 }
 
+// Row loads and stores are streamed (each row is read or written once per launch), so they carry
+// the nontemporal hint.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const nt_u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
     const unsigned w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -45,7 +50,8 @@ __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
 }
 
 __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
-    const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    const nt_f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p)),
+                   b = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p) + 1);
     x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
 }
 
@@ -56,17 +62,15 @@ __device__ __forceinline__ unsigned bf16_bits(float x) {
 }
 
 __device__ __forceinline__ void store8(__bf16 *p, const float (&x)[8]) {
-    uint4 u;
-    u.x = bf16_bits(x[0]) | (bf16_bits(x[1]) << 16);
-    u.y = bf16_bits(x[2]) | (bf16_bits(x[3]) << 16);
-    u.z = bf16_bits(x[4]) | (bf16_bits(x[5]) << 16);
-    u.w = bf16_bits(x[6]) | (bf16_bits(x[7]) << 16);
-    *reinterpret_cast<uint4 *>(p) = u;
+    const nt_u32x4 u = {bf16_bits(x[0]) | (bf16_bits(x[1]) << 16), bf16_bits(x[2]) | (bf16_bits(x[3]) << 16),
+                        bf16_bits(x[4]) | (bf16_bits(x[5]) << 16), bf16_bits(x[6]) | (bf16_bits(x[7]) << 16)};
+    __builtin_nontemporal_store(u, reinterpret_cast<nt_u32x4 *>(p));
 }
 
 __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    const nt_f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<nt_f32x4 *>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<nt_f32x4 *>(p) + 1);
 }
 
 template <int FMAP>
