@@ -9,7 +9,9 @@
 // operands, so it is HBM-bound and uses plain FMAs, not MFMA.  One workgroup of 4 waves owns a
 // 64-column slice of one chain's S: lane l holds column l of the slice, wave w rows
 // [w D/4, (w+1) D/4); each row access is 64 consecutive floats (256 B).  The four partial dot
-// products meet in LDS.
+// products meet in LDS.  When the states together exceed the 256 MiB memory-side cache they are
+// streamed with the nontemporal hint (nothing of them survives to the next step anyway); smaller
+// sets keep the default policy, which leaves them cache-resident from one step to the next.
 #include "la2_internal.h"
 
 namespace la2 {
@@ -21,7 +23,7 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
-template <typename E, int D, int DV>
+template <typename E, int D, int DV, bool STREAM>
 __global__ __launch_bounds__(256) void decode_kernel(const E *q, const E *k, const E *v, const float *decay, E *o,
                                                      float *state, int H) {
     constexpr int NSL = DV / 64, R = D / 4;
@@ -35,8 +37,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const E *q, const E *k, con
 #pragma unroll 8
     for (int r = 0; r < R; ++r) {
         const int i = wave * R + r;
-        const float s = fmaf(lam, Sc[(int64_t)i * DV], to_f32(kc[i]) * vn);
-        Sc[(int64_t)i * DV] = s;
+        float *const p = Sc + (int64_t)i * DV;
+        const float s = fmaf(lam, STREAM ? __builtin_nontemporal_load(p) : *p, to_f32(kc[i]) * vn);
+        if constexpr (STREAM)
+            __builtin_nontemporal_store(s, p);
+        else
+            *p = s;
         acc = fmaf(s, to_f32(qc[i]), acc);
     }
     __shared__ float red[4][64];
@@ -48,16 +54,27 @@ __global__ __launch_bounds__(256) void decode_kernel(const E *q, const E *k, con
     }
 }
 
+template <typename E, int D, int DV>
+void launch_policy(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
+                   int chains, int H, hipStream_t s) {
+    constexpr int64_t kCacheBytes = (int64_t)256 << 20;
+    const unsigned grid = (unsigned)chains * (unsigned)(DV / 64);
+    const bool stream = (int64_t)chains * D * DV * (int64_t)sizeof(float) > kCacheBytes;
+    if (stream)
+        hipLaunchKernelGGL((decode_kernel<E, D, DV, true>), dim3(grid), dim3(256), 0, s, static_cast<const E *>(q),
+                           static_cast<const E *>(k), static_cast<const E *>(v), decay, static_cast<E *>(o), state, H);
+    else
+        hipLaunchKernelGGL((decode_kernel<E, D, DV, false>), dim3(grid), dim3(256), 0, s, static_cast<const E *>(q),
+                           static_cast<const E *>(k), static_cast<const E *>(v), decay, static_cast<E *>(o), state, H);
+}
+
 template <typename E, int D>
 hipError_t launch_dv(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,
                      int chains, int H, int DV, hipStream_t s) {
-    const unsigned grid = (unsigned)chains * (unsigned)(DV / 64);
     if (DV == 64)
-        hipLaunchKernelGGL((decode_kernel<E, D, 64>), dim3(grid), dim3(256), 0, s, static_cast<const E *>(q),
-                           static_cast<const E *>(k), static_cast<const E *>(v), decay, static_cast<E *>(o), state, H);
+        launch_policy<E, D, 64>(q, k, v, decay, o, state, chains, H, s);
     else
-        hipLaunchKernelGGL((decode_kernel<E, D, 128>), dim3(grid), dim3(256), 0, s, static_cast<const E *>(q),
-                           static_cast<const E *>(k), static_cast<const E *>(v), decay, static_cast<E *>(o), state, H);
+        launch_policy<E, D, 128>(q, k, v, decay, o, state, chains, H, s);
     return hipGetLastError();
 }
 

@@ -142,6 +142,29 @@ def test_decode_steps_continue_a_prefill(dtype, d, dv, decay):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("B,d,dv", [(260, 128, 128), (513, 128, 64)])
+def test_decode_streamed_state(B, d, dv):
+    """Over 256 MiB of states (B x 16 heads) the decode step streams them with the nontemporal
+    policy: two steps from a random fp32 state, outputs and states of sampled sequences against the
+    oracle's state-carrying forward from the same state."""
+    H = 16
+    assert B * H * d * dv * 4 > (256 << 20)
+    x = inputs.make_random(B, H, 2, d, dv, dtype="bf16", seed=131 + dv, decay="heads", backward=False)
+    q, k, v, dec = to_dev(x)
+    s0 = seeded_state(B, H, d, dv, 7)
+    state = s0.to(DEV)
+    outs = [la2.decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), state, dec)
+            for t in range(2)]
+    torch.cuda.synchronize()
+    rows = [0, B // 2, B - 1]
+    ref_o, ref_s = oracle.forward_state(*(f64(x[n])[rows] for n in ("q", "k", "v")), lam_of(x),
+                                        s0[rows].double().numpy())
+    got = torch.stack(outs, dim=2)[rows]
+    eo, es = rel_err(f64(got), ref_o), rel_err(f64(state[rows]), ref_s)
+    print(B, d, dv, f"o {eo:.2e} state {es:.2e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_decode_step_from_zero_is_one_position():
     """From a zero state a decode step is the one-position forward: o = (k . q) v."""
     x = inputs.make_random(3, 5, 1, 128, 64, dtype="bf16", seed=5, decay="heads", backward=False)
