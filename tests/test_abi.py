@@ -104,6 +104,30 @@ def test_workspace(lib):
     assert lib.la2_workspace_bytes(1, 1, 64, 96, 64, 64, 1, 0) == ctypes.c_size_t(-1).value
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_workspace_plan_properties(lib, dtype):
+    """Host plan over many shapes.  The work items are the chains (bf16) or the chains' 64-wide value
+    slices (fp32); with fewer than the 256 CUs a chain is cut into min(256 // work, tiles) segments,
+    so when that is below 2 there are no segment states; otherwise the workspace holds a whole number (at least 2, at most one per tile) of
+    d x d_v fp32 states per chain, and the backward's is at least the forward's."""
+    block = 128 if dtype == torch.bfloat16 else 64
+    for B, H, T, d, dv in [(1, 1, 1024, 64, 64), (1, 16, 131072, 128, 128), (2, 40, 6144, 128, 128),
+                           (1, 40, 131072, 128, 128), (8, 16, 16384, 128, 128), (3, 5, 777, 128, 64),
+                           (16, 16, 4096, 128, 128), (64, 4, 100000, 64, 64), (1, 1, block, 128, 128),
+                           (1, 2, block + 1, 64, 128), (255, 1, 5000, 64, 64), (128, 1, 5000, 64, 64),
+                           (1, 1, 3, 64, 64)]:
+        chains, tiles = B * H, -(-T // block)
+        work = chains * (dv // 64 if dtype == torch.float32 else 1)
+        f = la2.la2_workspace_bytes(B, H, T, d, dv, block, dtype, False)
+        g = la2.la2_workspace_bytes(B, H, T, d, dv, block, dtype, True)
+        unit = chains * d * dv * 4
+        if min(256 // work, tiles) < 2:
+            assert f == 0, (B, H, T)
+        else:
+            assert f % unit == 0 and 2 <= f // unit <= tiles, (B, H, T, f // unit)
+        assert g >= f, (B, H, T)
+
+
 def fwds(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, s_in=P + 8 * MB, o=P + 3 * MB, s_out=P + 9 * MB, B=1, H=1,
          T=64, d=64, dv=64, block=64, dtype=1, ws=None, wsb=0):
     return lib.la2_forward_state(q, k, v, decay, s_in, o, s_out, B, H, T, d, dv, block, dtype, ws, wsb, None)
