@@ -1,16 +1,20 @@
 """Thin ctypes binding of ``include/la2.h``: argument marshalling only.
 
 Every step of the computation runs in the HIP library ``lib/libla2.so``; this
-module only checks tensors, passes their device pointers, sizes and torch's
-current HIP stream, and turns status codes into exceptions.  There is no CPU
-path: if the library is missing or a tensor is not on the GPU, it raises.
+module only checks tensors (shape, dtype, device, layout) against the sizes the
+C ABI is given, passes their device pointers, sizes and torch's current HIP
+stream, and turns status codes into exceptions.  There is no CPU path: if the
+library is missing or a tensor is not on the GPU, it raises.
 """
+import contextlib
 import ctypes
 import os
 
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2.so")
+# the same kernels with la2_test_set_plan (include/la2_test_hooks.h); loaded only by plan_override()
+TEST_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2_testhooks.so")
 LA2_ABI_VERSION = 8   # the include/la2.h version these signatures follow
 
 LA2_F32 = 0
@@ -26,7 +30,8 @@ EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_n
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
 
-_lib = None
+_lib = None          # the library every wrapper calls: the release one, or the test build inside plan_override()
+_release = None
 
 
 class LA2Error(RuntimeError):
@@ -36,9 +41,9 @@ class LA2Error(RuntimeError):
 
 
 def load_library(path=LIB_PATH):
-    """Load (once) and return the ctypes handle of the built HIP library."""
-    global _lib
-    if _lib is not None and path == LIB_PATH:
+    """Load (once) and return the ctypes handle of the built HIP library (the one the wrappers call)."""
+    global _lib, _release
+    if path == LIB_PATH and _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not built ({path}); run __graft_entry__.build()")
@@ -78,8 +83,33 @@ def load_library(path=LIB_PATH):
         raise RuntimeError(f"{path} has ABI version {lib.la2_abi_version()}, this binding expects "
                            f"{LA2_ABI_VERSION}; rebuild it with __graft_entry__.build()")
     if path == LIB_PATH:
-        _lib = lib
+        _lib = _release = lib
     return lib
+
+
+_test_lib = None
+
+
+@contextlib.contextmanager
+def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0):
+    """Run the wrappers on the test build of the library with forced plan choices (see
+    include/la2_test_hooks.h; 0 / False = automatic).  For tests: the forced plans cover code paths
+    that small shapes would not reach.  Not thread-safe."""
+    global _lib, _test_lib
+    load_library()
+    if _test_lib is None:
+        lib = load_library(TEST_LIB_PATH)
+        lib.la2_test_set_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+        lib.la2_test_set_plan.restype = ctypes.c_int
+        _test_lib = lib
+    _test_lib.la2_test_set_plan(int(seg_tiles), int(state_sub), int(slice_width), int(bool(separate_dkdv)),
+                                int(norm_segment))
+    _lib = _test_lib
+    try:
+        yield _test_lib
+    finally:
+        _test_lib.la2_test_set_plan(0, 0, 0, 0, 0)
+        _lib = _release
 
 
 def la2_status_string(status):
@@ -133,53 +163,105 @@ def _dev_ptr(t, name):
     return t.data_ptr()
 
 
+def _ptrs(device, *specs):
+    """Device pointers of the tensors in ``specs``, (tensor, name, shape, dtype, optional) each, after
+    checking every one is exactly what the C call will be told: first all shapes and dtypes (so that
+    these checks run without a GPU), then that each is contiguous, on the GPU and on ``device``.
+    None passes through where ``optional``."""
+    for t, name, shape, dtype, optional in specs:
+        if t is None:
+            if not optional:
+                raise ValueError(f"{name} is required")
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    out = []
+    for t, name, _, _, _ in specs:
+        if t is not None and t.device.type == "cuda" and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+        out.append(_dev_ptr(t, name))
+    return out
+
+
+def _dims(q, v, q_rank=4):
+    """(sizes, dtype code, device) of a call from its query- and value-role tensors: q [B, H, T, d]
+    (or [B, H, d] for one position) and v [..., d_v]; each tensor is checked by _arg."""
+    for name, t in (("q", q), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != q_rank:
+            raise ValueError(f"{name} must have {q_rank} dimensions, got shape {tuple(t.shape)}")
+    code = dtype_code(q.dtype)
+    return tuple(q.shape), v.shape[-1], code, q.device
+
+
+def _workspace(ws, device):
+    """(pointer, bytes) of an optional workspace: a contiguous device tensor of any dtype."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device.type == "cuda" and ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, the other tensors on {device}")
+    return _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size()
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _decay_ptr(decay):
+def _decay(decay, H):
+    """Spec of the per-head decays for _ptrs: fp32 [H], or None for lam = 1.  Their values are not
+    read here (that would wait for the GPU); the high-level functions check (0, 1]."""
+    return (decay, "decay", (H,), torch.float32, True)
+
+
+def check_decay(decay):
+    """Raise unless every per-head decay is in (0, 1] (lam = 0 would give 0^0 on the mask diagonal
+    and NaN where the kernels form lam^n as 2^(n log2 lam)).  Reads the values: synchronizes."""
     if decay is None:
-        return None
-    if decay.dtype != torch.float32:
-        raise TypeError("decay must be float32")
-    return _dev_ptr(decay, "decay")
+        return
+    if decay.dtype != torch.float32 or decay.dim() != 1:
+        raise TypeError("decay must be a float32 vector [H]")
+    if decay.numel() and not bool(((decay > 0) & (decay <= 1)).all()):
+        raise ValueError("every decay must lie in (0, 1]")
 
 
 def la2_forward(q, k, v, decay, o, block, workspace=None, stream=None):
     """Enqueue o = attention(q, k, v) on ``stream`` (default: torch's current stream)."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_forward(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
-        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    wp, ws = _workspace(workspace, dev)
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (o, "o", vs, dt, False))
+    st = load_library().la2_forward(*p, B, H, T, d, d_v, int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_forward")
 
 
-def _state_ptr(t, name):
-    if t is None:
-        return None
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
-    return _dev_ptr(t, name)
+def _state(t, name, shape):
+    """Spec of an optional fp32 state for _ptrs."""
+    return (t, name, shape, torch.float32, True)
 
 
 def la2_forward_state(q, k, v, decay, state_in, o, state_out, block, workspace=None, stream=None):
     """Enqueue o = attention(q, k, v) from the carried-in fp32 state ``state_in`` ([B, H, d, d_v] or
     None) and write the final state to ``state_out`` (same shape, may be ``state_in``, or None)."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    for name, t in (("state_in", state_in), ("state_out", state_out)):
-        if t is not None and tuple(t.shape) != (B, H, d, d_v):
-            raise ValueError(f"{name} must be [B, H, d, d_v] = {(B, H, d, d_v)}")
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_forward_state(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _state_ptr(state_in, "state_in"),
-        _dev_ptr(o, "o"), _state_ptr(state_out, "state_out"),
-        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    sshape = (B, H, d, d_v)
+    wp, ws = _workspace(workspace, dev)
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              _state(state_in, "state_in", sshape), (o, "o", vs, dt, False), _state(state_out, "state_out", sshape))
+    st = load_library().la2_forward_state(*p, B, H, T, d, d_v, int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_forward_state")
 
@@ -187,37 +269,38 @@ def la2_forward_state(q, k, v, decay, state_in, o, state_out, block, workspace=N
 def la2_decode_step(q, k, v, decay, o, state, stream=None):
     """Enqueue one token per chain: state <- lam state + k v^T (in place), o = state^T q.
     q, k: [B, H, d]; v, o: [B, H, d_v]; state: fp32 [B, H, d, d_v]."""
-    B, H, d = q.shape
-    d_v = v.shape[-1]
-    if tuple(state.shape) != (B, H, d, d_v):
-        raise ValueError(f"state must be [B, H, d, d_v] = {(B, H, d, d_v)}")
-    st = load_library().la2_decode_step(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
-        _state_ptr(state, "state"), B, H, d, d_v, dtype_code(q.dtype), _stream(stream))
+    (B, H, d), d_v, code, dev = _dims(q, v, q_rank=3)
+    dt = q.dtype
+    p = _ptrs(dev, (q, "q", (B, H, d), dt, False), (k, "k", (B, H, d), dt, False), (v, "v", (B, H, d_v), dt, False),
+              _decay(decay, H), (o, "o", (B, H, d_v), dt, False),
+              (state, "state", (B, H, d, d_v), torch.float32, False))
+    st = load_library().la2_decode_step(*p, B, H, d, d_v, code, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_decode_step")
 
 
 def la2_forward_normalized(q, k, v, decay, o, feature_map, block, workspace=None, stream=None):
     """Enqueue the normalized output o = phi(q)^T S / phi(q)^T z (feature_map 'identity' or 'elu1')."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_forward_normalized(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
-        B, H, T, d, d_v, feature_map_code(feature_map), int(block), dtype_code(q.dtype),
-        _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    wp, ws = _workspace(workspace, dev)
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (o, "o", vs, dt, False))
+    st = load_library().la2_forward_normalized(*p, B, H, T, d, d_v, feature_map_code(feature_map), int(block), code,
+                                               wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_forward_normalized")
 
 
 def la2_forward_serial(q, k, v, decay, o, stream=None):
     """Enqueue o = attention(q, k, v) computed one position after another (comparison kernel)."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    st = load_library().la2_forward_serial(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
-        B, H, T, d, d_v, dtype_code(q.dtype), _stream(stream))
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (o, "o", vs, dt, False))
+    st = load_library().la2_forward_serial(*p, B, H, T, d, d_v, code, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_forward_serial")
 
@@ -227,16 +310,16 @@ def la2_backward_normalized(q, k, v, decay, o, dout, dq, dk, dv, feature_map, bl
     """Enqueue (dq, dk, dv) = gradients of <o, dout> for the normalized forward that returned o.
     ``saved``: call la2_backward_normalized_saved, reusing what la2_forward_normalized on the same
     inputs left in ``workspace`` (which must then be the backward-sized workspace it was given)."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    wp, ws = _workspace(workspace, dev)
     lib = load_library()
     fn = lib.la2_backward_normalized_saved if saved else lib.la2_backward_normalized
-    st = fn(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(o, "o"),
-        _dev_ptr(dout, "dout"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
-        B, H, T, d, d_v, feature_map_code(feature_map), int(block), dtype_code(q.dtype),
-        _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (o, "o", vs, dt, False), (dout, "dout", vs, dt, False), (dq, "dq", qs, dt, False),
+              (dk, "dk", qs, dt, False), (dv, "dv", vs, dt, False))
+    st = fn(*p, B, H, T, d, d_v, feature_map_code(feature_map), int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_backward_normalized_saved" if saved else "la2_backward_normalized")
 
@@ -252,15 +335,16 @@ def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
     la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
     ``workspace``."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    wp, ws = _workspace(workspace, dev)
     lib = load_library()
     fn = lib.la2_backward_saved if saved else lib.la2_backward
-    st = fn(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _dev_ptr(dout, "dout"),
-        _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"),
-        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (dout, "dout", vs, dt, False), (dq, "dq", qs, dt, False), (dk, "dk", qs, dt, False),
+              (dv, "dv", vs, dt, False))
+    st = fn(*p, B, H, T, d, d_v, int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_backward_saved" if saved else "la2_backward")
 
@@ -269,17 +353,15 @@ def la2_backward_state(q, k, v, decay, state_in, dout, dstate_out, dq, dk, dv, d
                        stream=None):
     """Enqueue the backward of la2_forward_state: (dq, dk, dv) and d(state_in) (fp32 [B, H, d, d_v] or
     None) of <o, dout> + <state_out, dstate_out> (state_in, dstate_out: fp32 [B, H, d, d_v] or None)."""
-    B, H, T, d = q.shape
-    d_v = v.shape[-1]
-    for name, t in (("state_in", state_in), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
-        if t is not None and tuple(t.shape) != (B, H, d, d_v):
-            raise ValueError(f"{name} must be [B, H, d, d_v] = {(B, H, d, d_v)}")
-    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().la2_backward_state(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _decay_ptr(decay), _state_ptr(state_in, "state_in"),
-        _dev_ptr(dout, "dout"), _state_ptr(dstate_out, "dstate_out"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"),
-        _dev_ptr(dv, "dv"), _state_ptr(dstate_in, "dstate_in"),
-        B, H, T, d, d_v, int(block), dtype_code(q.dtype), _dev_ptr(workspace, "workspace"), ws, _stream(stream))
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    qs, vs, ss = (B, H, T, d), (B, H, T, d_v), (B, H, d, d_v)
+    wp, ws = _workspace(workspace, dev)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              _state(state_in, "state_in", ss), (dout, "dout", vs, dt, False), _state(dstate_out, "dstate_out", ss),
+              (dq, "dq", qs, dt, False), (dk, "dk", qs, dt, False), (dv, "dv", vs, dt, False),
+              _state(dstate_in, "dstate_in", ss))
+    st = load_library().la2_backward_state(*p, B, H, T, d, d_v, int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_backward_state")
 
@@ -289,12 +371,21 @@ def la2_backward_saved(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, 
     la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace, stream, saved=True)
 
 
-def _check_same(q, k, v, other=None):
+def _check_same(q, k, v, other=None, decay=None):
+    """Checks of the high-level functions before they allocate: q, k [B, H, T, d], v (and dout)
+    [B, H, T, d_v], one dtype and device, and every decay in (0, 1] (this reads the decays)."""
+    _dims(q, v)
     for name, t in (("k", k), ("v", v)) + ((("dout", other),) if other is not None else ()):
-        if t.dtype != q.dtype or t.device != q.device:
+        if not isinstance(t, torch.Tensor) or t.dtype != q.dtype or t.device != q.device:
             raise ValueError(f"{name} must match q in dtype and device")
     if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B, H, T, d] and v [B, H, T, d_v]")
+    if other is not None and other.shape != v.shape:
+        raise ValueError("dout must have the shape of v, [B, H, T, d_v]")
+    if decay is not None:
+        if not isinstance(decay, torch.Tensor) or tuple(decay.shape) != (q.shape[1],) or decay.device != q.device:
+            raise ValueError(f"decay must be a float32 [H] = [{q.shape[1]}] tensor on {q.device}")
+        check_decay(decay)
 
 
 def workspace_for(q, v, block, backward):
@@ -305,7 +396,7 @@ def workspace_for(q, v, block, backward):
 
 def forward(q, k, v, decay=None, block=128, workspace=None):
     """Allocate o (and the workspace if none is given) and run the forward pass."""
-    _check_same(q, k, v)
+    _check_same(q, k, v, decay=decay)
     o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = workspace_for(q, v, block, False)
@@ -316,7 +407,7 @@ def forward(q, k, v, decay=None, block=128, workspace=None):
 def forward_state(q, k, v, decay=None, block=128, state_in=None, workspace=None):
     """Allocate o and the final state and run the forward from ``state_in`` (None = zero state);
     returns (o, state_out)."""
-    _check_same(q, k, v)
+    _check_same(q, k, v, decay=decay)
     B, H, T, d = q.shape
     o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     state_out = torch.empty((B, H, d, v.shape[-1]), dtype=torch.float32, device=q.device)
@@ -334,7 +425,7 @@ def normalized_workspace_for(q, v, feature_map, block, backward=False):
 
 def forward_normalized(q, k, v, decay=None, block=128, feature_map="elu1", workspace=None):
     """Allocate o (and the workspace if none is given) and run the normalized forward."""
-    _check_same(q, k, v)
+    _check_same(q, k, v, decay=decay)
     o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     if workspace is None:
         workspace = normalized_workspace_for(q, v, feature_map, block)
@@ -344,7 +435,7 @@ def forward_normalized(q, k, v, decay=None, block=128, feature_map="elu1", works
 
 def forward_serial(q, k, v, decay=None):
     """Allocate o and run the token-serial recurrence."""
-    _check_same(q, k, v)
+    _check_same(q, k, v, decay=decay)
     o = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     la2_forward_serial(q, k, v, decay, o)
     return o
@@ -352,7 +443,7 @@ def forward_serial(q, k, v, decay=None):
 
 def backward_state(q, k, v, dout, decay=None, block=128, state_in=None, dstate_out=None, workspace=None):
     """Allocate (dq, dk, dv, dstate_in) and run the backward of forward_state."""
-    _check_same(q, k, v, dout)
+    _check_same(q, k, v, dout, decay=decay)
     B, H, T, d = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dstate_in = torch.empty((B, H, d, v.shape[-1]), dtype=torch.float32, device=q.device)
@@ -365,7 +456,7 @@ def backward_state(q, k, v, dout, decay=None, block=128, state_in=None, dstate_o
 def backward_normalized(q, k, v, o, dout, decay=None, block=128, feature_map="elu1", workspace=None, saved=False):
     """Allocate (dq, dk, dv) and run the normalized backward (o: the normalized forward's output;
     ``saved``: ``workspace`` is the backward-sized one the forward on the same inputs was given)."""
-    _check_same(q, k, v, dout)
+    _check_same(q, k, v, dout, decay=decay)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         if saved:
@@ -379,6 +470,8 @@ def decode_step(q, k, v, state, decay=None):
     """One token per chain from ``state`` (updated in place); q, k: [B, H, d], v: [B, H, d_v]; returns o."""
     if k.shape != q.shape or v.shape[:2] != q.shape[:2] or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k must be [B, H, d] and v [B, H, d_v] of one dtype")
+    if decay is not None:
+        check_decay(decay)
     o = torch.empty_like(v)
     la2_decode_step(q, k, v, decay, o, state)
     return o
@@ -387,7 +480,7 @@ def decode_step(q, k, v, state, decay=None):
 def backward(q, k, v, dout, decay=None, block=128, workspace=None, saved=False):
     """Allocate (dq, dk, dv) and run the backward pass (``saved``: reuse the forward's segment states,
     which requires the workspace that forward() was given)."""
-    _check_same(q, k, v, dout)
+    _check_same(q, k, v, dout, decay=decay)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         if saved:

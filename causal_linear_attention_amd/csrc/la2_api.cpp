@@ -9,7 +9,6 @@
 //   2. a prefix pass chains the deltas into each segment's start state,
 //   3. the output pass runs every segment from its start state.
 // With enough chains only step 3 runs, from a zero state.
-#include <cstdlib>
 #include <cstring>
 
 #include "la2.h"
@@ -18,6 +17,25 @@
 namespace {
 
 constexpr int kComputeUnits = 256;   // MI355X: 256 CUs in 8 XCDs
+
+// Plan choices a test can force.  Only the test build of the library (compiled with
+// LA2_TEST_HOOKS, exporting la2_test_set_plan) has a way to set them; in the release build they
+// are constant zeros, so its launch plan depends on the call's arguments alone.
+struct PlanOverride {
+    int64_t seg_tiles;      // > 0: tiles per segment of every split chain
+    int state_sub;          // > 0: state-pass pieces per segment (used when it divides the segment)
+    int slice_width;        // 64: bf16 128-wide values run as two 64-wide slices
+    int separate_dkdv;      // != 0: the two separate reverse scans instead of the fused dk/dv pass
+    int64_t norm_segment;   // > 0: positions per segment of the denominator scans
+};
+
+#ifdef LA2_TEST_HOOKS
+PlanOverride g_override{};
+const PlanOverride &forced() { return g_override; }
+#else
+constexpr PlanOverride kNoOverride{};
+constexpr const PlanOverride &forced() { return kNoOverride; }
+#endif
 
 struct Plan {
     int TB;          // tile length the kernels run with
@@ -34,13 +52,9 @@ struct Plan {
 // in two: half the chip).  Cutting each segment into `sub` pieces (at least 32 tiles each, so the
 // extra fp32 state written per piece stays small next to the tiles it sums) gives more workgroups;
 // sub is chosen to fill whole rounds of the 256 CUs best, and only when that gains 10%.
-// LA2_STATE_SUB forces it (any divisor of seg_tiles).
 int choose_sub(int64_t work, int nseg, int seg_tiles) {
     if (nseg < 2) return 1;
-    if (const char *env = std::getenv("LA2_STATE_SUB")) {
-        const long v = std::strtol(env, nullptr, 10);
-        return v > 0 && seg_tiles % v == 0 ? (int)v : 1;
-    }
+    if (const int v = forced().state_sub; v > 0) return seg_tiles % v == 0 ? v : 1;
     const int64_t base = work * (nseg - 1);
     auto fill = [&](int r) {
         const int64_t w = base * r, rounds = (w + kComputeUnits - 1) / kComputeUnits;
@@ -58,9 +72,17 @@ int choose_sub(int64_t work, int nseg, int seg_tiles) {
 
 int elem_size(int dtype) { return dtype == LA2_BF16 ? 2 : 4; }
 
-bool block_ok(int dtype, int block) {
-    if (dtype == LA2_BF16) return block == 64 || block == 128 || block == 256;
-    return block == 16 || block == 32 || block == 64;
+// Tile lengths a caller may ask for (page "Lightning Attention", section 2: ceil(T / T_B) tiles of
+// any length; section 4 sweeps 64, 128 and 256).
+bool block_ok(int block) { return block == 16 || block == 32 || block == 64 || block == 128 || block == 256; }
+
+// Tile length the output kernels run for a requested `block`.  The intra/inter split is exact for
+// every tile length, so the request is met by the nearest length a kernel is built for: bf16 tiles
+// are 64 or 128 positions (32-row MFMA blocks; a 256 tile's Q, K and V alone would fill LDS), fp32
+// tiles 16, 32 or 64.
+int run_tile(int dtype, int block) {
+    if (dtype == LA2_BF16) return block < 64 ? 64 : block > 128 ? 128 : block;
+    return block > 64 ? 64 : block;
 }
 
 // Value-slice width a kernel launch uses for a value tensor of width `w`.
@@ -75,31 +97,27 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int bloc
     const int64_t chains = B * H;
     if (chains > (int64_t)1 << 24 || T > lim / chains || chains * T > lim / 512) return LA2_ERR_BAD_SHAPE;
     if (!((d == 64 || d == 128) && (dv == 64 || dv == 128))) return LA2_ERR_UNSUPPORTED;
-    if (!block_ok(dtype, block)) return LA2_ERR_UNSUPPORTED;
+    if (!block_ok(block)) return LA2_ERR_UNSUPPORTED;
     return LA2_OK;
 }
 
 // `fused`: the plan of the fused bf16 dk/dv pass, which tiles by kDkdvTile and splits only T.
 Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype, bool fused = false) {
     Plan p{};
-    p.TB = fused ? la2::kDkdvTile : dtype == LA2_BF16 ? (block > 128 ? 128 : block) : block;
+    p.TB = fused ? la2::kDkdvTile : run_tile(dtype, block);
     const int64_t NT = (T + p.TB - 1) / p.TB;
     const int64_t chains = B * H;
     // Too few chains to fill the chip: split T into segments (one extra state pass over k and v,
     // whose result the backward reuses).  Running a 128-wide value as two 64-wide slices would
     // avoid that pass (the kernel's XCD-aware order serves both slices' q and k from one L2), but
     // each slice still forms the whole score block, about 0.6 of a full slice's work, and measured
-    // slower than segments once the backward reuses the forward's states; LA2_SLICE_WIDTH=64
-    // selects it.
-    p.narrow = false;
-    if (const char *env = std::getenv("LA2_SLICE_WIDTH"))
-        p.narrow = !fused && dtype == LA2_BF16 && dv == 128 && std::strtol(env, nullptr, 10) == 64;
+    // slower than segments once the backward reuses the forward's states; only a forced plan uses it.
+    p.narrow = !fused && dtype == LA2_BF16 && dv == 128 && forced().slice_width == 64;
     const int64_t slices = dv / slice_width(dtype, (int)dv, p.narrow);
     const int64_t work = chains * slices;
     int64_t seg_tiles = NT;
-    if (const char *env = std::getenv("LA2_SEGMENT_TILES")) {
-        const long v = std::strtol(env, nullptr, 10);
-        if (v > 0) seg_tiles = v < NT ? v : NT;
+    if (const int64_t v = forced().seg_tiles; v > 0) {
+        seg_tiles = v < NT ? v : NT;
     } else if (!p.narrow && work < kComputeUnits && NT > 1) {
         int64_t nseg = kComputeUnits / work;
         if (nseg > NT) nseg = NT;
@@ -115,11 +133,9 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
 }
 
 // The backward computes dk and dv in one fused pass where a kernel exists for the shape (bf16,
-// d = d_v); LA2_SEPARATE_DKDV=1 selects the two separate reverse scans instead.
+// d = d_v), else by two separate reverse scans.
 bool fused_dkdv(int64_t d, int64_t dv, int dtype) {
-    if (const char *env = std::getenv("LA2_SEPARATE_DKDV"))
-        if (std::strtol(env, nullptr, 10) != 0) return false;
-    return dtype == LA2_BF16 && la2::dkdv_supported((int)d, (int)dv);
+    return dtype == LA2_BF16 && la2::dkdv_supported((int)d, (int)dv) && !forced().separate_dkdv;
 }
 
 // Backward workspace: [S segment states, exactly as la2_forward leaves them][R segment states].
@@ -224,6 +240,13 @@ int output_scan(const void *a, const void *b, const void *c, void *y, const floa
 extern "C" {
 
 int la2_abi_version(void) { return LA2_ABI_VERSION; }
+
+#ifdef LA2_TEST_HOOKS
+int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment) {
+    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment};
+    return LA2_OK;
+}
+#endif
 
 const char *la2_status_string(int status) {
     switch (status) {
@@ -362,7 +385,6 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Segments of the denominator pass: enough (chain, segment) workgroups to give every compute unit
 // about 8, each segment at least 256 positions and a multiple of the kernel's 64-position chunk.
-// LA2_NORM_SEGMENT forces the segment length (positions).
 struct DenPlan {
     int64_t seg_len;
     int nseg;
@@ -376,10 +398,7 @@ DenPlan den_plan(int64_t chains, int64_t T) {
         if (nseg > most) nseg = most;
     }
     int64_t seg_len = (T + nseg - 1) / nseg;
-    if (const char *env = std::getenv("LA2_NORM_SEGMENT")) {
-        const long v = std::strtol(env, nullptr, 10);
-        if (v > 0) seg_len = v;
-    }
+    if (const int64_t v = forced().norm_segment; v > 0) seg_len = v;
     seg_len = (seg_len + 63) / 64 * 64;
     return DenPlan{seg_len, (int)((T + seg_len - 1) / seg_len)};
 }

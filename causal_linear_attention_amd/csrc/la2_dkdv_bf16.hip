@@ -2,8 +2,9 @@
 // dK and dV of one (chain, segment) in a single walk over its tiles, last to first.
 //
 // Both gradients are reverse scans that share one state (page "Lightning Attention",
-// lizeman.github.io llm-arch-kb, section 2, Steps 1-4, run backwards, with the per-head decay of
-// Lightning Attention-2, arXiv 2401.04658, section 3):
+// lizeman.github.io llm-arch-kb, section 2, Steps 1-4, run backwards).  The optional per-head decay
+// lam is not defined on the pages; it enters through the token recurrence S_t = lam S_{t-1} +
+// k_t v_t^T, whose chain-rule backward is:
 //   R_t  = lam R_{t+1} + q_t do_t^T                 (d x d_v, fp32 in MFMA accumulators)
 //   dk_t = R_t v_t,   dv_t = R_t^T k_t
 // Per tile of TB positions, with local rows i (outputs) and j (sources), j >= i inside the tile:

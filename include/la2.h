@@ -14,10 +14,10 @@
  * carried from tile to tile (Step 4).  With lam < 1 the mask M becomes
  * lam^(i-j) on and below the diagonal, the inter-tile rows are weighted
  * lam^(i+1) and the state update is S_b = lam^block S_{b-1} +
- * (diag(lam^(block-1-j)) K_b)^T V_b.  The backward pass ("tiling ... through
- * both forward and backward", Lightning Attention-2 abstract, arXiv 2401.04658)
- * produces dQ by the same forward-order scan and dK, dV by the mirrored
- * reverse-order scan of R_t = lam R_{t+1} + q_t do_t^T.
+ * (diag(lam^(block-1-j)) K_b)^T V_b.  The backward pass is tiled as well
+ * (Lightning Attention-2 abstract, arXiv 2401.04658 card): dQ by the same
+ * forward-order scan and dK, dV by the mirrored reverse-order scan of
+ * R_t = lam R_{t+1} + q_t do_t^T.
  *
  * Tensors.  Device pointers to contiguous row-major [B, H, T, d] (q, k, dq,
  * dk) and [B, H, T, d_v] (v, o, dout, dv) arrays of one element type `dtype`,
@@ -26,14 +26,16 @@
  * its values are read on the device and not validated (values outside (0, 1]
  * give unspecified results).
  *
- * Supported: d, d_v in {64, 128}; dtype LA2_BF16 with block in {64, 128, 256},
- * LA2_F32 with block in {16, 32, 64}.  `block` is the tile length asked for;
- * a kernel may run shorter tiles with the state handed over between them,
- * which gives the same result for any tile size (same page, section 2: the
- * split into intra- and inter-tile parts holds for every tile length), up to
- * rounding.  bf16 tiles are at most 128 positions (a block of 256 runs as two
- * 128-position tiles), and the bf16 backward with d = d_v computes dK and dV
- * in one fused reverse pass over 64-position tiles.
+ * Supported: d, d_v in {64, 128}; dtype LA2_BF16 or LA2_F32; block in
+ * {16, 32, 64, 128, 256} for both.  `block` is the tile length asked for: the
+ * split into intra- and inter-tile parts holds for every tile length (same
+ * page, section 2), so the kernels run the nearest tile length they are built
+ * for, with the state handed over between tiles, and the result is the same
+ * up to rounding.  bf16 output scans run 64-position tiles for block 16, 32
+ * and 64 and 128-position tiles for 128 and 256 (a 256 tile's Q, K and V
+ * alone would fill the 160 KiB of LDS at d = 128); fp32 scans run 16, 32 or
+ * 64 positions (64 for 128 and 256).  The bf16 backward with d = d_v computes
+ * dK and dV in one fused reverse pass over 64-position tiles.
  *
  * Ownership.  The caller allocates and frees every buffer, including the
  * workspace (la2_workspace_bytes tells its size; it may be 0, in which case

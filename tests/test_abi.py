@@ -72,9 +72,25 @@ def test_unsupported(lib):
     assert fwd(lib, d=96) == UNSUP
     assert fwd(lib, dv=256) == UNSUP
     assert fwd(lib, dtype=7) == UNSUP
-    assert fwd(lib, dtype=1, block=32) == UNSUP      # bf16 tiles: 64, 128, 256
-    assert fwd(lib, dtype=0, block=128) == UNSUP     # fp32 tiles: 16, 32, 64
-    assert bwd(lib, block=100) == UNSUP
+    for dtype in (0, 1):
+        for block in (0, 8, 48, 100, 512, -64):
+            assert fwd(lib, dtype=dtype, block=block) == UNSUP, (dtype, block)
+            assert bwd(lib, dtype=dtype, block=block) == UNSUP, (dtype, block)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_every_tile_length_is_accepted(lib, dtype):
+    """T_B in {16, 32, 64, 128, 256} for both dtypes (a request: the kernels run the nearest tile
+    length they are built for, bf16 64 or 128, fp32 16, 32 or 64, and the split into segments follows
+    that tile).  Checked through the workspace query, which validates like the calls do."""
+    bad = ctypes.c_size_t(-1).value
+    run = {16: 64, 32: 64, 64: 64, 128: 128, 256: 128} if dtype == 1 else {16: 16, 32: 32, 64: 64, 128: 64, 256: 64}
+    for block, tile in run.items():
+        # one chain of 64 tiles of the kernel's length: split into min(256, 64) = 64 segments
+        n = lib.la2_workspace_bytes(1, 1, 64 * tile, 64, 64, block, dtype, 0)
+        assert n != bad, block
+        assert n == 64 * 64 * 64 * 4, (block, n)         # 64 segment states of 64 x 64 fp32
+        assert lib.la2_workspace_bytes(1, 1, 64 * tile, 64, 64, block, dtype, 1) >= n
 
 
 def test_misaligned(lib):
@@ -258,7 +274,87 @@ def test_backward_normalized_validation(lib, saved):
 
 def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="on the GPU"):
         la2.la2_forward(q, q, q, None, torch.empty_like(q), 64)
     with pytest.raises(TypeError):
         la2.forward(q.half(), q.half(), q.half())
+
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(*shape, dtype=dtype)
+
+
+def test_binding_checks_every_shape_and_dtype():
+    """Every low-level wrapper checks each tensor against the sizes it passes to the C ABI (shapes
+    and dtypes are checked before the device, so these refusals run on the CPU): a short dout, a
+    decay of the wrong length or dtype, a state of the wrong shape never reach a kernel."""
+    B, H, T, d, dv = 2, 3, 40, 64, 128
+    q, k, v = _t(B, H, T, d), _t(B, H, T, d), _t(B, H, T, dv)
+    o, do, dq, dk, dvv = _t(B, H, T, dv), _t(B, H, T, dv), _t(B, H, T, d), _t(B, H, T, d), _t(B, H, T, dv)
+    dec = torch.full((H,), 0.9)
+    st = _t(B, H, d, dv, dtype=torch.float32)
+    cases = [
+        (lambda: la2.la2_forward(q, k[:, :, :-1], v, None, o, 64), ValueError, "k must have shape"),
+        (lambda: la2.la2_forward(q, k, v[..., :64], None, o, 64), ValueError, "o must have shape"),
+        (lambda: la2.la2_forward(q, k, v, None, o.float(), 64), TypeError, "o must be"),
+        (lambda: la2.la2_forward(q, k, v, dec[:2], o, 64), ValueError, "decay must have shape"),
+        (lambda: la2.la2_forward(q, k, v, dec.double(), o, 64), TypeError, "decay must be"),
+        (lambda: la2.la2_forward(q[0], k, v, None, o, 64), ValueError, "q must have 4 dimensions"),
+        (lambda: la2.la2_backward(q, k, v, None, do[:, :, :-1], dq, dk, dvv, 64), ValueError, "dout must have shape"),
+        (lambda: la2.la2_backward(q, k, v, None, do, dq, dk[..., :32], dvv, 64), ValueError, "dk must have shape"),
+        (lambda: la2.la2_backward(q, k, v, dec, do, dq, dk, dq, 64), ValueError, "dv must have shape"),
+        (lambda: la2.la2_backward_saved(q, k, v, None, do, dq.float(), dk, dvv, 64), TypeError, "dq must be"),
+        (lambda: la2.la2_forward_state(q, k, v, None, st[:1], o, st, 64), ValueError, "state_in must have shape"),
+        (lambda: la2.la2_forward_state(q, k, v, None, st, o, st.double(), 64), TypeError, "state_out must be"),
+        (lambda: la2.la2_backward_state(q, k, v, None, None, do, st.transpose(2, 3), dq, dk, dvv, st, 64),
+         ValueError, "dstate_out must have shape"),
+        (lambda: la2.la2_decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], None, o[:, :, 0], st[:, :2]), ValueError,
+         "state must have shape"),
+        (lambda: la2.la2_forward_normalized(q, k, v, dec, o[:1], "elu1", 64), ValueError, "o must have shape"),
+        (lambda: la2.la2_backward_normalized(q, k, v, None, o, do, dq, dk, dvv[..., :8], "elu1", 64), ValueError,
+         "dv must have shape"),
+        (lambda: la2.la2_forward_serial(q, k, v, torch.ones(H, 1), o), ValueError, "decay must have shape"),
+    ]
+    for fn, exc, msg in cases:
+        with pytest.raises(exc, match=msg):
+            fn()
+
+
+@pytest.mark.parametrize("bad", [0.0, -0.5, 1.5, float("nan"), float("inf")])
+def test_high_level_api_rejects_decay_outside_unit_interval(bad):
+    """lam must lie in (0, 1]: lam = 0 gives 0^0 on the mask diagonal, which the kernels form as
+    2^(0 * log2 0) = NaN; lam > 1 grows without bound."""
+    q = _t(1, 2, 16, 64)
+    dec = torch.tensor([0.5, bad])
+    for fn in (lambda: la2.forward(q, q, q, dec), lambda: la2.backward(q, q, q, q, dec),
+               lambda: la2.lightning_attention(q, q, q, dec), lambda: la2.forward_state(q, q, q, dec),
+               lambda: la2.forward_normalized(q, q, q, dec)):
+        with pytest.raises(ValueError, match=r"\(0, 1\]"):
+            fn()
+    with pytest.raises(ValueError, match="decay must be"):
+        la2.forward(q, q, q, torch.tensor([0.5]))          # one decay per head
+
+
+def test_release_library_has_no_plan_overrides(lib):
+    """Test knobs live only in the test build: the release library exports no override and reads no
+    environment variable, so its plan depends on the arguments alone."""
+    assert not hasattr(lib, "la2_test_set_plan")
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    assert "getenv" not in syms
+
+
+def test_test_build_forces_plans():
+    """The test build (libla2_testhooks.so) exports la2_test_set_plan; under binding.plan_override the
+    wrappers call it and the forced plan shows in the workspace it asks for."""
+    hooks = open(os.path.join(ROOT, "include", "la2_test_hooks.h")).read()
+    assert "la2_test_set_plan" in hooks
+    base = la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False)
+    assert base == 0                                  # 256 chains fill the GPU: no split
+    with binding.plan_override(seg_tiles=4) as tl:
+        assert hasattr(tl, "la2_test_set_plan")
+        # 32 tiles per chain in segments of 4: 8 segments, a state per segment
+        assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 256 * 8 * 128 * 128 * 4
+    with binding.plan_override(seg_tiles=4, state_sub=2):
+        assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 256 * 16 * 128 * 128 * 4
+    assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 0   # restored

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import causal_linear_attention_amd as la2
-from causal_linear_attention_amd import inputs
+from causal_linear_attention_amd import binding, inputs
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -73,12 +73,12 @@ def test_normalized_matches_oracle(case):
     run_case(*case, seed=101 + case[2])
 
 
-@pytest.mark.parametrize("seg", ["64", "128", "320"])
-def test_normalized_forced_segments(seg, monkeypatch):
+@pytest.mark.parametrize("seg", [64, 128, 320])
+def test_normalized_forced_segments(seg):
     """Denominator segments of a forced length: the segment sums chained across up to 16 segments."""
-    monkeypatch.setenv("LA2_NORM_SEGMENT", seg)
-    run_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=7)
-    run_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=8)
+    with binding.plan_override(norm_segment=seg):
+        run_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=7)
+        run_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=8)
 
 
 def test_normalized_ones_values_give_ones():
@@ -174,13 +174,13 @@ def test_backward_normalized_matches_oracle(case):
     run_backward_case(*case, seed=401 + case[2])
 
 
-@pytest.mark.parametrize("seg", ["64", "128", "320"])
-def test_backward_normalized_forced_segments(seg, monkeypatch):
+@pytest.mark.parametrize("seg", [64, 128, 320])
+def test_backward_normalized_forced_segments(seg):
     """Denominator scans over forced segments: forward and reverse carries across up to 16 segments,
     the reverse walk over a ragged last segment."""
-    monkeypatch.setenv("LA2_NORM_SEGMENT", seg)
-    run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
-    run_backward_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=12)
+    with binding.plan_override(norm_segment=seg):
+        run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
+        run_backward_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=12)
 
 
 # ---- backward reusing the forward's workspace ----------------------------------------------------

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import causal_linear_attention_amd as la2
-from causal_linear_attention_amd import inputs
+from causal_linear_attention_amd import binding, inputs
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -76,21 +76,15 @@ def test_forward_state_matches_oracle(case):
     assert torch.equal(o0, la2.forward(q, k, v, dec, block))
 
 
-@pytest.mark.parametrize("seg_tiles,slice_width,sub", [("1", None, None), ("3", None, None), (None, "64", None),
-                                                       ("2", "64", None), ("4", None, "2")])
-def test_forward_state_plans(seg_tiles, slice_width, sub, monkeypatch):
+@pytest.mark.parametrize("seg_tiles,slice_width,sub", [(1, 0, 0), (3, 0, 0), (0, 64, 0), (2, 64, 0), (4, 0, 2)])
+def test_forward_state_plans(seg_tiles, slice_width, sub):
     """Forced segment splits (prefix with a carried-in state), state pieces finer than the segments
     and 64-wide value slices."""
-    if seg_tiles:
-        monkeypatch.setenv("LA2_SEGMENT_TILES", seg_tiles)
-    if sub:
-        monkeypatch.setenv("LA2_STATE_SUB", sub)
-    if slice_width:
-        monkeypatch.setenv("LA2_SLICE_WIDTH", slice_width)
     x = inputs.make_random(2, 2, 600, 128, 128, dtype="bf16", seed=71, decay="heads", backward=False)
     s_in = seeded_state(2, 2, 128, 128, 73)
     q, k, v, dec = to_dev(x)
-    o, s_out = la2.forward_state(q, k, v, dec, 128, state_in=s_in.to(DEV))
+    with binding.plan_override(seg_tiles=seg_tiles, state_sub=sub, slice_width=slice_width):
+        o, s_out = la2.forward_state(q, k, v, dec, 128, state_in=s_in.to(DEV))
     ref_o, ref_s = oracle.forward_state(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), f64(s_in))
     torch.cuda.synchronize()
     assert rel_err(f64(o), ref_o) <= 2e-2 and rel_err(f64(s_out), ref_s) <= 2e-2
@@ -220,15 +214,13 @@ def test_backward_state_partial(with_in, with_out):
     check_backward_state(1, 3, 500, 64, 128, "bf16", 64, "heads", 19, with_in, with_out)
 
 
-@pytest.mark.parametrize("env", [{"LA2_SEGMENT_TILES": "2"}, {"LA2_SEGMENT_TILES": "4", "LA2_STATE_SUB": "2"},
-                                 {"LA2_SEPARATE_DKDV": "1", "LA2_SEGMENT_TILES": "3"},
-                                 {"LA2_SLICE_WIDTH": "64", "LA2_SEGMENT_TILES": "2"}],
+@pytest.mark.parametrize("plan", [{"seg_tiles": 2}, {"seg_tiles": 4, "state_sub": 2},
+                                  {"separate_dkdv": True, "seg_tiles": 3}, {"slice_width": 64, "seg_tiles": 2}],
                          ids=lambda e: ",".join(f"{k}={v}" for k, v in e.items()))
-def test_backward_state_plans(env, monkeypatch):
-    for k_, v_ in env.items():
-        monkeypatch.setenv(k_, v_)
-    check_backward_state(1, 2, 777, 128, 128, "bf16", 128, "heads", 23)
-    check_backward_state(1, 2, 601, 64, 64, "f32", 32, "heads", 29)
+def test_backward_state_plans(plan):
+    with binding.plan_override(**plan):
+        check_backward_state(1, 2, 777, 128, 128, "bf16", 128, "heads", 23)
+        check_backward_state(1, 2, 601, 64, 64, "f32", 32, "heads", 29)
 
 
 @pytest.mark.parametrize("dtype,d,block", [("bf16", 128, 128), ("bf16", 64, 64), ("f32", 64, 32)])
