@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     la2_backward_state,
     la2_decode_step,
     la2_forward,
+    la2_forward_noalloc,
     la2_forward_normalized,
     la2_forward_serial,
     la2_forward_state,

@@ -15,7 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2.so")
 # the same kernels with la2_test_set_plan (include/la2_test_hooks.h); loaded only by plan_override()
 TEST_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libla2_testhooks.so")
-LA2_ABI_VERSION = 8   # the include/la2.h version these signatures follow
+LA2_ABI_VERSION = 9   # the include/la2.h version these signatures follow
 
 LA2_F32 = 0
 LA2_BF16 = 1
@@ -25,7 +25,7 @@ LA2_PHI_IDENTITY = 0
 LA2_PHI_ELU1 = 1
 _FMAPS = {"identity": LA2_PHI_IDENTITY, "elu1": LA2_PHI_ELU1}
 
-EXPORTS = ("la2_forward", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
+EXPORTS = ("la2_forward", "la2_forward_noalloc", "la2_forward_state", "la2_decode_step", "la2_forward_normalized", "la2_forward_serial",
            "la2_backward", "la2_backward_state", "la2_backward_normalized", "la2_backward_normalized_saved",
            "la2_backward_saved", "la2_workspace_bytes", "la2_normalized_workspace_bytes", "la2_status_string",
            "la2_abi_version")
@@ -51,6 +51,8 @@ def load_library(path=LIB_PATH):
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.la2_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la2_forward.restype = i32
+    lib.la2_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+    lib.la2_forward_noalloc.restype = i32
     lib.la2_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la2_backward.restype = i32
     lib.la2_backward_saved.argtypes = lib.la2_backward.argtypes
@@ -244,6 +246,19 @@ def la2_forward(q, k, v, decay, o, block, workspace=None, stream=None):
     st = load_library().la2_forward(*p, B, H, T, d, d_v, int(block), code, wp, ws, _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_forward")
+
+
+def la2_forward_noalloc(q, k, v, decay, o, block, stream=None):
+    """Enqueue o = attention(q, k, v) with the library's static per-GPU scratch instead of a workspace
+    (no device allocation; calls that overlap in time on one GPU race on that scratch)."""
+    (B, H, T, d), d_v, code, dev = _dims(q, v)
+    dt = q.dtype
+    qs, vs = (B, H, T, d), (B, H, T, d_v)
+    p = _ptrs(dev, (q, "q", qs, dt, False), (k, "k", qs, dt, False), (v, "v", vs, dt, False), _decay(decay, H),
+              (o, "o", vs, dt, False))
+    st = load_library().la2_forward_noalloc(*p, B, H, T, d, d_v, int(block), code, _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_forward_noalloc")
 
 
 def _state(t, name, shape):

@@ -10,6 +10,7 @@
 //   3. the output pass runs every segment from its start state.
 // With enough chains only step 3 runs, from a zero state.
 #include <cstring>
+#include <mutex>
 
 #include "la2.h"
 #include "la2_internal.h"
@@ -52,7 +53,8 @@ struct Plan {
 // in two: half the chip).  Cutting each segment into `sub` pieces (at least 32 tiles each, so the
 // extra fp32 state written per piece stays small next to the tiles it sums) gives more workgroups;
 // sub is chosen to fill whole rounds of the 256 CUs best, and only when that gains 10%.
-int choose_sub(int64_t work, int nseg, int seg_tiles) {
+// `most` caps the pieces per segment (the no-alloc forward's states must fit its static scratch).
+int choose_sub(int64_t work, int nseg, int seg_tiles, int64_t most) {
     if (nseg < 2) return 1;
     if (const int v = forced().state_sub; v > 0) return seg_tiles % v == 0 ? v : 1;
     const int64_t base = work * (nseg - 1);
@@ -62,7 +64,7 @@ int choose_sub(int64_t work, int nseg, int seg_tiles) {
     };
     int best = 1;
     double bf = fill(1);
-    for (int r = 2; seg_tiles / r >= 32; ++r)
+    for (int r = 2; seg_tiles / r >= 32 && r <= most; ++r)
         if (seg_tiles % r == 0 && fill(r) > bf + 0.1) {
             best = r;
             bf = fill(r);
@@ -102,7 +104,11 @@ int check_sizes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int bloc
 }
 
 // `fused`: the plan of the fused bf16 dk/dv pass, which tiles by kDkdvTile and splits only T.
-Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype, bool fused = false) {
+// `cap`: most workspace bytes the plan may need (the state-pass pieces are limited to fit); without
+// forced choices, one piece per segment always fits 16 MiB (at most 256 segment states of
+// d x d_v <= 128 x 128 fp32).
+Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype, bool fused = false,
+               size_t cap = SIZE_MAX) {
     Plan p{};
     p.TB = fused ? la2::kDkdvTile : run_tile(dtype, block);
     const int64_t NT = (T + p.TB - 1) / p.TB;
@@ -125,7 +131,8 @@ Plan make_plan(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block
     }
     p.seg_tiles = (int)seg_tiles;
     p.nseg = (int)((NT + seg_tiles - 1) / seg_tiles);
-    p.sub = choose_sub(work, p.nseg, p.seg_tiles);
+    const size_t per_piece = (size_t)chains * p.nseg * d * dv * sizeof(float);
+    p.sub = choose_sub(work, p.nseg, p.seg_tiles, (int64_t)(cap / per_piece));
     const int64_t sub_tiles = seg_tiles / p.sub;
     p.nsub = p.nseg > 1 ? (int)((NT + sub_tiles - 1) / sub_tiles) : 1;
     p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nsub * d * dv * sizeof(float) : 0;
@@ -258,6 +265,8 @@ const char *la2_status_string(int status) {
         case LA2_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
         case LA2_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or smaller than la2_workspace_bytes";
         case LA2_ERR_HIP: return "HIP kernel launch failed";
+        case LA2_ERR_SCRATCH_TOO_SMALL:
+            return "the sizes need more segment-state scratch than the static buffer of la2_forward_noalloc holds";
         default: return "unknown status";
     }
 }
@@ -275,7 +284,8 @@ namespace {
 // `den` (fp32 [B, H, T] or nullptr): o_t is divided by den_t before it is stored (the normalized form).
 int forward_impl(const void *q, const void *k, const void *v, const float *decay, const float *state_in, void *o,
                  float *state_out, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
-                 void *workspace, size_t workspace_bytes, void *stream, const float *den = nullptr) {
+                 void *workspace, size_t workspace_bytes, void *stream, const float *den = nullptr,
+                 size_t cap = SIZE_MAX) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -286,7 +296,7 @@ int forward_impl(const void *q, const void *k, const void *v, const float *decay
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)(B * H * T * d) * es, nv = (size_t)(B * H * T * d_v) * es;
     const size_t ns = (size_t)(B * H * d * d_v) * sizeof(float);
-    const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+    const Plan pl = make_plan(B, H, T, d, d_v, block, dtype, false, cap);
     const Range ro = range_of(o, nv);
     const Range rdec = range_of(decay, decay ? (size_t)H * 4 : 0);
     const Range rsi = range_of(state_in, state_in ? ns : 0), rso = range_of(state_out, state_out ? ns : 0);
@@ -331,6 +341,57 @@ int la2_forward_state(const void *q, const void *k, const void *v, const float *
                       int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return forward_impl(q, k, v, decay, state_in, o, state_out, B, H, T, d, d_v, block, dtype, workspace,
                         workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of la2_forward_noalloc: the segment states of split chains, in a static device array that
+// each GPU the library runs on holds until the process ends.  Host code never uses the array's name
+// as an address (on the host it names a stand-in, not device memory): each device's address is
+// looked up once, with that device current, and kept.
+constexpr size_t kScratchBytes = LA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (hipGetDevice), looked up on its first use.
+int current_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LA2_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LA2_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la2_forward_noalloc(const void *q, const void *k, const void *v, const float *decay, void *o, int64_t B,
+                        int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *stream) {
+    if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
+    const int st = check_sizes(B, H, T, d, d_v, block, dtype);
+    if (st != LA2_OK) return st;
+    const size_t need = make_plan(B, H, T, d, d_v, block, dtype, false, kScratchBytes).ws_bytes;
+    if (need > kScratchBytes) return LA2_ERR_SCRATCH_TOO_SMALL;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int sst = current_scratch(&ws);
+        if (sst != LA2_OK) return sst;
+    }
+    // every segment state the prefix reads is written by the state pass first: nothing to clear
+    return forward_impl(q, k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block, dtype, ws,
+                        need > 0 ? kScratchBytes : 0, stream, nullptr, kScratchBytes);
 }
 
 int la2_decode_step(const void *q, const void *k, const void *v, const float *decay, void *o, float *state,

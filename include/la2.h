@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LA2_ABI_VERSION 8
+#define LA2_ABI_VERSION 9
 
 enum la2_dtype { LA2_F32 = 0, LA2_BF16 = 1 };
 
@@ -79,8 +79,12 @@ enum la2_status {
     LA2_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
     LA2_ERR_ALIAS = 5,               /* an output overlaps an input, another output or the workspace */
     LA2_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < la2_workspace_bytes(...) or NULL workspace */
-    LA2_ERR_HIP = 7                  /* a kernel launch failed (hipGetLastError) */
+    LA2_ERR_HIP = 7,                 /* a kernel launch failed (hipGetLastError) */
+    LA2_ERR_SCRATCH_TOO_SMALL = 8    /* la2_forward_noalloc: the sizes need more than its static scratch */
 };
+
+/* Bytes of the static device scratch of la2_forward_noalloc (per GPU). */
+#define LA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Forward: o = attention(q, k, v).
  *   q, k: [B, H, T, d]; v, o: [B, H, T, d_v]; decay: [H] fp32 or NULL.
@@ -92,6 +96,30 @@ enum la2_status {
 int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o,
                 int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* la2_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same o as
+ * la2_forward (the same kernels and plan), with no workspace argument: the
+ * segment states of split chains live in a static device array of
+ * LA2_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, which each
+ * GPU holds from the first call on it until the process ends.  The call uses
+ * the array of the current device (hipGetDevice); `stream` must belong to that
+ * device.  It calls no hipMalloc or hipFree, and no allocating routine.
+ *   The plan is la2_forward's, except that the state pass of split chains
+ *   cuts a segment into no more pieces than the scratch holds states for (the
+ *   result differs from la2_forward's only by rounding where that limit
+ *   applies); the automatic plan then always fits, since one piece per segment
+ *   needs at most 256 states of d x d_v <= 128 x 128 fp32 = 16 MiB.  Sizes
+ *   whose plan would still need more (only forced plans of a test build) are
+ *   rejected with LA2_ERR_SCRATCH_TOO_SMALL before anything is enqueued.
+ *   All calls on one GPU share its array, and it keeps the last call's states:
+ *   calls that overlap in time on one GPU (other streams, other threads, graph
+ *   replays in flight together) race on it and give wrong results.  Calls
+ *   ordered on one stream are safe.  Other arguments and errors as in
+ *   la2_forward. */
+int la2_forward_noalloc(const void *q, const void *k, const void *v, const float *decay, void *o,
+                        int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
+                        void *stream);
 
 /* Forward carried in from and out to a state: the same o, for a sequence whose
  * prefix is summarized by state_in, and the state after its last position.

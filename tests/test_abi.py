@@ -39,7 +39,7 @@ def test_version_and_status_strings(lib):
     ver = int(re.search(r"#define LA2_ABI_VERSION (\d+)", HEADER).group(1))
     assert la2.la2_abi_version() == ver
     assert binding.LA2_ABI_VERSION == ver
-    for code in range(8):
+    for code in range(9):
         s = la2.la2_status_string(code)
         assert s and s != "unknown status"
     assert la2.la2_status_string(99) == "unknown status"
@@ -358,3 +358,21 @@ def test_test_build_forces_plans():
     with binding.plan_override(seg_tiles=4, state_sub=2):
         assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 256 * 16 * 128 * 128 * 4
     assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 0   # restored
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """la2_forward_noalloc refuses, before anything is enqueued, sizes whose plan would need more
+    segment states than its static scratch holds (reachable only through a forced plan: one tile per
+    segment of a 2000-tile chain at d = d_v = 128 is 125 MiB of states), and validates like
+    la2_forward otherwise."""
+    SCR = 8
+    assert "LA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in HEADER
+    lib_ = la2.load_library()
+    assert lib_.la2_forward_noalloc(None, P + MB, P + 2 * MB, None, P + 3 * MB, 1, 1, 64, 64, 64, 64, 1, None) == NULLP
+    assert lib_.la2_forward_noalloc(P, P + MB, P + 2 * MB, None, P + 3 * MB, 1, 1, 64, 96, 64, 64, 1, None) == UNSUP
+    assert lib_.la2_forward_noalloc(P, P + MB, P + 2 * MB, None, P + 3 * MB, 0, 1, 64, 64, 64, 64, 1, None) == SHAPE
+    with binding.plan_override(seg_tiles=1) as tl:
+        st = tl.la2_forward_noalloc(P, P + 4096 * MB, P + 8192 * MB, None, P + 12288 * MB, 1, 1, 128 * 2000,
+                                    128, 128, 128, 1, None)
+        assert st == SCR
+    assert la2.la2_status_string(SCR) != "unknown status"
