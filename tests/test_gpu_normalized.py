@@ -91,35 +91,60 @@ def test_normalized_ones_values_give_ones():
     assert float((o.float() - 1.0).abs().max()) <= 2e-2
 
 
-def test_normalized_full_size_sampled():
+def test_normalized_full_size_whole():
     """The 1K-position length-sweep workload (128 x 16 chains, d = d_v = 128, bf16) with elu + 1,
-    at full size in one launch; the oracle on sampled whole chains."""
+    at full size in one launch, every output element against the oracle."""
     x = inputs.make("sweep131k_t1k")
     w = x["workload"]
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     dec = None if x["decay"] is None else x["decay"].to(DEV)
     o = la2.forward_normalized(q, k, v, dec, w.block, "elu1")
     torch.cuda.synchronize()
-    lam = lam_of(x)
-    for b, h in [(0, 0), (w.B - 1, 15), (w.B // 2, 7)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        lh = None if lam is None else lam[h:h + 1]
-        ref = oracle.forward_normalized(*(f64(x[n][sl]) for n in ("q", "k", "v")), lh, "elu1")
-        err = rel_err(f64(o[sl]), ref)
-        print("chain", b, h, f"{err:.2e}", flush=True)
-        assert err <= TOL["bf16"]
+    ref = oracle.forward_normalized(*(f64(x[n]) for n in ("q", "k", "v")), lam_of(x), "elu1")
+    err = rel_err(f64(o), ref)
+    print(f"{w.name} normalized forward, all {w.B * w.H} chains: max|err|/max|ref| = {err:.2e}", flush=True)
+    assert err <= TOL["bf16"]
 
 
 # ---- backward ----------------------------------------------------------------------------------
 #
-# The bar for dq and dk in bf16.  They are d pq = S dn + dden z and d pk = R v + y (times phi'), and
-# for the gradient of a ratio the two terms largely cancel: the exact dq of a one-position sequence
-# is 0 while each term is O(1).  On the bf16 path each term carries bf16 roundings of its own size
-# (phi(q), phi(k), dn and the MFMA operand S in bf16, dq stored in bf16 before the second term is
-# added), so the error is bounded relative to the terms, not to their difference.  The bar is
-# therefore max|gpu - ref| <= 2e-2 x max(max|ref|, max|numerator term|), the numerator term being the
-# plain backward of (phi(q), phi(k), v) for the output gradient dn = do / den (oracle, fp64).  dv has
-# no such cancellation and keeps 2e-2 x max|ref|; fp32 keeps 1e-5 x max|ref| throughout.
+# The bar is the one of every case: max|gpu - ref| <= 2e-2 x max|ref| (bf16), 1e-5 x max|ref| (fp32),
+# per gradient.  dv meets it.  dq and dk of the bf16 path do not everywhere: they are d pq = S dn +
+# dden z and d pk = R v + y (times phi'), and for the gradient of a ratio the two terms largely cancel
+# (the exact dq of a one-position sequence is 0 while each term is O(1); on random inputs the
+# numerator term is 7-10x dq).  Each term carries bf16 roundings of its own size (phi(k) ~ 1 + x is
+# stored in bf16, which keeps x to 2-3 bits at x ~ 0.1; the scores P, dn and the state S are MFMA
+# operands in bf16; o itself is the forward's bf16 output), so the error is a few per cent of dq.
+# Where a bf16 dq or dk misses the bar the case is reported as an expected failure with its
+# measured error (a result above 0.15 fails outright: that is a broken kernel, not rounding).
+
+
+def check_grads(case, got, ref, terms=None):
+    dtype = case[5]
+    if case[2] == 1 and terms is not None:
+        # one position: dq and dk are exactly 0 (o = v_0 whatever q and k), so only an absolute bound
+        # means anything; it is taken relative to the two O(1) terms that cancel
+        for name, g, t in zip(("dq", "dk"), got[:2], terms):
+            a, scale = float(np.max(np.abs(f64(g)))), float(np.max(np.abs(t)))
+            print(case, name, f"max|gpu| {a:.2e} against terms of {scale:.2e}", flush=True)
+            assert a <= TOL[dtype] * scale, (name, a, scale)
+        assert rel_err(f64(got[2]), ref[2]) <= TOL[dtype]
+        return
+    errs = [rel_err(f64(g), r) for g, r in zip(got, ref)]
+    ratio = "" if terms is None else " numerator term / ref: " + " ".join(
+        f"{float(np.max(np.abs(t))) / float(np.max(np.abs(r))):.1f}" for t, r in zip(terms, ref[:2]))
+    print(case, "dq dk dv max|err|/max|ref|", " ".join(f"{e:.2e}" for e in errs) + ratio, flush=True)
+    for g in got:
+        assert np.isfinite(f64(g)).all()
+    tol = TOL[dtype]
+    if dtype == "f32":
+        assert max(errs) <= tol, errs
+        return
+    assert errs[2] <= tol, ("dv", errs[2])
+    assert max(errs[:2]) <= 0.15, errs
+    if max(errs[:2]) > tol:
+        pytest.xfail(f"bf16 normalized backward above the 2e-2 bar: dq {errs[0]:.2e}, dk {errs[1]:.2e} of max|ref| "
+                     "(cancelling terms carry bf16 roundings)")
 
 
 def numerator_terms(x, fmap):
@@ -157,16 +182,8 @@ def run_backward_case(B, H, T, d, dv, dtype, block, decay, fmap, seed):
     dq, dk, dv_ = la2.backward_normalized(q, k, v, o, do, dec, block, fmap)
     ref = oracle.backward_normalized(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), fmap)
     torch.cuda.synchronize()
-    if dtype == "bf16":
-        terms = numerator_terms(x, fmap)
-        errs = [float(np.max(np.abs(f64(g) - r))) / max(float(np.max(np.abs(r))), float(np.max(np.abs(t))))
-                for g, r, t in zip((dq, dk), ref[:2], terms)] + [rel_err(f64(dv_), ref[2])]
-    else:
-        errs = [rel_err(f64(g), r) for g, r in zip((dq, dk, dv_), ref)]
-    print((B, H, T, d, dv, dtype, block, decay, fmap), " ".join(f"{e:.2e}" for e in errs), flush=True)
-    for g in (dq, dk, dv_):
-        assert np.isfinite(f64(g)).all()
-    assert max(errs) <= TOL[dtype], errs
+    check_grads((B, H, T, d, dv, dtype, block, decay, fmap), (dq, dk, dv_), ref,
+                numerator_terms(x, fmap) if dtype == "bf16" else None)
 
 
 @pytest.mark.parametrize("case", BN_CASES, ids=lambda c: "-".join(str(v) for v in c))
@@ -179,8 +196,8 @@ def test_backward_normalized_forced_segments(seg):
     """Denominator scans over forced segments: forward and reverse carries across up to 16 segments,
     the reverse walk over a ragged last segment."""
     with binding.plan_override(norm_segment=seg):
-        run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
         run_backward_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=12)
+        run_backward_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=11)
 
 
 # ---- backward reusing the forward's workspace ----------------------------------------------------
@@ -215,11 +232,4 @@ def test_backward_normalized_saved(case):
         for name, g, r in zip(("dq", "dk", "dv"), got, ref):
             assert torch.equal(g, r), (rep, name)
     oref = oracle.backward_normalized(*(f64(x[n]) for n in ("q", "k", "v", "do")), lam_of(x), fmap)
-    if dtype == "bf16":
-        terms = numerator_terms(x, fmap)
-        errs = [float(np.max(np.abs(f64(g) - r))) / max(float(np.max(np.abs(r))), float(np.max(np.abs(t))))
-                for g, r, t in zip(got[:2], oref[:2], terms)] + [rel_err(f64(got[2]), oref[2])]
-    else:
-        errs = [rel_err(f64(g), r) for g, r in zip(got, oref)]
-    print(case, " ".join(f"{e:.2e}" for e in errs), flush=True)
-    assert max(errs) <= TOL[dtype], errs
+    check_grads(case, got, oref)
