@@ -4,15 +4,16 @@ Workload: the fixed-token length sweep -- 131,072 tokens per batch at
 (B, T) = (128, 1K), (32, 4K), (8, 16K), (2, 64K), (1, 128K), H = 16 heads,
 d = d_v = 128, tile T_B = 128, no decay, bf16 in HBM with fp32 accumulation,
 synthetic seeded inputs.  One step is the whole hot path (la2_forward then
-la2_backward) over each of the five batches; every input is resident in HBM
-before the timed region starts.
+la2_backward_saved on the same workspace, the training step) over each of the
+five batches; every input is resident in HBM before the timed region starts.
 
 Prints one JSON line: whole-job tokens/s over the timed steps, the per-length
 tokens/s, the roofline of the dominant kernel measured with HIP events on the
 stream the kernels run on, and the CPU oracle's tokens/s on a bounded sample.
 The per-length forward / backward split comes from an instrumented pass of the
 same steps (HIP events around every call) run before the timed region; inside
-the timed region the only events bracket the dominant kernel's launch.
+the timed region the only events bracket the two calls of the 1K point, each one
+kernel launch (the backward's is the dominant kernel).
 """
 import argparse
 import json
@@ -27,13 +28,15 @@ if ROOT not in sys.path:
 
 METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roofline"
 
-# HBM bytes per launch of the forward output kernel at the 1K point, from rocprofv3 --pmc FETCH_SIZE
-# and WRITE_SIZE runs (one counter per run), each scaled by what the same counter reads for a plain
-# 1 GiB device copy (FETCH_SIZE x 1.9999, WRITE_SIZE x 1.0000).  Valid only for the kernel source they
-# were taken on (sha256 of la2_scan_bf16.hip followed by la2_bf16_common.h); for any other source the
-# roofline reports traffic as null.
-TRAFFIC_KERNEL_SHA256_16 = "e57aa0bdbebc71dc"
-TRAFFIC_BYTES_PER_LAUNCH = {"fetch": 1573061 * 1024, "write": 524288 * 1024}
+# HBM bytes per launch of the dominant kernels at the 1K point, from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs (one counter per run), each scaled by what the same counter reads for a plain 1 GiB
+# device copy (FETCH_SIZE x 1.9999, WRITE_SIZE x 1.0000).  Each figure is valid only for the kernel
+# source it was taken on (sha256 of the listed files, concatenated); for any other source the roofline
+# reports traffic as null.
+TRAFFIC = {
+    "bwd1": {"sources": ("la2_bwd1_bf16.hip", "la2_bf16_common.h"), "sha256_16": None, "bytes": None},
+    "fwd": {"sources": ("la2_scan_bf16.hip", "la2_bf16_common.h"), "sha256_16": None, "bytes": None},
+}
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
@@ -363,12 +366,17 @@ def _segments(chains, T, tile):
     return -(-nt // seg_tiles), seg_tiles
 
 
+def one_pass_backward(w):
+    """True where la2_backward_saved runs the one-pass backward: no decay, bf16, d = d_v = 128."""
+    return not w.decay and w.dtype == "bf16" and w.d == 128 and w.dv == 128
+
+
 def executed(w):
     """MFMA flops the bf16 kernels execute for one forward and one training-step backward
     (la2_backward_saved) over workload w (d = d_v): score and output products over the causal 32 x 32
     blocks of the tiles the kernels actually run (output scans min(max(T_B, 64), 128) positions, the
-    fused dK/dV pass 64), the inter products and state updates (2 d^2 each per token), and the
-    state-only passes of split chains (2 d^2 per token of every segment whose delta is needed)."""
+    backward kernels 64), the inter products and state updates (2 d^2 each per token), and the
+    state-only passes of split chains (2 d^2 per token of every segment whose state is needed)."""
     d, T, chains = w.d, w.T, w.B * w.H
     th = chains * T
     tf = min(max(w.block, 64), 128)
@@ -377,11 +385,18 @@ def executed(w):
     nseg, seg_tiles = _segments(chains, T, tf)
     state_f = 2 * d * d * chains * min(T, (nseg - 1) * seg_tiles * tf) if nseg > 1 else 0
     fwd = th * (intra_f + 4 * d * d) + state_f
-    # backward: dQ = forward scan of (do, v, k) reusing the forward's states; fused dK/dV over 64-tiles:
-    # per 64-tile 3 causal blocks of 2 score and 2 output products, 2 inter products, 1 state update
-    nseg64, seg64 = _segments(chains, T, 64)
-    state_b = 2 * d * d * chains * max(0, T - seg64 * 64) if nseg64 > 1 else 0
-    bwd = th * (intra_f + 4 * d * d) + th * (4 * 3 * 2 * 32 * 32 * d // 64 + 6 * d * d) + state_b
+    causal64 = 3 * 2 * 32 * 32 * d // 64      # per token: one product over 3 causal 32 x 32 blocks of a 64-tile
+    if one_pass_backward(w):
+        # one reverse walk over 64-tiles: 2 score and 3 output products, 3 inter products, 2 state updates
+        # (R and the undoing of S); the reverse state-only pass over every segment but the first
+        state_b = 2 * d * d * chains * max(0, T - seg_tiles * tf) if nseg > 1 else 0
+        bwd = th * (5 * causal64 + 10 * d * d) + state_b
+    else:
+        # dQ = forward scan of (do, v, k) reusing the forward's states; fused dK/dV over 64-tiles:
+        # 2 score and 2 output products, 2 inter products, 1 state update
+        nseg64, seg64 = _segments(chains, T, 64)
+        state_b = 2 * d * d * chains * max(0, T - seg64 * 64) if nseg64 > 1 else 0
+        bwd = th * (intra_f + 4 * d * d) + th * (4 * causal64 + 6 * d * d) + state_b
     return {"fwd_flops_executed": fwd, "bwd_flops_executed": bwd}
 
 
@@ -484,9 +499,11 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    # Dominant kernel: the forward-direction output scan; at the 1K point la2_forward is exactly one
-    # launch of it (2048 chains fill the GPU, no segment split), so its event time is that launch.
-    dom = next((i for i, c in enumerate(cases) if c["ws"] is None), None)
+    # Dominant kernel: at the 1K point (2048 chains fill the GPU, no chain is split) la2_forward is one
+    # launch of the forward output scan and la2_backward_saved one launch of its backward kernel (the
+    # one-pass backward without decay), so the event times around the two calls are those launches.
+    dom = next((i for i, c in enumerate(cases) if c["w"].backward and c["w"].dtype == "bf16"
+                and _segments(c["w"].B * c["w"].H, c["w"].T, 128)[0] == 1), None)
 
     def step(record=None, only=None):
         for i, c in enumerate(cases):
@@ -527,8 +544,11 @@ def main():
         step(dom_events[s_] if dom is not None else None, only=dom)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = (sum(dom_events[s_][dom][0].elapsed_time(dom_events[s_][dom][1]) for s_ in range(args.steps))
-              / args.steps) if dom is not None else None
+    if dom is not None:
+        dom_fwd_ms = sum(dom_events[s_][dom][0].elapsed_time(dom_events[s_][dom][1])
+                         for s_ in range(args.steps)) / args.steps
+        dom_bwd_ms = sum(dom_events[s_][dom][1].elapsed_time(dom_events[s_][dom][2])
+                         for s_ in range(args.steps)) / args.steps
 
     tokens_per_step = sum(c["w"].tokens for c in cases)
     value = tokens_per_step * args.steps / wall
@@ -566,29 +586,49 @@ def main():
     roofline = None
     import hashlib
     csrc = os.path.join(ROOT, "causal_linear_attention_amd", "csrc")
-    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
-                                  for f in ("la2_scan_bf16.hip", "la2_bf16_common.h"))).hexdigest()[:16]
-    traffic = (TRAFFIC_BYTES_PER_LAUNCH["fetch"] + TRAFFIC_BYTES_PER_LAUNCH["write"]
-               if sha == TRAFFIC_KERNEL_SHA256_16 else None)
+
+    def traffic(name):
+        t = TRAFFIC[name]
+        sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in t["sources"]))
+        return t["bytes"] if t["bytes"] is not None and sha.hexdigest()[:16] == t["sha256_16"] else None
+
     if dom is not None:
         w = cases[dom]["w"]
-        alg = algorithmic(w)
-        achieved = alg["fwd_bytes"] / (dom_ms * 1e-3) / 1e9
-        roofline = {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": (f"scan_bf16_kernel<D={w.d},DV={w.dv},TB={min(w.block, 128)},Forward,"
-                       f"decay={'true' if w.decay else 'false'}> (forward output scan)" if w.dtype == "bf16" else
-                       f"scan_f32_kernel<D={w.d},DV=64,TB={w.block},Forward,Output>"),
-            "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
-            "avg_launch_ms": round(dom_ms, 4),
-            "algorithmic_bytes_per_launch": alg["fwd_bytes"],
-            # MFMA rate from the flops the launch executes (causal 32 x 32 blocks of its 128-position
-            # tiles); mfma_frac_nominal from the pages' whole-tile count
-            "mfma_TFLOPs": round(executed(w)["fwd_flops_executed"] / (dom_ms * 1e-3) / 1e12, 1),
-            "mfma_frac": round(executed(w)["fwd_flops_executed"] / (dom_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "mfma_frac_nominal": round(alg["fwd_flops"] / (dom_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        alg, ex = algorithmic(w), executed(w)
+        fwd_gbs = alg["fwd_bytes"] / (dom_fwd_ms * 1e-3) / 1e9
+        fwd_tf = ex["fwd_flops_executed"] / (dom_fwd_ms * 1e-3) / 1e12
+        forward_kernel = {
+            "kernel": f"scan_bf16_kernel<D={w.d},DV={w.dv},TB={min(w.block, 128)},Forward,decay=false> "
+                      "(forward output scan, writing each chain's final state)",
+            "avg_launch_ms": round(dom_fwd_ms, 4), "achieved_GBs": round(fwd_gbs, 1),
+            "frac": round(fwd_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": alg["fwd_bytes"],
+            "traffic": traffic("fwd"), "mfma_TFLOPs": round(fwd_tf, 1),
+            "mfma_frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         }
+        if one_pass_backward(w):
+            achieved = alg["bwd_bytes"] / (dom_bwd_ms * 1e-3) / 1e9
+            bwd_tf = ex["bwd_flops_executed"] / (dom_bwd_ms * 1e-3) / 1e12
+            roofline = {
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic("bwd1"),
+                "kernel": "bwd1_bf16_kernel (one-pass backward: dq, dk, dv from q, k, v, dout and the final state)",
+                "launch": f"la2_backward_saved at T={w.T}, B={w.B}: one launch per call",
+                "avg_launch_ms": round(dom_bwd_ms, 4),
+                "algorithmic_bytes_per_launch": alg["bwd_bytes"],
+                # MFMA rate from the flops the launch executes (causal 32 x 32 blocks of its 64-position tiles)
+                "mfma_TFLOPs": round(bwd_tf, 1), "mfma_frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "mfma_frac_nominal": round(alg["bwd_flops"] / (dom_bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "forward_kernel": forward_kernel,
+            }
+        else:
+            roofline = {
+                "bound": "hbm", "achieved": forward_kernel["achieved_GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": forward_kernel["frac"], "traffic": forward_kernel["traffic"],
+                "kernel": forward_kernel["kernel"], "launch": f"la2_forward at T={w.T}, B={w.B}: one launch per call",
+                "avg_launch_ms": forward_kernel["avg_launch_ms"],
+                "algorithmic_bytes_per_launch": alg["fwd_bytes"],
+                "mfma_TFLOPs": forward_kernel["mfma_TFLOPs"], "mfma_frac": forward_kernel["mfma_frac"],
+            }
 
     cpu = None
     hostc = next((c for c in cases if c["host"] is not None), None)

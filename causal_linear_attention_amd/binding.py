@@ -93,7 +93,8 @@ _test_lib = None
 
 
 @contextlib.contextmanager
-def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0):
+def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0,
+                  two_pass_backward=False):
     """Run the wrappers on the test build of the library with forced plan choices (see
     include/la2_test_hooks.h; 0 / False = automatic).  For tests: the forced plans cover code paths
     that small shapes would not reach.  Not thread-safe."""
@@ -101,16 +102,17 @@ def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, 
     load_library()
     if _test_lib is None:
         lib = load_library(TEST_LIB_PATH)
-        lib.la2_test_set_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+        lib.la2_test_set_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                          ctypes.c_int]
         lib.la2_test_set_plan.restype = ctypes.c_int
         _test_lib = lib
     _test_lib.la2_test_set_plan(int(seg_tiles), int(state_sub), int(slice_width), int(bool(separate_dkdv)),
-                                int(norm_segment))
+                                int(norm_segment), int(bool(two_pass_backward)))
     _lib = _test_lib
     try:
         yield _test_lib
     finally:
-        _test_lib.la2_test_set_plan(0, 0, 0, 0, 0)
+        _test_lib.la2_test_set_plan(0, 0, 0, 0, 0, 0)
         _lib = _release
 
 
@@ -348,8 +350,8 @@ def la2_backward_normalized_saved(q, k, v, decay, o, dout, dq, dk, dv, feature_m
 
 def la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None, saved=False):
     """Enqueue (dq, dk, dv) = gradients of <attention(q, k, v), dout>.  ``saved``: call
-    la2_backward_saved, reusing the segment states the la2_forward call on the same inputs left in
-    ``workspace``."""
+    la2_backward_saved, reusing the states the la2_forward call on the same inputs left in
+    ``workspace`` (both calls given at least la2_workspace_bytes(..., backward=True) bytes)."""
     (B, H, T, d), d_v, code, dev = _dims(q, v)
     dt = q.dtype
     qs, vs = (B, H, T, d), (B, H, T, d_v)
@@ -382,7 +384,7 @@ def la2_backward_state(q, k, v, decay, state_in, dout, dstate_out, dq, dk, dv, d
 
 
 def la2_backward_saved(q, k, v, decay, dout, dq, dk, dv, block, workspace=None, stream=None):
-    """la2_backward reusing the forward's segment states in ``workspace`` (see include/la2.h)."""
+    """la2_backward reusing the forward's states in ``workspace`` (see include/la2.h)."""
     la2_backward(q, k, v, decay, dout, dq, dk, dv, block, workspace, stream, saved=True)
 
 
@@ -493,8 +495,8 @@ def decode_step(q, k, v, state, decay=None):
 
 
 def backward(q, k, v, dout, decay=None, block=128, workspace=None, saved=False):
-    """Allocate (dq, dk, dv) and run the backward pass (``saved``: reuse the forward's segment states,
-    which requires the workspace that forward() was given)."""
+    """Allocate (dq, dk, dv) and run the backward pass (``saved``: reuse the forward's states, which
+    requires the backward-sized workspace that forward() was given)."""
     _check_same(q, k, v, dout, decay=decay)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:

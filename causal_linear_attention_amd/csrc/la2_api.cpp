@@ -28,6 +28,7 @@ struct PlanOverride {
     int slice_width;        // 64: bf16 128-wide values run as two 64-wide slices
     int separate_dkdv;      // != 0: the two separate reverse scans instead of the fused dk/dv pass
     int64_t norm_segment;   // > 0: positions per segment of the denominator scans
+    int two_pass_backward;  // != 0: la2_backward_saved without decay by the dQ pass and the dK/dV pass
 };
 
 #ifdef LA2_TEST_HOOKS
@@ -145,14 +146,44 @@ bool fused_dkdv(int64_t d, int64_t dv, int dtype) {
     return dtype == LA2_BF16 && la2::dkdv_supported((int)d, (int)dv) && !forced().separate_dkdv;
 }
 
-// Backward workspace: [S segment states, exactly as la2_forward leaves them][R segment states].
-// Keeping the forward's S states in place lets la2_backward_saved skip recomputing them.
+// Shapes whose training step without decay runs the one-pass backward (la2_bwd1_bf16.hip).
+bool bwd1_shape(int64_t d, int64_t dv, int dtype) {
+    return dtype == LA2_BF16 && d == 128 && dv == 128 && !forced().separate_dkdv && !forced().two_pass_backward;
+}
+
+// Plan of the one-pass backward: the forward plan's segments (whose start states it reads), cut into
+// kBwd1Tile-position tiles; sub / nsub / ws_bytes describe its reverse state pass.
+Plan bwd1_plan(const Plan &fwd, int64_t chains, int64_t T, int64_t d, int64_t dv) {
+    Plan p{};
+    p.TB = la2::kBwd1Tile;
+    p.nseg = fwd.nseg;
+    p.seg_tiles = fwd.seg_tiles * (fwd.TB / la2::kBwd1Tile);
+    p.sub = choose_sub(chains, p.nseg, p.seg_tiles, INT32_MAX);
+    const int64_t sub_tiles = p.seg_tiles / p.sub;
+    const int64_t nt = (T + p.TB - 1) / p.TB;
+    p.nsub = p.nseg > 1 ? (int)((nt + sub_tiles - 1) / sub_tiles) : 1;
+    p.ws_bytes = p.nseg > 1 ? (size_t)chains * p.nsub * d * dv * sizeof(float) : 0;
+    return p;
+}
+
+// Backward workspace: [S segment states, exactly as la2_forward leaves them][each chain's final state
+// (shapes of the one-pass backward only), which la2_forward leaves there when given this much
+// workspace and no decay][R segment states].  Keeping the forward's states in place lets
+// la2_backward_saved skip recomputing them.
 size_t backward_ws_bytes(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype,
-                         size_t *s_bytes = nullptr) {
-    const size_t a = make_plan(B, H, T, d, dv, block, dtype).ws_bytes;
-    const size_t b = fused_dkdv(d, dv, dtype) ? make_plan(B, H, T, d, dv, block, dtype, true).ws_bytes : a;
+                         size_t *s_bytes = nullptr, size_t *f_bytes = nullptr) {
+    const Plan pl = make_plan(B, H, T, d, dv, block, dtype);
+    const size_t a = pl.ws_bytes;
+    size_t b = fused_dkdv(d, dv, dtype) ? make_plan(B, H, T, d, dv, block, dtype, true).ws_bytes : a;
+    size_t f = 0;
+    if (bwd1_shape(d, dv, dtype)) {
+        f = (size_t)(B * H) * d * dv * sizeof(float);
+        const size_t r = bwd1_plan(pl, B * H, T, d, dv).ws_bytes;
+        if (r > b) b = r;
+    }
     if (s_bytes) *s_bytes = a;
-    return a + b;
+    if (f_bytes) *f_bytes = f;
+    return a + f + b;
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -249,8 +280,9 @@ extern "C" {
 int la2_abi_version(void) { return LA2_ABI_VERSION; }
 
 #ifdef LA2_TEST_HOOKS
-int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment) {
-    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment};
+int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment,
+                      int two_pass_backward) {
+    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment, two_pass_backward};
     return LA2_OK;
 }
 #endif
@@ -285,7 +317,7 @@ namespace {
 int forward_impl(const void *q, const void *k, const void *v, const float *decay, const float *state_in, void *o,
                  float *state_out, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                  void *workspace, size_t workspace_bytes, void *stream, const float *den = nullptr,
-                 size_t cap = SIZE_MAX) {
+                 size_t cap = SIZE_MAX, bool train_final = false) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !o) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -316,6 +348,13 @@ int forward_impl(const void *q, const void *k, const void *v, const float *decay
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chains = B * H;
+    // Given room for the backward (and no decay), the forward also leaves each chain's final state in the
+    // workspace, where the one-pass backward of la2_backward_saved starts from it.
+    if (train_final && !state_out && !decay && bwd1_shape(d, d_v, dtype) && workspace) {
+        size_t a = 0, f = 0;
+        if (workspace_bytes >= backward_ws_bytes(B, H, T, d, d_v, block, dtype, &a, &f))
+            state_out = reinterpret_cast<float *>(static_cast<char *>(workspace) + a);
+    }
     if (pl.nseg > 1) {
         st = segment_states(k, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype, la2::Dir::Forward, workspace, s,
                             state_in);
@@ -333,7 +372,7 @@ int la2_forward(const void *q, const void *k, const void *v, const float *decay,
                 int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
                 void *stream) {
     return forward_impl(q, k, v, decay, nullptr, o, nullptr, B, H, T, d, d_v, block, dtype, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, nullptr, SIZE_MAX, true);
 }
 
 int la2_forward_state(const void *q, const void *k, const void *v, const float *decay, const float *state_in,
@@ -579,7 +618,7 @@ namespace {
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream, bool reuse_s, const float *state_in = nullptr,
-                  const float *dstate_out = nullptr, float *dstate_in = nullptr) {
+                  const float *dstate_out = nullptr, float *dstate_in = nullptr, bool one_pass = false) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -593,8 +632,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     const size_t ns = (size_t)(B * H * d * d_v) * sizeof(float);
     const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
     const bool fused = fused_dkdv(d, d_v, dtype);
-    size_t s_bytes = 0;
-    const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype, &s_bytes);
+    size_t s_bytes = 0, f_bytes = 0;
+    const size_t ws_need = backward_ws_bytes(B, H, T, d, d_v, block, dtype, &s_bytes, &f_bytes);
     const Range ins[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
                           range_of(decay, decay ? (size_t)H * 4 : 0), range_of(state_in, state_in ? ns : 0),
                           range_of(dstate_out, dstate_out ? ns : 0)};
@@ -612,7 +651,35 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     const int D = (int)d, DV = (int)d_v;
     st = LA2_OK;
     const bool split = pl.nseg > 1;
-    void *ws_r = workspace ? static_cast<char *>(workspace) + s_bytes : nullptr;
+    void *ws_r = workspace ? static_cast<char *>(workspace) + s_bytes + f_bytes : nullptr;
+    if (one_pass && reuse_s && !decay && !state_in && !dstate_out && !dstate_in && bwd1_shape(d, d_v, dtype)) {
+        // Training step without decay: dq, dk and dv in one reverse walk from the forward's segment start
+        // states and final states (left in the workspace), and the reverse states at the segment ends.
+        const Plan bp = bwd1_plan(pl, chains, T, d, d_v);
+        if (bp.nseg > 1 && (st = segment_states(q, dout, nullptr, chains, H, T, D, DV, bp, dtype, la2::Dir::Reverse,
+                                                ws_r, s)) != LA2_OK)
+            return st;
+        la2::Bwd1Args a{};
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.dout = dout;
+        a.dq = dq;
+        a.dk = dk;
+        a.dv = dv;
+        a.T = T;
+        a.nseg = bp.nseg;
+        a.seg_tiles = bp.seg_tiles;
+        a.chains = (int)chains;
+        a.s_states = split ? static_cast<const float *>(workspace) : nullptr;
+        a.s_sub = pl.sub;
+        a.s_nsub = pl.nsub;
+        a.s_final = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + s_bytes);
+        a.r_states = bp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
+        a.r_sub = bp.sub;
+        a.r_nsub = bp.nsub;
+        return la2::launch_bwd1_bf16(a, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+    }
     // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T, so
     // it reads the forward's S states ([d, d_v] per segment) transposed
     if (split && !reuse_s &&
@@ -676,7 +743,7 @@ int la2_backward_saved(const void *q, const void *k, const void *v, const float 
                        void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block,
                        int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return backward_impl(q, k, v, decay, dout, dq, dk, dv, B, H, T, d, d_v, block, dtype, workspace, workspace_bytes,
-                         stream, true);
+                         stream, true, nullptr, nullptr, nullptr, true);
 }
 
 int la2_backward_state(const void *q, const void *k, const void *v, const float *decay, const float *state_in,

@@ -130,4 +130,26 @@ struct DkdvArgs {
 bool dkdv_supported(int D, int DV);
 hipError_t launch_dkdv_bf16(const DkdvArgs &a, int D, hipStream_t s);
 
+// The whole backward without decay in one reverse walk (la2_bwd1_bf16.hip): dq, dk and dv of each
+// (chain, segment) over kBwd1Tile-position tiles, d = d_v = 128, bf16.  The forward state is carried
+// backwards from the state after the segment (the next segment's start state, or the chain's final
+// state for the last segment), the reverse state forwards from the state at the segment's end.
+constexpr int kBwd1Tile = 64;
+struct Bwd1Args {
+    const void *q, *k, *v, *dout;
+    void *dq, *dk, *dv;
+    int64_t T;
+    int nseg;
+    int seg_tiles;         // tiles of kBwd1Tile positions per segment
+    int chains;
+    const float *s_states; // fp32 [chains, s_nsub, D, D]: forward segment start states (segment p starts
+    int s_sub;             //   from entry p * s_sub), or nullptr when not split
+    int s_nsub;
+    const float *s_final;  // fp32 [chains, D, D]: each chain's state after its last position
+    const float *r_states; // fp32 [chains, r_nsub, D, D]: reverse states at the segments' ends, or nullptr
+    int r_sub;
+    int r_nsub;
+};
+hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s);
+
 }  // namespace la2

@@ -92,7 +92,11 @@ enum la2_status {
  *   workspace: device scratch of at least la2_workspace_bytes(..., 0) bytes,
  *   used for the per-segment states when a chain is split across workgroups.
  *   On completion those bytes hold the state each segment starts from, which
- *   la2_backward_saved can reuse. */
+ *   la2_backward_saved can reuse.  Without decay, with dtype LA2_BF16 and
+ *   d = d_v = 128, a workspace of at least la2_workspace_bytes(..., 1) bytes
+ *   also receives each chain's final state (fp32 [B, H, d, d_v], right after
+ *   the segment states), from which la2_backward_saved walks the sequence
+ *   backwards in one pass. */
 int la2_forward(const void *q, const void *k, const void *v, const float *decay, void *o,
                 int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
@@ -233,15 +237,21 @@ int la2_backward(const void *q, const void *k, const void *v, const float *decay
                  int64_t d_v, int block, int dtype, void *workspace, size_t workspace_bytes,
                  void *stream);
 
-/* Backward that reuses the segment start states of a preceding la2_forward (the
- * usual training step: forward, then backward on the same q, k, v), instead of
- * recomputing them from k and v.  Same arguments and results as la2_backward,
+/* Backward that reuses the states of a preceding la2_forward (the usual training
+ * step: forward, then backward on the same q, k, v), instead of recomputing them
+ * from k and v.  Same arguments and results as la2_backward (up to rounding),
  * with one more precondition: `workspace` is the pointer that the la2_forward
- * call on the same q, k, v, decay, sizes, block and dtype received, and its
- * first la2_workspace_bytes(..., 0) bytes are unchanged since that call (this
- * call leaves them unchanged too, so it may be repeated).  The library cannot
- * check this; with other contents dQ is wrong for chains split into segments.
- * When no chain is split (la2_workspace_bytes(..., 0) == 0) it is la2_backward. */
+ * call on the same q, k, v, decay, sizes, block and dtype received, with
+ * workspace_bytes of at least la2_workspace_bytes(..., 1) in both calls, and
+ * the states that forward left there are unchanged since (this call leaves
+ * them unchanged too, so it may be repeated).  The library cannot check this;
+ * with other contents the gradients are wrong.
+ * Without decay, with dtype LA2_BF16 and d = d_v = 128 it starts from each
+ * chain's final state and walks the sequence once in reverse: the state before
+ * a tile is the state after it minus that tile's k^T v (exact arithmetic of the
+ * undecayed recurrence), so dq, dk and dv come from one read of q, k, v and
+ * dout.  Otherwise it runs la2_backward's passes, with the forward's segment
+ * start states in place of their recomputation. */
 int la2_backward_saved(const void *q, const void *k, const void *v, const float *decay,
                        const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
                        int64_t T, int64_t d, int64_t d_v, int block, int dtype, void *workspace,

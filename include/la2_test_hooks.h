@@ -25,9 +25,11 @@ extern "C" {
  *   slice_width:   64 runs 128-wide bf16 values as two 64-wide slices
  *   separate_dkdv: non-zero computes dk and dv by two separate reverse scans
  *   norm_segment:  positions per segment of the normalized form's denominator scans
+ *   two_pass_backward: non-zero runs la2_backward_saved without decay (bf16, d = d_v = 128) as a dQ
+ *                  pass and a dK/dV pass instead of the one-pass backward
  * Returns LA2_OK. */
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv,
-                      int64_t norm_segment);
+                      int64_t norm_segment, int two_pass_backward);
 
 #ifdef __cplusplus
 }

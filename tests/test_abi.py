@@ -115,8 +115,12 @@ def test_workspace(lib):
     assert fwd(lib, T=1024, ws=P + 8 * MB, wsb=n - 1) == WS
     assert bwd(lib, T=1024, ws=None, wsb=0) == WS
     assert fwd(lib, T=1024, ws=P + MB, wsb=n) == ALIAS   # workspace on top of k
-    # enough chains to fill the GPU: no split, no workspace
-    assert la2.la2_workspace_bytes(16, 16, 4096, 128, 128, 128, torch.bfloat16, True) == 0
+    # enough chains to fill the GPU: no split, no segment states; the backward's workspace then holds only
+    # each chain's final state where the one-pass backward applies (bf16, d = d_v = 128)
+    assert la2.la2_workspace_bytes(16, 16, 4096, 128, 128, 128, torch.bfloat16, False) == 0
+    assert la2.la2_workspace_bytes(16, 16, 4096, 128, 128, 128, torch.bfloat16, True) == 256 * 128 * 128 * 4
+    assert la2.la2_workspace_bytes(16, 16, 4096, 64, 64, 64, torch.bfloat16, True) == 0
+    assert la2.la2_workspace_bytes(16, 16, 4096, 128, 128, 64, torch.float32, True) == 0
     assert lib.la2_workspace_bytes(1, 1, 64, 96, 64, 64, 1, 0) == ctypes.c_size_t(-1).value
 
 
