@@ -16,13 +16,17 @@
 // amplifies every rounding; decayed chains keep the two-pass backward.)  Reading each input once for
 // all three gradients moves 7 tensors per token instead of the 10 of a dQ pass plus a dK/dV pass.
 //
-// Workgroup of four waves (one per SIMD), 64-position tiles (two 32-row blocks).  Wave w = 2rb + ch
-// produces columns 64ch..64ch+63 of dV and dK for row block rb and of dQ for row block 1 - rb (the
-// causal block counts of those units differ, so that every wave has about the same work), and
-// updates eight of the 32 state blocks: waves 0 and 1 half of R each, waves 2 and 3 half of S.  LDS
-// holds the four input tiles, R^T and S^T in bf16 (MFMA operands of the inter-tile products) and
-// 8 KiB of output staging per wave: 160 KiB.  The next tile's inputs are loaded into registers once
-// the state updates are done and written to LDS at the end of the tile.
+// Workgroup of eight waves, two per SIMD, 64-position tiles (two 32-row blocks), in two roles:
+//   consumers (waves 0-3, c = 2rb + ch): columns 64ch..64ch+63 of dV, dK and dQ for row block rb
+//     (row block 0 has two source blocks for dV and dK and one for dQ, row block 1 the reverse);
+//   producers (waves 4-7, p = 4 + 2j + ch): the state blocks with rows kb in {2ch, 2ch + 1} (all four
+//     column blocks) of R (j = 0) or S (j = 1) and their bf16 copies in LDS.
+// Each SIMD runs one wave of each role, so the state updates and state copies overlap the gradient
+// products instead of following them.  Every wave loads an eighth of the next tile into registers
+// early in the tile and writes it to LDS once the tile's inputs are consumed.  LDS holds the four input tiles, R^T and S^T in
+// bf16 (MFMA operands of the inter-tile products) and 8 KiB of output staging per consumer: 160 KiB.
+// Per tile, three workgroup barriers: Y (S^T of the state before the tile is complete, dV and dK are
+// done with R^T), Z (every input of the tile is consumed) and X (the next tile and R^T are in LDS).
 #include "la2_bf16_common.h"
 
 namespace la2 {
@@ -32,17 +36,17 @@ using namespace dev;
 
 constexpr int D1 = 128;              // d = d_v
 constexpr int TB1 = 64;              // positions per tile
-constexpr int kW1 = 4;               // waves
+constexpr int kW1 = 8;               // waves: 4 consumers, then 4 producers
 constexpr int kT1 = 64 * kW1;        // threads
 constexpr int kTile1 = TB1 * D1;     // bf16 elements of one input tile
 constexpr int KS1 = D1 / 16;         // contraction steps over d
 constexpr int oQ1 = 0, oK1 = kTile1, oV1 = 2 * kTile1, oO1 = 3 * kTile1;   // q, k, v, dO tiles
 constexpr int oRT1 = 4 * kTile1;                                           // R^T [d_v][d] bf16
 constexpr int oST1 = oRT1 + D1 * D1;                                       // S^T [d_v][d] bf16
-constexpr int oOS1 = oST1 + D1 * D1;                                       // per-wave output staging
+constexpr int oOS1 = oST1 + D1 * D1;                                       // per-consumer output staging
 constexpr int kOS1 = 2 * 32 * 64;                                          //   (two units of 32 x 64)
-constexpr int kLds1 = oOS1 + kW1 * kOS1;
-constexpr int NCH1 = kTile1 / 8 / kT1;   // 16-byte chunks per thread and tile (4)
+constexpr int kLds1 = oOS1 + 4 * kOS1;
+constexpr int NCH1 = kTile1 / 8 / kT1;   // 16-byte chunks per thread and tile (2)
 static_assert(kLds1 * 2 <= 160 * 1024, "LDS");
 
 
@@ -78,25 +82,19 @@ __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid
     }
 }
 
-// bf16x8 with every element negated (sign bits flipped: exact).
-__device__ __forceinline__ bf16x8 neg8(const bf16x8 &f) {
-    u32x4 u = __builtin_bit_cast(u32x4, f);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) u[m] ^= 0x80008000u;
-    return __builtin_bit_cast(bf16x8, u);
-}
-
 // Per-lane LDS offsets (bf16 elements), computed once so that every LDS access in the tile loop is a
 // per-lane register plus a compile-time or per-block offset.  Tiles are [rows][128] with 16-byte
 // chunks XOR-swizzled by row (nat_off); the swizzle depends only on row % 16, so within a lane it is
 // the same for every row block, and the chunk index splits into bits the block offset cannot carry.
 struct LaneOff {
-    int pl[8];          // row col, chunk 2m + h (plain fragment reads and state writes; + 128 row0)
+    int pl[8];          // row col, chunk 2m + h (plain fragment reads; + 128 row0)
     int trn[4][2];      // transposed reads without permutation at k0 = 0 of column block nb (+ 128 k0),
                         // first and second 8-byte piece
     int trc[2][2][2];   // [PERM][n][piece] the same for this wave's column blocks 2ch + n
-    int pw[2][2];       // row col, chunk 4(2ch + i) + 2jp + h: where this wave's state
-                        // block rows kb = 2ch + i land in a transposed state
+    int pw[2][4];       // row col, chunk 4(2ch + i) + g, 8-byte half h: where accumulator entries
+                        // 4g..4g+3 of this wave's state blocks with rows kb = 2ch + i land in a
+                        // transposed state
+    int po[2][4];       // the same in a 64-column output staging row (chunk 4n + g)
 };
 
 __device__ __forceinline__ int tr_off(int lane, int perm, int half, int nb) {
@@ -125,7 +123,10 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane, int ch) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) L.pw[i][jp] = nat_off<D1>(col, 4 * (2 * ch + i) + 2 * jp + h);
+        for (int g = 0; g < 4; ++g) {
+            L.pw[i][g] = nat_off<D1>(col, 4 * (2 * ch + i) + g) + 4 * h;
+            L.po[i][g] = col * 64 + (((4 * i + g) ^ ((col >> 1) & 7)) << 3) + 4 * h;
+        }
     return L;
 }
 
@@ -142,14 +143,66 @@ __device__ __forceinline__ bf16x8 rd_tr(const u16 *s, int k0, const int (&off)[2
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// bf16x8 with every sign bit xor-ed with `sign` (0x80008000: every element negated, exactly; 0: as is).
+__device__ __forceinline__ bf16x8 flip8(const bf16x8 &f, unsigned int sign) {
+    u32x4 u = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) u[m] ^= sign;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ void lds_write8(u16 *s, int off, const u32x2 &v) {
+    *reinterpret_cast<u32x2 *>(s + off) = v;
+}
+
+// P of one 32 x 32 score block as the B operand of the value products.  Accumulator r of lane
+// (h, col) holds source row 8(r/4) + 4h + r%4 against output row col; pairs (2p, 2p + 1) are rounded
+// to bf16 together.  In the diagonal block the entries on the wrong side of the causal mask are
+// zeroed first (sources at or after the output row are kept for dV and dK, at or before for dQ).
+template <Unit U, bool DIAG>
+__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col) {
+    u32x4 w[2];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        float a = acc[2 * p], b = acc[2 * p + 1];
+        if (DIAG) {
+            const int dist = 4 * h - col + 8 * (p >> 1) + 2 * (p & 1);   // source - output of entry 2p
+            a = (U == Unit::DQ ? dist <= 0 : dist >= 0) ? a : 0.0f;
+            b = (U == Unit::DQ ? dist + 1 <= 0 : dist + 1 >= 0) ? b : 0.0f;
+        }
+        w[p >> 2][p & 3] = pack_bf16(a, b);
+    }
+    pf[0] = __builtin_bit_cast(bf16x8, w[0]);
+    pf[1] = __builtin_bit_cast(bf16x8, w[1]);
+}
+
+// The intra-tile contribution of source block u to a unit: scores of the block's 32 source rows
+// against the unit's 32 output rows (B operand bf), then P times the value rows of the block.
+template <Unit U, bool DIAG>
+__device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf)[KS1], const u16 *sA,
+                                            const u16 *sC, int u, const LaneOff &L, int h, int col) {
+    const f32x16 zero = {};
+    f32x16 acc = mfma(rd_plain(sA, u * 32, 0, L), bf[0], zero);
+#pragma unroll
+    for (int ks = 1; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
+    bf16x8 pf[2];
+    block_p<U, DIAG>(acc, pf, h, col);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) oacc[n] = mfma(rd_tr(sC, u * 32 + 16 * x, L.trc[1][n]), pf[x], oacc[n]);
+}
+
 // One output unit of a wave: columns 64ch..64ch+63 (two 32-column blocks) of the output rows in
 // block `orow`, as O^T accumulators (lane col holds output row orow*32 + col).
 //   DV: rows s of dV; scores Q[t] . K[s] for t >= s; value dO; inter R^T K^T
 //   DK: rows s of dK; scores dO[t] . V[s] for t >= s; value Q; inter R V^T
 //   DQ: rows t of dQ; scores V[s] . dO[t] for s <= t; value K; inter S dO^T
+// The inter product always runs (a state that is still zero contributes zeros), so the first
+// contraction step starts from a zero accumulator operand instead of cleared registers.
 template <Unit U>
 __device__ __forceinline__ void out_unit(f32x16 (&oacc)[2], const u16 *smem, int orow, int ch, int lane,
-                                         const LaneOff &L, bool inter) {
+                                         const LaneOff &L) {
     const int h = lane >> 5, col = lane & 31;
     const u16 *sB = smem + (U == Unit::DV ? oK1 : U == Unit::DK ? oV1 : oO1);   // output-row role
     const u16 *sA = smem + (U == Unit::DV ? oQ1 : U == Unit::DK ? oO1 : oV1);   // source-row role
@@ -158,215 +211,203 @@ __device__ __forceinline__ void out_unit(f32x16 (&oacc)[2], const u16 *smem, int
     bf16x8 bf[KS1];
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks) bf[ks] = rd_plain(sB, orow * 32, ks, L);
+    // fully unrolled: bf[] must be indexed by constants (a runtime index into a register array is
+    // lowered to chains of selects)
+    const f32x16 zero = {};
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int ks = 0; ks < KS1; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0f;
-    if (inter) {
-        // fully unrolled: bf[] must be indexed by constants (a runtime index into a register array is
-        // lowered to chains of selects)
-#pragma unroll
-        for (int ks = 0; ks < KS1; ++ks)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int cb = 2 * ch + n;
-                // DV: R^T rows (d_v) from plain reads; DK, DQ: R or S rows (d) through transpose reads
-                const bf16x8 a = U == Unit::DV ? rd_plain(sSt, cb * 32, ks, L) : rd_tr(sSt, 16 * ks, L.trc[0][n]);
-                oacc[n] = mfma(a, bf[ks], oacc[n]);
-            }
-    }
-    // intra-tile: source blocks u (u >= orow for DV, DK; u <= orow for DQ)
-    const int ulo = U == Unit::DQ ? 0 : orow;
-    const int uhi = U == Unit::DQ ? orow : TB1 / 32 - 1;
-    for (int u = ulo; u <= uhi; ++u) {
-        asm volatile("" ::: "memory");
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
-        // accumulator r holds source row u*32 + 8(r/4) + 4h + r%4 for output row orow*32 + col; only the
-        // diagonal block (u == orow) has entries on the wrong side of the causal mask
-        bf16x8 pf[2];
-        if (u == orow) {
-            const int base = 4 * h - col;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dist = base + 8 * (r >> 2) + (r & 3);   // source - output
-                const bool keep = U == Unit::DQ ? dist <= 0 : dist >= 0;
-                pf[r >> 3][r & 7] = (__bf16)(keep ? acc[r] : 0.0f);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)acc[r];
+        for (int n = 0; n < 2; ++n) {
+            // DV: R^T rows (d_v) from plain reads; DK, DQ: R or S rows (d) through transpose reads
+            const bf16x8 a = U == Unit::DV ? rd_plain(sSt, (2 * ch + n) * 32, ks, L) : rd_tr(sSt, 16 * ks, L.trc[0][n]);
+            oacc[n] = mfma(a, bf[ks], ks == 0 ? zero : oacc[n]);
         }
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) oacc[n] = mfma(rd_tr(sC, u * 32 + 16 * x, L.trc[1][n]), pf[x], oacc[n]);
-    }
+    // intra-tile: the whole source block below (dQ) or above (dV, dK) the diagonal, where there is one,
+    // then the diagonal block
+    if (U == Unit::DQ ? orow == 1 : orow == 0)
+        intra_block<U, false>(oacc, bf, sA, sC, U == Unit::DQ ? 0 : 1, L, h, col);
+    intra_block<U, true>(oacc, bf, sA, sC, orow, L, h, col);
 }
 
-// One wave's part of the walk over the tiles of one (chain, segment).  Wave w = 2rb + ch: units as in
-// the header; state blocks: waves 0, 1 the R blocks with kb in {2ch, 2ch + 1}, waves 2, 3 the S blocks
-// with kb in {2ch, 2ch + 1} (eight blocks each, all four nb).
-__device__ __forceinline__ void bwd1_wave(const Bwd1Args &p, u16 *smem, int chain, int seg, int wave, int lane0) {
-    const int rb = wave >> 1, ch = wave & 1;
-    const bool s_kind = wave >= 2;   // this wave's state blocks are S (else R)
-    const int kb0 = 2 * ch;
-    const int tid = threadIdx.x;
-    int h = lane0 >> 5, col = lane0 & 31;
-    const int64_t T = p.T;
-    const int64_t NT = (T + TB1 - 1) / TB1;
-    const int64_t tile_lo = (int64_t)seg * p.seg_tiles;
-    const int64_t tile_hi = min(tile_lo + p.seg_tiles, NT);
-    const int ntiles = (int)(tile_hi - tile_lo);
+// The tiles of one (chain, segment), walked from the last to the first.
+struct Walk1 {
+    int64_t T, tile_hi, base;
+    int ntiles;
+    __device__ int64_t t0(int it) const { return (tile_hi - 1 - it) * TB1; }
+};
 
-    const LaneOff L = lane_offsets(lane0, ch);
-    const int64_t base = (int64_t)chain * T * D1;
-    const u16 *gq = static_cast<const u16 *>(p.q) + base, *gk = static_cast<const u16 *>(p.k) + base;
-    const u16 *gv = static_cast<const u16 *>(p.v) + base, *go = static_cast<const u16 *>(p.dout) + base;
-    u16 *gdq = static_cast<u16 *>(p.dq) + base, *gdk = static_cast<u16 *>(p.dk) + base,
-        *gdv = static_cast<u16 *>(p.dv) + base;
+__device__ __forceinline__ Walk1 walk_of(const Bwd1Args &p, int chain, int seg) {
+    Walk1 w;
+    w.T = p.T;
+    const int64_t NT = (p.T + TB1 - 1) / TB1, tile_lo = (int64_t)seg * p.seg_tiles;
+    w.tile_hi = min(tile_lo + p.seg_tiles, NT);
+    w.ntiles = (int)(w.tile_hi - tile_lo);
+    w.base = (int64_t)chain * p.T * D1;
+    return w;
+}
+
+// Producer wave: state blocks with rows kb in {2ch, 2ch + 1} of R (SK = false) or S (SK = true).
+// R_b = R_{b+1} + Q_b^T dO_b is formed at the top of tile b but published as R^T only after barrier
+// Y (dV and dK of tile b use R_{b+1}); S_{b-1} = S_b - K_b^T V_b is published before Y for dQ.
+template <bool SK>
+__device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain, int seg, int ch, int lane) {
+    const Walk1 w = walk_of(p, chain, seg);
+    const int kb0 = 2 * ch, tid = threadIdx.x;
+    const int h = lane >> 5, col = lane & 31;
+    const unsigned int sign = SK ? 0x80008000u : 0u;   // S is updated with -K
+    const LaneOff L = lane_offsets(lane, ch);
+    const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
+    const u16 *gv = static_cast<const u16 *>(p.v) + w.base, *go = static_cast<const u16 *>(p.dout) + w.base;
     // R at the segment's end (0 for the last segment), S after the segment's last position
-    const float *gR = seg < p.nseg - 1
-                          ? p.r_states + ((int64_t)chain * p.r_nsub + state_index(seg, p.r_sub, p.r_nsub, true)) * D1 * D1
-                          : nullptr;
-    const float *gS = seg < p.nseg - 1 ? p.s_states + ((int64_t)chain * p.s_nsub + (seg + 1) * p.s_sub) * D1 * D1
-                                       : p.s_final + (int64_t)chain * D1 * D1;
+    const float *g = nullptr;
+    if (SK)
+        g = seg < p.nseg - 1 ? p.s_states + ((int64_t)chain * p.s_nsub + (seg + 1) * p.s_sub) * D1 * D1
+                             : p.s_final + (int64_t)chain * D1 * D1;
+    else if (seg < p.nseg - 1)
+        g = p.r_states + ((int64_t)chain * p.r_nsub + state_index(seg, p.r_sub, p.r_nsub, true)) * D1 * D1;
 
     f32x16 sacc[8];
-    {
-        const float *g = s_kind ? gS : gR;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int kb = kb0 + s / 4, nb = s % 4;
+    for (int s = 0; s < 8; ++s) {
+        const int kb = kb0 + s / 4, nb = s % 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
         }
     }
-    // this wave's blocks as R^T or S^T (bf16, [d_v][d]) into LDS
+    // the blocks as R^T or S^T (bf16, [d_v][d]) into LDS: accumulator entries 4g..4g+3 of a lane are
+    // four consecutive d of one d_v row, one 8-byte write
     auto write_state = [&]() {
-        u16 *dst = smem + (s_kind ? oST1 : oRT1);
+        u16 *dst = smem + (SK ? oST1 : oRT1);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int nb = s % 4;
+        for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int jp = 0; jp < 2; ++jp) {
-                u32x2 a, c;
-                a[0] = pack_bf16(sacc[s][8 * jp + 0], sacc[s][8 * jp + 1]);
-                a[1] = pack_bf16(sacc[s][8 * jp + 2], sacc[s][8 * jp + 3]);
-                c[0] = pack_bf16(sacc[s][8 * jp + 4], sacc[s][8 * jp + 5]);
-                c[1] = pack_bf16(sacc[s][8 * jp + 6], sacc[s][8 * jp + 7]);
-                lds_write(dst, nb * 32 * D1 + L.pw[s / 4][jp], join_halves(a, c));
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 v = {pack_bf16(sacc[s][4 * q], sacc[s][4 * q + 1]),
+                                 pack_bf16(sacc[s][4 * q + 2], sacc[s][4 * q + 3])};
+                lds_write8(dst, (s % 4) * 32 * D1 + L.pw[s / 4][q], v);
             }
-        }
     };
 
-    auto tile_of = [&](int it) -> int64_t { return tile_hi - 1 - it; };
     Staged1 st;
-    load_tile1(st, gq, gk, gv, go, tile_of(0) * TB1, T, tid);
+    load_tile1(st, gq, gk, gv, go, w.t0(0), w.T, tid);
     store_tile1(st, smem, tid);
-    if (!s_kind) write_state();
-    lds_barrier();
-    bool r_nonzero = gR != nullptr;
+    if (!SK) write_state();
+    lds_barrier();   // X: the first tile and R^T
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t t0 = tile_of(it) * TB1;
-        const bool more = it + 1 < ntiles;
-        const int lane = lane0;
-
-        // state updates of this wave's blocks: R += Q^T dO (the old R^T stays in LDS for this tile), or
-        // S -= K^T V (the state before this tile) followed by S^T in bf16 for dQ; each operand
-        // fragment is read once per 16 positions and shared by the blocks that use it
+    for (int it = 0; it < w.ntiles; ++it) {
+        const bool more = it + 1 < w.ntiles;
+        // R += Q^T dO, or S -= K^T V; each operand fragment is read once per 16 positions and shared
+        // by the blocks that use it
         {
-            const u16 *sA = smem + (s_kind ? oK1 : oQ1), *sC = smem + (s_kind ? oV1 : oO1);
-#pragma unroll 1
+            const u16 *sA = smem + (SK ? oK1 : oQ1), *sC = smem + (SK ? oV1 : oO1);
+#pragma unroll
             for (int x = 0; x < TB1 / 16; ++x) {
                 bf16x8 fa[2], fc[4];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    // this wave's state row blocks kb0 + i are its column blocks 2ch + i
-                    fa[i] = rd_tr(sA, 16 * x, L.trc[0][i]);
-                    if (s_kind) fa[i] = neg8(fa[i]);
-                }
+                for (int i = 0; i < 2; ++i)   // state row blocks kb0 + i are column blocks 2ch + i of the tile
+                    fa[i] = flip8(rd_tr(sA, 16 * x, L.trc[0][i]), sign);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) fc[i] = rd_tr(sC, 16 * x, L.trn[i]);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) sacc[s] = mfma(fa[s / 4], fc[s % 4], sacc[s]);
             }
         }
-        if (s_kind) write_state();
-        // the next tile's inputs: in flight while this tile's three gradients are formed
-        if (more) load_tile1(st, gq, gk, gv, go, tile_of(it + 1) * TB1, T, tid);
-
-        // Each unit is staged in this wave's own 8 KiB of LDS and stored as whole 128-byte row pieces
-        // as soon as it is done, so that at most one unit's accumulators are held at a time.
-        u16 *ob = smem + oOS1 + wave * kOS1;
-        auto stage = [&](const f32x16 (&acc)[2], u16 *dst) {
-            // 16 lanes writing one chunk of 16 consecutive rows (or reading whole rows) hit 16 bank groups
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int jp = 0; jp < 2; ++jp) {
-                    u32x2 a, c;
-                    a[0] = pack_bf16(acc[n][8 * jp + 0], acc[n][8 * jp + 1]);
-                    a[1] = pack_bf16(acc[n][8 * jp + 2], acc[n][8 * jp + 3]);
-                    c[0] = pack_bf16(acc[n][8 * jp + 4], acc[n][8 * jp + 5]);
-                    c[1] = pack_bf16(acc[n][8 * jp + 6], acc[n][8 * jp + 7]);
-                    const int chk = 4 * n + 2 * jp + h;
-                    lds_write(dst, col * 64 + ((chk ^ ((col >> 1) & 7)) << 3), join_halves(a, c));
-                }
-        };
-        auto store = [&](const u16 *src, u16 *g, int orow) {
-            const __amdgpu_buffer_rsrc_t ry = make_rsrc(g + t0 * D1, (T - t0) * D1 * 2);
-            u32x4 v[4];
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
-                v[s2] = *reinterpret_cast<const u32x4 *>(src + row * 64 + ((chk ^ ((row >> 1) & 7)) << 3));
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
-                bstore16(ry, ((orow * 32 + row) * D1 + ch * 64 + chk * 8) * 2, v[s2]);
-            }
-        };
-        {
-            f32x16 oacc[2];
-            out_unit<Unit::DV>(oacc, smem, rb, ch, lane, L, r_nonzero);
-            stage(oacc, ob);
-            out_unit<Unit::DK>(oacc, smem, rb, ch, lane, L, r_nonzero);
-            stage(oacc, ob + 2048);
-            store(ob, gdv, rb);
-            store(ob + 2048, gdk, rb);
-        }
-        lds_barrier();   // S^T of the state before this tile is complete
-        {
-            f32x16 oacc[2];
-            out_unit<Unit::DQ>(oacc, smem, 1 - rb, ch, lane, L, true);
-            stage(oacc, ob);
-            store(ob, gdq, 1 - rb);
-        }
-        lds_barrier();   // every wave is done with this tile's inputs, R^T and S^T
-        if (!s_kind) write_state();
-        r_nonzero = true;
+        if (SK) write_state();
+        // this wave's part of the next tile: in flight while the consumers form this tile's gradients
+        if (more) load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+        lds_barrier();   // Y
+        if (!SK) write_state();
+        lds_barrier();   // Z
         if (more) store_tile1(st, smem, tid);
-        lds_barrier();
+        lds_barrier();   // X
+    }
+}
+
+// Consumer wave c = 2rb + ch.  Each unit is staged in the wave's own 8 KiB of LDS and stored as whole
+// 128-byte row pieces, so that at most one unit's accumulators are held at a time.
+__device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
+    const Walk1 w = walk_of(p, chain, seg);
+    const int rb = c >> 1, ch = c & 1, tid = threadIdx.x;
+    const LaneOff L = lane_offsets(lane, ch);
+    const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
+    const u16 *gv = static_cast<const u16 *>(p.v) + w.base, *go = static_cast<const u16 *>(p.dout) + w.base;
+    u16 *gdq = static_cast<u16 *>(p.dq) + w.base, *gdk = static_cast<u16 *>(p.dk) + w.base,
+        *gdv = static_cast<u16 *>(p.dv) + w.base;
+    u16 *ob = smem + oOS1 + c * kOS1;
+    // [32 rows][64 columns] with 16-byte chunks XOR-swizzled by row pair; a lane's accumulator entries
+    // 4g..4g+3 are four consecutive columns of its row, one 8-byte write
+    auto stage = [&](const f32x16 (&acc)[2], u16 *dst) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 v = {pack_bf16(acc[n][4 * q], acc[n][4 * q + 1]),
+                                 pack_bf16(acc[n][4 * q + 2], acc[n][4 * q + 3])};
+                lds_write8(dst, L.po[n][q], v);
+            }
+    };
+    auto store = [&](const u16 *src, u16 *g, int64_t t0) {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(g + t0 * D1, (w.T - t0) * D1 * 2);
+        u32x4 v[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
+            v[s2] = *reinterpret_cast<const u32x4 *>(src + row * 64 + ((chk ^ ((row >> 1) & 7)) << 3));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
+            bstore16(ry, ((rb * 32 + row) * D1 + ch * 64 + chk * 8) * 2, v[s2]);
+        }
+    };
+
+    Staged1 st;
+    load_tile1(st, gq, gk, gv, go, w.t0(0), w.T, tid);
+    store_tile1(st, smem, tid);
+    lds_barrier();   // X: the first tile and R^T
+    for (int it = 0; it < w.ntiles; ++it) {
+        const int64_t t0 = w.t0(it);
+        const bool more = it + 1 < w.ntiles;
+        // this wave's part of the next tile
+        if (more) load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+        {
+            f32x16 oacc[2];
+            out_unit<Unit::DV>(oacc, smem, rb, ch, lane, L);
+            stage(oacc, ob);
+            out_unit<Unit::DK>(oacc, smem, rb, ch, lane, L);
+            stage(oacc, ob + 2048);
+            store(ob, gdv, t0);
+            store(ob + 2048, gdk, t0);
+        }
+        lds_barrier();   // Y: S^T of the state before this tile is complete
+        {
+            f32x16 oacc[2];
+            out_unit<Unit::DQ>(oacc, smem, rb, ch, lane, L);
+            stage(oacc, ob);
+        }
+        lds_barrier();   // Z
+        if (more) store_tile1(st, smem, tid);
+        store(ob, gdq, t0);
+        lds_barrier();   // X
     }
 }
 
 __global__ __launch_bounds__(kT1, 1) void bwd1_bf16_kernel(Bwd1Args p) {
     __shared__ __attribute__((aligned(16))) u16 smem[kLds1];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index as a scalar: every branch on a wave's role is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int seg = blockIdx.x % p.nseg;
     const int chain = blockIdx.x / p.nseg;
     const int64_t NT = (p.T + TB1 - 1) / TB1;
     if ((int64_t)seg * p.seg_tiles >= NT) return;
-    bwd1_wave(p, smem, chain, seg, wave, lane);
+    if (wave < 4)
+        consumer(p, smem, chain, seg, wave, lane);
+    else if (wave < 6)
+        producer<false>(p, smem, chain, seg, wave & 1, lane);
+    else
+        producer<true>(p, smem, chain, seg, wave & 1, lane);
 }
 
 }  // namespace
