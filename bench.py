@@ -33,9 +33,13 @@ METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roo
 # device copy (FETCH_SIZE x 1.9999, WRITE_SIZE x 1.0000).  Each figure is valid only for the kernel
 # source it was taken on (sha256 of the listed files, concatenated); for any other source the roofline
 # reports traffic as null.
+# At the 1K point: the backward reads q, k, v, dO and the final states (2176.4 MiB) and writes dq, dk, dv
+# (1536.2 MiB); the forward reads q, k, v (1536.4 MiB) and writes o and the final states (640.0 MiB).
 TRAFFIC = {
-    "bwd1": {"sources": ("la2_bwd1_bf16.hip", "la2_bf16_common.h"), "sha256_16": None, "bytes": None},
-    "fwd": {"sources": ("la2_scan_bf16.hip", "la2_bf16_common.h"), "sha256_16": None, "bytes": None},
+    "bwd1": {"sources": ("la2_bwd1_bf16.hip", "la2_bf16_common.h"), "sha256_16": "c4bae2b3ec7c4c5d",
+             "bytes": 3892959028},
+    "fwd": {"sources": ("la2_scan_bf16.hip", "la2_bf16_common.h"), "sha256_16": "e57aa0bdbebc71dc",
+            "bytes": 2282085142},
 }
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0

@@ -35,7 +35,8 @@
  * and 64 and 128-position tiles for 128 and 256 (a 256 tile's Q, K and V
  * alone would fill the 160 KiB of LDS at d = 128); fp32 scans run 16, 32 or
  * 64 positions (64 for 128 and 256).  The bf16 backward with d = d_v computes
- * dK and dV in one fused reverse pass over 64-position tiles.
+ * dK and dV in one fused reverse pass over 64-position tiles; without decay at
+ * d = d_v = 128, la2_backward_saved computes dQ, dK and dV in one reverse pass.
  *
  * Ownership.  The caller allocates and frees every buffer, including the
  * workspace (la2_workspace_bytes tells its size; it may be 0, in which case
