@@ -515,6 +515,10 @@ struct NormLayout {
     size_t den_off, dden_off, dn_off;
     size_t z_off, z_bytes, y_off;
     size_t scan_off, scan_bytes;
+    // bf16 backward only (dq from the centered feature map, la2_norm.hip mode 7): the per-segment
+    // sums of phi(k) for its mean m, phi(k) - m, the scan U of (dout, v, phi(k) - m) and that scan's
+    // segment states, a_t = dout_t . (prefix sum of v)_t and the segment sums of v
+    size_t m_off, kap_off, u_off, a_off, vz_off, us_off, us_bytes;
     size_t total;
     DenPlan dp;
 };
@@ -536,6 +540,17 @@ NormLayout norm_layout(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, i
     L.dn_off = L.dden_off + (backward ? rows_f32 : 0);
     L.y_off = L.dn_off + (backward ? align256((size_t)(chains * T * dv) * elem_size(dtype)) : 0);
     L.total = L.y_off + (backward ? L.z_bytes : 0);
+    if (backward && dtype == LA2_BF16) {
+        const size_t tile_bytes = align256((size_t)(chains * T * d) * elem_size(dtype));
+        L.m_off = L.total;
+        L.kap_off = L.m_off + align256((size_t)chains * L.dp.nseg * d * sizeof(float));
+        L.u_off = L.kap_off + tile_bytes;
+        L.a_off = L.u_off + tile_bytes;
+        L.vz_off = L.a_off + rows_f32;
+        L.us_off = L.vz_off + (L.dp.nseg > 1 ? align256((size_t)chains * L.dp.nseg * dv * sizeof(float)) : 0);
+        L.us_bytes = align256(make_plan(B, H, T, d, dv, block, dtype).ws_bytes);
+        L.total = L.us_off + L.us_bytes;
+    }
     return L;
 }
 
@@ -558,7 +573,7 @@ la2::DenArgs den_args(const void *q, const void *k, const float *decay, char *ws
 }
 
 // Scan modes of launch_vscan (la2_norm.hip).
-constexpr int kVZSeg = 0, kVDen = 1, kVDQ = 2, kVYSeg = 3, kVDK = 4;
+constexpr int kVZSeg = 0, kVDen = 1, kVDQ = 2, kVYSeg = 3, kVDK = 4, kVMean = 5, kVKappa = 6, kVDQN = 7;
 
 }  // namespace
 
@@ -618,9 +633,10 @@ namespace {
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream, bool reuse_s, const float *state_in = nullptr,
-                  const float *dstate_out = nullptr, float *dstate_in = nullptr, bool one_pass = false) {
+                  const float *dstate_out = nullptr, float *dstate_in = nullptr, bool one_pass = false,
+                  bool skip_dq = false) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA2_ERR_NULL_POINTER;
+    if (!q || !k || !v || !dout || (!dq && !skip_dq) || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
     if (st != LA2_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
@@ -637,8 +653,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     const Range ins[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv), range_of(dout, nv),
                           range_of(decay, decay ? (size_t)H * 4 : 0), range_of(state_in, state_in ? ns : 0),
                           range_of(dstate_out, dstate_out ? ns : 0)};
-    const Range outs[5] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv), range_of(workspace, ws_need),
-                           range_of(dstate_in, dstate_in ? ns : 0)};
+    const Range outs[5] = {range_of(dq, skip_dq ? 0 : nq), range_of(dk, nq), range_of(dv, nv),
+                           range_of(workspace, ws_need), range_of(dstate_in, dstate_in ? ns : 0)};
     for (int i = 0; i < 5; ++i) {
         for (int j = 0; j < 7; ++j)
             if (overlap(outs[i], ins[j])) return LA2_ERR_ALIAS;
@@ -652,7 +668,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     st = LA2_OK;
     const bool split = pl.nseg > 1;
     void *ws_r = workspace ? static_cast<char *>(workspace) + s_bytes + f_bytes : nullptr;
-    if (one_pass && reuse_s && !decay && !state_in && !dstate_out && !dstate_in && bwd1_shape(d, d_v, dtype)) {
+    if (one_pass && !skip_dq && reuse_s && !decay && !state_in && !dstate_out && !dstate_in &&
+        bwd1_shape(d, d_v, dtype)) {
         // Training step without decay: dq, dk and dv in one reverse walk from the forward's segment start
         // states and final states (left in the workspace), and the reverse states at the segment ends.
         const Plan bp = bwd1_plan(pl, chains, T, d, d_v);
@@ -682,13 +699,15 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     }
     // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T, so
     // it reads the forward's S states ([d, d_v] per segment) transposed
-    if (split && !reuse_s &&
-        (st = segment_states(k, v, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Forward, workspace, s,
-                             state_in)) != LA2_OK)
-        return st;
-    if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 1,
-                          s, state_in)) != LA2_OK)
-        return st;
+    if (!skip_dq) {
+        if (split && !reuse_s &&
+            (st = segment_states(k, v, decay, chains, H, T, D, DV, pl, dtype, la2::Dir::Forward, workspace, s,
+                                 state_in)) != LA2_OK)
+            return st;
+        if ((st = output_scan(dout, v, k, dq, decay, chains, H, T, DV, D, pl, dtype, la2::Dir::Forward, workspace, 1,
+                              s, state_in)) != LA2_OK)
+            return st;
+    }
     if (fused) {
         // dk_t = R_t v_t and dv_t = R_t^T k_t in one reverse pass, R_t = lam R_{t+1} + q_t do_t^T
         const Plan fp = make_plan(B, H, T, d, d_v, block, dtype, true);
@@ -801,16 +820,52 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
     // 2. dn = do / den, dden = -(do . o) / den
     if (la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)
         return LA2_ERR_HIP;
+    const bool centered = dtype == LA2_BF16;
+    if (centered) {
+        // bf16: dq of the centered feature map (la2_norm.hip, mode 7), every step in fp32 except the scan U
+        // of (dout, v, phi(k) - m), whose values are small against the result
+        la2::DenArgs c = a;
+        c.msum = reinterpret_cast<float *>(ws + L.m_off);
+        c.kap = ws + L.kap_off;
+        if (la2::launch_vscan(c, (int)d, dtype, feature_map, kVMean, s) != hipSuccess ||
+            la2::launch_vscan(c, (int)d, dtype, feature_map, kVKappa, s) != hipSuccess)
+            return LA2_ERR_HIP;
+        // a_t = dout_t . Vbar_t: the denominator scan with (query, key) = (dout, v) and the identity map
+        la2::DenArgs va = c;
+        va.q = dout;
+        va.k = v;
+        va.pq = va.pk = nullptr;
+        va.den = reinterpret_cast<float *>(ws + L.a_off);
+        va.zseg = L.dp.nseg > 1 ? reinterpret_cast<float *>(ws + L.vz_off) : nullptr;
+        if ((va.nseg > 1 && la2::launch_vscan(va, (int)d_v, dtype, 0, kVZSeg, s) != hipSuccess) ||
+            la2::launch_vscan(va, (int)d_v, dtype, 0, kVDen, s) != hipSuccess)
+            return LA2_ERR_HIP;
+        // U = the forward scan with (query, key, value) = (dout, v, phi(k) - m), as the dQ pass of the
+        // plain backward: its state is (sum kap v^T)^T
+        const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+        void *uws = L.us_bytes ? ws + L.us_off : nullptr;
+        if (pl.nseg > 1 && (st = segment_states(c.kap, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype,
+                                                la2::Dir::Forward, uws, s)) != LA2_OK)
+            return st;
+        if ((st = output_scan(dout, v, c.kap, ws + L.u_off, decay, chains, H, T, (int)d_v, (int)d, pl, dtype,
+                              la2::Dir::Forward, uws, 1, s)) != LA2_OK)
+            return st;
+        c.u = ws + L.u_off;
+        c.arow = va.den;
+        c.g = dq;
+        if (la2::launch_vscan(c, (int)d, dtype, feature_map, kVDQN, s) != hipSuccess) return LA2_ERR_HIP;
+    }
     // 3. the numerator's gradients: the plain backward on (phi(q), phi(k), v) with output gradient dn;
-    //    dv is final, dq and dk hold the gradients with respect to phi(q), phi(k) so far
-    st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, dq, dk, dv, B, H, T, d, d_v, block, dtype,
-                       L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, saved);
+    //    dv is final, dq (fp32 only) and dk hold the gradients with respect to phi(q), phi(k) so far
+    st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, centered ? nullptr : dq, dk, dv, B, H, T,
+                       d, d_v, block, dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, saved,
+                       nullptr, nullptr, nullptr, false, centered);
     if (st != LA2_OK) return st;
-    // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place),
-    //    dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative
+    // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place; fp32
+    //    only), dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative
     a.dden = dden;
     a.g = dq;
-    if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDQ, s) != hipSuccess) return LA2_ERR_HIP;
+    if (!centered && la2::launch_vscan(a, (int)d, dtype, feature_map, kVDQ, s) != hipSuccess) return LA2_ERR_HIP;
     a.g = dk;
     a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.y_off) : nullptr;   // the forward's z sums stay
     if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVYSeg, s) != hipSuccess) return LA2_ERR_HIP;

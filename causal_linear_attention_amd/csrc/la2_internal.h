@@ -89,6 +89,11 @@ struct DenArgs {
     void *g;               // [chains, T, D]: dq (mode 2) or dk (mode 4), updated in place
     const float *decay;    // [H] or nullptr (lam = 1)
     float *zseg;           // fp32 [chains, nseg, D]: per-segment sums
+    float *msum;           // fp32 [chains, nseg, D]: plain (undecayed) per-segment sums of phi(k) (mode 5 out,
+                           // modes 6 and 7 in: the chain's mean m of phi(k))
+    void *kap;             // [chains, T, D]: phi(k) - m (mode 6 out)
+    const void *u;         // [chains, T, D]: the scan of (dout, v, phi(k) - m) (mode 7 in)
+    const float *arow;     // fp32 [chains, T]: dout_t . (decayed prefix sum of v)_t (mode 7 in)
     int64_t T;
     int64_t seg_len;       // positions per segment, a multiple of 64
     int H;

@@ -82,19 +82,36 @@ __device__ __forceinline__ float phi_deriv(float x) {
 }
 
 // Modes of the d-vector scan.  Forward ones run the decayed prefix sum z_t = lam z_{t-1} + x_t of
-// x_t = phi(k_t); reverse ones the suffix sum y_t = lam y_{t+1} + x_t of x_t = dden_t phi(q_t).
+// x_t = phi(k_t) (mode 7: of phi(k_t) - m); reverse ones the suffix sum y_t = lam y_{t+1} + x_t of
+// x_t = dden_t phi(q_t).
 enum : int {
     kZSeg = 0,   // forward: each segment's own sum (z at its last position from zero), segments 0..nseg-2
     kDen = 1,    // forward: den_t = phi(q_t) . z_t (and phi(q), phi(k) where asked for)
     kDQ = 2,     // forward: dq_t = (dq_t + dden_t z_t) (.) phi'(q_t), in place
     kYSeg = 3,   // reverse: each segment's own sum referred to its first position, segments 1..nseg-1
-    kDK = 4      // reverse: dk_t = (dk_t + y_t) (.) phi'(k_t), in place
+    kDK = 4,     // reverse: dk_t = (dk_t + y_t) (.) phi'(k_t), in place
+    kMean = 5,   // plain sum of phi(k) over each segment (no decay), every segment
+    kKappa = 6,  // kap_t = phi(k_t) - m, m = the chain's mean of phi(k)
+    kDQN = 7     // forward: dq of the normalized form from u, arow, den and z of phi(k) - m (below)
 };
+
+// Mode 7.  With phi(k_s) = m + kap_s (m the chain's mean of phi(k), a constant vector), the gradient
+// with respect to phi(q_t) of <o, do>, (S_t do_t - (do_t . o_t) z_t) / den_t, is rewritten so that
+// no two large terms cancel in bf16:
+//   a_t = do_t . Vbar_t (Vbar the decayed prefix sum of v),  U_t = sum_{s<=t} lam^(t-s) kap_s (v_s . do_t),
+//   zk_t = the decayed prefix sum of kap,  ell_t = sum_{s<=t} lam^(t-s),  sigma_t = phi(q_t) . m,
+//   S_t do_t = m a_t + U_t,   z_t = ell_t m + zk_t,   den_t = sigma_t ell_t + phi(q_t) . zk_t,
+//   c_t = do_t . o_t = (sigma_t a_t + phi(q_t) . U_t) / den_t,
+//   G_t = a_t - c_t ell_t = ((phi(q_t) . zk_t) a_t - ell_t (phi(q_t) . U_t)) / den_t,
+//   d phi(q_t) = (U_t - c_t zk_t + G_t m) / den_t.
+// U comes from the bf16 tile scan of (do, v, kap) (kap is small, so its bf16 rounding and that of the
+// scan's products are small against the result), a_t from the mode-1 scan of (do, v); every other
+// quantity here is fp32.
 
 template <typename E, int D, int FMAP, int MODE>
 __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
     constexpr bool REV = MODE == kYSeg || MODE == kDK;
-    constexpr bool SUMS = MODE == kZSeg || MODE == kYSeg;
+    constexpr bool SUMS = MODE == kZSeg || MODE == kYSeg || MODE == kMean;
     constexpr int CPR = D / 8;                  // threads per row (8 dims each)
     constexpr int G = kThreadsN / CPR;          // position groups
     constexpr int PPG = kChunkN / G;            // positions per group per chunk
@@ -103,10 +120,10 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
     __shared__ float zc[2][D];
 
     const int tid = threadIdx.x, c8 = tid % CPR, g = tid / CPR;
-    const int nseg_here = SUMS ? p.nseg - 1 : p.nseg;
+    const int nseg_here = SUMS && MODE != kMean ? p.nseg - 1 : p.nseg;
     const int chain = blockIdx.x / nseg_here;
     const int seg = blockIdx.x % nseg_here + (MODE == kYSeg ? 1 : 0);
-    const float l2 = p.decay ? log2f(p.decay[chain % p.H]) : 0.0f;
+    const float l2 = p.decay && MODE != kMean ? log2f(p.decay[chain % p.H]) : 0.0f;
     const float lam = exp2f(l2);
     const float lamG = exp2f((float)PPG * l2);
     const int64_t s0 = (int64_t)seg * p.seg_len;
@@ -126,12 +143,24 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
     const bool keep_phi = MODE == kDen && FMAP != 0 && p.pq != nullptr;
     E *pqc = keep_phi ? static_cast<E *>(p.pq) + row0 * D + c8 * 8 : nullptr;
     E *pkc = keep_phi ? static_cast<E *>(p.pk) + row0 * D + c8 * 8 : nullptr;
-    E *gc = (MODE == kDQ || MODE == kDK) ? static_cast<E *>(p.g) + row0 * D + c8 * 8 : nullptr;
+    E *gc = (MODE == kDQ || MODE == kDK || MODE == kDQN) ? static_cast<E *>(p.g) + row0 * D + c8 * 8 : nullptr;
     const float *ddc = (MODE == kDQ || REV) ? p.dden + row0 : nullptr;
+    E *kapc = MODE == kKappa ? static_cast<E *>(p.kap) + row0 * D + c8 * 8 : nullptr;
+    const E *uc = MODE == kDQN ? static_cast<const E *>(p.u) + row0 * D + c8 * 8 : nullptr;
+    // modes 6 and 7: this thread's 8 dims of the chain's mean of phi(k)
+    float mloc[8] = {};
+    if constexpr (MODE == kKappa || MODE == kDQN) {
+        const float *ms = p.msum + (int64_t)chain * p.nseg * D + c8 * 8;
+        for (int j = 0; j < p.nseg; ++j)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) mloc[m] += ms[(int64_t)j * D + m];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) mloc[m] /= (float)p.T;
+    }
 
     // what is carried into the segment: Horner over the other segments' sums in walk order,
     // z <- lam^seg_len z + sum_j
-    if (tid < D) {
+    if (tid < D && MODE != kKappa) {
         float z = 0.0f;
         if constexpr (!SUMS) {
             const float lamS = exp2f((float)p.seg_len * l2);
@@ -140,6 +169,18 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                 for (int j = p.nseg - 1; j > seg; --j) z = fmaf(z, lamS, zs[(int64_t)j * D]);
             } else {
                 for (int j = 0; j < seg; ++j) z = fmaf(z, lamS, zs[(int64_t)j * D]);
+            }
+        }
+        if constexpr (MODE == kDQN) {
+            // the sums are of phi(k): take off m times the decayed count of the s0 positions before
+            if (s0 > 0) {
+                const float *ms = p.msum + (int64_t)chain * p.nseg * D + tid;
+                float m = 0.0f;
+                for (int j = 0; j < p.nseg; ++j) m += ms[(int64_t)j * D];
+                m /= (float)p.T;
+                const double lam_d = (double)lam;
+                const double cnt = l2 == 0.0f ? (double)s0 : (1.0 - pow(lam_d, (double)s0)) / (1.0 - lam_d);
+                z = (float)((double)z - (double)m * cnt);
             }
         }
         zc[0][tid] = z;
@@ -164,6 +205,11 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                     load8(kc + t * D, xx[i]);
 #pragma unroll
                     for (int m = 0; m < 8; ++m) xx[i][m] = phi<FMAP>(xx[i][m]);
+                    if constexpr (MODE == kKappa || MODE == kDQN) {
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) xx[i][m] -= mloc[m];
+                        if constexpr (MODE == kKappa) store8(kapc + t * D, xx[i]);
+                    }
                     if constexpr (MODE == kDen) {
                         load8(qc + t * D, qq[i]);
 #pragma unroll
@@ -182,6 +228,7 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                 }
             }
         }
+        if constexpr (MODE == kKappa) continue;   // elementwise only
         // this run's decayed sum, the running sum at its last step when starting from zero
         float loc[8];
 #pragma unroll
@@ -216,6 +263,42 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
 #pragma unroll
                     for (int w = 1; w < CPR; w <<= 1) pd += __shfl_xor(pd, w, CPR);
                     if (real(r) && c8 == 0) p.den[row0 + pos(r)] = pd;
+                } else if constexpr (MODE == kDQN) {
+                    // z is the decayed prefix sum of phi(k) - m through this position
+                    const bool ok = real(r);
+                    const int64_t t = ok ? pos(r) : 0;
+                    float ur[8] = {}, qr[8] = {}, pq[8];
+                    if (ok) {
+                        load8(uc + t * D, ur);
+                        load8(qc + t * D, qr);
+                    }
+                    float sg = 0.0f, pu = 0.0f, pz = 0.0f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        pq[m] = phi<FMAP>(qr[m]);
+                        sg = fmaf(pq[m], mloc[m], sg);
+                        pu = fmaf(pq[m], ur[m], pu);
+                        pz = fmaf(pq[m], z[m], pz);
+                    }
+#pragma unroll
+                    for (int w = 1; w < CPR; w <<= 1) {
+                        sg += __shfl_xor(sg, w, CPR);
+                        pu += __shfl_xor(pu, w, CPR);
+                        pz += __shfl_xor(pz, w, CPR);
+                    }
+                    if (ok) {
+                        const float dn = p.den[row0 + t], av = p.arow[row0 + t];
+                        const double lam_d = (double)lam;
+                        const float ell = l2 == 0.0f ? (float)(t + 1)
+                                                     : (float)((1.0 - pow(lam_d, (double)(t + 1))) / (1.0 - lam_d));
+                        const float rd = 1.0f / dn;
+                        const float c = (sg * av + pu) * rd, G = (pz * av - ell * pu) * rd;
+                        float gr[8];
+#pragma unroll
+                        for (int m = 0; m < 8; ++m)
+                            gr[m] = (ur[m] - c * z[m] + G * mloc[m]) * rd * phi_deriv<FMAP>(qr[m]);
+                        store8(gc + t * D, gr);
+                    }
                 } else if (real(r)) {
                     const int64_t t = pos(r);
                     float gr[8], xr[8];
@@ -236,7 +319,7 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
         buf ^= 1;
     }
     if constexpr (SUMS) {
-        if (tid < D) p.zseg[((int64_t)chain * p.nseg + seg) * D + tid] = zc[buf][tid];
+        if (tid < D) (MODE == kMean ? p.msum : p.zseg)[((int64_t)chain * p.nseg + seg) * D + tid] = zc[buf][tid];
     }
 }
 
@@ -275,6 +358,9 @@ hipError_t launch_vs(const DenArgs &a, int mode, hipStream_t s) {
     const bool sums = mode == kZSeg || mode == kYSeg;
     const unsigned grid = (unsigned)a.chains * (unsigned)(sums ? a.nseg - 1 : a.nseg);
     switch (mode) {
+        case kMean: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kMean>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kKappa: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kKappa>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kDQN: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQN>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
         case kZSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kZSeg>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
         case kDen: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDen>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
         case kDQ: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQ>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
@@ -294,7 +380,7 @@ hipError_t launch_vs_e(const DenArgs &a, int D, int mode, hipStream_t s) {
 hipError_t launch_vscan(const DenArgs &a, int D, int dtype, int fmap, int mode, hipStream_t s) {
     const bool sums = mode == kZSeg || mode == kYSeg;
     if (!(D == 64 || D == 128) || a.chains <= 0 || a.nseg < (sums ? 2 : 1) || a.seg_len % kChunkN != 0 ||
-        (fmap != 0 && fmap != 1) || mode < kZSeg || mode > kDK)
+        (fmap != 0 && fmap != 1) || mode < kZSeg || mode > kDQN)
         return hipErrorInvalidValue;
     if (dtype == 1)
         return fmap ? launch_vs_e<__bf16, 1>(a, D, mode, s) : launch_vs_e<__bf16, 0>(a, D, mode, s);

@@ -186,7 +186,12 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
  *     d pq_t = S_t dn_t + dden_t z_t,
  *     d pk_t = R_t v_t + sum_{s >= t} lam^(s-t) dden_s pq_s,   dv_t = R_t^T pk_t,
  *     dq = d pq (.) phi'(q),   dk = d pk (.) phi'(k),
- * R the reverse state of the numerator with output gradient dn.
+ * R the reverse state of the numerator with output gradient dn.  The two
+ * terms of d pq largely cancel, so with dtype LA2_BF16 dq is formed from
+ * phi(k) = m + kap (m the chain's mean of phi(k)): the bf16 tile scan runs over
+ * the small kap, and the parts that cancel (built from m, the prefix sums of v
+ * and kap and the exact do_t . o_t) are combined in fp32; equal to the formula
+ * above in exact arithmetic.
  *   o: the output la2_forward_normalized returned for these inputs (read).
  *   The denominator and phi(q), phi(k) are recomputed; the numerator's part
  *   runs through the same passes as la2_backward.  Other arguments as in

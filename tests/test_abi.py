@@ -212,8 +212,13 @@ def test_forward_normalized_validation(lib):
     assert big >= la2.la2_workspace_bytes(1, 2, 1 << 16, 128, 128, 128, torch.bfloat16, False) + 2 * 128 * 4
     assert lib.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, 3, 64, 1, 0) == ctypes.c_size_t(-1).value
     assert lib.la2_normalized_workspace_bytes(1, 1, 64, 96, 64, 1, 64, 1, 0) == ctypes.c_size_t(-1).value
-    # the backward adds dden (fp32 per position) and dn (one output-sized gradient)
-    assert la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.bfloat16, True) == n + 256 + 64 * 64 * 2
+    # the backward adds dden (fp32 per position) and dn (one output-sized gradient); in bf16 also the
+    # segment sums of phi(k) for its mean, phi(k) - m and the scan U (two q-sized tensors) and a_t (fp32
+    # per position)
+    assert la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.float32, True) == (
+        la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.float32) + 256 + 64 * 64 * 4)
+    assert la2.la2_normalized_workspace_bytes(1, 1, 64, 64, 64, "elu1", 64, torch.bfloat16, True) == (
+        n + 256 + 64 * 64 * 2 + 256 + 2 * 64 * 64 * 2 + 256)
 
 
 def ser(lib, q=P, k=P + MB, v=P + 2 * MB, decay=None, o=P + 3 * MB, B=1, H=1, T=64, d=64, dv=64, dtype=1):

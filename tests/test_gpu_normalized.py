@@ -109,14 +109,12 @@ def test_normalized_full_size_whole():
 # ---- backward ----------------------------------------------------------------------------------
 #
 # The bar is the one of every case: max|gpu - ref| <= 2e-2 x max|ref| (bf16), 1e-5 x max|ref| (fp32),
-# per gradient.  dv meets it.  dq and dk of the bf16 path do not everywhere: they are d pq = S dn +
-# dden z and d pk = R v + y (times phi'), and for the gradient of a ratio the two terms largely cancel
-# (the exact dq of a one-position sequence is 0 while each term is O(1); on random inputs the
-# numerator term is 7-10x dq).  Each term carries bf16 roundings of its own size (phi(k) ~ 1 + x is
-# stored in bf16, which keeps x to 2-3 bits at x ~ 0.1; the scores P, dn and the state S are MFMA
-# operands in bf16; o itself is the forward's bf16 output), so the error is a few per cent of dq.
-# Where a bf16 dq or dk misses the bar the case is reported as an expected failure with its
-# measured error (a result above 0.15 fails outright: that is a broken kernel, not rounding).
+# per gradient.  dq and dk are d pq = S dn + dden z and d pk = R v + y (times phi'), and for the
+# gradient of a ratio the two terms largely cancel (the exact dq of a one-position sequence is 0
+# while each term is O(1); on random inputs the numerator term is 6-20x dq).  The bf16 dq is
+# therefore computed from phi(k) = m + kap with m the chain's mean of phi(k) (la2_norm.hip, mode 7):
+# only the scan over the small kap runs on bf16 MFMA operands, and the terms that cancel are formed
+# in fp32.  dk's terms cancel by about 2x and keep the plain path.
 
 
 def check_grads(case, got, ref, terms=None):
@@ -140,11 +138,8 @@ def check_grads(case, got, ref, terms=None):
     if dtype == "f32":
         assert max(errs) <= tol, errs
         return
-    assert errs[2] <= tol, ("dv", errs[2])
-    assert max(errs[:2]) <= 0.15, errs
-    if max(errs[:2]) > tol:
-        pytest.xfail(f"bf16 normalized backward above the 2e-2 bar: dq {errs[0]:.2e}, dk {errs[1]:.2e} of max|ref| "
-                     "(cancelling terms carry bf16 roundings)")
+    for name, e in zip(("dq", "dk", "dv"), errs):
+        assert e <= tol, (name, e)
 
 
 def numerator_terms(x, fmap):
