@@ -77,6 +77,9 @@ def parse():
                     help="sequence lengths in K for --compare")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device-to-device copies (reference for HBM byte counters)")
+    ap.add_argument("--stream", action="store_true",
+                    help="time the test build's plain HBM stream (16-byte lane accesses, 1 GiB per buffer) at the "
+                         "read:write mixes of the tile kernels, over launch shapes and both cache policies")
     args = ap.parse_args()
     single = args.workload is not None
     if args.steps is None:
@@ -95,6 +98,49 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * src.element_size(), "copies": 5}))
+
+
+def stream_bench(args):
+    """The bandwidth a plain stream reaches on this GPU for the kernels' read:write mixes: a copy (1:1),
+    the forward output scan (3 tensors read, 1 written) and the one-pass backward (4 read, 3 written).
+    Each dst = the sum of the srcs, 1 GiB per buffer, grid-stride over 16-byte chunks; the best of a
+    sweep of launch shapes, with and without the nontemporal hint.  A ceiling for the tile kernels'
+    GB/s that includes what HBM, the fabric and the memory pipeline of this chip deliver to 16-byte
+    lane accesses, which the 8 TB/s peak does not."""
+    import torch
+    from causal_linear_attention_amd import binding
+
+    nbytes = 1 << 30
+    bufs = [torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(7)]
+    mixes = {"copy 1:1": (1, 1), "forward 3:1": (3, 1), "backward 4:3": (4, 3)}
+    shapes = [(b, t) for b in (256, 512, 1024, 2048, 4096, 8192) for t in (256, 512)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    results, rows = {}, []
+    for name, (ns, nd) in mixes.items():
+        srcs, dsts = bufs[:ns], bufs[ns:ns + nd]
+        best = None
+        for nt in (1, 0):
+            for b, t in shapes:
+                for _ in range(2):
+                    binding.stream_probe(srcs, dsts, b, t, nt)
+                torch.cuda.synchronize()
+                reps = 5
+                ev[0].record()
+                for _ in range(reps):
+                    binding.stream_probe(srcs, dsts, b, t, nt)
+                ev[1].record()
+                torch.cuda.synchronize()
+                ms = ev[0].elapsed_time(ev[1]) / reps
+                gbs = (ns + nd) * nbytes / (ms * 1e-3) / 1e9
+                rows.append({"mix": name, "nontemporal": bool(nt), "blocks": b, "threads": t,
+                             "ms": round(ms, 4), "GBs": round(gbs, 1)})
+                if best is None or gbs > best["GBs"]:
+                    best = rows[-1]
+        results[name] = best
+        print(f"[stream] {name}: best {best['GBs']} GB/s ({best['blocks']} x {best['threads']}, "
+              f"nontemporal {best['nontemporal']})", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "plain HBM stream, best launch shape per read:write mix", "unit": "GB/s",
+                      "bytes_per_buffer": nbytes, "peak": PEAK_HBM_GBS, "best": results, "all": rows}), flush=True)
 
 
 def decode_bench(args):
@@ -453,6 +499,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stream:
+        stream_bench(args)
         return
     if args.decode:
         decode_bench(args)

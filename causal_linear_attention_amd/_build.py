@@ -3,9 +3,10 @@
 Every source is compiled by hipcc for gfx950 only; objects go to ``_build/``
 (not committed) and are linked into one shared library with a plain C ABI
 (``include/la2.h``).  A second library, ``lib/libla2_testhooks.so``, links the
-same kernel objects with the C ABI compiled under ``LA2_TEST_HOOKS``: it also
-exports ``la2_test_set_plan`` (``include/la2_test_hooks.h``), through which
-the tests force work decompositions.  Nothing but the tests loads it.
+same kernel objects with the C ABI compiled under ``LA2_TEST_HOOKS`` and a plain
+HBM stream kernel: it also exports ``la2_test_set_plan``, through which the tests
+force work decompositions, and ``la2_test_stream``, which ``bench.py --stream``
+times (``include/la2_test_hooks.h``).  Nothing else loads it.
 """
 import concurrent.futures
 import os
@@ -56,7 +57,8 @@ def build_library(verbose=False, extra=()):
     """Compile every source and link ``libla2.so`` and ``libla2_testhooks.so``; returns the release path."""
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    jobs = [(s, tuple(extra), "") for s in SOURCES] + [("la2_api.cpp", tuple(extra) + ("-DLA2_TEST_HOOKS",), ".hooks")]
+    jobs = ([(s, tuple(extra), "") for s in SOURCES] +
+            [("la2_api.cpp", tuple(extra) + ("-DLA2_TEST_HOOKS",), ".hooks"), ("la2_stream.hip", tuple(extra), "")])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         results = list(ex.map(lambda j: _compile(*j), jobs))
     if verbose:
@@ -66,7 +68,8 @@ def build_library(verbose=False, extra=()):
     objs = [o for o, _ in results[:len(SOURCES)]]
     _link(objs, LIB)
     api = objs.index(os.path.join(OBJDIR, "la2_api.cpp.o"))
-    _link(objs[:api] + [results[-1][0]] + objs[api + 1:], TEST_LIB)
+    # the test build: the API with the plan overrides, and the measurement stream
+    _link(objs[:api] + [results[-2][0]] + objs[api + 1:] + [results[-1][0]], TEST_LIB)
     return LIB
 
 

@@ -92,20 +92,47 @@ def load_library(path=LIB_PATH):
 _test_lib = None
 
 
-@contextlib.contextmanager
-def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0,
-                  two_pass_backward=False):
-    """Run the wrappers on the test build of the library with forced plan choices (see
-    include/la2_test_hooks.h; 0 / False = automatic).  For tests: the forced plans cover code paths
-    that small shapes would not reach.  Not thread-safe."""
-    global _lib, _test_lib
+def _load_test_library():
+    global _test_lib
     load_library()
     if _test_lib is None:
         lib = load_library(TEST_LIB_PATH)
         lib.la2_test_set_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                                           ctypes.c_int]
         lib.la2_test_set_plan.restype = ctypes.c_int
+        lib.la2_test_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                        ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+        lib.la2_test_stream.restype = ctypes.c_int
         _test_lib = lib
+    return _test_lib
+
+
+def stream_probe(srcs, dsts, blocks, threads, nontemporal, stream=None):
+    """Enqueue the test build's plain HBM stream (include/la2_test_hooks.h): every dst = the sum of the
+    srcs (same-sized, contiguous CUDA tensors), 16-byte lane accesses; for measuring the bandwidth the
+    tile kernels' read:write mixes can reach."""
+    lib = _load_test_library()
+    nbytes = srcs[0].numel() * srcs[0].element_size()
+    for t in list(srcs) + list(dsts):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()) or t.numel() * t.element_size() != nbytes:
+            raise ValueError("stream_probe takes contiguous CUDA tensors of one size")
+    sp = (ctypes.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
+    dp = (ctypes.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
+    st = lib.la2_test_stream(sp, len(srcs), dp, len(dsts), nbytes, int(blocks), int(threads), int(bool(nontemporal)),
+                             _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_test_stream")
+
+
+@contextlib.contextmanager
+def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0,
+                  two_pass_backward=False):
+    """Run the wrappers on the test build of the library with forced plan choices (see
+    include/la2_test_hooks.h; 0 / False = automatic).  For tests: the forced plans cover code paths
+    that small shapes would not reach.  Not thread-safe."""
+    global _lib
+    _load_test_library()
     _test_lib.la2_test_set_plan(int(seg_tiles), int(state_sub), int(slice_width), int(bool(separate_dkdv)),
                                 int(norm_segment), int(bool(two_pass_backward)))
     _lib = _test_lib

@@ -1,14 +1,16 @@
 /*
- * la2_test_hooks.h -- plan overrides of the test build of the library.
+ * la2_test_hooks.h -- plan overrides and a measurement stream of the test build
+ * of the library.
  *
- * Only lib/libla2_testhooks.so (the same sources compiled with LA2_TEST_HOOKS)
- * exports this function; the release library lib/libla2.so does not, and its
- * launch plan depends on the call's arguments alone.  The tests use it to
+ * Only lib/libla2_testhooks.so (the same sources compiled with LA2_TEST_HOOKS,
+ * plus la2_stream.hip) exports these functions; the release library
+ * lib/libla2.so does not, and its launch plan depends on the call's arguments
+ * alone.  The tests use it to
  * force work decompositions that the automatic plan would not pick for small
  * shapes, so that those code paths are checked against the oracle.
  *
- * It sets process-wide state read by every later call of that library: not
- * thread-safe, and meant for single-threaded test processes only.
+ * la2_test_set_plan sets process-wide state read by every later call of that
+ * library: not thread-safe, and meant for single-threaded test processes only.
  */
 #ifndef LA2_TEST_HOOKS_H
 #define LA2_TEST_HOOKS_H
@@ -30,6 +32,17 @@ extern "C" {
  * Returns LA2_OK. */
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv,
                       int64_t norm_segment, int two_pass_backward);
+
+/* A plain HBM stream, for measuring what the tile kernels' read:write mixes can reach:
+ * dst_j = src_0 + ... + src_{nsrc-1} (u32 lanes) over `bytes` bytes of each device buffer, read and
+ * written as 16-byte lane accesses by a grid-stride loop of `blocks` workgroups of `threads`
+ * threads, with the nontemporal cache hint when `nontemporal` is non-zero; enqueued on `stream`.
+ *   src: nsrc (1-4) device pointers; dst: ndst (1-3) device pointers; all 16-byte aligned,
+ *   bytes a multiple of 16; threads a multiple of 64 in [64, 1024].
+ * Returns LA2_OK, LA2_ERR_BAD_SHAPE, LA2_ERR_NULL_POINTER (a NULL or misaligned pointer) or
+ * LA2_ERR_HIP. */
+int la2_test_stream(const void *const *src, int nsrc, void *const *dst, int ndst, size_t bytes,
+                    int blocks, int threads, int nontemporal, void *stream);
 
 #ifdef __cplusplus
 }

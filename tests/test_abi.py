@@ -347,7 +347,7 @@ def test_high_level_api_rejects_decay_outside_unit_interval(bad):
 def test_release_library_has_no_plan_overrides(lib):
     """Test knobs live only in the test build: the release library exports no override and reads no
     environment variable, so its plan depends on the arguments alone."""
-    assert not hasattr(lib, "la2_test_set_plan")
+    assert not hasattr(lib, "la2_test_set_plan") and not hasattr(lib, "la2_test_stream")
     import subprocess
     syms = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     assert "getenv" not in syms
@@ -367,6 +367,19 @@ def test_test_build_forces_plans():
     with binding.plan_override(seg_tiles=4, state_sub=2):
         assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 256 * 16 * 128 * 128 * 4
     assert la2.la2_workspace_bytes(64, 4, 4096, 128, 128, 128, torch.bfloat16, False) == 0   # restored
+
+
+def test_stream_probe_validates_before_launch():
+    """The test build's measurement stream refuses bad arguments before anything is enqueued."""
+    tl = binding._load_test_library()
+    src = (ctypes.c_void_p * 1)(0x100000)
+    dst = (ctypes.c_void_p * 1)(0x200000)
+    assert tl.la2_test_stream(src, 0, dst, 1, 1 << 20, 256, 256, 1, None) == SHAPE       # no source
+    assert tl.la2_test_stream(src, 1, dst, 4, 1 << 20, 256, 256, 1, None) == SHAPE       # too many outputs
+    assert tl.la2_test_stream(src, 1, dst, 1, (1 << 20) + 8, 256, 256, 1, None) == SHAPE
+    assert tl.la2_test_stream(src, 1, dst, 1, 1 << 20, 256, 96, 1, None)  == SHAPE       # not whole waves
+    bad = (ctypes.c_void_p * 1)(0x100008)
+    assert tl.la2_test_stream(bad, 1, dst, 1, 1 << 20, 256, 256, 1, None) == NULLP          # misaligned
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch():
