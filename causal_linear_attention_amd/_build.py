@@ -23,7 +23,7 @@ LIB = os.path.join(LIBDIR, "libla2.so")
 TEST_LIB = os.path.join(LIBDIR, "libla2_testhooks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["la2_scan_bf16.hip", "la2_bwd1_bf16.hip", "la2_state_bf16.hip", "la2_dkdv_bf16.hip", "la2_scan_f32.hip", "la2_prefix.hip", "la2_decode.hip", "la2_norm.hip",
+SOURCES = ["la2_scan_bf16.hip", "la2_fwd1_bf16.hip", "la2_bwd1_bf16.hip", "la2_state_bf16.hip", "la2_dkdv_bf16.hip", "la2_scan_f32.hip", "la2_prefix.hip", "la2_decode.hip", "la2_norm.hip",
            "la2_serial.hip", "la2_api.cpp"]
 
 FLAGS = [

@@ -29,6 +29,7 @@ struct PlanOverride {
     int separate_dkdv;      // != 0: the two separate reverse scans instead of the fused dk/dv pass
     int64_t norm_segment;   // > 0: positions per segment of the denominator scans
     int two_pass_backward;  // != 0: la2_backward_saved without decay by the dQ pass and the dK/dV pass
+    int legacy_forward;     // != 0: forward-direction bf16 output passes on the 8-wave scan kernel only
 };
 
 #ifdef LA2_TEST_HOOKS
@@ -223,6 +224,25 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
                   hipStream_t s) {
     const int DV = slice_width(dtype, args.DVT, pl.narrow);
     if (dtype == LA2_BF16 && mode == la2::Mode::StateOnly) return la2::launch_state_bf16(args, D, DV, pl.TB, dir, s);
+    if (dtype == LA2_BF16 && mode == la2::Mode::Output && dir == la2::Dir::Forward && !forced().legacy_forward &&
+        D == 128 && DV == 128 && args.nslice == 1 && !args.decay && !args.den && !args.has_init) {
+        // without decay at d = d_v = 128: the producer/consumer scan over 64-position tiles
+        la2::Fwd1Args f{};
+        f.q = args.a;
+        f.k = args.b;
+        f.v = args.c;
+        f.y = args.y;
+        f.T = args.T;
+        f.seg_len = (int64_t)args.seg_tiles * pl.TB;
+        f.nseg = args.nseg;
+        f.chains = args.chains;
+        f.states = args.nseg > 1 ? args.states : nullptr;
+        f.states_t = args.states_t;
+        f.sub = args.sub;
+        f.nsub = args.nsub;
+        f.state_out = args.state_out;
+        return la2::launch_fwd1_bf16(f, s);
+    }
     return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, s)
                              : la2::launch_scan_f32(args, D, DV, pl.TB, dir, mode, s);
 }
@@ -281,8 +301,9 @@ int la2_abi_version(void) { return LA2_ABI_VERSION; }
 
 #ifdef LA2_TEST_HOOKS
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment,
-                      int two_pass_backward) {
-    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment, two_pass_backward};
+                      int two_pass_backward, int legacy_forward) {
+    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment, two_pass_backward,
+                              legacy_forward};
     return LA2_OK;
 }
 #endif

@@ -27,19 +27,16 @@
 // bf16 (MFMA operands of the inter-tile products) and 8 KiB of output staging per consumer: 160 KiB.
 // Per tile, three workgroup barriers: Y (S^T of the state before the tile is complete, dV and dK are
 // done with R^T), Z (every input of the tile is consumed) and X (the next tile and R^T are in LDS).
-#include "la2_bf16_common.h"
+#include "la2_tile64_bf16.h"
 
 namespace la2 {
 namespace {
 
 using namespace dev;
+using namespace t64;
 
-constexpr int D1 = 128;              // d = d_v
-constexpr int TB1 = 64;              // positions per tile
 constexpr int kW1 = 8;               // waves: 4 consumers, then 4 producers
 constexpr int kT1 = 64 * kW1;        // threads
-constexpr int kTile1 = TB1 * D1;     // bf16 elements of one input tile
-constexpr int KS1 = D1 / 16;         // contraction steps over d
 constexpr int oQ1 = 0, oK1 = kTile1, oV1 = 2 * kTile1, oO1 = 3 * kTile1;   // q, k, v, dO tiles
 constexpr int oRT1 = 4 * kTile1;                                           // R^T [d_v][d] bf16
 constexpr int oST1 = oRT1 + D1 * D1;                                       // S^T [d_v][d] bf16
@@ -82,151 +79,18 @@ __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid
     }
 }
 
-// Per-lane LDS offsets (bf16 elements), computed once so that every LDS access in the tile loop is a
-// per-lane register plus a compile-time or per-block offset.  Tiles are [rows][128] with 16-byte
-// chunks XOR-swizzled by row (nat_off); the swizzle depends only on row % 16, so within a lane it is
-// the same for every row block, and the chunk index splits into bits the block offset cannot carry.
-struct LaneOff {
-    int pl[8];          // row col, chunk 2m + h (plain fragment reads; + 128 row0)
-    int trn[4][2];      // transposed reads without permutation at k0 = 0 of column block nb (+ 128 k0),
-                        // first and second 8-byte piece
-    int trc[2][2][2];   // [PERM][n][piece] the same for this wave's column blocks 2ch + n
-    int pw[2][4];       // row col, chunk 4(2ch + i) + g, 8-byte half h: where accumulator entries
-                        // 4g..4g+3 of this wave's state blocks with rows kb = 2ch + i land in a
-                        // transposed state
-    int po[2][4];       // the same in a 64-column output staging row (chunk 4n + g)
-};
-
-__device__ __forceinline__ int tr_off(int lane, int perm, int half, int nb) {
-    const int g = lane >> 4, j = lane & 15, hh = g >> 1;
-    const int cl = 2 * (g & 1) + ((j & 3) >> 1);   // chunk bits below the column block's
-    const int rl = (perm ? 4 * hh : 8 * hh) + (j >> 2) + (half ? (perm ? 8 : 4) : 0);
-    const int S = swz<D1>(rl);
-    return rl * D1 + ((((4 * nb) ^ (S & 12)) | (cl ^ (S & 3))) << 3) + 4 * (j & 1);
-}
-
-__device__ __forceinline__ LaneOff lane_offsets(int lane, int ch) {
-    LaneOff L;
-    const int h = lane >> 5, col = lane & 31;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) L.pl[m] = nat_off<D1>(col, 2 * m + h);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) L.trn[nb][half] = tr_off(lane, 0, half, nb);
-#pragma unroll
-    for (int perm = 0; perm < 2; ++perm)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) L.trc[perm][n][half] = tr_off(lane, perm, half, 2 * ch + n);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            L.pw[i][g] = nat_off<D1>(col, 4 * (2 * ch + i) + g) + 4 * h;
-            L.po[i][g] = col * 64 + (((4 * i + g) ^ ((col >> 1) & 7)) << 3) + 4 * h;
-        }
-    return L;
-}
-
-// Fragment (either MFMA side) of rows row0 + col, 8 consecutive columns 16m + 8h.. of a tile.
-__device__ __forceinline__ bf16x8 rd_plain(const u16 *s, int row0, int m, const LaneOff &L) {
-    return lds_read(s, row0 * D1 + L.pl[m]);
-}
-
-// A transposing fragment (frag_tr) at k0 (a multiple of 16) from the two piece offsets `off`.
-__device__ __forceinline__ bf16x8 rd_tr(const u16 *s, int k0, const int (&off)[2]) {
-    const u32x2 a = __builtin_bit_cast(u32x2, tr_read(s, k0 * D1 + off[0]));
-    const u32x2 b = __builtin_bit_cast(u32x2, tr_read(s, k0 * D1 + off[1]));
-    const u32x4 w = {a[0], a[1], b[0], b[1]};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-// bf16x8 with every sign bit xor-ed with `sign` (0x80008000: every element negated, exactly; 0: as is).
-__device__ __forceinline__ bf16x8 flip8(const bf16x8 &f, unsigned int sign) {
-    u32x4 u = __builtin_bit_cast(u32x4, f);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) u[m] ^= sign;
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ void lds_write8(u16 *s, int off, const u32x2 &v) {
-    *reinterpret_cast<u32x2 *>(s + off) = v;
-}
-
-// P of one 32 x 32 score block as the B operand of the value products.  Accumulator r of lane
-// (h, col) holds source row 8(r/4) + 4h + r%4 against output row col; pairs (2p, 2p + 1) are rounded
-// to bf16 together.  In the diagonal block the entries on the wrong side of the causal mask are
-// zeroed first (sources at or after the output row are kept for dV and dK, at or before for dQ).
-template <Unit U, bool DIAG>
-__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col) {
-    u32x4 w[2];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        float a = acc[2 * p], b = acc[2 * p + 1];
-        if (DIAG) {
-            const int dist = 4 * h - col + 8 * (p >> 1) + 2 * (p & 1);   // source - output of entry 2p
-            a = (U == Unit::DQ ? dist <= 0 : dist >= 0) ? a : 0.0f;
-            b = (U == Unit::DQ ? dist + 1 <= 0 : dist + 1 >= 0) ? b : 0.0f;
-        }
-        w[p >> 2][p & 3] = pack_bf16(a, b);
-    }
-    pf[0] = __builtin_bit_cast(bf16x8, w[0]);
-    pf[1] = __builtin_bit_cast(bf16x8, w[1]);
-}
-
-// The intra-tile contribution of source block u to a unit: scores of the block's 32 source rows
-// against the unit's 32 output rows (B operand bf), then P times the value rows of the block.
-template <Unit U, bool DIAG>
-__device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf)[KS1], const u16 *sA,
-                                            const u16 *sC, int u, const LaneOff &L, int h, int col) {
-    const f32x16 zero = {};
-    f32x16 acc = mfma(rd_plain(sA, u * 32, 0, L), bf[0], zero);
-#pragma unroll
-    for (int ks = 1; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
-    bf16x8 pf[2];
-    block_p<U, DIAG>(acc, pf, h, col);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) oacc[n] = mfma(rd_tr(sC, u * 32 + 16 * x, L.trc[1][n]), pf[x], oacc[n]);
-}
-
-// One output unit of a wave: columns 64ch..64ch+63 (two 32-column blocks) of the output rows in
-// block `orow`, as O^T accumulators (lane col holds output row orow*32 + col).
-//   DV: rows s of dV; scores Q[t] . K[s] for t >= s; value dO; inter R^T K^T
+// One output unit of a wave: columns 64ch..64ch+63 of the output rows in block `orow`.
+//   DV: rows s of dV; scores Q[t] . K[s] for t >= s; value dO; inter R^T K^T (R^T rows read plain)
 //   DK: rows s of dK; scores dO[t] . V[s] for t >= s; value Q; inter R V^T
 //   DQ: rows t of dQ; scores V[s] . dO[t] for s <= t; value K; inter S dO^T
-// The inter product always runs (a state that is still zero contributes zeros), so the first
-// contraction step starts from a zero accumulator operand instead of cleared registers.
 template <Unit U>
 __device__ __forceinline__ void out_unit(f32x16 (&oacc)[2], const u16 *smem, int orow, int ch, int lane,
                                          const LaneOff &L) {
-    const int h = lane >> 5, col = lane & 31;
     const u16 *sB = smem + (U == Unit::DV ? oK1 : U == Unit::DK ? oV1 : oO1);   // output-row role
     const u16 *sA = smem + (U == Unit::DV ? oQ1 : U == Unit::DK ? oO1 : oV1);   // source-row role
     const u16 *sC = smem + (U == Unit::DV ? oO1 : U == Unit::DK ? oQ1 : oK1);   // value role
     const u16 *sSt = smem + (U == Unit::DQ ? oST1 : oRT1);
-    bf16x8 bf[KS1];
-#pragma unroll
-    for (int ks = 0; ks < KS1; ++ks) bf[ks] = rd_plain(sB, orow * 32, ks, L);
-    // fully unrolled: bf[] must be indexed by constants (a runtime index into a register array is
-    // lowered to chains of selects)
-    const f32x16 zero = {};
-#pragma unroll
-    for (int ks = 0; ks < KS1; ++ks)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            // DV: R^T rows (d_v) from plain reads; DK, DQ: R or S rows (d) through transpose reads
-            const bf16x8 a = U == Unit::DV ? rd_plain(sSt, (2 * ch + n) * 32, ks, L) : rd_tr(sSt, 16 * ks, L.trc[0][n]);
-            oacc[n] = mfma(a, bf[ks], ks == 0 ? zero : oacc[n]);
-        }
-    // intra-tile: the whole source block below (dQ) or above (dV, dK) the diagonal, where there is one,
-    // then the diagonal block
-    if (U == Unit::DQ ? orow == 1 : orow == 0)
-        intra_block<U, false>(oacc, bf, sA, sC, U == Unit::DQ ? 0 : 1, L, h, col);
-    intra_block<U, true>(oacc, bf, sA, sC, orow, L, h, col);
+    unit_products<U == Unit::DQ, U == Unit::DV>(oacc, sB, sA, sC, sSt, orow, ch, lane, L);
 }
 
 // The tiles of one (chain, segment), walked from the last to the first.

@@ -1,0 +1,223 @@
+// la2_fwd1_bf16.hip -- the forward output scan without decay at d = d_v = 128 in bf16, as producer and
+// consumer waves over 64-position tiles.
+//
+// Page "Lightning Attention" (lizeman.github.io llm-arch-kb), section 2, Steps 1-4: per tile b of
+// 64 positions (local rows t = outputs, s = sources)
+//   O_b = mask(Q_b K_b^T) V_b + Q_b S_{b-1}    (intra: sources s <= t; inter: the state before the tile)
+//   S_b = S_{b-1} + K_b^T V_b                  (the state update on the unmasked tile)
+// and, with a key/value pair of roles (b, c) and a query role a, the same scan serves the dQ pass of
+// the two-pass backward and the scan U of the normalized backward (its state read transposed).
+//
+// Workgroup of eight waves, two per SIMD, in two roles (the layout of the one-pass backward):
+//   consumers (waves 0-3, c = 2rb + ch): columns 64ch..64ch+63 of the output rows in block rb;
+//   producers (waves 4-7, p): the fp32 state rows 32p..32p+31 (all 128 columns) in registers,
+//     updated with the tile's K^T V and published as a bf16 copy S^T in LDS.
+// The state update of tile b overlaps the consumers' products of tile b on every SIMD; S_b's copy
+// replaces S_{b-1}'s only after barrier Y, when every consumer is done reading it.  The next tile's
+// q, k and v go global -> LDS by direct loads into the second of two tile buffers, issued at the top
+// of the tile, so they have the whole tile to land.  Two barriers per tile: Y and X (the next tile
+// and S_b's copy in LDS).  LDS: 2 x (q, k, v) 96 KiB, S^T 32 KiB, output staging 4 x 4 KiB.
+#include "la2_tile64_bf16.h"
+
+namespace la2 {
+namespace {
+
+using namespace dev;
+using namespace t64;
+
+constexpr int kTF = 512;                      // threads: 4 consumers, then 4 producers
+constexpr int oQF = 0, oKF = kTile1, oVF = 2 * kTile1;   // within a tile buffer
+constexpr int kBufF = 3 * kTile1;             // one buffer of the three input tiles
+constexpr int oSTF = 2 * kBufF;               // S^T [d_v][d] bf16
+constexpr int oOSF = oSTF + D1 * D1;          // per-consumer output staging, 32 x 64
+constexpr int kOSF = 32 * 64;
+constexpr int kLdsF = oOSF + 4 * kOSF;
+static_assert(kLdsF * 2 <= 160 * 1024, "LDS");
+static_assert(kWaves == 8, "the direct loads split a tile over eight waves");
+
+// The 64-position tiles of one (chain, segment), first to last.
+struct WalkF {
+    int64_t T, t_lo, base;
+    int ntiles;
+    __device__ int64_t t0(int it) const { return t_lo + (int64_t)it * TB1; }
+};
+
+__device__ __forceinline__ WalkF walk_of(const Fwd1Args &p, int chain, int seg) {
+    WalkF w;
+    w.T = p.T;
+    w.t_lo = (int64_t)seg * p.seg_len;
+    const int64_t t_hi = min(p.T, w.t_lo + p.seg_len);
+    w.ntiles = (int)((t_hi - w.t_lo + TB1 - 1) / TB1);
+    w.base = (int64_t)chain * p.T * D1;
+    return w;
+}
+
+// The tile starting at t0 of q, k and v into one LDS buffer (rows past T arrive as zeros).
+__device__ __forceinline__ void dma_tile_f(u16 *buf, const u16 *gq, const u16 *gk, const u16 *gv, int64_t t0,
+                                           int64_t T, int wave, int lane) {
+    const int64_t bytes = (T - t0) * D1 * 2;
+    dma_rows<D1, TB1>(make_rsrc(gq + t0 * D1, bytes), buf + oQF, D1, wave, lane);
+    dma_rows<D1, TB1>(make_rsrc(gk + t0 * D1, bytes), buf + oKF, D1, wave, lane);
+    dma_rows<D1, TB1>(make_rsrc(gv + t0 * D1, bytes), buf + oVF, D1, wave, lane);
+}
+
+// Producer p: state rows 32p..32p+31 of S (d x d_v), four 32 x 32 blocks (column blocks jb).
+__device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int pw, int lane) {
+    const WalkF w = walk_of(p, chain, seg);
+    const int wave = 4 + pw, h = lane >> 5, col = lane & 31;
+    // per-lane LDS offsets: transposed reads of K's column block pw and of V's four column blocks, and
+    // where accumulator entries 4q..4q+3 (state rows 32pw + 8q + 4h..) land in a row of S^T
+    int trk[2], trv[4][2], pwq[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        trk[half] = tr_off(lane, 0, half, pw);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) trv[jb][half] = tr_off(lane, 0, half, jb);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pwq[q] = nat_off<D1>(col, 4 * pw + q) + 4 * h;
+    const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
+    const u16 *gv = static_cast<const u16 *>(p.v) + w.base;
+    const bool last_seg = seg == p.nseg - 1;
+    const bool final_state = last_seg && p.state_out != nullptr;
+
+    // the state the segment starts from: zero, or the segment's entry of the start states ([D][DV], or
+    // [DV][D] when read transposed)
+    f32x16 sacc[4];
+    const float *g = seg > 0 && p.states != nullptr
+                         ? p.states + ((int64_t)chain * p.nsub + state_index(seg, p.sub, p.nsub, false)) * D1 * D1
+                         : nullptr;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = pw * 32 + 8 * (r >> 2) + 4 * h + (r & 3), j = jb * 32 + col;
+            sacc[jb][r] = g != nullptr ? g[p.states_t ? (int64_t)j * D1 + i : (int64_t)i * D1 + j] : 0.0f;
+        }
+    // the bf16 copy S^T ([d_v][d]): accumulator entries 4q..4q+3 are four consecutive d of one d_v row
+    auto write_state = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 v = {pack_bf16(sacc[jb][4 * q], sacc[jb][4 * q + 1]),
+                                 pack_bf16(sacc[jb][4 * q + 2], sacc[jb][4 * q + 3])};
+                lds_write8(smem + oSTF, jb * 32 * D1 + pwq[q], v);
+            }
+    };
+
+    dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, wave, lane);
+    write_state();
+    wait_vm();
+    lds_barrier();   // X: the first tile and S^T
+    for (int it = 0; it < w.ntiles; ++it) {
+        const bool more = it + 1 < w.ntiles;
+        const u16 *cur = smem + (it & 1) * kBufF;
+        if (more) dma_tile_f(smem + ((it + 1) & 1) * kBufF, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
+        // S += K^T V over the tile's 64 positions (the last tile's update only for the final state)
+        if (more || final_state) {
+            const u16 *sK = cur + oKF, *sV = cur + oVF;
+#pragma unroll
+            for (int x = 0; x < TB1 / 16; ++x) {
+                const bf16x8 fa = rd_tr(sK, 16 * x, trk);
+                bf16x8 fc[4];
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
+            }
+        }
+        lds_barrier();   // Y: every consumer is done with S_{b-1}^T
+        if (more) write_state();
+        wait_vm();
+        lds_barrier();   // X: the next tile and S_b^T
+    }
+    if (final_state) {
+        float *so = p.state_out + (int64_t)chain * D1 * D1;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = pw * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                so[(int64_t)i * D1 + jb * 32 + col] = sacc[jb][r];
+            }
+    }
+}
+
+// Consumer c = 2rb + ch: the output unit of row block rb, columns 64ch..64ch+63, staged in the wave's
+// own 4 KiB of LDS and stored as whole 128-byte row pieces at the top of the next tile.
+__device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
+    const WalkF w = walk_of(p, chain, seg);
+    const int rb = c >> 1, ch = c & 1;
+    const LaneOff L = lane_offsets(lane, ch);
+    const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
+    const u16 *gv = static_cast<const u16 *>(p.v) + w.base;
+    u16 *gy = static_cast<u16 *>(p.y) + w.base;
+    u16 *ob = smem + oOSF + c * kOSF;
+    auto stage = [&](const f32x16 (&acc)[2]) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 v = {pack_bf16(acc[n][4 * q], acc[n][4 * q + 1]),
+                                 pack_bf16(acc[n][4 * q + 2], acc[n][4 * q + 3])};
+                lds_write8(ob, L.po[n][q], v);
+            }
+    };
+    auto store = [&](int64_t t0) {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(gy + t0 * D1, (w.T - t0) * D1 * 2);
+        u32x4 v[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
+            v[s2] = *reinterpret_cast<const u32x4 *>(ob + row * 64 + ((chk ^ ((row >> 1) & 7)) << 3));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int qd = lane + 64 * s2, row = qd / 8, chk = qd % 8;
+            bstore16(ry, ((rb * 32 + row) * D1 + ch * 64 + chk * 8) * 2, v[s2]);
+        }
+    };
+
+    dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, c, lane);
+    wait_vm();
+    lds_barrier();   // X: the first tile and S^T
+    for (int it = 0; it < w.ntiles; ++it) {
+        const u16 *cur = smem + (it & 1) * kBufF;
+        if (it + 1 < w.ntiles) dma_tile_f(smem + ((it + 1) & 1) * kBufF, gq, gk, gv, w.t0(it + 1), w.T, c, lane);
+        if (it > 0) store(w.t0(it - 1));
+        {
+            f32x16 oacc[2];
+            unit_products<true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L);
+            stage(oacc);
+        }
+        lds_barrier();   // Y
+        wait_vm();
+        lds_barrier();   // X
+    }
+    store(w.t0(w.ntiles - 1));
+}
+
+__global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
+    __shared__ __attribute__((aligned(16))) u16 smem[kLdsF];
+    // the wave index as a scalar: every branch on a wave's role is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int seg = blockIdx.x % p.nseg;
+    const int chain = blockIdx.x / p.nseg;
+    if ((int64_t)seg * p.seg_len >= p.T) return;
+    if (wave < 4)
+        consumer_f(p, smem, chain, seg, wave, lane);
+    else
+        producer_f(p, smem, chain, seg, wave - 4, lane);
+}
+
+}  // namespace
+
+hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
+    if (a.seg_len <= 0 || a.seg_len % TB1 != 0) return hipErrorInvalidValue;
+    const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
+    hipLaunchKernelGGL(fwd1_bf16_kernel, dim3(items), dim3(kTF), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace la2

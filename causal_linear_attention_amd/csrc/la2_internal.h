@@ -135,6 +135,23 @@ struct DkdvArgs {
 bool dkdv_supported(int D, int DV);
 hipError_t launch_dkdv_bf16(const DkdvArgs &a, int D, hipStream_t s);
 
+// The forward-direction output scan without decay at d = d_v = 128, bf16 (la2_fwd1_bf16.hip): y_t =
+// sum_{s<=t} (a_t . b_s) c_s + a_t S_in for each (chain, segment) over 64-position tiles, producer
+// waves holding S = sum b^T c in registers beside the consumer waves forming y.
+struct Fwd1Args {
+    const void *q, *k, *v;  // query, key and value roles [chains, T, 128]
+    void *y;                // output [chains, T, 128]
+    int64_t T;
+    int64_t seg_len;        // positions per segment, a multiple of 64
+    int nseg;
+    int chains;
+    const float *states;    // fp32 segment start states ([chains, nsub, D, D]) or nullptr (unsplit)
+    int states_t;           // 1: the entries are stored transposed ([DV][D])
+    int sub, nsub;          // states entry of segment s: state_index(s, sub, nsub, false)
+    float *state_out;       // fp32 [chains, D, D]: the state after the last position, or nullptr
+};
+hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s);
+
 // The whole backward without decay in one reverse walk (la2_bwd1_bf16.hip): dq, dk and dv of each
 // (chain, segment) over kBwd1Tile-position tiles, d = d_v = 128, bf16.  The forward state is carried
 // backwards from the state after the segment (the next segment's start state, or the chain's final
