@@ -34,12 +34,12 @@ METRIC = "fwd+bwd tokens/sec on 1 MI355X vs T (1K–128K); % bf16 MFMA / HBM roo
 # source it was taken on (sha256 of the listed files, concatenated); for any other source the roofline
 # reports traffic as null.
 # At the 1K point: the backward reads q, k, v, dO and the final states (2176.4 MiB) and writes dq, dk, dv
-# (1536.2 MiB); the forward reads q, k, v (1536.4 MiB) and writes o and the final states (640.0 MiB).
+# (1536.3 MiB); the forward reads q, k, v (1536.2 MiB) and writes o and the final states (640.0 MiB).
 TRAFFIC = {
-    "bwd1": {"sources": ("la2_bwd1_bf16.hip", "la2_bf16_common.h"), "sha256_16": "c4bae2b3ec7c4c5d",
-             "bytes": 3892959028},
-    "fwd": {"sources": ("la2_scan_bf16.hip", "la2_bf16_common.h"), "sha256_16": "e57aa0bdbebc71dc",
-            "bytes": 2282085142},
+    "bwd1": {"sources": ("la2_bwd1_bf16.hip", "la2_tile64_bf16.h", "la2_bf16_common.h"),
+             "sha256_16": "28503fc811547c04", "bytes": 3893079176},
+    "fwd": {"sources": ("la2_fwd1_bf16.hip", "la2_tile64_bf16.h", "la2_bf16_common.h"),
+            "sha256_16": "11cd89c49999eff5", "bytes": 2281999341},
 }
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
@@ -417,29 +417,32 @@ def _segments(chains, T, tile):
 
 
 def one_pass_backward(w):
-    """True where la2_backward_saved runs the one-pass backward: no decay, bf16, d = d_v = 128."""
+    """True where la2_backward_saved runs the one-pass backward, and la2_forward the producer/consumer
+    scan over 64-position tiles: no decay, bf16, d = d_v = 128."""
     return not w.decay and w.dtype == "bf16" and w.d == 128 and w.dv == 128
 
 
 def executed(w):
     """MFMA flops the bf16 kernels execute for one forward and one training-step backward
     (la2_backward_saved) over workload w (d = d_v): score and output products over the causal 32 x 32
-    blocks of the tiles the kernels actually run (output scans min(max(T_B, 64), 128) positions, the
-    backward kernels 64), the inter products and state updates (2 d^2 each per token), and the
-    state-only passes of split chains (2 d^2 per token of every segment whose state is needed)."""
+    blocks of the tiles the kernels actually run (without decay at d = 128 the forward and backward
+    kernels run 64 positions, otherwise output scans min(max(T_B, 64), 128) and the backward kernels
+    64), the inter products and state updates (2 d^2 each per token), and the state-only passes of
+    split chains (2 d^2 per token of every segment whose state is needed)."""
     d, T, chains = w.d, w.T, w.B * w.H
     th = chains * T
-    tf = min(max(w.block, 64), 128)
+    tf = 64 if one_pass_backward(w) else min(max(w.block, 64), 128)
     nb = tf // 32
     intra_f = (nb + 1) * 32 * d * 2           # per token: Q K^T and P V over (nb + 1) / 2 blocks of 32
-    nseg, seg_tiles = _segments(chains, T, tf)
-    state_f = 2 * d * d * chains * min(T, (nseg - 1) * seg_tiles * tf) if nseg > 1 else 0
+    tp = min(max(w.block, 64), 128)           # the plan's tile: segments are whole tiles of it
+    nseg, seg_tiles = _segments(chains, T, tp)
+    state_f = 2 * d * d * chains * min(T, (nseg - 1) * seg_tiles * tp) if nseg > 1 else 0
     fwd = th * (intra_f + 4 * d * d) + state_f
     causal64 = 3 * 2 * 32 * 32 * d // 64      # per token: one product over 3 causal 32 x 32 blocks of a 64-tile
     if one_pass_backward(w):
         # one reverse walk over 64-tiles: 2 score and 3 output products, 3 inter products, 2 state updates
         # (R and the undoing of S); the reverse state-only pass over every segment but the first
-        state_b = 2 * d * d * chains * max(0, T - seg_tiles * tf) if nseg > 1 else 0
+        state_b = 2 * d * d * chains * max(0, T - seg_tiles * tp) if nseg > 1 else 0
         bwd = th * (5 * causal64 + 10 * d * d) + state_b
     else:
         # dQ = forward scan of (do, v, k) reusing the forward's states; fused dK/dV over 64-tiles:
@@ -651,8 +654,8 @@ def main():
         fwd_gbs = alg["fwd_bytes"] / (dom_fwd_ms * 1e-3) / 1e9
         fwd_tf = ex["fwd_flops_executed"] / (dom_fwd_ms * 1e-3) / 1e12
         forward_kernel = {
-            "kernel": f"scan_bf16_kernel<D={w.d},DV={w.dv},TB={min(w.block, 128)},Forward,decay=false> "
-                      "(forward output scan, writing each chain's final state)",
+            "kernel": "fwd1_bf16_kernel (forward output scan over 64-position tiles, writing each chain's final "
+                      "state)",
             "avg_launch_ms": round(dom_fwd_ms, 4), "achieved_GBs": round(fwd_gbs, 1),
             "frac": round(fwd_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": alg["fwd_bytes"],
             "traffic": traffic("fwd"), "mfma_TFLOPs": round(fwd_tf, 1),
