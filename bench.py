@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--stream", action="store_true",
                     help="time the test build's plain HBM stream (16-byte lane accesses, 1 GiB per buffer) at the "
                          "read:write mixes of the tile kernels, over launch shapes and both cache policies")
+    ap.add_argument("--cache-probe", action="store_true",
+                    help="time the test build's memory-side cache probe: a state-only pass fused ahead of the "
+                         "output pass against the two as separate launches, over item sizes")
     args = ap.parse_args()
     single = args.workload is not None
     if args.steps is None:
@@ -141,6 +144,51 @@ def stream_bench(args):
               f"nontemporal {best['nontemporal']})", file=sys.stderr, flush=True)
     print(json.dumps({"metric": "plain HBM stream, best launch shape per read:write mix", "unit": "GB/s",
                       "bytes_per_buffer": nbytes, "peak": PEAK_HBM_GBS, "best": results, "all": rows}), flush=True)
+
+
+def cache_probe_bench(args):
+    """Whether a state-only pass fused ahead of the output pass could take its second read of k and v
+    from the memory-side cache instead of HBM: four 512 MiB tensors (q, k, v, o of 16 chains x 128K
+    positions x 128 bf16, the 128K point) cut into items of L positions, one workgroup per item and
+    one per CU (la2_test_reread).  Per L: phase B alone (the output pass), A then B in one workgroup,
+    A alone, and A; B as two launches (the split-chain plan's order).  The best of 10 launches each."""
+    import torch
+    from causal_linear_attention_amd import binding
+
+    nbytes = 512 << 20
+    q, k, v, o = (torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(4))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best_ms(modes, nt, item, reps=10):
+        best = None
+        for _ in range(reps):
+            ev[0].record()
+            for m in modes:
+                binding.reread_probe(q, k, v, o, item, m, nt)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1])
+            best = ms if best is None else min(best, ms)
+        return best
+
+    for _ in range(20):                       # some tens of ms of work first: clocks settle
+        binding.reread_probe(q, k, v, o, 1 << 18, 1, 1)
+    torch.cuda.synchronize()
+    rows = []
+    for L in (256, 512, 1024, 2048, 4096, 8192):
+        item = L * 128 * 2
+        for nt in (1, 0):
+            r = {"L": L, "items": nbytes // item, "nontemporal": bool(nt),
+                 "B_ms": round(best_ms((0,), nt, item), 4), "A_then_B_ms": round(best_ms((1,), nt, item), 4),
+                 "A_ms": round(best_ms((2,), nt, item), 4), "A_B_two_launches_ms": round(best_ms((2, 0), nt, item), 4)}
+            r["fused_over_B"] = round(r["A_then_B_ms"] / r["B_ms"], 3)
+            r["two_launches_over_B"] = round(r["A_B_two_launches_ms"] / r["B_ms"], 3)
+            rows.append(r)
+            print(f"[cache] L={L} nt={nt}: B {r['B_ms']} ms, A then B {r['A_then_B_ms']} ms "
+                  f"({r['fused_over_B']}x), A {r['A_ms']} ms, A; B {r['A_B_two_launches_ms']} ms "
+                  f"({r['two_launches_over_B']}x)", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "memory-side cache re-read probe (state-only pass fused ahead of the output pass)",
+                      "unit": "ms", "bytes_per_tensor": nbytes, "rows": rows}), flush=True)
 
 
 def decode_bench(args):
@@ -505,6 +553,9 @@ def main():
         return
     if args.stream:
         stream_bench(args)
+        return
+    if args.cache_probe:
+        cache_probe_bench(args)
         return
     if args.decode:
         decode_bench(args)

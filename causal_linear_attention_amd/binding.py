@@ -104,6 +104,9 @@ def _load_test_library():
                                         ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p]
         lib.la2_test_stream.restype = ctypes.c_int
+        lib.la2_test_reread.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int,
+                                                                 ctypes.c_int, ctypes.c_void_p]
+        lib.la2_test_reread.restype = ctypes.c_int
         _test_lib = lib
     return _test_lib
 
@@ -123,6 +126,21 @@ def stream_probe(srcs, dsts, blocks, threads, nontemporal, stream=None):
                              _stream(stream))
     if st != 0:
         raise LA2Error(st, "la2_test_stream")
+
+
+def reread_probe(q, k, v, o, item_bytes, mode, nontemporal, stream=None):
+    """Enqueue the test build's memory-side cache probe (include/la2_test_hooks.h): per item of
+    item_bytes, phase A reads k and v, phase B reads q, k, v and writes o; mode 0 = B, 1 = A then B,
+    2 = A.  Same-sized contiguous CUDA tensors."""
+    lib = _load_test_library()
+    nbytes = q.numel() * q.element_size()
+    for t in (q, k, v, o):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()) or t.numel() * t.element_size() != nbytes:
+            raise ValueError("reread_probe takes contiguous CUDA tensors of one size")
+    st = lib.la2_test_reread(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), nbytes, int(item_bytes), int(mode),
+                             int(bool(nontemporal)), _stream(stream))
+    if st != 0:
+        raise LA2Error(st, "la2_test_reread")
 
 
 @contextlib.contextmanager

@@ -46,6 +46,19 @@ int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int sep
 int la2_test_stream(const void *const *src, int nsrc, void *const *dst, int ndst, size_t bytes,
                     int blocks, int threads, int nontemporal, void *stream);
 
+/* Enqueue on `stream` a probe of the memory-side cache (test build only): device buffers q, k, v, o of
+ * `bytes` each are cut into items of `item_bytes`, one workgroup of 512 threads (144 KiB of LDS, one
+ * per CU) per item.  Phase A reads the item's k and v; phase B reads its q, k, v and writes its o.
+ * mode 0: B alone; 1: A then B in the same workgroup (A's loads with the default cache policy, so B's
+ * second read of k and v may come from the cache); 2: A alone (writes one 16-byte chunk per item
+ * into o).  nontemporal sets the hint on B's accesses (and on A's in mode 2).  The time of mode 1
+ * against modes 0 and 2 shows what a state-only pass fused ahead of the output pass would cost at
+ * that item size.  bytes a multiple of item_bytes (at most 2^31 - 1 items), item_bytes a multiple
+ * of 16, pointers 16-byte aligned.  Returns LA2_OK, LA2_ERR_BAD_SHAPE, LA2_ERR_NULL_POINTER or
+ * LA2_ERR_HIP. */
+int la2_test_reread(const void *q, const void *k, const void *v, void *o, size_t bytes, size_t item_bytes,
+                    int mode, int nontemporal, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

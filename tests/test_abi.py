@@ -347,7 +347,7 @@ def test_high_level_api_rejects_decay_outside_unit_interval(bad):
 def test_release_library_has_no_plan_overrides(lib):
     """Test knobs live only in the test build: the release library exports no override and reads no
     environment variable, so its plan depends on the arguments alone."""
-    assert not hasattr(lib, "la2_test_set_plan") and not hasattr(lib, "la2_test_stream")
+    assert not any(hasattr(lib, n) for n in ("la2_test_set_plan", "la2_test_stream", "la2_test_reread"))
     import subprocess
     syms = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     assert "getenv" not in syms
@@ -380,6 +380,18 @@ def test_stream_probe_validates_before_launch():
     assert tl.la2_test_stream(src, 1, dst, 1, 1 << 20, 256, 96, 1, None)  == SHAPE       # not whole waves
     bad = (ctypes.c_void_p * 1)(0x100008)
     assert tl.la2_test_stream(bad, 1, dst, 1, 1 << 20, 256, 256, 1, None) == NULLP          # misaligned
+
+
+def test_reread_probe_validates_before_launch():
+    """The test build's memory-side cache probe refuses bad arguments before anything is enqueued."""
+    tl = binding._load_test_library()
+    p = [0x100000, 0x200000, 0x300000, 0x400000]
+    assert tl.la2_test_reread(*p, 1 << 20, 1 << 12, 3, 1, None) == SHAPE                 # no such mode
+    assert tl.la2_test_reread(*p, 1 << 20, 24, 0, 1, None) == SHAPE                      # not 16-byte items
+    assert tl.la2_test_reread(*p, 1 << 20, 3 << 10, 0, 1, None) == SHAPE                 # ragged last item
+    assert tl.la2_test_reread(*p, 0, 1 << 12, 0, 1, None) == SHAPE
+    assert tl.la2_test_reread(p[0], 0x200008, p[2], p[3], 1 << 20, 1 << 12, 0, 1, None) == NULLP   # misaligned
+    assert tl.la2_test_reread(p[0], p[1], p[2], None, 1 << 20, 1 << 12, 0, 1, None) == NULLP
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch():
