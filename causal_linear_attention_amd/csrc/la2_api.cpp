@@ -596,6 +596,35 @@ la2::DenArgs den_args(const void *q, const void *k, const float *decay, char *ws
 // Scan modes of launch_vscan (la2_norm.hip).
 constexpr int kVZSeg = 0, kVDen = 1, kVDQ = 2, kVYSeg = 3, kVDK = 4, kVMean = 5, kVKappa = 6, kVDQN = 7;
 
+// The normalized forward as one launch of the 64-position producer/consumer scan (la2_fwd1_bf16.hip):
+// bf16 at d = d_v = 128 without decay, on chains the plan does not split.
+bool fused_normalized(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype,
+                      const float *decay) {
+    if (dtype != LA2_BF16 || d != 128 || dv != 128 || decay || forced().legacy_forward) return false;
+    const Plan pl = make_plan(B, H, T, d, dv, block, dtype);
+    return pl.nseg == 1 && slice_width(dtype, (int)dv, pl.narrow) == dv;
+}
+
+// o, and where given phi(q), phi(k) (elu + 1 only) and the denominators, of the fused normalized forward.
+hipError_t launch_fused_normalized(const void *q, const void *k, const void *v, void *o, void *pq, void *pk,
+                                   float *den, int64_t chains, int64_t T, int feature_map, hipStream_t s) {
+    la2::Fwd1Args f{};
+    f.q = q;
+    f.k = k;
+    f.v = v;
+    f.y = o;
+    f.T = T;
+    f.seg_len = (T + 63) / 64 * 64;
+    f.nseg = 1;
+    f.chains = (int)chains;
+    f.sub = f.nsub = 1;
+    f.norm = feature_map == LA2_PHI_ELU1 ? 2 : 1;
+    f.pq = pq;
+    f.pk = pk;
+    f.den = den;
+    return la2::launch_fwd1_bf16(f, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -636,6 +665,23 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
     const int64_t chains = B * H;
+    // bf16 at d = d_v = 128 without decay, chains the plan does not split: one launch applies phi to
+    // the tiles and forms numerator and denominator together.  Given room for the backward it also
+    // leaves phi(q), phi(k) and the denominators where la2_backward_normalized_saved reads them, and
+    // (denominator segments of split chains) each segment's sum of phi(k), which the bf16 dq carries.
+    if (fused_normalized(B, H, T, d, d_v, block, dtype, decay)) {
+        const bool for_bwd =
+            workspace && workspace_bytes >= norm_layout(B, H, T, d, d_v, feature_map, block, dtype, true).total;
+        if (launch_fused_normalized(q, k, v, o, for_bwd && L.phi ? ws : nullptr, for_bwd && L.phi ? ws + L.phi : nullptr,
+                                    for_bwd ? reinterpret_cast<float *>(ws + L.den_off) : nullptr, chains, T,
+                                    feature_map, s) != hipSuccess)
+            return LA2_ERR_HIP;
+        if (for_bwd && L.dp.nseg > 1 &&
+            la2::launch_vscan(den_args(q, k, decay, ws, L, H, T, chains), (int)d, dtype, feature_map, kVZSeg, s) !=
+                hipSuccess)
+            return LA2_ERR_HIP;
+        return LA2_OK;
+    }
     // 1. denominator den_t = phi(q_t) . z_t (fp32), and phi(q), phi(k) for the numerator
     const la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
     if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess) return LA2_ERR_HIP;
@@ -832,11 +878,19 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
     la2::DenArgs a = den_args(q, k, decay, ws, L, H, T, chains);
     float *dden = reinterpret_cast<float *>(ws + L.dden_off);
     void *dn = ws + L.dn_off;
-    // 1. the forward's denominator, phi(q), phi(k) (recomputed unless the forward left them)
+    // 1. the forward's denominator, phi(q), phi(k) (recomputed unless the forward left them), the way the
+    //    forward forms them: where it is one fused launch, that launch again, its o put in dn's place
+    //    (overwritten next)
     if (!saved) {
-        if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess)
-            return LA2_ERR_HIP;
-        if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
+        if (fused_normalized(B, H, T, d, d_v, block, dtype, decay)) {
+            if (launch_fused_normalized(q, k, v, dn, a.pq, a.pk, a.den, chains, T, feature_map, s) != hipSuccess ||
+                (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess))
+                return LA2_ERR_HIP;
+        } else {
+            if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess)
+                return LA2_ERR_HIP;
+            if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
+        }
     }
     // 2. dn = do / den, dden = -(do . o) / den
     if (la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)

@@ -17,6 +17,17 @@
 // q, k and v go global -> LDS by direct loads into the second of two tile buffers, issued at the top
 // of the tile, so they have the whole tile to land.  Two barriers per tile: Y and X (the next tile
 // and S_b's copy in LDS).  LDS: 2 x (q, k, v) 96 KiB, S^T 32 KiB, output staging 4 x 4 KiB.
+//
+// The normalized form (page "Lightning Attention", section 1: numerator over denominator, with a
+// feature map phi on q and k): o_t = S_t^T phi(q_t) / (phi(q_t) . z_t), z_t = sum_{s<=t} phi(k_s).
+// phi is applied to the q and k tiles in LDS (elu + 1: after barrier Y, where every wave waits for
+// its share of the next tile's direct loads, it transforms the chunks those loads filled; rows past
+// the sequence stay zero), so the numerator is the plain scan on phi(q), phi(k) rounded to bf16.  The denominator comes from the same rounded values: its
+// intra-tile part is the sum of each output row's kept fp32 scores, its inter part the product of the
+// row with z before the tile, which the producers keep in fp32 from their K^T operands (column sums of
+// phi(K)) and publish beside S^T as two bf16 rows (z rounded, and the remainder rounded) of an
+// otherwise zero [32][128] tile, so that the consumers take it with 8 more MFMAs beside their inter
+// product.  Each output row is divided in fp32 before it is rounded.
 #include "la2_tile64_bf16.h"
 
 namespace la2 {
@@ -31,7 +42,8 @@ constexpr int kBufF = 3 * kTile1;             // one buffer of the three input t
 constexpr int oSTF = 2 * kBufF;               // S^T [d_v][d] bf16
 constexpr int oOSF = oSTF + D1 * D1;          // per-consumer output staging, 32 x 64
 constexpr int kOSF = 32 * 64;
-constexpr int kLdsF = oOSF + 4 * kOSF;
+constexpr int oZF = oOSF + 4 * kOSF;          // the normalized form: z before the tile, [32][128] bf16
+constexpr int kLdsF = oZF + 32 * D1;
 static_assert(kLdsF * 2 <= 160 * 1024, "LDS");
 static_assert(kWaves == 8, "the direct loads split a tile over eight waves");
 
@@ -61,7 +73,38 @@ __device__ __forceinline__ void dma_tile_f(u16 *buf, const u16 *gq, const u16 *g
     dma_rows<D1, TB1>(make_rsrc(gv + t0 * D1, bytes), buf + oVF, D1, wave, lane);
 }
 
+__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+
+// phi = elu + 1 on the chunks of the q and k tiles in `buf` that dma_tile_f's share `share` filled
+// (rows past the sequence stay zero), and the transformed chunks to pq, pk where asked for.  Only the
+// wave that issued those loads may call it, after waiting for them: no other wave touches the chunks.
+__device__ __forceinline__ void phi_share(u16 *buf, const Fwd1Args &p, int64_t base, int64_t t0, int64_t T,
+                                          int share, int lane) {
+    const int64_t bytes = (T - t0) * D1 * 2;
+    u16 *gpq = p.pq ? static_cast<u16 *>(p.pq) + base + t0 * D1 : nullptr;
+    u16 *gpk = p.pk ? static_cast<u16 *>(p.pk) + base + t0 * D1 : nullptr;
+#pragma unroll
+    for (int s = 0; s < kTile1 / (512 * kWaves); ++s) {
+        const int i = share + kWaves * s, c = 64 * i + lane, row = c / (D1 / 8);
+        const int lc = (c % (D1 / 8)) ^ swz<D1>(row);
+        if (t0 + row >= T) continue;
+#pragma unroll
+        for (int tns = 0; tns < 2; ++tns) {
+            u16 *l = buf + (tns ? oKF : oQF) + 8 * c;
+            u32x4 x = *reinterpret_cast<const u32x4 *>(l);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = pack_bf16(elu1(__builtin_bit_cast(float, x[j] << 16)),
+                                 elu1(__builtin_bit_cast(float, x[j] & 0xffff0000u)));
+            *reinterpret_cast<u32x4 *>(l) = x;
+            u16 *g = tns ? gpk : gpq;
+            if (g) bstore16(make_rsrc(g, bytes), (row * D1 + lc * 8) * 2, x);
+        }
+    }
+}
+
 // Producer p: state rows 32p..32p+31 of S (d x d_v), four 32 x 32 blocks (column blocks jb).
+template <int NM>
 __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int pw, int lane) {
     const WalkF w = walk_of(p, chain, seg);
     const int wave = 4 + pw, h = lane >> 5, col = lane & 31;
@@ -94,7 +137,11 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
             const int i = pw * 32 + 8 * (r >> 2) + 4 * h + (r & 3), j = jb * 32 + col;
             sacc[jb][r] = g != nullptr ? g[p.states_t ? (int64_t)j * D1 + i : (int64_t)i * D1 + j] : 0.0f;
         }
-    // the bf16 copy S^T ([d_v][d]): accumulator entries 4q..4q+3 are four consecutive d of one d_v row
+    // the normalized form: this lane's half (positions 8h.. of every 16) of the prefix sum of phi(k) in
+    // state row 32pw + col
+    float zacc = 0.0f;
+    // the bf16 copy S^T ([d_v][d]): accumulator entries 4q..4q+3 are four consecutive d of one d_v row;
+    // and z (fp32), whole in every lane after adding the partner lane's half
     auto write_state = [&]() {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
@@ -104,16 +151,34 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                                  pack_bf16(sacc[jb][4 * q + 2], sacc[jb][4 * q + 3])};
                 lds_write8(smem + oSTF, jb * 32 * D1 + pwq[q], v);
             }
+        if constexpr (NM > 0) {
+            const unsigned int zu = __builtin_bit_cast(unsigned int, zacc);
+            const auto r = __builtin_amdgcn_permlane32_swap(zu, zu, false, false);
+            const float z = __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
+            // z of column 32pw + col in row 0 (rounded to bf16) and row 1 (the remainder) of the z tile;
+            // lanes h = 0 write row 0, h = 1 row 1
+            const u16 zh = __builtin_bit_cast(u16, (__bf16)z);
+            const float zr = z - __builtin_bit_cast(float, (unsigned int)zh << 16);
+            const int dcol = pw * 32 + col;
+            smem[oZF + nat_off<D1>(h, dcol >> 3) + (dcol & 7)] = h == 0 ? zh : __builtin_bit_cast(u16, (__bf16)zr);
+        }
     };
-
     dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, wave, lane);
+    if constexpr (NM > 0) {
+        // the z tile's zero rows 2..31 (rows 0 and 1 come with every copy of the state)
+        const u32x4 zz = {0u, 0u, 0u, 0u};
+        for (int i = (wave - 4) * 64 + lane; i < 30 * D1 / 8; i += 256)
+            *reinterpret_cast<u32x4 *>(smem + oZF + 2 * D1 + 8 * i) = zz;
+    }
     write_state();
     wait_vm();
+    if constexpr (NM == 2) phi_share(smem, p, w.base, w.t0(0), w.T, wave, lane);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
         const bool more = it + 1 < w.ntiles;
         const u16 *cur = smem + (it & 1) * kBufF;
-        if (more) dma_tile_f(smem + ((it + 1) & 1) * kBufF, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
+        u16 *nxt = smem + ((it + 1) & 1) * kBufF;
+        if (more) dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
         // S += K^T V over the tile's 64 positions (the last tile's update only for the final state)
         if (more || final_state) {
             const u16 *sK = cur + oKF, *sV = cur + oVF;
@@ -125,11 +190,19 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                 for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
+                if constexpr (NM > 0) {
+                    // fa: state row 32pw + col of K^T at positions 16x + 8h .. 16x + 8h + 7
+                    const u32x4 u = __builtin_bit_cast(u32x4, fa);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        zacc += __builtin_bit_cast(float, u[j] << 16) + __builtin_bit_cast(float, u[j] & 0xffff0000u);
+                }
             }
         }
-        lds_barrier();   // Y: every consumer is done with S_{b-1}^T
+        lds_barrier();   // Y: every consumer is done with S_{b-1}^T (and z before the tile)
         if (more) write_state();
         wait_vm();
+        if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, wave, lane);
         lds_barrier();   // X: the next tile and S_b^T
     }
     if (final_state) {
@@ -146,6 +219,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
 
 // Consumer c = 2rb + ch: the output unit of row block rb, columns 64ch..64ch+63, staged in the wave's
 // own 4 KiB of LDS and stored as whole 128-byte row pieces at the top of the next tile.
+template <int NM>
 __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
     const WalkF w = walk_of(p, chain, seg);
     const int rb = c >> 1, ch = c & 1;
@@ -181,23 +255,45 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
 
     dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, c, lane);
     wait_vm();
+    if constexpr (NM == 2) phi_share(smem, p, w.base, w.t0(0), w.T, c, lane);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
         const u16 *cur = smem + (it & 1) * kBufF;
-        if (it + 1 < w.ntiles) dma_tile_f(smem + ((it + 1) & 1) * kBufF, gq, gk, gv, w.t0(it + 1), w.T, c, lane);
+        u16 *nxt = smem + ((it + 1) & 1) * kBufF;
+        const bool more = it + 1 < w.ntiles;
+        if (more) dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, c, lane);
         if (it > 0) store(w.t0(it - 1));
         {
             f32x16 oacc[2];
-            unit_products<true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L);
+            if constexpr (NM > 0) {
+                float dpart;
+                unit_products<true, true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L,
+                                                &dpart, smem + oZF);
+                const unsigned int du = __builtin_bit_cast(unsigned int, dpart);
+                const auto r = __builtin_amdgcn_permlane32_swap(du, du, false, false);
+                const float den =
+                    __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
+                const float inv = 1.0f / den;
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[n][e] *= inv;
+                const int64_t t = w.t0(it) + rb * 32 + (lane & 31);
+                if (p.den != nullptr && ch == 0 && lane < 32 && t < w.T) p.den[(int64_t)chain * w.T + t] = den;
+            } else {
+                unit_products<true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L);
+            }
             stage(oacc);
         }
         lds_barrier();   // Y
         wait_vm();
+        if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, c, lane);
         lds_barrier();   // X
     }
     store(w.t0(w.ntiles - 1));
 }
 
+template <int NM>
 __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
     __shared__ __attribute__((aligned(16))) u16 smem[kLdsF];
     // the wave index as a scalar: every branch on a wave's role is uniform
@@ -206,17 +302,23 @@ __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
     const int chain = blockIdx.x / p.nseg;
     if ((int64_t)seg * p.seg_len >= p.T) return;
     if (wave < 4)
-        consumer_f(p, smem, chain, seg, wave, lane);
+        consumer_f<NM>(p, smem, chain, seg, wave, lane);
     else
-        producer_f(p, smem, chain, seg, wave - 4, lane);
+        producer_f<NM>(p, smem, chain, seg, wave - 4, lane);
 }
 
 }  // namespace
 
 hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
-    if (a.seg_len <= 0 || a.seg_len % TB1 != 0) return hipErrorInvalidValue;
+    if (a.seg_len <= 0 || a.seg_len % TB1 != 0 || a.norm < 0 || a.norm > 2) return hipErrorInvalidValue;
+    // the normalized form keeps z per chain from zero: unsplit chains only
+    if (a.norm != 0 && (a.nseg != 1 || a.states != nullptr || a.state_out != nullptr)) return hipErrorInvalidValue;
     const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
-    hipLaunchKernelGGL(fwd1_bf16_kernel, dim3(items), dim3(kTF), 0, s, a);
+    switch (a.norm) {
+        case 0: hipLaunchKernelGGL(fwd1_bf16_kernel<0>, dim3(items), dim3(kTF), 0, s, a); break;
+        case 1: hipLaunchKernelGGL(fwd1_bf16_kernel<1>, dim3(items), dim3(kTF), 0, s, a); break;
+        default: hipLaunchKernelGGL(fwd1_bf16_kernel<2>, dim3(items), dim3(kTF), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

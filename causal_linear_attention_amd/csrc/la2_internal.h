@@ -149,6 +149,11 @@ struct Fwd1Args {
     int states_t;           // 1: the entries are stored transposed ([DV][D])
     int sub, nsub;          // states entry of segment s: state_index(s, sub, nsub, false)
     float *state_out;       // fp32 [chains, D, D]: the state after the last position, or nullptr
+    // the normalized form (norm = 1: identity feature map, 2: elu + 1; 0: the plain scan): each output
+    // row is divided by phi(q_t) . z_t, z_t the prefix sum of phi(k_s); unsplit chains only (nseg = 1)
+    int norm;
+    void *pq, *pk;          // where phi(q), phi(k) are also written (bf16 [chains, T, 128]), or nullptr
+    float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr
 };
 hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s);
 

@@ -94,9 +94,10 @@ __device__ __forceinline__ void lds_write8(u16 *s, int off, const u32x2 &v) {
 // P of one 32 x 32 score block as the B operand of the value products.  Accumulator r of lane
 // (h, col) holds source row 8(r/4) + 4h + r%4 against output row col; pairs (2p, 2p + 1) are rounded
 // to bf16 together.  In the diagonal block the entries on the wrong side of the causal mask are
-// zeroed first (SRC_BEFORE: sources at or before the output row are kept, else at or after).
-template <bool SRC_BEFORE, bool DIAG>
-__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col) {
+// zeroed first (SRC_BEFORE: sources at or before the output row are kept, else at or after).  RS:
+// the lane's kept fp32 scores are also added to *rs (half of the output row's sum over the block).
+template <bool SRC_BEFORE, bool DIAG, bool RS = false>
+__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col, float *rs = nullptr) {
     u32x4 w[2];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -106,6 +107,7 @@ __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int 
             a = (SRC_BEFORE ? dist <= 0 : dist >= 0) ? a : 0.0f;
             b = (SRC_BEFORE ? dist + 1 <= 0 : dist + 1 >= 0) ? b : 0.0f;
         }
+        if constexpr (RS) *rs += a + b;
         w[p >> 2][p & 3] = pack_bf16(a, b);
     }
     pf[0] = __builtin_bit_cast(bf16x8, w[0]);
@@ -114,15 +116,16 @@ __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int 
 
 // The intra-tile contribution of source block u to a unit: scores of the block's 32 source rows
 // against the unit's 32 output rows (B operand bf), then P times the value rows of the block.
-template <bool SRC_BEFORE, bool DIAG>
+template <bool SRC_BEFORE, bool DIAG, bool RS = false>
 __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf)[KS1], const u16 *sA,
-                                            const u16 *sC, int u, const LaneOff &L, int h, int col) {
+                                            const u16 *sC, int u, const LaneOff &L, int h, int col,
+                                            float *rs = nullptr) {
     const f32x16 zero = {};
     f32x16 acc = mfma(rd_plain(sA, u * 32, 0, L), bf[0], zero);
 #pragma unroll
     for (int ks = 1; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
     bf16x8 pf[2];
-    block_p<SRC_BEFORE, DIAG>(acc, pf, h, col);
+    block_p<SRC_BEFORE, DIAG, RS>(acc, pf, h, col, rs);
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -137,13 +140,29 @@ __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf
 // else at or after) times the value tile sC.  The inter product always runs (a state that is still
 // zero contributes zeros), so the first contraction step starts from a zero accumulator operand
 // instead of cleared registers.
-template <bool SRC_BEFORE, bool INTER_PLAIN>
+// DEN (the normalized form): *den = the lane's half of the output row's denominator: its half of the
+// row's kept fp32 scores, plus (lanes 0..31) the product of the sB row with a vector z (the prefix sum
+// of the source rows before the tile) that sZ holds as a [32][128] tile whose row 0 is z rounded to
+// bf16, row 1 the rounding's remainder rounded to bf16, and the other rows zero; the partner lane
+// (lane ^ 32) holds the other half of the scores.
+template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false>
 __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, const u16 *sA, const u16 *sC,
-                                              const u16 *sSt, int orow, int ch, int lane, const LaneOff &L) {
+                                              const u16 *sSt, int orow, int ch, int lane, const LaneOff &L,
+                                              float *den = nullptr, const u16 *sZ = nullptr) {
     const int h = lane >> 5, col = lane & 31;
     bf16x8 bf[KS1];
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks) bf[ks] = rd_plain(sB, orow * 32, ks, L);
+    float dd = 0.0f;
+    if constexpr (DEN) {
+        // rows 0 and 1 of the product land in accumulator entries 0 and 1 of lanes 0..31 (h = 0); the
+        // entries of lanes 32..63 are rows 4 and 5, zero
+        const f32x16 zero = {};
+        f32x16 dacc = mfma(rd_plain(sZ, 0, 0, L), bf[0], zero);
+#pragma unroll
+        for (int ks = 1; ks < KS1; ++ks) dacc = mfma(rd_plain(sZ, 0, ks, L), bf[ks], dacc);
+        dd = dacc[0] + dacc[1];
+    }
     // fully unrolled: bf[] must be indexed by constants (a runtime index into a register array is
     // lowered to chains of selects)
     const f32x16 zero = {};
@@ -157,8 +176,9 @@ __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, 
     // intra-tile: the whole source block before (SRC_BEFORE) or after the diagonal, where there is one,
     // then the diagonal block
     if (SRC_BEFORE ? orow == 1 : orow == 0)
-        intra_block<SRC_BEFORE, false>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col);
-    intra_block<SRC_BEFORE, true>(oacc, bf, sA, sC, orow, L, h, col);
+        intra_block<SRC_BEFORE, false, DEN>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col, &dd);
+    intra_block<SRC_BEFORE, true, DEN>(oacc, bf, sA, sC, orow, L, h, col, &dd);
+    if constexpr (DEN) *den = dd;
 }
 
 }  // namespace t64

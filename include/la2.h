@@ -170,6 +170,13 @@ int la2_decode_step(const void *q, const void *k, const void *v, const float *de
  *   the numerator then runs through the same tiled scan as la2_forward (on
  *   phi(q), phi(k) rounded to `dtype`), each output row divided by its
  *   denominator in fp32 and rounded to `dtype` once when it is stored.
+ *   Except in bf16 at d = d_v = 128 without decay, where the chains fill the
+ *   GPU unsplit: there one launch reads q, k, v once and writes o, applying
+ *   phi to the tiles in on-chip memory; numerator and denominator both come
+ *   from phi(q), phi(k) rounded to bf16 (the denominator's sums in fp32), and
+ *   with a workspace of la2_normalized_workspace_bytes(..., 1) bytes it also
+ *   writes phi(q), phi(k) and the denominators there for
+ *   la2_backward_normalized_saved.
  *   Other arguments as in la2_forward; workspace: at least
  *   la2_normalized_workspace_bytes(..., 0) bytes (phi(q) and phi(k) for
  *   LA2_PHI_ELU1, one fp32 denominator per position, per-segment sums and

@@ -30,7 +30,9 @@ extern "C" {
  *   two_pass_backward: non-zero runs la2_backward_saved without decay (bf16, d = d_v = 128) as a dQ
  *                  pass and a dK/dV pass instead of the one-pass backward
  *   legacy_forward: non-zero runs the forward-direction bf16 output scans without decay at
- *                  d = d_v = 128 on the eight-wave scan kernel instead of the producer/consumer one
+ *                  d = d_v = 128 on the eight-wave scan kernel instead of the producer/consumer one,
+ *                  and la2_forward_normalized there as its denominator pass and numerator scan
+ *                  instead of the one fused launch
  * Returns LA2_OK. */
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv,
                       int64_t norm_segment, int two_pass_backward, int legacy_forward);

@@ -65,7 +65,14 @@ CASES = [
     (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
     (3, 1, 1, 64, 64, "bf16", 64, "heads", "elu1"),        # one position: o = v
     (2, 2, 65, 128, 64, "f32", 16, 0.5, "elu1"),           # strong decay
+] + [
+    # bf16, d = d_v = 128, no decay, chains the plan leaves unsplit: one fused launch (phi on the tiles)
+    (4, 64, 300, 128, 128, "bf16", 128, "none", "elu1"),   # ragged last tile
+    (16, 16, 1, 128, 128, "bf16", 128, "none", "elu1"),    # one position: o = v
+    (2, 128, 130, 128, 128, "bf16", 64, "none", "identity"),
+    (1, 256, 64, 128, 128, "bf16", 256, "none", "elu1"),   # one whole tile
 ]
+FUSED = CASES[-4:]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c))
@@ -79,6 +86,29 @@ def test_normalized_forced_segments(seg):
     with binding.plan_override(norm_segment=seg):
         run_case(1, 2, 1000, 128, 128, "bf16", 128, "heads", "elu1", seed=7)
         run_case(1, 2, 1000, 64, 64, "f32", 64, "heads", "elu1", seed=8)
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "-".join(str(v) for v in c))
+def test_fused_normalized_against_two_pass(case):
+    """The fused launch against the denominator pass + numerator scan it replaces (forced through the
+    test build): both within the bar of the oracle and of each other (their denominators differ in
+    rounding: phi in bf16 against phi in fp32); and with the backward-sized workspace, where it also
+    writes phi(q), phi(k) and the denominators, bitwise the same o."""
+    B, H, T, d, dv, dtype, block, decay, fmap = case
+    o = run_case(*case, seed=211 + T)
+    with binding.plan_override(legacy_forward=True):
+        o_old = run_case(*case, seed=211 + T)
+    d_ = rel_err(f64(o), f64(o_old))
+    print(case, f"fused vs two passes {d_:.2e}", flush=True)
+    assert d_ <= TOL[dtype]
+    x = inputs.make_random(B, H, T, d, dv, dtype=dtype, seed=211 + T, decay=decay, backward=False)
+    if fmap == "identity":
+        x["q"], x["k"] = positive(x["q"]), positive(x["k"])
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    ws = la2.normalized_workspace_for(q, v, fmap, block, backward=True)
+    o_ws = la2.forward_normalized(q, k, v, None, block, fmap, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ws, o)
 
 
 def test_normalized_ones_values_give_ones():
@@ -164,6 +194,8 @@ BN_CASES = [
     (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
     (3, 1, 1, 64, 64, "bf16", 64, "heads", "elu1"),        # one position
     (2, 2, 65, 128, 64, "f32", 16, 0.5, "elu1"),           # strong decay
+    (4, 64, 300, 128, 128, "bf16", 128, "none", "elu1"),   # the fused forward's phi and denominators
+    (2, 128, 130, 128, 128, "bf16", 64, "none", "identity"),
 ]
 
 
@@ -203,6 +235,8 @@ SAVED_CASES = [
     (16, 16, 200, 128, 64, "bf16", 128, "none", "elu1"),   # 256 chains: nothing split
     (1, 3, 777, 64, 64, "f32", 32, "heads", "elu1"),
     (1, 4, 513, 128, 128, "bf16", 256, "heads", "identity"),
+    (4, 64, 300, 128, 128, "bf16", 128, "none", "elu1"),   # phi(q), phi(k), den from the fused forward
+    (2, 128, 130, 128, 128, "bf16", 64, "none", "identity"),
 ]
 
 
