@@ -288,9 +288,10 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                     }
                     if (ok) {
                         const float dn = p.den[row0 + t], av = p.arow[row0 + t];
-                        const double lam_d = (double)lam;
+                        // ell_t = sum_{s<=t} lam^(t-s); 1 - lam >= 0.004 for every head's decay, so fp32 holds
+                        // it to ~1e-6 relative
                         const float ell = l2 == 0.0f ? (float)(t + 1)
-                                                     : (float)((1.0 - pow(lam_d, (double)(t + 1))) / (1.0 - lam_d));
+                                                     : (1.0f - exp2f((float)(t + 1) * l2)) / (1.0f - lam);
                         const float rd = 1.0f / dn;
                         const float c = (sg * av + pu) * rd, G = (pz * av - ell * pu) * rd;
                         float gr[8];
