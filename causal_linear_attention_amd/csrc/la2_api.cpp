@@ -225,8 +225,8 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
     const int DV = slice_width(dtype, args.DVT, pl.narrow);
     if (dtype == LA2_BF16 && mode == la2::Mode::StateOnly) return la2::launch_state_bf16(args, D, DV, pl.TB, dir, s);
     if (dtype == LA2_BF16 && mode == la2::Mode::Output && dir == la2::Dir::Forward && !forced().legacy_forward &&
-        D == 128 && DV == 128 && args.nslice == 1 && !args.decay && !args.den && !args.has_init) {
-        // without decay at d = d_v = 128: the producer/consumer scan over 64-position tiles
+        D == 128 && DV == 128 && args.nslice == 1 && !args.den && !args.has_init) {
+        // at d = d_v = 128: the producer/consumer scan over 64-position tiles
         la2::Fwd1Args f{};
         f.q = args.a;
         f.k = args.b;
@@ -241,6 +241,8 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
         f.sub = args.sub;
         f.nsub = args.nsub;
         f.state_out = args.state_out;
+        f.decay = args.decay;
+        f.H = args.H;
         return la2::launch_fwd1_bf16(f, s);
     }
     return dtype == LA2_BF16 ? la2::launch_scan_bf16(args, D, DV, pl.TB, dir, s)

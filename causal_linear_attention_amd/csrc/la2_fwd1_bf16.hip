@@ -5,6 +5,9 @@
 // 64 positions (local rows t = outputs, s = sources)
 //   O_b = mask(Q_b K_b^T) V_b + Q_b S_{b-1}    (intra: sources s <= t; inter: the state before the tile)
 //   S_b = S_{b-1} + K_b^T V_b                  (the state update on the unmasked tile)
+// and with a per-head decay lam (the recurrence S_t = lam S_{t-1} + k_t v_t^T):
+//   O_b[t] = sum_{s<=t} lam^(t-s) (q_t . k_s) v_s + lam^(t+1) q_t S_{b-1},
+//   S_b = lam^64 S_{b-1} + sum_j lam^(63-j) k_j v_j^T.
 // and, with a key/value pair of roles (b, c) and a query role a, the same scan serves the dQ pass of
 // the two-pass backward and the scan U of the normalized backward (its state read transposed).
 //
@@ -103,8 +106,12 @@ __device__ __forceinline__ void phi_share(u16 *buf, const Fwd1Args &p, int64_t b
     }
 }
 
+__device__ __forceinline__ float chain_l2(const Fwd1Args &p, int chain) {
+    return p.decay != nullptr ? log2f(p.decay[chain % p.H]) : 0.0f;
+}
+
 // Producer p: state rows 32p..32p+31 of S (d x d_v), four 32 x 32 blocks (column blocks jb).
-template <int NM>
+template <int NM, bool DEC>
 __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int pw, int lane) {
     const WalkF w = walk_of(p, chain, seg);
     const int wave = 4 + pw, h = lane >> 5, col = lane & 31;
@@ -140,6 +147,17 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
     // the normalized form: this lane's half (positions 8h.. of every 16) of the prefix sum of phi(k) in
     // state row 32pw + col
     float zacc = 0.0f;
+    // a decay: lam^64 per tile on the state, and lam^(63 - j) on the K^T operand's position j =
+    // 16x + 8h + e (element e of the fragment of step x)
+    float wk[DEC ? TB1 / 16 : 1][8], lam64 = 1.0f;
+    const float l2 = DEC ? chain_l2(p, chain) : 0.0f;
+    if constexpr (DEC) {
+        lam64 = exp2f(64.0f * l2);
+#pragma unroll
+        for (int x = 0; x < TB1 / 16; ++x)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wk[x][e] = exp2f(l2 * (float)(TB1 - 1 - (16 * x + 8 * h + e)));
+    }
     // the bf16 copy S^T ([d_v][d]): accumulator entries 4q..4q+3 are four consecutive d of one d_v row;
     // and z (fp32), whole in every lane after adding the partner lane's half
     auto write_state = [&]() {
@@ -182,9 +200,35 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         // S += K^T V over the tile's 64 positions (the last tile's update only for the final state)
         if (more || final_state) {
             const u16 *sK = cur + oKF, *sV = cur + oVF;
+            if (DEC && !more) {
+                // the final state's tile: its n real rows, lam^n on the state and lam^(n - 1 - j) on row j
+                const int n = (int)min((int64_t)TB1, w.T - w.t0(it));
+                lam64 = exp2f(l2 * (float)n);
+#pragma unroll
+                for (int x = 0; x < TB1 / 16; ++x)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 16 * x + 8 * h + e;
+                        wk[x][e] = j < n ? exp2f(l2 * (float)(n - 1 - j)) : 0.0f;
+                    }
+            }
+            if constexpr (DEC) {
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[jb][r] *= lam64;
+            }
 #pragma unroll
             for (int x = 0; x < TB1 / 16; ++x) {
-                const bf16x8 fa = rd_tr(sK, 16 * x, trk);
+                bf16x8 fa = rd_tr(sK, 16 * x, trk);
+                if constexpr (DEC) {
+                    u32x4 u = __builtin_bit_cast(u32x4, fa);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        u[j] = pack_bf16(__builtin_bit_cast(float, u[j] << 16) * wk[x][2 * j],
+                                         __builtin_bit_cast(float, u[j] & 0xffff0000u) * wk[x][2 * j + 1]);
+                    fa = __builtin_bit_cast(bf16x8, u);
+                }
                 bf16x8 fc[4];
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
@@ -219,11 +263,13 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
 
 // Consumer c = 2rb + ch: the output unit of row block rb, columns 64ch..64ch+63, staged in the wave's
 // own 4 KiB of LDS and stored as whole 128-byte row pieces at the top of the next tile.
-template <int NM>
+template <int NM, bool DEC>
 __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
     const WalkF w = walk_of(p, chain, seg);
     const int rb = c >> 1, ch = c & 1;
     const LaneOff L = lane_offsets(lane, ch);
+    DecayW dwt = {};   // read only with a decay
+    if constexpr (DEC) dwt = decay_weights(chain_l2(p, chain), rb, lane);
     const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
     const u16 *gv = static_cast<const u16 *>(p.v) + w.base;
     u16 *gy = static_cast<u16 *>(p.y) + w.base;
@@ -267,8 +313,8 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
             f32x16 oacc[2];
             if constexpr (NM > 0) {
                 float dpart;
-                unit_products<true, true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L,
-                                                &dpart, smem + oZF);
+                unit_products<true, true, true, false>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
+                                                       lane, L, &dpart, smem + oZF, dwt);
                 const unsigned int du = __builtin_bit_cast(unsigned int, dpart);
                 const auto r = __builtin_amdgcn_permlane32_swap(du, du, false, false);
                 const float den =
@@ -281,7 +327,8 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
                 const int64_t t = w.t0(it) + rb * 32 + (lane & 31);
                 if (p.den != nullptr && ch == 0 && lane < 32 && t < w.T) p.den[(int64_t)chain * w.T + t] = den;
             } else {
-                unit_products<true, true>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch, lane, L);
+                unit_products<true, true, false, DEC>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
+                                                      lane, L, nullptr, nullptr, dwt);
             }
             stage(oacc);
         }
@@ -293,7 +340,7 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
     store(w.t0(w.ntiles - 1));
 }
 
-template <int NM>
+template <int NM, bool DEC>
 __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
     __shared__ __attribute__((aligned(16))) u16 smem[kLdsF];
     // the wave index as a scalar: every branch on a wave's role is uniform
@@ -302,9 +349,9 @@ __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
     const int chain = blockIdx.x / p.nseg;
     if ((int64_t)seg * p.seg_len >= p.T) return;
     if (wave < 4)
-        consumer_f<NM>(p, smem, chain, seg, wave, lane);
+        consumer_f<NM, DEC>(p, smem, chain, seg, wave, lane);
     else
-        producer_f<NM>(p, smem, chain, seg, wave - 4, lane);
+        producer_f<NM, DEC>(p, smem, chain, seg, wave - 4, lane);
 }
 
 }  // namespace
@@ -313,11 +360,17 @@ hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
     if (a.seg_len <= 0 || a.seg_len % TB1 != 0 || a.norm < 0 || a.norm > 2) return hipErrorInvalidValue;
     // the normalized form keeps z per chain from zero: unsplit chains only
     if (a.norm != 0 && (a.nseg != 1 || a.states != nullptr || a.state_out != nullptr)) return hipErrorInvalidValue;
+    // a decay: the plain scan only
+    if (a.decay != nullptr && (a.norm != 0 || a.H <= 0)) return hipErrorInvalidValue;
     const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
+    if (a.decay != nullptr) {
+        hipLaunchKernelGGL((fwd1_bf16_kernel<0, true>), dim3(items), dim3(kTF), 0, s, a);
+        return hipGetLastError();
+    }
     switch (a.norm) {
-        case 0: hipLaunchKernelGGL(fwd1_bf16_kernel<0>, dim3(items), dim3(kTF), 0, s, a); break;
-        case 1: hipLaunchKernelGGL(fwd1_bf16_kernel<1>, dim3(items), dim3(kTF), 0, s, a); break;
-        default: hipLaunchKernelGGL(fwd1_bf16_kernel<2>, dim3(items), dim3(kTF), 0, s, a); break;
+        case 0: hipLaunchKernelGGL((fwd1_bf16_kernel<0, false>), dim3(items), dim3(kTF), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((fwd1_bf16_kernel<1, false>), dim3(items), dim3(kTF), 0, s, a); break;
+        default: hipLaunchKernelGGL((fwd1_bf16_kernel<2, false>), dim3(items), dim3(kTF), 0, s, a); break;
     }
     return hipGetLastError();
 }

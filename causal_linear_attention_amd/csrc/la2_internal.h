@@ -154,6 +154,8 @@ struct Fwd1Args {
     int norm;
     void *pq, *pk;          // where phi(q), phi(k) are also written (bf16 [chains, T, 128]), or nullptr
     float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr
+    const float *decay;     // per-head decay lam ([H] fp32, chain c is head c % H), or nullptr for lam = 1;
+    int H;                  //   the plain scan only
 };
 hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s);
 

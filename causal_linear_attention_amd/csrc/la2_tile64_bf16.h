@@ -96,12 +96,18 @@ __device__ __forceinline__ void lds_write8(u16 *s, int off, const u32x2 &v) {
 // to bf16 together.  In the diagonal block the entries on the wrong side of the causal mask are
 // zeroed first (SRC_BEFORE: sources at or before the output row are kept, else at or after).  RS:
 // the lane's kept fp32 scores are also added to *rs (half of the output row's sum over the block).
-template <bool SRC_BEFORE, bool DIAG, bool RS = false>
-__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col, float *rs = nullptr) {
+// DEC (a decay): each score is multiplied by wt[r] first (decay_weights below).
+template <bool SRC_BEFORE, bool DIAG, bool RS = false, bool DEC = false>
+__device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col, float *rs,
+                                        const float (&wt)[16]) {
     u32x4 w[2];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         float a = acc[2 * p], b = acc[2 * p + 1];
+        if constexpr (DEC) {
+            a *= wt[2 * p];
+            b *= wt[2 * p + 1];
+        }
         if (DIAG) {
             const int dist = 4 * h - col + 8 * (p >> 1) + 2 * (p & 1);   // source - output of entry 2p
             a = (SRC_BEFORE ? dist <= 0 : dist >= 0) ? a : 0.0f;
@@ -116,20 +122,42 @@ __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int 
 
 // The intra-tile contribution of source block u to a unit: scores of the block's 32 source rows
 // against the unit's 32 output rows (B operand bf), then P times the value rows of the block.
-template <bool SRC_BEFORE, bool DIAG, bool RS = false>
+template <bool SRC_BEFORE, bool DIAG, bool RS, bool DEC>
 __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf)[KS1], const u16 *sA,
-                                            const u16 *sC, int u, const LaneOff &L, int h, int col,
-                                            float *rs = nullptr) {
+                                            const u16 *sC, int u, const LaneOff &L, int h, int col, float *rs,
+                                            const float (&wt)[16]) {
     const f32x16 zero = {};
     f32x16 acc = mfma(rd_plain(sA, u * 32, 0, L), bf[0], zero);
 #pragma unroll
     for (int ks = 1; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
     bf16x8 pf[2];
-    block_p<SRC_BEFORE, DIAG, RS>(acc, pf, h, col, rs);
+    block_p<SRC_BEFORE, DIAG, RS, DEC>(acc, pf, h, col, rs, wt);
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int n = 0; n < 2; ++n) oacc[n] = mfma(rd_tr(sC, u * 32 + 16 * x, L.trc[1][n]), pf[x], oacc[n]);
+}
+
+// The weights of a decay lam = 2^l2 for the forward direction, per lane (h, col) of a unit in row block
+// orow: wd[r] = lam^(t - s) for accumulator entry r of the diagonal score block where s <= t, else 0
+// (t = col, s = 8(r/4) + 4h + r%4 within the block); wf[r] = lam^(t - s) for the full block before it
+// (t - s = 32 + col - s, row block 1 only); *wi = lam^(orow*32 + col + 1), the inter product's weight
+// (the state is the one before the tile).  Every exponent is non-negative.
+struct DecayW {
+    float wd[16], wf[16], wi;
+};
+
+__device__ __forceinline__ DecayW decay_weights(float l2, int orow, int lane) {
+    const int h = lane >> 5, col = lane & 31;
+    DecayW w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int s = 8 * (r >> 2) + 4 * h + (r & 3);
+        w.wd[r] = s <= col ? exp2f(l2 * (float)(col - s)) : 0.0f;
+        w.wf[r] = orow == 1 ? exp2f(l2 * (float)(32 + col - s)) : 0.0f;
+    }
+    w.wi = exp2f(l2 * (float)(orow * 32 + col + 1));
+    return w;
 }
 
 // One output unit of a wave: columns 64ch..64ch+63 (two 32-column blocks) of the output rows in block
@@ -145,10 +173,11 @@ __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf
 // of the source rows before the tile) that sZ holds as a [32][128] tile whose row 0 is z rounded to
 // bf16, row 1 the rounding's remainder rounded to bf16, and the other rows zero; the partner lane
 // (lane ^ 32) holds the other half of the scores.
-template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false>
+// DEC (a decay, SRC_BEFORE only): the inter product is weighted by dw.wi and the scores by dw.wd, wf.
+template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false, bool DEC = false>
 __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, const u16 *sA, const u16 *sC,
                                               const u16 *sSt, int orow, int ch, int lane, const LaneOff &L,
-                                              float *den = nullptr, const u16 *sZ = nullptr) {
+                                              float *den, const u16 *sZ, const DecayW &dw) {
     const int h = lane >> 5, col = lane & 31;
     bf16x8 bf[KS1];
 #pragma unroll
@@ -173,12 +202,28 @@ __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, 
             const bf16x8 a = INTER_PLAIN ? rd_plain(sSt, (2 * ch + n) * 32, ks, L) : rd_tr(sSt, 16 * ks, L.trc[0][n]);
             oacc[n] = mfma(a, bf[ks], ks == 0 ? zero : oacc[n]);
         }
+    static_assert(!DEC || SRC_BEFORE, "decay weights are for the forward direction");
+    if constexpr (DEC) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[n][e] *= dw.wi;
+    }
     // intra-tile: the whole source block before (SRC_BEFORE) or after the diagonal, where there is one,
     // then the diagonal block
     if (SRC_BEFORE ? orow == 1 : orow == 0)
-        intra_block<SRC_BEFORE, false, DEN>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col, &dd);
-    intra_block<SRC_BEFORE, true, DEN>(oacc, bf, sA, sC, orow, L, h, col, &dd);
+        intra_block<SRC_BEFORE, false, DEN, DEC>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col, &dd, dw.wf);
+    intra_block<SRC_BEFORE, true, DEN, DEC>(oacc, bf, sA, sC, orow, L, h, col, &dd, dw.wd);
     if constexpr (DEN) *den = dd;
+}
+
+// The unit without a denominator or a decay.
+template <bool SRC_BEFORE, bool INTER_PLAIN>
+__device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, const u16 *sA, const u16 *sC,
+                                              const u16 *sSt, int orow, int ch, int lane, const LaneOff &L) {
+    const DecayW none = {};   // not read
+    unit_products<SRC_BEFORE, INTER_PLAIN, false, false>(oacc, sB, sA, sC, sSt, orow, ch, lane, L, nullptr, nullptr,
+                                                         none);
 }
 
 }  // namespace t64

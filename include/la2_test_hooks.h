@@ -29,8 +29,8 @@ extern "C" {
  *   norm_segment:  positions per segment of the normalized form's denominator scans
  *   two_pass_backward: non-zero runs la2_backward_saved without decay (bf16, d = d_v = 128) as a dQ
  *                  pass and a dK/dV pass instead of the one-pass backward
- *   legacy_forward: non-zero runs the forward-direction bf16 output scans without decay at
- *                  d = d_v = 128 on the eight-wave scan kernel instead of the producer/consumer one,
+ *   legacy_forward: non-zero runs the forward-direction bf16 output scans at d = d_v = 128
+ *                  on the eight-wave scan kernel instead of the producer/consumer one,
  *                  and la2_forward_normalized there as its denominator pass and numerator scan
  *                  instead of the one fused launch
  * Returns LA2_OK. */
