@@ -607,9 +607,11 @@ bool fused_normalized(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, in
     return pl.nseg == 1 && slice_width(dtype, (int)dv, pl.narrow) == dv;
 }
 
-// o, and where given phi(q), phi(k) (elu + 1 only) and the denominators, of the fused normalized forward.
+// o, and where given phi(q), phi(k) (elu + 1 only), the denominators and the sums of phi(k) over the
+// denominator plan's segments (msum, for the bf16 backward's mean), of the fused normalized forward.
 hipError_t launch_fused_normalized(const void *q, const void *k, const void *v, void *o, void *pq, void *pk,
-                                   float *den, int64_t chains, int64_t T, int feature_map, hipStream_t s) {
+                                   float *den, float *msum, int64_t msum_seg, int64_t chains, int64_t T,
+                                   int feature_map, hipStream_t s) {
     la2::Fwd1Args f{};
     f.q = q;
     f.k = k;
@@ -624,6 +626,8 @@ hipError_t launch_fused_normalized(const void *q, const void *k, const void *v, 
     f.pq = pq;
     f.pk = pk;
     f.den = den;
+    f.msum = msum;
+    f.msum_seg = msum_seg;
     return la2::launch_fwd1_bf16(f, s);
 }
 
@@ -669,14 +673,16 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
     const int64_t chains = B * H;
     // bf16 at d = d_v = 128 without decay, chains the plan does not split: one launch applies phi to
     // the tiles and forms numerator and denominator together.  Given room for the backward it also
-    // leaves phi(q), phi(k) and the denominators where la2_backward_normalized_saved reads them, and
-    // (denominator segments of split chains) each segment's sum of phi(k), which the bf16 dq carries.
+    // leaves phi(q), phi(k), the denominators and each denominator segment's plain sum of phi(k) (the
+    // bf16 backward's mean) where la2_backward_normalized_saved reads them, and (denominator segments of
+    // split chains) each segment's sum of phi(k), which the bf16 dq carries.
     if (fused_normalized(B, H, T, d, d_v, block, dtype, decay)) {
-        const bool for_bwd =
-            workspace && workspace_bytes >= norm_layout(B, H, T, d, d_v, feature_map, block, dtype, true).total;
+        const NormLayout LB = norm_layout(B, H, T, d, d_v, feature_map, block, dtype, true);
+        const bool for_bwd = workspace && workspace_bytes >= LB.total;
         if (launch_fused_normalized(q, k, v, o, for_bwd && L.phi ? ws : nullptr, for_bwd && L.phi ? ws + L.phi : nullptr,
-                                    for_bwd ? reinterpret_cast<float *>(ws + L.den_off) : nullptr, chains, T,
-                                    feature_map, s) != hipSuccess)
+                                    for_bwd ? reinterpret_cast<float *>(ws + L.den_off) : nullptr,
+                                    for_bwd ? reinterpret_cast<float *>(ws + LB.m_off) : nullptr, LB.dp.seg_len, chains,
+                                    T, feature_map, s) != hipSuccess)
             return LA2_ERR_HIP;
         if (for_bwd && L.dp.nseg > 1 &&
             la2::launch_vscan(den_args(q, k, decay, ws, L, H, T, chains), (int)d, dtype, feature_map, kVZSeg, s) !=
@@ -885,7 +891,8 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
     //    (overwritten next)
     if (!saved) {
         if (fused_normalized(B, H, T, d, d_v, block, dtype, decay)) {
-            if (launch_fused_normalized(q, k, v, dn, a.pq, a.pk, a.den, chains, T, feature_map, s) != hipSuccess ||
+            if (launch_fused_normalized(q, k, v, dn, a.pq, a.pk, a.den, reinterpret_cast<float *>(ws + L.m_off),
+                                        L.dp.seg_len, chains, T, feature_map, s) != hipSuccess ||
                 (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVZSeg, s) != hipSuccess))
                 return LA2_ERR_HIP;
         } else {
@@ -904,7 +911,10 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
         la2::DenArgs c = a;
         c.msum = reinterpret_cast<float *>(ws + L.m_off);
         c.kap = ws + L.kap_off;
-        if (la2::launch_vscan(c, (int)d, dtype, feature_map, kVMean, s) != hipSuccess ||
+        // the segment sums of phi(k) for its mean: left by the forward where it is one fused launch (any
+        // constant m makes the rewrite exact, so they may come from phi(k) rounded to bf16)
+        if ((!fused_normalized(B, H, T, d, d_v, block, dtype, decay) &&
+             la2::launch_vscan(c, (int)d, dtype, feature_map, kVMean, s) != hipSuccess) ||
             la2::launch_vscan(c, (int)d, dtype, feature_map, kVKappa, s) != hipSuccess)
             return LA2_ERR_HIP;
         // a_t = dout_t . Vbar_t: the denominator scan with (query, key) = (dout, v) and the identity map

@@ -145,8 +145,14 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
             sacc[jb][r] = g != nullptr ? g[p.states_t ? (int64_t)j * D1 + i : (int64_t)i * D1 + j] : 0.0f;
         }
     // the normalized form: this lane's half (positions 8h.. of every 16) of the prefix sum of phi(k) in
-    // state row 32pw + col
-    float zacc = 0.0f;
+    // state row 32pw + col; and the whole sum where the last segment sum was written
+    float zacc = 0.0f, zmark = 0.0f;
+    auto z_whole = [&]() {
+        const unsigned int zu = __builtin_bit_cast(unsigned int, zacc);
+        const auto r = __builtin_amdgcn_permlane32_swap(zu, zu, false, false);
+        return __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
+    };
+    const bool sums = NM > 0 && p.msum != nullptr;
     // a decay: lam^64 per tile on the state, and lam^(63 - j) on the K^T operand's position j =
     // 16x + 8h + e (element e of the fragment of step x)
     float wk[DEC ? TB1 / 16 : 1][8], lam64 = 1.0f;
@@ -170,9 +176,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                 lds_write8(smem + oSTF, jb * 32 * D1 + pwq[q], v);
             }
         if constexpr (NM > 0) {
-            const unsigned int zu = __builtin_bit_cast(unsigned int, zacc);
-            const auto r = __builtin_amdgcn_permlane32_swap(zu, zu, false, false);
-            const float z = __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
+            const float z = z_whole();
             // z of column 32pw + col in row 0 (rounded to bf16) and row 1 (the remainder) of the z tile;
             // lanes h = 0 write row 0, h = 1 row 1
             const u16 zh = __builtin_bit_cast(u16, (__bf16)z);
@@ -197,8 +201,9 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         const u16 *cur = smem + (it & 1) * kBufF;
         u16 *nxt = smem + ((it + 1) & 1) * kBufF;
         if (more) dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
-        // S += K^T V over the tile's 64 positions (the last tile's update only for the final state)
-        if (more || final_state) {
+        // S += K^T V over the tile's 64 positions (the last tile's update only for the final state or the
+        // segment sums of phi(k))
+        if (more || final_state || sums) {
             const u16 *sK = cur + oKF, *sV = cur + oVF;
             if (DEC && !more) {
                 // the final state's tile: its n real rows, lam^n on the state and lam^(n - 1 - j) on row j
@@ -241,6 +246,16 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                     for (int j = 0; j < 4; ++j)
                         zacc += __builtin_bit_cast(float, u[j] << 16) + __builtin_bit_cast(float, u[j] & 0xffff0000u);
                 }
+            }
+        }
+        if constexpr (NM > 0) {
+            // the sum of phi(k) over a segment of msum_seg positions, written at its last tile
+            const int64_t t_end = w.t0(it) + TB1;
+            if (sums && (!more || t_end % p.msum_seg == 0)) {
+                const float z = z_whole();
+                const int64_t nms = (w.T + p.msum_seg - 1) / p.msum_seg, ms = (t_end - 1) / p.msum_seg;
+                if (h == 0) p.msum[((int64_t)chain * nms + ms) * D1 + pw * 32 + col] = z - zmark;
+                zmark = z;
             }
         }
         lds_barrier();   // Y: every consumer is done with S_{b-1}^T (and z before the tile)
@@ -358,6 +373,7 @@ __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
 
 hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
     if (a.seg_len <= 0 || a.seg_len % TB1 != 0 || a.norm < 0 || a.norm > 2) return hipErrorInvalidValue;
+    if (a.msum != nullptr && (a.norm == 0 || a.msum_seg <= 0 || a.msum_seg % TB1 != 0)) return hipErrorInvalidValue;
     // the normalized form keeps z per chain from zero: unsplit chains only
     if (a.norm != 0 && (a.nseg != 1 || a.states != nullptr || a.state_out != nullptr)) return hipErrorInvalidValue;
     // a decay: the plain scan only

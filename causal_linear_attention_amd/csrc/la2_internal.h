@@ -154,6 +154,8 @@ struct Fwd1Args {
     int norm;
     void *pq, *pk;          // where phi(q), phi(k) are also written (bf16 [chains, T, 128]), or nullptr
     float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr
+    float *msum;            // where each msum_seg-position segment's sum of phi(k) is also written (fp32
+    int64_t msum_seg;       //   [chains, ceil(T / msum_seg), 128]; msum_seg a multiple of 64), or nullptr
     const float *decay;     // per-head decay lam ([H] fp32, chain c is head c % H), or nullptr for lam = 1;
     int H;                  //   the plain scan only
 };
