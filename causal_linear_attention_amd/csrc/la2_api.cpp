@@ -911,11 +911,12 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
         la2::DenArgs c = a;
         c.msum = reinterpret_cast<float *>(ws + L.m_off);
         c.kap = ws + L.kap_off;
-        // the segment sums of phi(k) for its mean: left by the forward where it is one fused launch (any
-        // constant m makes the rewrite exact, so they may come from phi(k) rounded to bf16)
-        if ((!fused_normalized(B, H, T, d, d_v, block, dtype, decay) &&
-             la2::launch_vscan(c, (int)d, dtype, feature_map, kVMean, s) != hipSuccess) ||
-            la2::launch_vscan(c, (int)d, dtype, feature_map, kVKappa, s) != hipSuccess)
+        // where the forward is one fused launch: the segment sums of phi(k) for its mean are the
+        // forward's (any constant m makes the rewrite exact, so they may come from phi(k) rounded to
+        // bf16), and U's scan forms kap = phi(k) - m from k on chip (its chains are unsplit too)
+        const bool fused = fused_normalized(B, H, T, d, d_v, block, dtype, decay);
+        if (!fused && (la2::launch_vscan(c, (int)d, dtype, feature_map, kVMean, s) != hipSuccess ||
+                       la2::launch_vscan(c, (int)d, dtype, feature_map, kVKappa, s) != hipSuccess))
             return LA2_ERR_HIP;
         // a_t = dout_t . Vbar_t: the denominator scan with (query, key) = (dout, v) and the identity map
         la2::DenArgs va = c;
@@ -929,14 +930,31 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
             return LA2_ERR_HIP;
         // U = the forward scan with (query, key, value) = (dout, v, phi(k) - m), as the dQ pass of the
         // plain backward: its state is (sum kap v^T)^T
-        const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
-        void *uws = L.us_bytes ? ws + L.us_off : nullptr;
-        if (pl.nseg > 1 && (st = segment_states(c.kap, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype,
-                                                la2::Dir::Forward, uws, s)) != LA2_OK)
-            return st;
-        if ((st = output_scan(dout, v, c.kap, ws + L.u_off, decay, chains, H, T, (int)d_v, (int)d, pl, dtype,
-                              la2::Dir::Forward, uws, 1, s)) != LA2_OK)
-            return st;
+        if (fused) {
+            la2::Fwd1Args f{};
+            f.q = dout;
+            f.k = v;
+            f.v = k;
+            f.y = ws + L.u_off;
+            f.T = T;
+            f.seg_len = (T + 63) / 64 * 64;
+            f.nseg = 1;
+            f.chains = (int)chains;
+            f.sub = f.nsub = 1;
+            f.norm = feature_map == LA2_PHI_ELU1 ? 4 : 3;
+            f.msum = c.msum;
+            f.msum_seg = L.dp.seg_len;
+            if (la2::launch_fwd1_bf16(f, s) != hipSuccess) return LA2_ERR_HIP;
+        } else {
+            const Plan pl = make_plan(B, H, T, d, d_v, block, dtype);
+            void *uws = L.us_bytes ? ws + L.us_off : nullptr;
+            if (pl.nseg > 1 && (st = segment_states(c.kap, v, decay, chains, H, T, (int)d, (int)d_v, pl, dtype,
+                                                    la2::Dir::Forward, uws, s)) != LA2_OK)
+                return st;
+            if ((st = output_scan(dout, v, c.kap, ws + L.u_off, decay, chains, H, T, (int)d_v, (int)d, pl, dtype,
+                                  la2::Dir::Forward, uws, 1, s)) != LA2_OK)
+                return st;
+        }
         c.u = ws + L.u_off;
         c.arow = va.den;
         c.g = dq;

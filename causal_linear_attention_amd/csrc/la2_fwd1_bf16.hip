@@ -110,6 +110,48 @@ __device__ __forceinline__ float chain_l2(const Fwd1Args &p, int chain) {
     return p.decay != nullptr ? log2f(p.decay[chain % p.H]) : 0.0f;
 }
 
+// The value tile as kappa = phi(x) - m (NM = 3: identity, 4: elu + 1) on the chunks of `buf` that
+// dma_tile_f's share `share` filled, with m[8 lc + e] in mv[e] (lc the lane's column block, the same
+// for both of its chunks; rows past the sequence stay zero): the scan of the normalized backward's bf16
+// dq, whose value role is the centered feature map of the keys.  Only the wave that issued those loads
+// may call it, after waiting for them.
+template <int NM>
+__device__ __forceinline__ void center_share(u16 *buf, int64_t t0, int64_t T, int share, int lane,
+                                             const float (&mv)[8]) {
+#pragma unroll
+    for (int s = 0; s < kTile1 / (512 * kWaves); ++s) {
+        const int i = share + kWaves * s, c = 64 * i + lane, row = c / (D1 / 8);
+        if (t0 + row >= T) continue;
+        u16 *l = buf + oVF + 8 * c;
+        u32x4 x = *reinterpret_cast<const u32x4 *>(l);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float lo = __builtin_bit_cast(float, x[j] << 16), hi = __builtin_bit_cast(float, x[j] & 0xffff0000u);
+            if constexpr (NM == 4) {
+                lo = elu1(lo);
+                hi = elu1(hi);
+            }
+            x[j] = pack_bf16(lo - mv[2 * j], hi - mv[2 * j + 1]);
+        }
+        *reinterpret_cast<u32x4 *>(l) = x;
+    }
+}
+
+// m[8 lc + e] for the column block lc of the lane's chunks in share `share`: the chain's mean of the
+// feature map of the keys, from the sums over the segments of msum_seg positions.
+__device__ __forceinline__ void center_means(const Fwd1Args &p, int chain, int share, int lane, float (&mv)[8]) {
+    const int c0 = 64 * share + lane, row0 = c0 / (D1 / 8), lc = (c0 % (D1 / 8)) ^ swz<D1>(row0);
+    const int64_t nms = (p.T + p.msum_seg - 1) / p.msum_seg;
+    const float *ms = p.msum + (int64_t)chain * nms * D1 + lc * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] = 0.0f;
+    for (int64_t j = 0; j < nms; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mv[e] += ms[j * D1 + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mv[e] /= (float)p.T;
+}
+
 // Producer p: state rows 32p..32p+31 of S (d x d_v), four 32 x 32 blocks (column blocks jb).
 template <int NM, bool DEC>
 __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int chain, int seg, int pw, int lane) {
@@ -152,7 +194,10 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         const auto r = __builtin_amdgcn_permlane32_swap(zu, zu, false, false);
         return __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
     };
-    const bool sums = NM > 0 && p.msum != nullptr;
+    constexpr bool NRM = NM == 1 || NM == 2;   // the normalized forward (z, denominators)
+    const bool sums = NRM && p.msum != nullptr;
+    float mv[8];
+    if constexpr (NM >= 3) center_means(p, chain, wave, lane, mv);
     // a decay: lam^64 per tile on the state, and lam^(63 - j) on the K^T operand's position j =
     // 16x + 8h + e (element e of the fragment of step x)
     float wk[DEC ? TB1 / 16 : 1][8], lam64 = 1.0f;
@@ -175,7 +220,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                                  pack_bf16(sacc[jb][4 * q + 2], sacc[jb][4 * q + 3])};
                 lds_write8(smem + oSTF, jb * 32 * D1 + pwq[q], v);
             }
-        if constexpr (NM > 0) {
+        if constexpr (NRM) {
             const float z = z_whole();
             // z of column 32pw + col in row 0 (rounded to bf16) and row 1 (the remainder) of the z tile;
             // lanes h = 0 write row 0, h = 1 row 1
@@ -186,7 +231,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         }
     };
     dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, wave, lane);
-    if constexpr (NM > 0) {
+    if constexpr (NRM) {
         // the z tile's zero rows 2..31 (rows 0 and 1 come with every copy of the state)
         const u32x4 zz = {0u, 0u, 0u, 0u};
         for (int i = (wave - 4) * 64 + lane; i < 30 * D1 / 8; i += 256)
@@ -195,6 +240,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
     write_state();
     wait_vm();
     if constexpr (NM == 2) phi_share(smem, p, w.base, w.t0(0), w.T, wave, lane);
+    if constexpr (NM >= 3) center_share<NM>(smem, w.t0(0), w.T, wave, lane, mv);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
         const bool more = it + 1 < w.ntiles;
@@ -239,7 +285,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                 for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
-                if constexpr (NM > 0) {
+                if constexpr (NRM) {
                     // fa: state row 32pw + col of K^T at positions 16x + 8h .. 16x + 8h + 7
                     const u32x4 u = __builtin_bit_cast(u32x4, fa);
 #pragma unroll
@@ -248,7 +294,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                 }
             }
         }
-        if constexpr (NM > 0) {
+        if constexpr (NRM) {
             // the sum of phi(k) over a segment of msum_seg positions, written at its last tile
             const int64_t t_end = w.t0(it) + TB1;
             if (sums && (!more || t_end % p.msum_seg == 0)) {
@@ -262,6 +308,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         if (more) write_state();
         wait_vm();
         if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, wave, lane);
+        if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, wave, lane, mv);
         lds_barrier();   // X: the next tile and S_b^T
     }
     if (final_state) {
@@ -316,7 +363,10 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
 
     dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, c, lane);
     wait_vm();
+    float mv[8];
+    if constexpr (NM >= 3) center_means(p, chain, c, lane, mv);
     if constexpr (NM == 2) phi_share(smem, p, w.base, w.t0(0), w.T, c, lane);
+    if constexpr (NM >= 3) center_share<NM>(smem, w.t0(0), w.T, c, lane, mv);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
         const u16 *cur = smem + (it & 1) * kBufF;
@@ -326,7 +376,7 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
         if (it > 0) store(w.t0(it - 1));
         {
             f32x16 oacc[2];
-            if constexpr (NM > 0) {
+            if constexpr (NM == 1 || NM == 2) {
                 float dpart;
                 unit_products<true, true, true, false>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
                                                        lane, L, &dpart, smem + oZF, dwt);
@@ -350,6 +400,7 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
         lds_barrier();   // Y
         wait_vm();
         if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, c, lane);
+        if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, c, lane, mv);
         lds_barrier();   // X
     }
     store(w.t0(w.ntiles - 1));
@@ -372,8 +423,10 @@ __global__ __launch_bounds__(kTF, 1) void fwd1_bf16_kernel(Fwd1Args p) {
 }  // namespace
 
 hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
-    if (a.seg_len <= 0 || a.seg_len % TB1 != 0 || a.norm < 0 || a.norm > 2) return hipErrorInvalidValue;
+    if (a.seg_len <= 0 || a.seg_len % TB1 != 0 || a.norm < 0 || a.norm > 4) return hipErrorInvalidValue;
     if (a.msum != nullptr && (a.norm == 0 || a.msum_seg <= 0 || a.msum_seg % TB1 != 0)) return hipErrorInvalidValue;
+    // the centered value tile needs the segment sums of the feature map of the keys
+    if (a.norm >= 3 && a.msum == nullptr) return hipErrorInvalidValue;
     // the normalized form keeps z per chain from zero: unsplit chains only
     if (a.norm != 0 && (a.nseg != 1 || a.states != nullptr || a.state_out != nullptr)) return hipErrorInvalidValue;
     // a decay: the plain scan only
@@ -386,7 +439,9 @@ hipError_t launch_fwd1_bf16(const Fwd1Args &a, hipStream_t s) {
     switch (a.norm) {
         case 0: hipLaunchKernelGGL((fwd1_bf16_kernel<0, false>), dim3(items), dim3(kTF), 0, s, a); break;
         case 1: hipLaunchKernelGGL((fwd1_bf16_kernel<1, false>), dim3(items), dim3(kTF), 0, s, a); break;
-        default: hipLaunchKernelGGL((fwd1_bf16_kernel<2, false>), dim3(items), dim3(kTF), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((fwd1_bf16_kernel<2, false>), dim3(items), dim3(kTF), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((fwd1_bf16_kernel<3, false>), dim3(items), dim3(kTF), 0, s, a); break;
+        default: hipLaunchKernelGGL((fwd1_bf16_kernel<4, false>), dim3(items), dim3(kTF), 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -150,7 +150,9 @@ struct Fwd1Args {
     int sub, nsub;          // states entry of segment s: state_index(s, sub, nsub, false)
     float *state_out;       // fp32 [chains, D, D]: the state after the last position, or nullptr
     // the normalized form (norm = 1: identity feature map, 2: elu + 1; 0: the plain scan): each output
-    // row is divided by phi(q_t) . z_t, z_t the prefix sum of phi(k_s); unsplit chains only (nseg = 1)
+    // row is divided by phi(q_t) . z_t, z_t the prefix sum of phi(k_s); unsplit chains only (nseg = 1).
+    // norm = 3 (identity), 4 (elu + 1): the plain scan with the value role v replaced by phi(v) - m, m
+    // the chain's mean of phi(v) from msum (the normalized backward's centered keys); unsplit only
     int norm;
     void *pq, *pk;          // where phi(q), phi(k) are also written (bf16 [chains, T, 128]), or nullptr
     float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr
