@@ -30,6 +30,7 @@ struct PlanOverride {
     int64_t norm_segment;   // > 0: positions per segment of the denominator scans
     int two_pass_backward;  // != 0: la2_backward_saved without decay by the dQ pass and the dK/dV pass
     int legacy_forward;     // != 0: forward-direction bf16 output passes on the 8-wave scan kernel only
+    int legacy_dkdv;        // != 0: the fused dk/dv pass on its 8-wave kernel only
 };
 
 #ifdef LA2_TEST_HOOKS
@@ -303,9 +304,9 @@ int la2_abi_version(void) { return LA2_ABI_VERSION; }
 
 #ifdef LA2_TEST_HOOKS
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment,
-                      int two_pass_backward, int legacy_forward) {
+                      int two_pass_backward, int legacy_forward, int legacy_dkdv) {
     g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment, two_pass_backward,
-                              legacy_forward};
+                              legacy_forward, legacy_dkdv};
     return LA2_OK;
 }
 #endif
@@ -789,6 +790,27 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         if (fp.nseg > 1 && (st = segment_states(q, dout, decay, chains, H, T, D, DV, fp, dtype, la2::Dir::Reverse,
                                                 ws_r, s, dstate_out)) != LA2_OK)
             return st;
+        if (d == 128 && d_v == 128 && !dstate_out && !dstate_in && !forced().legacy_dkdv) {
+            // d = d_v = 128, no carried state: the producer/consumer walk of the one-pass backward without
+            // its dQ and S (la2_bwd1_bf16.hip), R from the reverse states at the segment ends
+            la2::Bwd1Args a{};
+            a.q = q;
+            a.k = k;
+            a.v = v;
+            a.dout = dout;
+            a.dk = dk;
+            a.dv = dv;
+            a.T = T;
+            a.nseg = fp.nseg;
+            a.seg_tiles = fp.seg_tiles;
+            a.chains = (int)chains;
+            a.r_states = fp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
+            a.r_sub = fp.sub;
+            a.r_nsub = fp.nsub;
+            a.decay = decay;
+            a.H = (int)H;
+            return la2::launch_bwd1_bf16(a, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
+        }
         la2::DkdvArgs a{};
         a.q = q;
         a.k = k;

@@ -27,6 +27,13 @@
 // bf16 (MFMA operands of the inter-tile products) and 8 KiB of output staging per consumer: 160 KiB.
 // Per tile, three workgroup barriers: Y (S^T of the state before the tile is complete, dV and dK are
 // done with R^T), Z (every input of the tile is consumed) and X (the next tile and R^T are in LDS).
+//
+// The same kernel without dQ and S (ONE = false) is the dK/dV pass of the two-pass backward, with an
+// optional per-head decay lam (the recurrence R_t = lam R_{t+1} + q_t do_t^T; R here is the state after
+// the tile, at its last position + 1):
+//   dV_b[t] = sum_{s>=t} lam^(s-t) (q_s . k_t) do_s + lam^(64-t) k_t R_{b+1},   likewise dK_b with
+//   (do, v, q);   R_b = lam^64 R_{b+1} + sum_j lam^j q_j do_j^T.
+// The S producers then only stage tiles.
 #include "la2_tile64_bf16.h"
 
 namespace la2 {
@@ -83,14 +90,19 @@ __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid
 //   DV: rows s of dV; scores Q[t] . K[s] for t >= s; value dO; inter R^T K^T (R^T rows read plain)
 //   DK: rows s of dK; scores dO[t] . V[s] for t >= s; value Q; inter R V^T
 //   DQ: rows t of dQ; scores V[s] . dO[t] for s <= t; value K; inter S dO^T
-template <Unit U>
+template <Unit U, bool DEC = false>
 __device__ __forceinline__ void out_unit(f32x16 (&oacc)[2], const u16 *smem, int orow, int ch, int lane,
-                                         const LaneOff &L) {
+                                         const LaneOff &L, const DecayW &dw) {
     const u16 *sB = smem + (U == Unit::DV ? oK1 : U == Unit::DK ? oV1 : oO1);   // output-row role
     const u16 *sA = smem + (U == Unit::DV ? oQ1 : U == Unit::DK ? oO1 : oV1);   // source-row role
     const u16 *sC = smem + (U == Unit::DV ? oO1 : U == Unit::DK ? oQ1 : oK1);   // value role
     const u16 *sSt = smem + (U == Unit::DQ ? oST1 : oRT1);
-    unit_products<U == Unit::DQ, U == Unit::DV>(oacc, sB, sA, sC, sSt, orow, ch, lane, L);
+    unit_products<U == Unit::DQ, U == Unit::DV, false, DEC>(oacc, sB, sA, sC, sSt, orow, ch, lane, L, nullptr,
+                                                            nullptr, dw);
+}
+
+__device__ __forceinline__ float chain_l2(const Bwd1Args &p, int chain) {
+    return p.decay != nullptr ? log2f(p.decay[chain % p.H]) : 0.0f;
 }
 
 // The tiles of one (chain, segment), walked from the last to the first.
@@ -113,8 +125,10 @@ __device__ __forceinline__ Walk1 walk_of(const Bwd1Args &p, int chain, int seg) 
 // Producer wave: state blocks with rows kb in {2ch, 2ch + 1} of R (SK = false) or S (SK = true).
 // R_b = R_{b+1} + Q_b^T dO_b is formed at the top of tile b but published as R^T only after barrier
 // Y (dV and dK of tile b use R_{b+1}); S_{b-1} = S_b - K_b^T V_b is published before Y for dQ.
-template <bool SK>
+// Without dQ (ONE = false) the S producers hold no state and only stage their part of each tile.
+template <bool SK, bool ONE, bool DEC>
 __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain, int seg, int ch, int lane) {
+    constexpr bool HOLD = ONE || !SK;   // this wave holds a state
     const Walk1 w = walk_of(p, chain, seg);
     const int kb0 = 2 * ch, tid = threadIdx.x;
     const int h = lane >> 5, col = lane & 31;
@@ -124,28 +138,41 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
     const u16 *gv = static_cast<const u16 *>(p.v) + w.base, *go = static_cast<const u16 *>(p.dout) + w.base;
     // R at the segment's end (0 for the last segment), S after the segment's last position
     const float *g = nullptr;
-    if (SK)
+    if (SK && ONE)
         g = seg < p.nseg - 1 ? p.s_states + ((int64_t)chain * p.s_nsub + (seg + 1) * p.s_sub) * D1 * D1
                              : p.s_final + (int64_t)chain * D1 * D1;
-    else if (seg < p.nseg - 1)
+    else if (!SK && seg < p.nseg - 1)
         g = p.r_states + ((int64_t)chain * p.r_nsub + state_index(seg, p.r_sub, p.r_nsub, true)) * D1 * D1;
 
-    f32x16 sacc[8];
+    f32x16 sacc[HOLD ? 8 : 1];
+    if constexpr (HOLD) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int kb = kb0 + s / 4, nb = s % 4;
+        for (int s = 0; s < 8; ++s) {
+            const int kb = kb0 + s / 4, nb = s % 4;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
+            }
         }
+    }
+    // a decay: lam^64 per tile on R, and lam^j on the Q^T operand's position j = 16x + 8h + e
+    float wq[DEC ? TB1 / 16 : 1][8], lam64 = 1.0f;
+    if constexpr (DEC) {
+        const float l2 = chain_l2(p, chain);
+        lam64 = exp2f(64.0f * l2);
+#pragma unroll
+        for (int x = 0; x < TB1 / 16; ++x)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wq[x][e] = exp2f(l2 * (float)(16 * x + 8 * h + e));
     }
     // the blocks as R^T or S^T (bf16, [d_v][d]) into LDS: accumulator entries 4g..4g+3 of a lane are
     // four consecutive d of one d_v row, one 8-byte write
     auto write_state = [&]() {
+        if constexpr (!HOLD) return;
         u16 *dst = smem + (SK ? oST1 : oRT1);
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
+        for (int s = 0; s < (HOLD ? 8 : 0); ++s)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const u32x2 v = {pack_bf16(sacc[s][4 * q], sacc[s][4 * q + 1]),
@@ -164,14 +191,29 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
         const bool more = it + 1 < w.ntiles;
         // R += Q^T dO, or S -= K^T V; each operand fragment is read once per 16 positions and shared
         // by the blocks that use it
-        {
+        if constexpr (HOLD) {
             const u16 *sA = smem + (SK ? oK1 : oQ1), *sC = smem + (SK ? oV1 : oO1);
+            if constexpr (DEC) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[s][r] *= lam64;
+            }
 #pragma unroll
             for (int x = 0; x < TB1 / 16; ++x) {
                 bf16x8 fa[2], fc[4];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)   // state row blocks kb0 + i are column blocks 2ch + i of the tile
+                for (int i = 0; i < 2; ++i) {   // state row blocks kb0 + i are column blocks 2ch + i of the tile
                     fa[i] = flip8(rd_tr(sA, 16 * x, L.trc[0][i]), sign);
+                    if constexpr (DEC) {
+                        u32x4 u = __builtin_bit_cast(u32x4, fa[i]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            u[j] = pack_bf16(__builtin_bit_cast(float, u[j] << 16) * wq[x][2 * j],
+                                             __builtin_bit_cast(float, u[j] & 0xffff0000u) * wq[x][2 * j + 1]);
+                        fa[i] = __builtin_bit_cast(bf16x8, u);
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) fc[i] = rd_tr(sC, 16 * x, L.trn[i]);
 #pragma unroll
@@ -191,6 +233,7 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
 
 // Consumer wave c = 2rb + ch.  Each unit is staged in the wave's own 8 KiB of LDS and stored as whole
 // 128-byte row pieces, so that at most one unit's accumulators are held at a time.
+template <bool ONE, bool DEC>
 __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
     const Walk1 w = walk_of(p, chain, seg);
     const int rb = c >> 1, ch = c & 1, tid = threadIdx.x;
@@ -200,6 +243,8 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
     u16 *gdq = static_cast<u16 *>(p.dq) + w.base, *gdk = static_cast<u16 *>(p.dk) + w.base,
         *gdv = static_cast<u16 *>(p.dv) + w.base;
     u16 *ob = smem + oOS1 + c * kOS1;
+    DecayW dwt = {};   // read only with a decay
+    if constexpr (DEC) dwt = decay_weights<false>(chain_l2(p, chain), rb, lane);
     // [32 rows][64 columns] with 16-byte chunks XOR-swizzled by row pair; a lane's accumulator entries
     // 4g..4g+3 are four consecutive columns of its row, one 8-byte write
     auto stage = [&](const f32x16 (&acc)[2], u16 *dst) {
@@ -238,26 +283,27 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
         if (more) load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
         {
             f32x16 oacc[2];
-            out_unit<Unit::DV>(oacc, smem, rb, ch, lane, L);
+            out_unit<Unit::DV, DEC>(oacc, smem, rb, ch, lane, L, dwt);
             stage(oacc, ob);
-            out_unit<Unit::DK>(oacc, smem, rb, ch, lane, L);
+            out_unit<Unit::DK, DEC>(oacc, smem, rb, ch, lane, L, dwt);
             stage(oacc, ob + 2048);
             store(ob, gdv, t0);
             store(ob + 2048, gdk, t0);
         }
         lds_barrier();   // Y: S^T of the state before this tile is complete
-        {
+        if constexpr (ONE) {
             f32x16 oacc[2];
-            out_unit<Unit::DQ>(oacc, smem, rb, ch, lane, L);
+            out_unit<Unit::DQ>(oacc, smem, rb, ch, lane, L, dwt);
             stage(oacc, ob);
         }
         lds_barrier();   // Z
         if (more) store_tile1(st, smem, tid);
-        store(ob, gdq, t0);
+        if constexpr (ONE) store(ob, gdq, t0);
         lds_barrier();   // X
     }
 }
 
+template <bool ONE, bool DEC>
 __global__ __launch_bounds__(kT1, 1) void bwd1_bf16_kernel(Bwd1Args p) {
     __shared__ __attribute__((aligned(16))) u16 smem[kLds1];
     // the wave index as a scalar: every branch on a wave's role is uniform
@@ -267,18 +313,25 @@ __global__ __launch_bounds__(kT1, 1) void bwd1_bf16_kernel(Bwd1Args p) {
     const int64_t NT = (p.T + TB1 - 1) / TB1;
     if ((int64_t)seg * p.seg_tiles >= NT) return;
     if (wave < 4)
-        consumer(p, smem, chain, seg, wave, lane);
+        consumer<ONE, DEC>(p, smem, chain, seg, wave, lane);
     else if (wave < 6)
-        producer<false>(p, smem, chain, seg, wave & 1, lane);
+        producer<false, ONE, DEC>(p, smem, chain, seg, wave & 1, lane);
     else
-        producer<true>(p, smem, chain, seg, wave & 1, lane);
+        producer<true, ONE, DEC>(p, smem, chain, seg, wave & 1, lane);
 }
 
 }  // namespace
 
 hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s) {
     const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
-    hipLaunchKernelGGL(bwd1_bf16_kernel, dim3(items), dim3(kT1), 0, s, a);
+    if (a.dq != nullptr && a.decay != nullptr) return hipErrorInvalidValue;   // no one-pass walk with a decay
+    if (a.decay != nullptr && a.H <= 0) return hipErrorInvalidValue;
+    if (a.dq != nullptr)
+        hipLaunchKernelGGL((bwd1_bf16_kernel<true, false>), dim3(items), dim3(kT1), 0, s, a);
+    else if (a.decay != nullptr)
+        hipLaunchKernelGGL((bwd1_bf16_kernel<false, true>), dim3(items), dim3(kT1), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd1_bf16_kernel<false, false>), dim3(items), dim3(kT1), 0, s, a);
     return hipGetLastError();
 }
 

@@ -331,7 +331,7 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
     const int rb = c >> 1, ch = c & 1;
     const LaneOff L = lane_offsets(lane, ch);
     DecayW dwt = {};   // read only with a decay
-    if constexpr (DEC) dwt = decay_weights(chain_l2(p, chain), rb, lane);
+    if constexpr (DEC) dwt = decay_weights<true>(chain_l2(p, chain), rb, lane);
     const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
     const u16 *gv = static_cast<const u16 *>(p.v) + w.base;
     u16 *gy = static_cast<u16 *>(p.y) + w.base;

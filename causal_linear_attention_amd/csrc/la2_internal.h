@@ -182,6 +182,10 @@ struct Bwd1Args {
     const float *r_states; // fp32 [chains, r_nsub, D, D]: reverse states at the segments' ends, or nullptr
     int r_sub;
     int r_nsub;
+    // dq = nullptr: dk and dv only (the dK/dV pass of the two-pass backward; s_states, s_final unused),
+    // with the per-head decay lam ([H] fp32, chain c is head c % H) or nullptr for lam = 1
+    const float *decay;
+    int H;
 };
 hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s);
 

@@ -138,25 +138,28 @@ __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf
         for (int n = 0; n < 2; ++n) oacc[n] = mfma(rd_tr(sC, u * 32 + 16 * x, L.trc[1][n]), pf[x], oacc[n]);
 }
 
-// The weights of a decay lam = 2^l2 for the forward direction, per lane (h, col) of a unit in row block
-// orow: wd[r] = lam^(t - s) for accumulator entry r of the diagonal score block where s <= t, else 0
-// (t = col, s = 8(r/4) + 4h + r%4 within the block); wf[r] = lam^(t - s) for the full block before it
-// (t - s = 32 + col - s, row block 1 only); *wi = lam^(orow*32 + col + 1), the inter product's weight
-// (the state is the one before the tile).  Every exponent is non-negative.
+// The weights of a decay lam = 2^l2, per lane (h, col) of a unit in row block orow, for accumulator
+// entry r (output row t = col, source row s = 8(r/4) + 4h + r%4 within their blocks).  Forward
+// (SRC_BEFORE): wd[r] = lam^(t - s) in the diagonal score block where s <= t, else 0; wf[r] =
+// lam^(32 + t - s) in the full block before it (row block 1 only); wi = lam^(orow*32 + col + 1), the
+// inter product's weight (the state is the one before the tile).  Reverse: wd[r] = lam^(s - t) where
+// s >= t, else 0; wf[r] = lam^(32 + s - t) in the full block after it (row block 0 only); wi =
+// lam^(64 - orow*32 - col) (the state is the one after the tile).  Every exponent is non-negative.
 struct DecayW {
     float wd[16], wf[16], wi;
 };
 
+template <bool SRC_BEFORE>
 __device__ __forceinline__ DecayW decay_weights(float l2, int orow, int lane) {
     const int h = lane >> 5, col = lane & 31;
     DecayW w;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int s = 8 * (r >> 2) + 4 * h + (r & 3);
-        w.wd[r] = s <= col ? exp2f(l2 * (float)(col - s)) : 0.0f;
-        w.wf[r] = orow == 1 ? exp2f(l2 * (float)(32 + col - s)) : 0.0f;
+        const int s = 8 * (r >> 2) + 4 * h + (r & 3), dist = SRC_BEFORE ? col - s : s - col;
+        w.wd[r] = dist >= 0 ? exp2f(l2 * (float)dist) : 0.0f;
+        w.wf[r] = orow == (SRC_BEFORE ? 1 : 0) ? exp2f(l2 * (float)(32 + dist)) : 0.0f;
     }
-    w.wi = exp2f(l2 * (float)(orow * 32 + col + 1));
+    w.wi = exp2f(l2 * (float)(SRC_BEFORE ? orow * 32 + col + 1 : TB1 - orow * 32 - col));
     return w;
 }
 
@@ -173,7 +176,7 @@ __device__ __forceinline__ DecayW decay_weights(float l2, int orow, int lane) {
 // of the source rows before the tile) that sZ holds as a [32][128] tile whose row 0 is z rounded to
 // bf16, row 1 the rounding's remainder rounded to bf16, and the other rows zero; the partner lane
 // (lane ^ 32) holds the other half of the scores.
-// DEC (a decay, SRC_BEFORE only): the inter product is weighted by dw.wi and the scores by dw.wd, wf.
+// DEC (a decay): the inter product is weighted by dw.wi and the scores by dw.wd, wf (decay_weights).
 template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false, bool DEC = false>
 __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, const u16 *sA, const u16 *sC,
                                               const u16 *sSt, int orow, int ch, int lane, const LaneOff &L,
@@ -202,7 +205,6 @@ __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, 
             const bf16x8 a = INTER_PLAIN ? rd_plain(sSt, (2 * ch + n) * 32, ks, L) : rd_tr(sSt, 16 * ks, L.trc[0][n]);
             oacc[n] = mfma(a, bf[ks], ks == 0 ? zero : oacc[n]);
         }
-    static_assert(!DEC || SRC_BEFORE, "decay weights are for the forward direction");
     if constexpr (DEC) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)

@@ -33,9 +33,11 @@ extern "C" {
  *                  on the eight-wave scan kernel instead of the producer/consumer one,
  *                  and la2_forward_normalized there as its denominator pass and numerator scan
  *                  instead of the one fused launch
+ *   legacy_dkdv:   non-zero runs the fused dK/dV pass at d = d_v = 128 on its eight-wave kernel instead
+ *                  of the producer/consumer walk of the one-pass backward
  * Returns LA2_OK. */
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv,
-                      int64_t norm_segment, int two_pass_backward, int legacy_forward);
+                      int64_t norm_segment, int two_pass_backward, int legacy_forward, int legacy_dkdv);
 
 /* A plain HBM stream, for measuring what the tile kernels' read:write mixes can reach:
  * dst_j = src_0 + ... + src_{nsrc-1} (u32 lanes) over `bytes` bytes of each device buffer, read and
