@@ -23,10 +23,13 @@
 //
 // The normalized form (page "Lightning Attention", section 1: numerator over denominator, with a
 // feature map phi on q and k): o_t = S_t^T phi(q_t) / (phi(q_t) . z_t), z_t = sum_{s<=t} phi(k_s).
-// phi is applied to the q and k tiles in LDS (elu + 1: after barrier Y, where every wave waits for
-// its share of the next tile's direct loads, it transforms the chunks those loads filled; rows past
-// the sequence stay zero), so the numerator is the plain scan on phi(q), phi(k) rounded to bf16.  The denominator comes from the same rounded values: its
-// intra-tile part is the sum of each output row's kept fp32 scores, its inter part the product of the
+// phi is applied to the q and k tiles on their way into LDS (rows past the sequence stay zero), so the
+// numerator is the plain scan on phi(q), phi(k) rounded to bf16.  With elu + 1, k goes through the
+// producers' registers: k of tile b + 1 is loaded at the top of tile b - 1 and, transformed, written to
+// LDS at the top of tile b, beside the consumers' products of tile b; q arrives by direct loads, and
+// each wave transforms the chunks its own loads filled after barrier Y, once they have landed (so only
+// half the transform waits between barriers Y and X).  The denominator comes from the same rounded
+// values: its intra-tile part is the sum of each output row's kept fp32 scores, its inter part the product of the
 // row with z before the tile, which the producers keep in fp32 from their K^T operands (column sums of
 // phi(K)) and publish beside S^T as two bf16 rows (z rounded, and the remainder rounded) of an
 // otherwise zero [32][128] tile, so that the consumers take it with 8 more MFMAs beside their inter
@@ -76,11 +79,65 @@ __device__ __forceinline__ void dma_tile_f(u16 *buf, const u16 *gq, const u16 *g
     dma_rows<D1, TB1>(make_rsrc(gv + t0 * D1, bytes), buf + oVF, D1, wave, lane);
 }
 
-__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+// Only the q and v tiles of the tile starting at t0 (the elu + 1 form, whose k goes through the
+// producers' registers).
+__device__ __forceinline__ void dma_qv_f(u16 *buf, const u16 *gq, const u16 *gv, int64_t t0, int64_t T, int wave,
+                                         int lane) {
+    const int64_t bytes = (T - t0) * D1 * 2;
+    dma_rows<D1, TB1>(make_rsrc(gq + t0 * D1, bytes), buf + oQF, D1, wave, lane);
+    dma_rows<D1, TB1>(make_rsrc(gv + t0 * D1, bytes), buf + oVF, D1, wave, lane);
+}
+
+// elu + 1: x + 1 above zero, e^x at or below.  e^x clamped to [0, 1] (the clamp output modifier of
+// the exp instruction) is e^min(x, 0), and e^x >= x + 1 everywhere, so the larger of x + 1 and the
+// clamped exponential is elu + 1 without a compare and select; the NaN-propagating maximum keeps a
+// NaN input NaN.
+__device__ __forceinline__ float elu1(float x) {
+    const float e = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.44269502f), 0.0f, 1.0f);
+    return __builtin_elementwise_maximum(x + 1.0f, e);
+}
+
+// The k chunks of one tile that producer pw carries in registers (the elu + 1 form): chunks
+// c = 64 i + lane, i = pw + 4 s, of each tile, placed where dma_rows would put them.
+constexpr int kKC = kTile1 / 8 / 256;   // chunks per lane (4)
+struct KRegs {
+    u32x4 k[kKC];
+};
+
+__device__ __forceinline__ void load_k(KRegs &r, const u16 *gk, int64_t t0, int64_t T, int pw, int lane) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(gk + t0 * D1, (T - t0) * D1 * 2);
+#pragma unroll
+    for (int s = 0; s < kKC; ++s) {
+        const int c = 64 * (pw + 4 * s) + lane, row = c / (D1 / 8), lc = (c % (D1 / 8)) ^ swz<D1>(row);
+        r.k[s] = bload(rk, (row * D1 + lc * 8) * 2);
+    }
+}
+
+// phi = elu + 1 on the loaded chunks (rows past the sequence arrive as zeros and stay zero) into the
+// k tile of `buf`, and to pk where asked for.
+__device__ __forceinline__ void put_k(KRegs &r, u16 *buf, const Fwd1Args &p, int64_t base, int64_t t0, int64_t T,
+                                      int pw, int lane) {
+    u16 *gpk = p.pk ? static_cast<u16 *>(p.pk) + base + t0 * D1 : nullptr;
+#pragma unroll
+    for (int s = 0; s < kKC; ++s) {
+        const int c = 64 * (pw + 4 * s) + lane, row = c / (D1 / 8), lc = (c % (D1 / 8)) ^ swz<D1>(row);
+        const bool real = t0 + row < T;
+        u32x4 x = r.k[s];
+        if (real) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[j] = pack_bf16(elu1(__builtin_bit_cast(float, x[j] << 16)),
+                                 elu1(__builtin_bit_cast(float, x[j] & 0xffff0000u)));
+        }
+        *reinterpret_cast<u32x4 *>(buf + oKF + 8 * c) = x;
+        if (gpk && real) bstore16(make_rsrc(gpk, (T - t0) * D1 * 2), (row * D1 + lc * 8) * 2, x);
+    }
+}
 
 // phi = elu + 1 on the chunks of the q and k tiles in `buf` that dma_tile_f's share `share` filled
 // (rows past the sequence stay zero), and the transformed chunks to pq, pk where asked for.  Only the
 // wave that issued those loads may call it, after waiting for them: no other wave touches the chunks.
+template <bool WITH_K = true>
 __device__ __forceinline__ void phi_share(u16 *buf, const Fwd1Args &p, int64_t base, int64_t t0, int64_t T,
                                           int share, int lane) {
     const int64_t bytes = (T - t0) * D1 * 2;
@@ -92,7 +149,7 @@ __device__ __forceinline__ void phi_share(u16 *buf, const Fwd1Args &p, int64_t b
         const int lc = (c % (D1 / 8)) ^ swz<D1>(row);
         if (t0 + row >= T) continue;
 #pragma unroll
-        for (int tns = 0; tns < 2; ++tns) {
+        for (int tns = 0; tns < (WITH_K ? 2 : 1); ++tns) {
             u16 *l = buf + (tns ? oKF : oQF) + 8 * c;
             u32x4 x = *reinterpret_cast<const u32x4 *>(l);
 #pragma unroll
@@ -238,78 +295,93 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
             *reinterpret_cast<u32x4 *>(smem + oZF + 2 * D1 + 8 * i) = zz;
     }
     write_state();
+    // the elu + 1 form: k of tile it + 1 waits in registers during tile it - 1 and goes to LDS,
+    // transformed, at the top of tile it, beside the consumers' products; q is transformed after barrier Y
+    KRegs kr;
+    if (NM == 2 && w.ntiles > 1) load_k(kr, gk, w.t0(1), w.T, pw, lane);
     wait_vm();
     if constexpr (NM == 2) phi_share(smem, p, w.base, w.t0(0), w.T, wave, lane);
     if constexpr (NM >= 3) center_share<NM>(smem, w.t0(0), w.T, wave, lane, mv);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
         const bool more = it + 1 < w.ntiles;
-        const u16 *cur = smem + (it & 1) * kBufF;
-        u16 *nxt = smem + ((it + 1) & 1) * kBufF;
-        if (more) dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
-        // S += K^T V over the tile's 64 positions (the last tile's update only for the final state or the
-        // segment sums of phi(k))
-        if (more || final_state || sums) {
-            const u16 *sK = cur + oKF, *sV = cur + oVF;
-            if (DEC && !more) {
-                // the final state's tile: its n real rows, lam^n on the state and lam^(n - 1 - j) on row j
-                const int n = (int)min((int64_t)TB1, w.T - w.t0(it));
-                lam64 = exp2f(l2 * (float)n);
-#pragma unroll
-                for (int x = 0; x < TB1 / 16; ++x)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = 16 * x + 8 * h + e;
-                        wk[x][e] = j < n ? exp2f(l2 * (float)(n - 1 - j)) : 0.0f;
-                    }
+        // the two tile buffers are distinct and nothing else touches them, which the restrict
+        // qualifiers state: without that the compiler makes the transposed fragment reads of this
+        // tile wait for the next tile's direct loads
+        [&](const u16 *__restrict__ cur, u16 *__restrict__ nxt) __attribute__((always_inline)) {
+            if constexpr (NM == 2) {
+                if (more) {
+                    dma_qv_f(nxt, gq, gv, w.t0(it + 1), w.T, wave, lane);
+                    put_k(kr, nxt, p, w.base, w.t0(it + 1), w.T, pw, lane);
+                    if (it + 2 < w.ntiles) load_k(kr, gk, w.t0(it + 2), w.T, pw, lane);
+                }
+            } else if (more) {
+                dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, wave, lane);
             }
-            if constexpr (DEC) {
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[jb][r] *= lam64;
-            }
-#pragma unroll
-            for (int x = 0; x < TB1 / 16; ++x) {
-                bf16x8 fa = rd_tr(sK, 16 * x, trk);
+            // S += K^T V over the tile's 64 positions (the last tile's update only for the final state or the
+            // segment sums of phi(k))
+            if (more || final_state || sums) {
+                const u16 *sK = cur + oKF, *sV = cur + oVF;
+                if (DEC && !more) {
+                    // the final state's tile: its n real rows, lam^n on the state and lam^(n - 1 - j) on row j
+                    const int n = (int)min((int64_t)TB1, w.T - w.t0(it));
+                    lam64 = exp2f(l2 * (float)n);
+    #pragma unroll
+                    for (int x = 0; x < TB1 / 16; ++x)
+    #pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int j = 16 * x + 8 * h + e;
+                            wk[x][e] = j < n ? exp2f(l2 * (float)(n - 1 - j)) : 0.0f;
+                        }
+                }
                 if constexpr (DEC) {
-                    u32x4 u = __builtin_bit_cast(u32x4, fa);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        u[j] = pack_bf16(__builtin_bit_cast(float, u[j] << 16) * wk[x][2 * j],
-                                         __builtin_bit_cast(float, u[j] & 0xffff0000u) * wk[x][2 * j + 1]);
-                    fa = __builtin_bit_cast(bf16x8, u);
+    #pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) sacc[jb][r] *= lam64;
                 }
-                bf16x8 fc[4];
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
-                if constexpr (NRM) {
-                    // fa: state row 32pw + col of K^T at positions 16x + 8h .. 16x + 8h + 7
-                    const u32x4 u = __builtin_bit_cast(u32x4, fa);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        zacc += __builtin_bit_cast(float, u[j] << 16) + __builtin_bit_cast(float, u[j] & 0xffff0000u);
+    #pragma unroll
+                for (int x = 0; x < TB1 / 16; ++x) {
+                    bf16x8 fa = rd_tr(sK, 16 * x, trk);
+                    if constexpr (DEC) {
+                        u32x4 u = __builtin_bit_cast(u32x4, fa);
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            u[j] = pack_bf16(__builtin_bit_cast(float, u[j] << 16) * wk[x][2 * j],
+                                             __builtin_bit_cast(float, u[j] & 0xffff0000u) * wk[x][2 * j + 1]);
+                        fa = __builtin_bit_cast(bf16x8, u);
+                    }
+                    bf16x8 fc[4];
+    #pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
+    #pragma unroll
+                    for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
+                    if constexpr (NRM) {
+                        // fa: state row 32pw + col of K^T at positions 16x + 8h .. 16x + 8h + 7
+                        const u32x4 u = __builtin_bit_cast(u32x4, fa);
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            zacc += __builtin_bit_cast(float, u[j] << 16) + __builtin_bit_cast(float, u[j] & 0xffff0000u);
+                    }
                 }
             }
-        }
-        if constexpr (NRM) {
-            // the sum of phi(k) over a segment of msum_seg positions, written at its last tile
-            const int64_t t_end = w.t0(it) + TB1;
-            if (sums && (!more || t_end % p.msum_seg == 0)) {
-                const float z = z_whole();
-                const int64_t nms = (w.T + p.msum_seg - 1) / p.msum_seg, ms = (t_end - 1) / p.msum_seg;
-                if (h == 0) p.msum[((int64_t)chain * nms + ms) * D1 + pw * 32 + col] = z - zmark;
-                zmark = z;
+            if constexpr (NRM) {
+                // the sum of phi(k) over a segment of msum_seg positions, written at its last tile
+                const int64_t t_end = w.t0(it) + TB1;
+                if (sums && (!more || t_end % p.msum_seg == 0)) {
+                    const float z = z_whole();
+                    const int64_t nms = (w.T + p.msum_seg - 1) / p.msum_seg, ms = (t_end - 1) / p.msum_seg;
+                    if (h == 0) p.msum[((int64_t)chain * nms + ms) * D1 + pw * 32 + col] = z - zmark;
+                    zmark = z;
+                }
             }
-        }
-        lds_barrier();   // Y: every consumer is done with S_{b-1}^T (and z before the tile)
-        if (more) write_state();
-        wait_vm();
-        if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, wave, lane);
-        if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, wave, lane, mv);
-        lds_barrier();   // X: the next tile and S_b^T
+            lds_barrier();   // Y: every consumer is done with S_{b-1}^T (and z before the tile)
+            if (more) write_state();
+            wait_vm();
+            if (NM == 2 && more) phi_share<false>(nxt, p, w.base, w.t0(it + 1), w.T, wave, lane);
+            if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, wave, lane, mv);
+            lds_barrier();   // X: the next tile and S_b^T
+        }(smem + (it & 1) * kBufF, smem + ((it + 1) & 1) * kBufF);
     }
     if (final_state) {
         float *so = p.state_out + (int64_t)chain * D1 * D1;
@@ -369,39 +441,47 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
     if constexpr (NM >= 3) center_share<NM>(smem, w.t0(0), w.T, c, lane, mv);
     lds_barrier();   // X: the first tile and S^T
     for (int it = 0; it < w.ntiles; ++it) {
-        const u16 *cur = smem + (it & 1) * kBufF;
-        u16 *nxt = smem + ((it + 1) & 1) * kBufF;
         const bool more = it + 1 < w.ntiles;
-        if (more) dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, c, lane);
-        if (it > 0) store(w.t0(it - 1));
-        {
-            f32x16 oacc[2];
-            if constexpr (NM == 1 || NM == 2) {
-                float dpart;
-                unit_products<true, true, true, false>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
-                                                       lane, L, &dpart, smem + oZF, dwt);
-                const unsigned int du = __builtin_bit_cast(unsigned int, dpart);
-                const auto r = __builtin_amdgcn_permlane32_swap(du, du, false, false);
-                const float den =
-                    __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
-                const float inv = 1.0f / den;
-#pragma unroll
-                for (int n = 0; n < 2; ++n)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[n][e] *= inv;
-                const int64_t t = w.t0(it) + rb * 32 + (lane & 31);
-                if (p.den != nullptr && ch == 0 && lane < 32 && t < w.T) p.den[(int64_t)chain * w.T + t] = den;
-            } else {
-                unit_products<true, true, false, DEC>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
-                                                      lane, L, nullptr, nullptr, dwt);
+        // the two tile buffers are distinct and nothing else touches them, which the restrict
+        // qualifiers state: without that the compiler makes the transposed fragment reads of this
+        // tile wait for the next tile's direct loads
+        [&](const u16 *__restrict__ cur, u16 *__restrict__ nxt) __attribute__((always_inline)) {
+            if (more) {
+                if constexpr (NM == 2)
+                    dma_qv_f(nxt, gq, gv, w.t0(it + 1), w.T, c, lane);
+                else
+                    dma_tile_f(nxt, gq, gk, gv, w.t0(it + 1), w.T, c, lane);
             }
-            stage(oacc);
-        }
-        lds_barrier();   // Y
-        wait_vm();
-        if (NM == 2 && more) phi_share(nxt, p, w.base, w.t0(it + 1), w.T, c, lane);
-        if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, c, lane, mv);
-        lds_barrier();   // X
+            if (it > 0) store(w.t0(it - 1));
+            {
+                f32x16 oacc[2];
+                if constexpr (NM == 1 || NM == 2) {
+                    float dpart;
+                    unit_products<true, true, true, false>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
+                                                           lane, L, &dpart, smem + oZF, dwt);
+                    const unsigned int du = __builtin_bit_cast(unsigned int, dpart);
+                    const auto r = __builtin_amdgcn_permlane32_swap(du, du, false, false);
+                    const float den =
+                        __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
+                    const float inv = 1.0f / den;
+    #pragma unroll
+                    for (int n = 0; n < 2; ++n)
+    #pragma unroll
+                        for (int e = 0; e < 16; ++e) oacc[n][e] *= inv;
+                    const int64_t t = w.t0(it) + rb * 32 + (lane & 31);
+                    if (p.den != nullptr && ch == 0 && lane < 32 && t < w.T) p.den[(int64_t)chain * w.T + t] = den;
+                } else {
+                    unit_products<true, true, false, DEC>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
+                                                          lane, L, nullptr, nullptr, dwt);
+                }
+                stage(oacc);
+            }
+            lds_barrier();   // Y
+            wait_vm();
+            if (NM == 2 && more) phi_share<false>(nxt, p, w.base, w.t0(it + 1), w.T, c, lane);
+            if (NM >= 3 && more) center_share<NM>(nxt, w.t0(it + 1), w.T, c, lane, mv);
+            lds_barrier();   // X
+        }(smem + (it & 1) * kBufF, smem + ((it + 1) & 1) * kBufF);
     }
     store(w.t0(w.ntiles - 1));
 }
