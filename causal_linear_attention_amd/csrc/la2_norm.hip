@@ -39,9 +39,28 @@ __device__ __forceinline__ float phi(float x) {
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
-    const nt_u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
-    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+// Eight elements of a row as loaded (unpacked to fp32 where they are used), so that a chunk's loads
+// can all be issued before its first store: the compiler cannot move a load above a store through
+// another pointer of the same type.
+template <typename E> struct Raw8;
+template <> struct Raw8<__bf16> {
+    nt_u32x4 u;
+};
+template <> struct Raw8<float> {
+    nt_f32x4 a, b;
+};
+
+__device__ __forceinline__ void load_raw(const __bf16 *p, Raw8<__bf16> &r) {
+    r.u = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
+}
+
+__device__ __forceinline__ void load_raw(const float *p, Raw8<float> &r) {
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p) + 1);
+}
+
+__device__ __forceinline__ void unpack(const Raw8<__bf16> &r, float (&x)[8]) {
+    const unsigned w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         x[2 * m] = __uint_as_float(w[m] << 16);
@@ -49,10 +68,15 @@ __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
     }
 }
 
-__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
-    const nt_f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p)),
-                   b = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4 *>(p) + 1);
-    x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w, x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+__device__ __forceinline__ void unpack(const Raw8<float> &r, float (&x)[8]) {
+    x[0] = r.a.x, x[1] = r.a.y, x[2] = r.a.z, x[3] = r.a.w, x[4] = r.b.x, x[5] = r.b.y, x[6] = r.b.z, x[7] = r.b.w;
+}
+
+template <typename E>
+__device__ __forceinline__ void load8(const E *p, float (&x)[8]) {
+    Raw8<E> r;
+    load_raw(p, r);
+    unpack(r, x);
 }
 
 // round to nearest even (finite inputs)
@@ -229,6 +253,31 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
             }
         }
         if constexpr (MODE == kKappa) continue;   // elementwise only
+        // the rows the second phase reads, all issued now (see Raw8)
+        constexpr bool ROWS2 = MODE == kDQ || MODE == kDK || MODE == kDQN;
+        constexpr int P2 = ROWS2 ? PPG : 1;
+        Raw8<E> ra[P2], rb[P2];   // DQN: u, q; DQ, DK: g, and q or k
+        float sa[P2], sb[P2];     // DQN: den, arow; DQ: dden
+        if constexpr (ROWS2) {
+#pragma unroll
+            for (int i = 0; i < PPG; ++i) {
+                const int64_t r = c0 + g * PPG + i;
+                sa[i] = sb[i] = 0.0f;
+                if (real(r)) {
+                    const int64_t t = pos(r);
+                    if constexpr (MODE == kDQN) {
+                        load_raw(uc + t * D, ra[i]);
+                        load_raw(qc + t * D, rb[i]);
+                        sa[i] = p.den[row0 + t];
+                        sb[i] = p.arow[row0 + t];
+                    } else {
+                        load_raw(gc + t * D, ra[i]);
+                        load_raw((MODE == kDQ ? qc : kc) + t * D, rb[i]);
+                        if constexpr (MODE == kDQ) sa[i] = ddc[t];
+                    }
+                }
+            }
+        }
         // this run's decayed sum, the running sum at its last step when starting from zero
         float loc[8];
 #pragma unroll
@@ -269,8 +318,8 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                     const int64_t t = ok ? pos(r) : 0;
                     float ur[8] = {}, qr[8] = {}, pq[8];
                     if (ok) {
-                        load8(uc + t * D, ur);
-                        load8(qc + t * D, qr);
+                        unpack(ra[i], ur);
+                        unpack(rb[i], qr);
                     }
                     float sg = 0.0f, pu = 0.0f, pz = 0.0f;
 #pragma unroll
@@ -287,7 +336,7 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                         pz += __shfl_xor(pz, w, CPR);
                     }
                     if (ok) {
-                        const float dn = p.den[row0 + t], av = p.arow[row0 + t];
+                        const float dn = sa[i], av = sb[i];
                         // ell_t = sum_{s<=t} lam^(t-s); 1 - lam >= 0.004 for every head's decay, so fp32 holds
                         // it to ~1e-6 relative
                         const float ell = l2 == 0.0f ? (float)(t + 1)
@@ -303,9 +352,9 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                 } else if (real(r)) {
                     const int64_t t = pos(r);
                     float gr[8], xr[8];
-                    load8(gc + t * D, gr);
-                    load8((MODE == kDQ ? qc : kc) + t * D, xr);
-                    const float dd = MODE == kDQ ? ddc[t] : 1.0f;
+                    unpack(ra[i], gr);
+                    unpack(rb[i], xr);
+                    const float dd = MODE == kDQ ? sa[i] : 1.0f;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) gr[m] = fmaf(dd, z[m], gr[m]) * phi_deriv<FMAP>(xr[m]);
                     store8(gc + t * D, gr);
