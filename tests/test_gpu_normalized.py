@@ -71,8 +71,10 @@ CASES = [
     (16, 16, 1, 128, 128, "bf16", 128, "none", "elu1"),    # one position: o = v
     (2, 128, 130, 128, 128, "bf16", 64, "none", "identity"),
     (1, 256, 64, 128, 128, "bf16", 256, "none", "elu1"),   # one whole tile
+    (2, 128, 65, 128, 128, "bf16", 64, "none", "elu1"),    # two tiles, the second with one real row
+    (1, 256, 129, 128, 128, "bf16", 128, "none", "elu1"),  # three tiles: k loaded two tiles ahead
 ]
-FUSED = CASES[-4:]
+FUSED = CASES[-6:]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c))
