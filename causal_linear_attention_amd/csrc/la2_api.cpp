@@ -706,11 +706,15 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
 namespace {
 
 // reuse_s: the S segment states that la2_forward left at the start of the workspace are still there.
+// nk_dden (the normalized form's backward, with skip_dq): the rows' denominator gradients; where the
+// dK/dV walk runs on unsplit chains it then also adds the denominator's part of dk and the feature
+// map's derivative (nk_elu: elu + 1, else the identity) and sets *nk_done.
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream, bool reuse_s, const float *state_in = nullptr,
                   const float *dstate_out = nullptr, float *dstate_in = nullptr, bool one_pass = false,
-                  bool skip_dq = false) {
+                  bool skip_dq = false, const float *nk_dden = nullptr, bool nk_elu = false,
+                  bool *nk_done = nullptr) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dout || (!dq && !skip_dq) || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
@@ -809,6 +813,11 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
             a.r_nsub = fp.nsub;
             a.decay = decay;
             a.H = (int)H;
+            if (nk_dden && skip_dq && !decay && fp.nseg == 1) {
+                a.dden = nk_dden;
+                a.nk_elu = nk_elu ? 1 : 0;
+                if (nk_done) *nk_done = true;
+            }
             return la2::launch_bwd1_bf16(a, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
         }
         la2::DkdvArgs a{};
@@ -983,16 +992,20 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
         if (la2::launch_vscan(c, (int)d, dtype, feature_map, kVDQN, s) != hipSuccess) return LA2_ERR_HIP;
     }
     // 3. the numerator's gradients: the plain backward on (phi(q), phi(k), v) with output gradient dn;
-    //    dv is final, dq (fp32 only) and dk hold the gradients with respect to phi(q), phi(k) so far
+    //    dv is final, dq (fp32 only) and dk hold the gradients with respect to phi(q), phi(k) so far --
+    //    except where the dK/dV walk runs on unsplit chains (bf16, d = d_v = 128, no decay): there it
+    //    also takes dden and returns the final dk
+    bool nk_done = false;
     st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, centered ? nullptr : dq, dk, dv, B, H, T,
                        d, d_v, block, dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, saved,
-                       nullptr, nullptr, nullptr, false, centered);
+                       nullptr, nullptr, nullptr, false, centered, dden, feature_map == LA2_PHI_ELU1, &nk_done);
     if (st != LA2_OK) return st;
     // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place; fp32
     //    only), dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative
     a.dden = dden;
     a.g = dq;
     if (!centered && la2::launch_vscan(a, (int)d, dtype, feature_map, kVDQ, s) != hipSuccess) return LA2_ERR_HIP;
+    if (nk_done) return LA2_OK;
     a.g = dk;
     a.zseg = L.z_bytes ? reinterpret_cast<float *>(ws + L.y_off) : nullptr;   // the forward's z sums stay
     if (a.nseg > 1 && la2::launch_vscan(a, (int)d, dtype, feature_map, kVYSeg, s) != hipSuccess) return LA2_ERR_HIP;

@@ -34,6 +34,15 @@
 //   dV_b[t] = sum_{s>=t} lam^(s-t) (q_s . k_t) do_s + lam^(64-t) k_t R_{b+1},   likewise dK_b with
 //   (do, v, q);   R_b = lam^64 R_{b+1} + sum_j lam^j q_j do_j^T.
 // The S producers then only stage tiles.
+//
+// With the gradient of the normalized form's denominators (NK; page "Lightning Attention", section 1:
+// o_t = n_t / den_t, den_t = phi(q_t) . z_t), run on (phi(q), phi(k), v, dn) with dn_t = do_t / den_t
+// and given dden_t = -(do_t . o_t) / den_t, the walk forms the whole gradient with respect to k:
+//   d phi(k_s) = sum_{t>=s} (dn_t . v_s + dden_t) phi(q_t),   dk_s = d phi(k_s) (.) phi'(k_s),
+// the score of every pair (t, s) taking dden_t on top, the later tiles' part y_{b+1} = sum over them of
+// dden_t phi(q_t) (a d-vector the R producers carry beside R), and phi'(k) = min(phi(k), 1) for
+// elu + 1 (1 for the identity), from the phi(k) tile; dk is rounded once.  S^T's LDS, unused without
+// dQ, holds the tile's dden and y.
 #include "la2_tile64_bf16.h"
 
 namespace la2 {
@@ -48,6 +57,7 @@ constexpr int oQ1 = 0, oK1 = kTile1, oV1 = 2 * kTile1, oO1 = 3 * kTile1;   // q,
 constexpr int oRT1 = 4 * kTile1;                                           // R^T [d_v][d] bf16
 constexpr int oST1 = oRT1 + D1 * D1;                                       // S^T [d_v][d] bf16
 constexpr int oOS1 = oST1 + D1 * D1;                                       // per-consumer output staging
+constexpr int oDD1 = oST1, oY1 = oST1 + 2 * TB1;   // NK (no S^T): the tile's dden, y (fp32, 64 and 128)
 constexpr int kOS1 = 2 * 32 * 64;                                          //   (two units of 32 x 64)
 constexpr int kLds1 = oOS1 + 4 * kOS1;
 constexpr int NCH1 = kTile1 / 8 / kT1;   // 16-byte chunks per thread and tile (2)
@@ -90,15 +100,46 @@ __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid
 //   DV: rows s of dV; scores Q[t] . K[s] for t >= s; value dO; inter R^T K^T (R^T rows read plain)
 //   DK: rows s of dK; scores dO[t] . V[s] for t >= s; value Q; inter R V^T
 //   DQ: rows t of dQ; scores V[s] . dO[t] for s <= t; value K; inter S dO^T
-template <Unit U, bool DEC = false>
+template <Unit U, bool DEC = false, bool NK = false>
 __device__ __forceinline__ void out_unit(f32x16 (&oacc)[2], const u16 *smem, int orow, int ch, int lane,
                                          const LaneOff &L, const DecayW &dw) {
     const u16 *sB = smem + (U == Unit::DV ? oK1 : U == Unit::DK ? oV1 : oO1);   // output-row role
     const u16 *sA = smem + (U == Unit::DV ? oQ1 : U == Unit::DK ? oO1 : oV1);   // source-row role
     const u16 *sC = smem + (U == Unit::DV ? oO1 : U == Unit::DK ? oQ1 : oK1);   // value role
     const u16 *sSt = smem + (U == Unit::DQ ? oST1 : oRT1);
-    unit_products<U == Unit::DQ, U == Unit::DV, false, DEC>(oacc, sB, sA, sC, sSt, orow, ch, lane, L, nullptr,
-                                                            nullptr, dw);
+    constexpr bool ADD = NK && U == Unit::DK;
+    unit_products<U == Unit::DQ, U == Unit::DV, false, DEC, ADD>(
+        oacc, sB, sA, sC, sSt, orow, ch, lane, L, nullptr, nullptr, dw,
+        ADD ? reinterpret_cast<const float *>(smem + oDD1) : nullptr);
+}
+
+// NK: the DK unit's accumulators (rows s of block orow, columns 64ch..64ch+63) plus y, times phi'(k_s)
+// (elu + 1: min(phi(k), 1) from the phi(k) tile; the identity: 1).  Entries 4q..4q+3 of acc[n] are
+// columns 32n + 8q + 4h .. + 3 of the unit.
+__device__ __forceinline__ void nk_finish(f32x16 (&oacc)[2], const u16 *smem, int orow, int ch, int lane, bool elu) {
+    const int h = lane >> 5, col = lane & 31;
+    const float *sY = reinterpret_cast<const float *>(smem + oY1);
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c0 = 64 * ch + 32 * n + 8 * q + 4 * h;
+            const float4 y = *reinterpret_cast<const float4 *>(sY + c0);
+            float g[4] = {oacc[n][4 * q] + y.x, oacc[n][4 * q + 1] + y.y, oacc[n][4 * q + 2] + y.z,
+                          oacc[n][4 * q + 3] + y.w};
+            if (elu) {
+                const u32x2 kk = *reinterpret_cast<const u32x2 *>(smem + oK1 + nat_off<D1>(orow * 32 + col, c0 >> 3) +
+                                                                  (c0 & 7));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const unsigned int w = kk[j >> 1];
+                    const float pk = __builtin_bit_cast(float, (j & 1) ? (w & 0xffff0000u) : (w << 16));
+                    g[j] *= fminf(pk, 1.0f);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oacc[n][4 * q + j] = g[j];
+        }
 }
 
 __device__ __forceinline__ float chain_l2(const Bwd1Args &p, int chain) {
@@ -126,9 +167,11 @@ __device__ __forceinline__ Walk1 walk_of(const Bwd1Args &p, int chain, int seg) 
 // R_b = R_{b+1} + Q_b^T dO_b is formed at the top of tile b but published as R^T only after barrier
 // Y (dV and dK of tile b use R_{b+1}); S_{b-1} = S_b - K_b^T V_b is published before Y for dQ.
 // Without dQ (ONE = false) the S producers hold no state and only stage their part of each tile.
-template <bool SK, bool ONE, bool DEC>
+template <bool SK, bool ONE, bool DEC, bool NK>
 __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain, int seg, int ch, int lane) {
     constexpr bool HOLD = ONE || !SK;   // this wave holds a state
+    constexpr bool YR = NK && !SK;              // NK: this wave carries its 64 entries of y
+    constexpr bool DDS = NK && SK;              // NK: wave 6 stages each tile's dden
     const Walk1 w = walk_of(p, chain, seg);
     const int kb0 = 2 * ch, tid = threadIdx.x;
     const int h = lane >> 5, col = lane & 31;
@@ -168,6 +211,25 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
     }
     // the blocks as R^T or S^T (bf16, [d_v][d]) into LDS: accumulator entries 4g..4g+3 of a lane are
     // four consecutive d of one d_v row, one 8-byte write
+    // NK: y of state rows d = 32(kb0 + i) + col (fp32, the same in both halves of the wave), and the
+    // next tile's dden (one position per lane) for wave 6
+    float ytot[YR ? 2 : 1] = {}, ddn = 0.0f;
+    const float *gdd = DDS ? p.dden + (int64_t)chain * p.T : nullptr;
+    auto load_dd = [&](int64_t t0) {
+        if constexpr (DDS) ddn = ch == 0 && t0 + lane < w.T ? gdd[t0 + lane] : 0.0f;
+    };
+    auto store_dd = [&]() {
+        if constexpr (DDS)
+            if (ch == 0) reinterpret_cast<float *>(smem + oDD1)[lane] = ddn;
+    };
+    auto write_y = [&]() {
+        if constexpr (YR)
+            if (h == 0) {
+                float *sY = reinterpret_cast<float *>(smem + oY1);
+                sY[kb0 * 32 + col] = ytot[0];
+                sY[(kb0 + 1) * 32 + col] = ytot[1];
+            }
+    };
     auto write_state = [&]() {
         if constexpr (!HOLD) return;
         u16 *dst = smem + (SK ? oST1 : oRT1);
@@ -183,8 +245,11 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
 
     Staged1 st;
     load_tile1(st, gq, gk, gv, go, w.t0(0), w.T, tid);
+    load_dd(w.t0(0));
     store_tile1(st, smem, tid);
+    store_dd();
     if (!SK) write_state();
+    write_y();
     lds_barrier();   // X: the first tile and R^T
 
     for (int it = 0; it < w.ntiles; ++it) {
@@ -199,12 +264,29 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[s][r] *= lam64;
             }
+            float ypart[YR ? 2 : 1] = {};
 #pragma unroll
             for (int x = 0; x < TB1 / 16; ++x) {
                 bf16x8 fa[2], fc[4];
+                float dd[YR ? 8 : 1];
+                if constexpr (YR) {
+                    // dden at the positions 16x + 8h + e of the fragments' elements e
+                    const float *sDd = reinterpret_cast<const float *>(smem + oDD1) + 16 * x + 8 * h;
+                    const float4 a0 = *reinterpret_cast<const float4 *>(sDd),
+                                 a1 = *reinterpret_cast<const float4 *>(sDd + 4);
+                    dd[0] = a0.x, dd[1] = a0.y, dd[2] = a0.z, dd[3] = a0.w;
+                    dd[4] = a1.x, dd[5] = a1.y, dd[6] = a1.z, dd[7] = a1.w;
+                }
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {   // state row blocks kb0 + i are column blocks 2ch + i of the tile
                     fa[i] = flip8(rd_tr(sA, 16 * x, L.trc[0][i]), sign);
+                    if constexpr (YR) {
+                        const u32x4 u = __builtin_bit_cast(u32x4, fa[i]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            ypart[i] += dd[2 * j] * __builtin_bit_cast(float, u[j] << 16) +
+                                        dd[2 * j + 1] * __builtin_bit_cast(float, u[j] & 0xffff0000u);
+                    }
                     if constexpr (DEC) {
                         u32x4 u = __builtin_bit_cast(u32x4, fa[i]);
 #pragma unroll
@@ -219,21 +301,38 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
 #pragma unroll
                 for (int s = 0; s < 8; ++s) sacc[s] = mfma(fa[s / 4], fc[s % 4], sacc[s]);
             }
+            if constexpr (YR) {
+                // the two halves of the wave hold positions 8h.. of every 16: add the partner's
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const unsigned int yu = __builtin_bit_cast(unsigned int, ypart[i]);
+                    const auto r = __builtin_amdgcn_permlane32_swap(yu, yu, false, false);
+                    ytot[i] += __builtin_bit_cast(float, (unsigned int)r[0]) +
+                               __builtin_bit_cast(float, (unsigned int)r[1]);
+                }
+            }
         }
         if (SK) write_state();
         // this wave's part of the next tile: in flight while the consumers form this tile's gradients
-        if (more) load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+        if (more) {
+            load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+            load_dd(w.t0(it + 1));
+        }
         lds_barrier();   // Y
         if (!SK) write_state();
+        write_y();
         lds_barrier();   // Z
-        if (more) store_tile1(st, smem, tid);
+        if (more) {
+            store_tile1(st, smem, tid);
+            store_dd();
+        }
         lds_barrier();   // X
     }
 }
 
 // Consumer wave c = 2rb + ch.  Each unit is staged in the wave's own 8 KiB of LDS and stored as whole
 // 128-byte row pieces, so that at most one unit's accumulators are held at a time.
-template <bool ONE, bool DEC>
+template <bool ONE, bool DEC, bool NK>
 __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain, int seg, int c, int lane) {
     const Walk1 w = walk_of(p, chain, seg);
     const int rb = c >> 1, ch = c & 1, tid = threadIdx.x;
@@ -285,7 +384,8 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
             f32x16 oacc[2];
             out_unit<Unit::DV, DEC>(oacc, smem, rb, ch, lane, L, dwt);
             stage(oacc, ob);
-            out_unit<Unit::DK, DEC>(oacc, smem, rb, ch, lane, L, dwt);
+            out_unit<Unit::DK, DEC, NK>(oacc, smem, rb, ch, lane, L, dwt);
+            if constexpr (NK) nk_finish(oacc, smem, rb, ch, lane, p.nk_elu != 0);
             stage(oacc, ob + 2048);
             store(ob, gdv, t0);
             store(ob + 2048, gdk, t0);
@@ -303,8 +403,9 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
     }
 }
 
-template <bool ONE, bool DEC>
+template <bool ONE, bool DEC, bool NK = false>
 __global__ __launch_bounds__(kT1, 1) void bwd1_bf16_kernel(Bwd1Args p) {
+    static_assert(!NK || (!ONE && !DEC), "the normalized dk terms ride on the dK/dV walk without decay");
     __shared__ __attribute__((aligned(16))) u16 smem[kLds1];
     // the wave index as a scalar: every branch on a wave's role is uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -313,11 +414,11 @@ __global__ __launch_bounds__(kT1, 1) void bwd1_bf16_kernel(Bwd1Args p) {
     const int64_t NT = (p.T + TB1 - 1) / TB1;
     if ((int64_t)seg * p.seg_tiles >= NT) return;
     if (wave < 4)
-        consumer<ONE, DEC>(p, smem, chain, seg, wave, lane);
+        consumer<ONE, DEC, NK>(p, smem, chain, seg, wave, lane);
     else if (wave < 6)
-        producer<false, ONE, DEC>(p, smem, chain, seg, wave & 1, lane);
+        producer<false, ONE, DEC, NK>(p, smem, chain, seg, wave & 1, lane);
     else
-        producer<true, ONE, DEC>(p, smem, chain, seg, wave & 1, lane);
+        producer<true, ONE, DEC, NK>(p, smem, chain, seg, wave & 1, lane);
 }
 
 }  // namespace
@@ -326,6 +427,12 @@ hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s) {
     const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
     if (a.dq != nullptr && a.decay != nullptr) return hipErrorInvalidValue;   // no one-pass walk with a decay
     if (a.decay != nullptr && a.H <= 0) return hipErrorInvalidValue;
+    if (a.dden != nullptr) {
+        // y starts from zero at the chain's end: unsplit chains only
+        if (a.dq != nullptr || a.decay != nullptr || a.nseg != 1 || a.r_states != nullptr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((bwd1_bf16_kernel<false, false, true>), dim3(items), dim3(kT1), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.dq != nullptr)
         hipLaunchKernelGGL((bwd1_bf16_kernel<true, false>), dim3(items), dim3(kT1), 0, s, a);
     else if (a.decay != nullptr)

@@ -186,6 +186,10 @@ struct Bwd1Args {
     // with the per-head decay lam ([H] fp32, chain c is head c % H) or nullptr for lam = 1
     const float *decay;
     int H;
+    // the normalized form's dk (dq = nullptr, no decay, unsplit chains): dden [chains, T] fp32, the
+    // gradient of each row's denominator, or nullptr; nk_elu != 0: phi = elu + 1 (else the identity)
+    const float *dden;
+    int nk_elu;
 };
 hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s);
 

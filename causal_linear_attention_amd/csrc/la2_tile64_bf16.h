@@ -96,10 +96,11 @@ __device__ __forceinline__ void lds_write8(u16 *s, int off, const u32x2 &v) {
 // to bf16 together.  In the diagonal block the entries on the wrong side of the causal mask are
 // zeroed first (SRC_BEFORE: sources at or before the output row are kept, else at or after).  RS:
 // the lane's kept fp32 scores are also added to *rs (half of the output row's sum over the block).
-// DEC (a decay): each score is multiplied by wt[r] first (decay_weights below).
-template <bool SRC_BEFORE, bool DIAG, bool RS = false, bool DEC = false>
+// DEC (a decay): each score is multiplied by wt[r] first (decay_weights below).  ADD: ad[r] is added
+// to each score first (a value per source row: the normalized form's denominator gradient).
+template <bool SRC_BEFORE, bool DIAG, bool RS = false, bool DEC = false, bool ADD = false>
 __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int h, int col, float *rs,
-                                        const float (&wt)[16]) {
+                                        const float (&wt)[16], const float (&ad)[16]) {
     u32x4 w[2];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -107,6 +108,10 @@ __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int 
         if constexpr (DEC) {
             a *= wt[2 * p];
             b *= wt[2 * p + 1];
+        }
+        if constexpr (ADD) {
+            a += ad[2 * p];
+            b += ad[2 * p + 1];
         }
         if (DIAG) {
             const int dist = 4 * h - col + 8 * (p >> 1) + 2 * (p & 1);   // source - output of entry 2p
@@ -121,17 +126,30 @@ __device__ __forceinline__ void block_p(const f32x16 &acc, bf16x8 (&pf)[2], int 
 }
 
 // The intra-tile contribution of source block u to a unit: scores of the block's 32 source rows
-// against the unit's 32 output rows (B operand bf), then P times the value rows of the block.
-template <bool SRC_BEFORE, bool DIAG, bool RS, bool DEC>
+// against the unit's 32 output rows (B operand bf), then P times the value rows of the block.  ADD:
+// sAdd[j] (fp32, per source position j of the tile) is added to every score of source row j.
+template <bool SRC_BEFORE, bool DIAG, bool RS, bool DEC, bool ADD = false>
 __device__ __forceinline__ void intra_block(f32x16 (&oacc)[2], const bf16x8 (&bf)[KS1], const u16 *sA,
                                             const u16 *sC, int u, const LaneOff &L, int h, int col, float *rs,
-                                            const float (&wt)[16]) {
+                                            const float (&wt)[16], const float *sAdd = nullptr) {
     const f32x16 zero = {};
     f32x16 acc = mfma(rd_plain(sA, u * 32, 0, L), bf[0], zero);
 #pragma unroll
     for (int ks = 1; ks < KS1; ++ks) acc = mfma(rd_plain(sA, u * 32, ks, L), bf[ks], acc);
+    float add[16] = {};
+    if constexpr (ADD) {
+        // accumulator entries 4g..4g+3 are source rows u*32 + 8g + 4h .. + 3: one 16-byte read each
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 v = *reinterpret_cast<const float4 *>(sAdd + u * 32 + 8 * g + 4 * h);
+            add[4 * g] = v.x;
+            add[4 * g + 1] = v.y;
+            add[4 * g + 2] = v.z;
+            add[4 * g + 3] = v.w;
+        }
+    }
     bf16x8 pf[2];
-    block_p<SRC_BEFORE, DIAG, RS, DEC>(acc, pf, h, col, rs, wt);
+    block_p<SRC_BEFORE, DIAG, RS, DEC, ADD>(acc, pf, h, col, rs, wt, add);
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -177,10 +195,13 @@ __device__ __forceinline__ DecayW decay_weights(float l2, int orow, int lane) {
 // bf16, row 1 the rounding's remainder rounded to bf16, and the other rows zero; the partner lane
 // (lane ^ 32) holds the other half of the scores.
 // DEC (a decay): the inter product is weighted by dw.wi and the scores by dw.wd, wf (decay_weights).
-template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false, bool DEC = false>
+// ADD: sAdd[j] (fp32, per source position j of the tile) is added to every score of source row j
+// before it is masked and packed.
+template <bool SRC_BEFORE, bool INTER_PLAIN, bool DEN = false, bool DEC = false, bool ADD = false>
 __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, const u16 *sA, const u16 *sC,
                                               const u16 *sSt, int orow, int ch, int lane, const LaneOff &L,
-                                              float *den, const u16 *sZ, const DecayW &dw) {
+                                              float *den, const u16 *sZ, const DecayW &dw,
+                                              const float *sAdd = nullptr) {
     const int h = lane >> 5, col = lane & 31;
     bf16x8 bf[KS1];
 #pragma unroll
@@ -214,8 +235,9 @@ __device__ __forceinline__ void unit_products(f32x16 (&oacc)[2], const u16 *sB, 
     // intra-tile: the whole source block before (SRC_BEFORE) or after the diagonal, where there is one,
     // then the diagonal block
     if (SRC_BEFORE ? orow == 1 : orow == 0)
-        intra_block<SRC_BEFORE, false, DEN, DEC>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col, &dd, dw.wf);
-    intra_block<SRC_BEFORE, true, DEN, DEC>(oacc, bf, sA, sC, orow, L, h, col, &dd, dw.wd);
+        intra_block<SRC_BEFORE, false, DEN, DEC, ADD>(oacc, bf, sA, sC, SRC_BEFORE ? 0 : 1, L, h, col, &dd, dw.wf,
+                                                      sAdd);
+    intra_block<SRC_BEFORE, true, DEN, DEC, ADD>(oacc, bf, sA, sC, orow, L, h, col, &dd, dw.wd, sAdd);
     if constexpr (DEN) *den = dd;
 }
 

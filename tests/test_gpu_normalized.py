@@ -220,6 +220,29 @@ def test_backward_normalized_matches_oracle(case):
     run_backward_case(*case, seed=401 + case[2])
 
 
+@pytest.mark.parametrize("fmap,T", [("elu1", 200), ("elu1", 65), ("identity", 130)])
+def test_normalized_dk_in_the_walk(fmap, T):
+    """bf16, d = d_v = 128, no decay, unsplit chains: the dK/dV walk takes the denominator's part of dk
+    and the feature map's derivative on board (dk rounded once).  Against the oracle, and against the
+    separate reverse scan over dden phi(q) it replaces (the walk forced off through the test build)."""
+    x = inputs.make_random(2, 128, T, 128, 128, dtype="bf16", seed=707 + T, decay="none", backward=True)
+    if fmap == "identity":
+        x["q"], x["k"] = positive(x["q"]), positive(x["k"])
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o = la2.forward_normalized(q, k, v, None, 128, fmap)
+    dq, dk, dv_ = la2.backward_normalized(q, k, v, o, do, None, 128, fmap)
+    with binding.plan_override(legacy_dkdv=True):
+        dq_s, dk_s, dv_s = la2.backward_normalized(q, k, v, o, do, None, 128, fmap)
+    torch.cuda.synchronize()
+    ref = oracle.backward_normalized(*(f64(x[n]) for n in ("q", "k", "v", "do")), None, fmap)
+    e_walk, e_scan = rel_err(f64(dk), ref[1]), rel_err(f64(dk_s), ref[1])
+    print(fmap, T, f"dk max|err|/max|ref|: in the walk {e_walk:.2e}, separate scan {e_scan:.2e}", flush=True)
+    assert e_walk <= TOL["bf16"] and rel_err(f64(dk), f64(dk_s)) <= TOL["bf16"]
+    assert torch.equal(dq, dq_s)
+    for g, r in ((dq, ref[0]), (dv_, ref[2])):
+        assert rel_err(f64(g), r) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("seg", [64, 128, 320])
 def test_backward_normalized_forced_segments(seg):
     """Denominator scans over forced segments: forward and reverse carries across up to 16 segments,
