@@ -950,14 +950,15 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
                        la2::launch_vscan(c, (int)d, dtype, feature_map, kVKappa, s) != hipSuccess))
             return LA2_ERR_HIP;
         // a_t = dout_t . Vbar_t: the denominator scan with (query, key) = (dout, v) and the identity map
+        // (where the scan U below is one fused launch, that launch forms it as its rows' sums)
         la2::DenArgs va = c;
         va.q = dout;
         va.k = v;
         va.pq = va.pk = nullptr;
         va.den = reinterpret_cast<float *>(ws + L.a_off);
         va.zseg = L.dp.nseg > 1 ? reinterpret_cast<float *>(ws + L.vz_off) : nullptr;
-        if ((va.nseg > 1 && la2::launch_vscan(va, (int)d_v, dtype, 0, kVZSeg, s) != hipSuccess) ||
-            la2::launch_vscan(va, (int)d_v, dtype, 0, kVDen, s) != hipSuccess)
+        if (!fused && ((va.nseg > 1 && la2::launch_vscan(va, (int)d_v, dtype, 0, kVZSeg, s) != hipSuccess) ||
+                       la2::launch_vscan(va, (int)d_v, dtype, 0, kVDen, s) != hipSuccess))
             return LA2_ERR_HIP;
         // U = the forward scan with (query, key, value) = (dout, v, phi(k) - m), as the dQ pass of the
         // plain backward: its state is (sum kap v^T)^T
@@ -967,6 +968,7 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
             f.k = v;
             f.v = k;
             f.y = ws + L.u_off;
+            f.den = va.den;   // a_t
             f.T = T;
             f.seg_len = (T + 63) / 64 * 64;
             f.nseg = 1;

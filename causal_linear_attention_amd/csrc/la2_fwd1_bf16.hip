@@ -9,7 +9,9 @@
 //   O_b[t] = sum_{s<=t} lam^(t-s) (q_t . k_s) v_s + lam^(t+1) q_t S_{b-1},
 //   S_b = lam^64 S_{b-1} + sum_j lam^(63-j) k_j v_j^T.
 // and, with a key/value pair of roles (b, c) and a query role a, the same scan serves the dQ pass of
-// the two-pass backward and the scan U of the normalized backward (its state read transposed).
+// the two-pass backward and the scan U of the normalized backward (its state read transposed); the
+// latter, with (a, b) = (do, v), also writes each row's do_t . (the prefix sum of v through t), by
+// the normalized form's denominator machinery below without the division.
 //
 // Workgroup of eight waves, two per SIMD, in two roles (the layout of the one-pass backward):
 //   consumers (waves 0-3, c = 2rb + ch): columns 64ch..64ch+63 of the output rows in block rb;
@@ -251,7 +253,8 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         const auto r = __builtin_amdgcn_permlane32_swap(zu, zu, false, false);
         return __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
     };
-    constexpr bool NRM = NM == 1 || NM == 2;   // the normalized forward (z, denominators)
+    constexpr bool NRM = NM == 1 || NM == 2;   // the normalized forward (its segment sums of phi(k))
+    constexpr bool ZS = NM >= 1;               // z and the rows' sums (every normalized instance)
     const bool sums = NRM && p.msum != nullptr;
     float mv[8];
     if constexpr (NM >= 3) center_means(p, chain, wave, lane, mv);
@@ -277,7 +280,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                                  pack_bf16(sacc[jb][4 * q + 2], sacc[jb][4 * q + 3])};
                 lds_write8(smem + oSTF, jb * 32 * D1 + pwq[q], v);
             }
-        if constexpr (NRM) {
+        if constexpr (ZS) {
             const float z = z_whole();
             // z of column 32pw + col in row 0 (rounded to bf16) and row 1 (the remainder) of the z tile;
             // lanes h = 0 write row 0, h = 1 row 1
@@ -288,7 +291,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
         }
     };
     dma_tile_f(smem, gq, gk, gv, w.t0(0), w.T, wave, lane);
-    if constexpr (NRM) {
+    if constexpr (ZS) {
         // the z tile's zero rows 2..31 (rows 0 and 1 come with every copy of the state)
         const u32x4 zz = {0u, 0u, 0u, 0u};
         for (int i = (wave - 4) * 64 + lane; i < 30 * D1 / 8; i += 256)
@@ -356,7 +359,7 @@ __device__ __forceinline__ void producer_f(const Fwd1Args &p, u16 *smem, int cha
                     for (int jb = 0; jb < 4; ++jb) fc[jb] = rd_tr(sV, 16 * x, trv[jb]);
     #pragma unroll
                     for (int jb = 0; jb < 4; ++jb) sacc[jb] = mfma(fa, fc[jb], sacc[jb]);
-                    if constexpr (NRM) {
+                    if constexpr (ZS) {
                         // fa: state row 32pw + col of K^T at positions 16x + 8h .. 16x + 8h + 7
                         const u32x4 u = __builtin_bit_cast(u32x4, fa);
     #pragma unroll
@@ -455,7 +458,7 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
             if (it > 0) store(w.t0(it - 1));
             {
                 f32x16 oacc[2];
-                if constexpr (NM == 1 || NM == 2) {
+                if constexpr (NM >= 1) {
                     float dpart;
                     unit_products<true, true, true, false>(oacc, cur + oQF, cur + oKF, cur + oVF, smem + oSTF, rb, ch,
                                                            lane, L, &dpart, smem + oZF, dwt);
@@ -463,11 +466,13 @@ __device__ __forceinline__ void consumer_f(const Fwd1Args &p, u16 *smem, int cha
                     const auto r = __builtin_amdgcn_permlane32_swap(du, du, false, false);
                     const float den =
                         __builtin_bit_cast(float, (unsigned int)r[0]) + __builtin_bit_cast(float, (unsigned int)r[1]);
-                    const float inv = 1.0f / den;
-    #pragma unroll
-                    for (int n = 0; n < 2; ++n)
-    #pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[n][e] *= inv;
+                    if constexpr (NM <= 2) {   // the scans U are not divided
+                        const float inv = 1.0f / den;
+#pragma unroll
+                        for (int n = 0; n < 2; ++n)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) oacc[n][e] *= inv;
+                    }
                     const int64_t t = w.t0(it) + rb * 32 + (lane & 31);
                     if (p.den != nullptr && ch == 0 && lane < 32 && t < w.T) p.den[(int64_t)chain * w.T + t] = den;
                 } else {

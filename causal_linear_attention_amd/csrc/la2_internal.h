@@ -155,7 +155,8 @@ struct Fwd1Args {
     // the chain's mean of phi(v) from msum (the normalized backward's centered keys); unsplit only
     int norm;
     void *pq, *pk;          // where phi(q), phi(k) are also written (bf16 [chains, T, 128]), or nullptr
-    float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr
+    float *den;             // where the denominators are also written (fp32 [chains, T]), or nullptr;
+                            //   norm 3, 4: q_t . (the prefix sum of k through t), the rows undivided
     float *msum;            // where each msum_seg-position segment's sum of phi(k) is also written (fp32
     int64_t msum_seg;       //   [chains, ceil(T / msum_seg), 128]; msum_seg a multiple of 64), or nullptr
     const float *decay;     // per-head decay lam ([H] fp32, chain c is head c % H), or nullptr for lam = 1;
