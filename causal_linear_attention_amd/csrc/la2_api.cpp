@@ -705,17 +705,30 @@ int la2_forward_normalized(const void *q, const void *k, const void *v, const fl
 
 namespace {
 
+// Where the normalized backward's dK/dV walk takes the denominator's part of dk and forms dn = do / den
+// itself: bf16, d = d_v = 128, no decay, chains the dK/dV plan does not split.
+bool nk_walk(int64_t B, int64_t H, int64_t T, int64_t d, int64_t dv, int block, int dtype, const float *decay) {
+    if (dtype != LA2_BF16 || d != 128 || dv != 128 || decay || forced().legacy_dkdv || !fused_dkdv(d, dv, dtype))
+        return false;
+    return make_plan(B, H, T, d, dv, block, dtype, true).nseg == 1;
+}
+
 // reuse_s: the S segment states that la2_forward left at the start of the workspace are still there.
-// nk_dden (the normalized form's backward, with skip_dq): the rows' denominator gradients; where the
-// dK/dV walk runs on unsplit chains it then also adds the denominator's part of dk and the feature
-// map's derivative (nk_elu: elu + 1, else the identity) and sets *nk_done.
+// nk_dden, nk_den (the normalized form's backward, with skip_dq, where nk_walk holds): the rows'
+// denominator gradients and denominators; dout is then do, and the dK/dV walk forms dn = do / den,
+// adds the denominator's part of dk and the feature map's derivative (nk_elu: elu + 1, else the
+// identity) and sets *nk_done.
 int backward_impl(const void *q, const void *k, const void *v, const float *decay, const void *dout, void *dq,
                   void *dk, void *dv, int64_t B, int64_t H, int64_t T, int64_t d, int64_t d_v, int block, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream, bool reuse_s, const float *state_in = nullptr,
                   const float *dstate_out = nullptr, float *dstate_in = nullptr, bool one_pass = false,
                   bool skip_dq = false, const float *nk_dden = nullptr, bool nk_elu = false,
-                  bool *nk_done = nullptr) {
+                  bool *nk_done = nullptr, const float *nk_den = nullptr) {
     if (dtype != LA2_F32 && dtype != LA2_BF16) return LA2_ERR_UNSUPPORTED;
+    // dout given as do rather than dn: only the walk that divides it may run
+    if ((nk_den != nullptr) != (nk_dden != nullptr) ||
+        (nk_den && (!skip_dq || state_in || dstate_out || dstate_in || !nk_walk(B, H, T, d, d_v, block, dtype, decay))))
+        return LA2_ERR_UNSUPPORTED;
     if (!q || !k || !v || !dout || (!dq && !skip_dq) || !dk || !dv) return LA2_ERR_NULL_POINTER;
     int st = check_sizes(B, H, T, d, d_v, block, dtype);
     if (st != LA2_OK) return st;
@@ -815,6 +828,7 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
             a.H = (int)H;
             if (nk_dden && skip_dq && !decay && fp.nseg == 1) {
                 a.dden = nk_dden;
+                a.den = nk_den;
                 a.nk_elu = nk_elu ? 1 : 0;
                 if (nk_done) *nk_done = true;
             }
@@ -932,10 +946,13 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
             if (la2::launch_vscan(a, (int)d, dtype, feature_map, kVDen, s) != hipSuccess) return LA2_ERR_HIP;
         }
     }
-    // 2. dn = do / den, dden = -(do . o) / den
-    if (la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)
-        return LA2_ERR_HIP;
     const bool centered = dtype == LA2_BF16;
+    // where the dK/dV walk takes the denominator's dk it also forms dn = do / den as it stages each tile,
+    // and the centered dq combination writes dden: no pass over o
+    const bool nk = centered && nk_walk(B, H, T, d, d_v, block, dtype, decay);
+    // 2. dn = do / den, dden = -(do . o) / den
+    if (!nk && la2::launch_grad_rows(o, dout, a.den, dn, dden, chains * T, (int)d_v, dtype, s) != hipSuccess)
+        return LA2_ERR_HIP;
     if (centered) {
         // bf16: dq of the centered feature map (la2_norm.hip, mode 7), every step in fp32 except the scan U
         // of (dout, v, phi(k) - m), whose values are small against the result
@@ -991,16 +1008,18 @@ int backward_normalized_impl(const void *q, const void *k, const void *v, const 
         c.u = ws + L.u_off;
         c.arow = va.den;
         c.g = dq;
+        c.dden_out = nk ? dden : nullptr;
         if (la2::launch_vscan(c, (int)d, dtype, feature_map, kVDQN, s) != hipSuccess) return LA2_ERR_HIP;
     }
     // 3. the numerator's gradients: the plain backward on (phi(q), phi(k), v) with output gradient dn;
     //    dv is final, dq (fp32 only) and dk hold the gradients with respect to phi(q), phi(k) so far --
-    //    except where the dK/dV walk runs on unsplit chains (bf16, d = d_v = 128, no decay): there it
-    //    also takes dden and returns the final dk
+    //    except where the dK/dV walk runs on unsplit chains (nk): there it reads do and den for dn, also
+    //    takes dden and returns the final dk
     bool nk_done = false;
-    st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, dn, centered ? nullptr : dq, dk, dv, B, H, T,
-                       d, d_v, block, dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream, saved,
-                       nullptr, nullptr, nullptr, false, centered, dden, feature_map == LA2_PHI_ELU1, &nk_done);
+    st = backward_impl(L.phi ? a.pq : q, L.phi ? a.pk : k, v, decay, nk ? dout : dn, centered ? nullptr : dq, dk, dv,
+                       B, H, T, d, d_v, block, dtype, L.scan_bytes ? ws + L.scan_off : nullptr, L.scan_bytes, stream,
+                       saved, nullptr, nullptr, nullptr, false, centered, nk ? dden : nullptr,
+                       feature_map == LA2_PHI_ELU1, &nk_done, nk ? a.den : nullptr);
     if (st != LA2_OK) return st;
     // 4. the denominator's: dq_t += dden_t z_t (the forward segment sums of phi(k) are still in place; fp32
     //    only), dk_t += sum_{s >= t} lam^(s-t) dden_s phi(q_s); then the feature map's derivative

@@ -37,7 +37,8 @@
 //
 // With the gradient of the normalized form's denominators (NK; page "Lightning Attention", section 1:
 // o_t = n_t / den_t, den_t = phi(q_t) . z_t), run on (phi(q), phi(k), v, dn) with dn_t = do_t / den_t
-// and given dden_t = -(do_t . o_t) / den_t, the walk forms the whole gradient with respect to k:
+// (formed here: each do row is scaled by 1 / den_t in fp32 and rounded on its way into LDS) and given
+// dden_t = -(do_t . o_t) / den_t, the walk forms the whole gradient with respect to k:
 //   d phi(k_s) = sum_{t>=s} (dn_t . v_s + dden_t) phi(q_t),   dk_s = d phi(k_s) (.) phi'(k_s),
 // the score of every pair (t, s) taking dden_t on top, the later tiles' part y_{b+1} = sum over them of
 // dden_t phi(q_t) (a d-vector the R producers carry beside R), and phi'(k) = min(phi(k), 1) for
@@ -68,10 +69,13 @@ enum class Unit { DV, DK, DQ };
 
 struct Staged1 {
     u32x4 q[NCH1], k[NCH1], v[NCH1], o[NCH1];
+    float den[NCH1];   // DS: the denominators of the dO chunks' rows
 };
 
+// DS: the dO role is do, its rows divided by den (the chain's [T] denominators) when staged.
+template <bool DS = false>
 __device__ __forceinline__ void load_tile1(Staged1 &r, const u16 *q, const u16 *k, const u16 *v, const u16 *o,
-                                           int64_t t0, int64_t T, int tid) {
+                                           const float *den, int64_t t0, int64_t T, int tid) {
     const int64_t bytes = (T - t0) * D1 * 2;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + t0 * D1, bytes), rk = make_rsrc(k + t0 * D1, bytes),
                                  rv = make_rsrc(v + t0 * D1, bytes), ro = make_rsrc(o + t0 * D1, bytes);
@@ -82,9 +86,14 @@ __device__ __forceinline__ void load_tile1(Staged1 &r, const u16 *q, const u16 *
         r.k[s] = bload(rk, off);
         r.v[s] = bload(rv, off);
         r.o[s] = bload(ro, off);
+        if constexpr (DS) {
+            const int64_t t = t0 + cid / (D1 / 8);
+            r.den[s] = t < T ? den[t] : 1.0f;   // rows past the end are zeros
+        }
     }
 }
 
+template <bool DS = false>
 __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid) {
 #pragma unroll
     for (int s = 0; s < NCH1; ++s) {
@@ -92,7 +101,15 @@ __device__ __forceinline__ void store_tile1(const Staged1 &r, u16 *smem, int tid
         lds_write(smem + oQ1, off, r.q[s]);
         lds_write(smem + oK1, off, r.k[s]);
         lds_write(smem + oV1, off, r.v[s]);
-        lds_write(smem + oO1, off, r.o[s]);
+        u32x4 o = r.o[s];
+        if constexpr (DS) {
+            const float rd = 1.0f / r.den[s];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = pack_bf16(__builtin_bit_cast(float, o[j] << 16) * rd,
+                                 __builtin_bit_cast(float, o[j] & 0xffff0000u) * rd);
+        }
+        lds_write(smem + oO1, off, o);
     }
 }
 
@@ -179,6 +196,7 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
     const LaneOff L = lane_offsets(lane, ch);
     const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
     const u16 *gv = static_cast<const u16 *>(p.v) + w.base, *go = static_cast<const u16 *>(p.dout) + w.base;
+    const float *gden = NK ? p.den + (int64_t)chain * p.T : nullptr;
     // R at the segment's end (0 for the last segment), S after the segment's last position
     const float *g = nullptr;
     if (SK && ONE)
@@ -244,9 +262,9 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
     };
 
     Staged1 st;
-    load_tile1(st, gq, gk, gv, go, w.t0(0), w.T, tid);
+    load_tile1<NK>(st, gq, gk, gv, go, gden, w.t0(0), w.T, tid);
     load_dd(w.t0(0));
-    store_tile1(st, smem, tid);
+    store_tile1<NK>(st, smem, tid);
     store_dd();
     if (!SK) write_state();
     write_y();
@@ -315,7 +333,7 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
         if (SK) write_state();
         // this wave's part of the next tile: in flight while the consumers form this tile's gradients
         if (more) {
-            load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+            load_tile1<NK>(st, gq, gk, gv, go, gden, w.t0(it + 1), w.T, tid);
             load_dd(w.t0(it + 1));
         }
         lds_barrier();   // Y
@@ -323,7 +341,7 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
         write_y();
         lds_barrier();   // Z
         if (more) {
-            store_tile1(st, smem, tid);
+            store_tile1<NK>(st, smem, tid);
             store_dd();
         }
         lds_barrier();   // X
@@ -339,6 +357,7 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
     const LaneOff L = lane_offsets(lane, ch);
     const u16 *gq = static_cast<const u16 *>(p.q) + w.base, *gk = static_cast<const u16 *>(p.k) + w.base;
     const u16 *gv = static_cast<const u16 *>(p.v) + w.base, *go = static_cast<const u16 *>(p.dout) + w.base;
+    const float *gden = NK ? p.den + (int64_t)chain * p.T : nullptr;
     u16 *gdq = static_cast<u16 *>(p.dq) + w.base, *gdk = static_cast<u16 *>(p.dk) + w.base,
         *gdv = static_cast<u16 *>(p.dv) + w.base;
     u16 *ob = smem + oOS1 + c * kOS1;
@@ -372,14 +391,14 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
     };
 
     Staged1 st;
-    load_tile1(st, gq, gk, gv, go, w.t0(0), w.T, tid);
-    store_tile1(st, smem, tid);
+    load_tile1<NK>(st, gq, gk, gv, go, gden, w.t0(0), w.T, tid);
+    store_tile1<NK>(st, smem, tid);
     lds_barrier();   // X: the first tile and R^T
     for (int it = 0; it < w.ntiles; ++it) {
         const int64_t t0 = w.t0(it);
         const bool more = it + 1 < w.ntiles;
         // this wave's part of the next tile
-        if (more) load_tile1(st, gq, gk, gv, go, w.t0(it + 1), w.T, tid);
+        if (more) load_tile1<NK>(st, gq, gk, gv, go, gden, w.t0(it + 1), w.T, tid);
         {
             f32x16 oacc[2];
             out_unit<Unit::DV, DEC>(oacc, smem, rb, ch, lane, L, dwt);
@@ -397,7 +416,7 @@ __device__ __forceinline__ void consumer(const Bwd1Args &p, u16 *smem, int chain
             stage(oacc, ob);
         }
         lds_barrier();   // Z
-        if (more) store_tile1(st, smem, tid);
+        if (more) store_tile1<NK>(st, smem, tid);
         if constexpr (ONE) store(ob, gdq, t0);
         lds_barrier();   // X
     }
@@ -429,7 +448,8 @@ hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s) {
     if (a.decay != nullptr && a.H <= 0) return hipErrorInvalidValue;
     if (a.dden != nullptr) {
         // y starts from zero at the chain's end: unsplit chains only
-        if (a.dq != nullptr || a.decay != nullptr || a.nseg != 1 || a.r_states != nullptr) return hipErrorInvalidValue;
+        if (a.dq != nullptr || a.decay != nullptr || a.nseg != 1 || a.r_states != nullptr || a.den == nullptr)
+            return hipErrorInvalidValue;
         hipLaunchKernelGGL((bwd1_bf16_kernel<false, false, true>), dim3(items), dim3(kT1), 0, s, a);
         return hipGetLastError();
     }

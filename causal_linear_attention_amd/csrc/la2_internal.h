@@ -94,6 +94,7 @@ struct DenArgs {
     void *kap;             // [chains, T, D]: phi(k) - m (mode 6 out)
     const void *u;         // [chains, T, D]: the scan of (dout, v, phi(k) - m) (mode 7 in)
     const float *arow;     // fp32 [chains, T]: dout_t . (decayed prefix sum of v)_t (mode 7 in)
+    float *dden_out;       // fp32 [chains, T]: where mode 7 also writes dden_t = -(dout_t . o_t) / den_t, or nullptr
     int64_t T;
     int64_t seg_len;       // positions per segment, a multiple of 64
     int H;
@@ -188,9 +189,13 @@ struct Bwd1Args {
     const float *decay;
     int H;
     // the normalized form's dk (dq = nullptr, no decay, unsplit chains): dden [chains, T] fp32, the
-    // gradient of each row's denominator, or nullptr; nk_elu != 0: phi = elu + 1 (else the identity)
+    // gradient of each row's denominator, or nullptr; nk_elu != 0: phi = elu + 1 (else the identity);
+    // den [chains, T] fp32, the rows' denominators (required with dden): dout is then the normalized
+    // output's gradient do, and the walk's output-gradient role is dn_t = do_t / den_t, formed as each
+    // row is staged
     const float *dden;
     int nk_elu;
+    const float *den;
 };
 hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s);
 

@@ -129,8 +129,9 @@ enum : int {
 //   G_t = a_t - c_t ell_t = ((phi(q_t) . zk_t) a_t - ell_t (phi(q_t) . U_t)) / den_t,
 //   d phi(q_t) = (U_t - c_t zk_t + G_t m) / den_t.
 // U comes from the bf16 tile scan of (do, v, kap) (kap is small, so its bf16 rounding and that of the
-// scan's products are small against the result), a_t from the mode-1 scan of (do, v); every other
-// quantity here is fp32.
+// scan's products are small against the result), a_t from the mode-1 scan of (do, v) or as the row
+// sums of that tile scan; every other quantity here is fp32.  Where asked, the gradient of each row's
+// denominator, dden_t = -c_t / den_t, is written too (c_t from these terms, not from the bf16 o).
 
 template <typename E, int D, int FMAP, int MODE>
 __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
@@ -343,6 +344,8 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                                                      : (1.0f - exp2f((float)(t + 1) * l2)) / (1.0f - lam);
                         const float rd = 1.0f / dn;
                         const float c = (sg * av + pu) * rd, G = (pz * av - ell * pu) * rd;
+                        // the gradient of den_t, -(do_t . o_t) / den_t
+                        if (c8 == 0 && p.dden_out) p.dden_out[row0 + t] = -c * rd;
                         float gr[8];
 #pragma unroll
                         for (int m = 0; m < 8; ++m)
