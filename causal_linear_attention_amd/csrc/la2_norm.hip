@@ -10,13 +10,14 @@
 // (elu + 1 only) and den_t in fp32; the numerator scan's output pass divides each row by its den_t
 // before it stores it.
 //
-// Denominator kernel layout: one workgroup of 256 threads per (chain, segment) walks the segment in
-// chunks of 64 positions.  Thread (c8, g) owns 8 consecutive feature dims (c8 of D/8) and a run of
-// 64 / G consecutive positions (group g of G = 256 / (D/8)); the D/8 threads of a group are
+// Denominator kernel layout: one workgroup of NT = 256 threads (512 for mode 7 below) per (chain,
+// segment) walks the segment in chunks of 64 positions.  Thread (c8, g) owns 8 consecutive feature
+// dims (c8 of D/8) and a run of 64 / G consecutive positions (group g of G = NT / (D/8)); the D/8 threads of a group are
 // consecutive lanes, so a row is one contiguous 2D- or 4D-byte read and a dot product over d is a
-// butterfly across those lanes.  Per chunk: each group forms its run's decayed sum, the groups'
-// sums are chained in LDS (Horner with lam^(run length)), then each group rewalks its run from
-// its carried-in z and forms den_t.  Chains with few rows of work are cut into segments whose
+// butterfly across those lanes.  Per chunk: each group forms its run's decayed sum, one thread per
+// dimension scans the groups' sums in LDS (Horner with lam^(run length)) into the sum entering each
+// run and carries the chunk's total to the next chunk, then each group rewalks its run from its
+// carried-in z and forms den_t.  Chains with few rows of work are cut into segments whose
 // start vectors come from a separate pass over the earlier segments' sums.
 #include "la2_internal.h"
 
@@ -133,16 +134,22 @@ enum : int {
 // sums of that tile scan; every other quantity here is fp32.  Where asked, the gradient of each row's
 // denominator, dden_t = -c_t / den_t, is written too (c_t from these terms, not from the bf16 o).
 
+// Threads per workgroup: mode 7 holds the most per position (its runs of half the length keep it
+// under 128 VGPRs, four waves per SIMD), the others 256.
+constexpr int vscan_threads(int mode) { return mode == kDQN ? 2 * kThreadsN : kThreadsN; }
+
 template <typename E, int D, int FMAP, int MODE>
-__global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
+__global__ __launch_bounds__(vscan_threads(MODE)) void vscan_kernel(DenArgs p) {
     constexpr bool REV = MODE == kYSeg || MODE == kDK;
     constexpr bool SUMS = MODE == kZSeg || MODE == kYSeg || MODE == kMean;
+    constexpr int NT = vscan_threads(MODE);
     constexpr int CPR = D / 8;                  // threads per row (8 dims each)
-    constexpr int G = kThreadsN / CPR;          // position groups
+    constexpr int G = NT / CPR;                 // position groups
     constexpr int PPG = kChunkN / G;            // positions per group per chunk
     static_assert(PPG >= 1 && kChunkN % G == 0, "layout");
-    __shared__ float part[G][D];
-    __shared__ float zc[2][D];
+    // each run's own sum, then (after the scan over the runs) the sum entering it; two chunks' worth,
+    // so that a chunk's runs may write theirs while the previous chunk's are still being read
+    __shared__ float part[2][G][D];
 
     const int tid = threadIdx.x, c8 = tid % CPR, g = tid / CPR;
     const int nseg_here = SUMS && MODE != kMean ? p.nseg - 1 : p.nseg;
@@ -184,7 +191,8 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
     }
 
     // what is carried into the segment: Horner over the other segments' sums in walk order,
-    // z <- lam^seg_len z + sum_j
+    // z <- lam^seg_len z + sum_j; threads tid < D then carry dimension tid from chunk to chunk
+    float carry = 0.0f;
     if (tid < D && MODE != kKappa) {
         float z = 0.0f;
         if constexpr (!SUMS) {
@@ -208,9 +216,8 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                 z = (float)((double)z - (double)m * cnt);
             }
         }
-        zc[0][tid] = z;
+        carry = z;
     }
-    __syncthreads();
 
     int buf = 0;
     for (int64_t c0 = 0; c0 < steps; c0 += kChunkN) {
@@ -288,15 +295,22 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) loc[m] = fmaf(loc[m], lam, xx[i][m]);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) part[g][c8 * 8 + m] = loc[m];
+        for (int m = 0; m < 8; ++m) part[buf][g][c8 * 8 + m] = loc[m];
         __syncthreads();
-        // the sum entering this run: the chunk's carry, then the earlier runs of the chunk
+        // the scan over the chunk's runs, one dimension per thread: each entry becomes the sum entering
+        // its run (the chunk's carry, then the earlier runs), and the carry moves past the chunk
+        if (tid < D) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float x = part[buf][j][tid];
+                part[buf][j][tid] = carry;
+                carry = fmaf(carry, lamG, x);
+            }
+        }
+        __syncthreads();
         float z[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) z[m] = zc[buf][c8 * 8 + m];
-        for (int j = 0; j < g; ++j)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) z[m] = fmaf(z[m], lamG, part[j][c8 * 8 + m]);
+        for (int m = 0; m < 8; ++m) z[m] = part[buf][g][c8 * 8 + m];
         if constexpr (SUMS) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) z[m] = fmaf(z[m], lamG, loc[m]);
@@ -364,15 +378,10 @@ __global__ __launch_bounds__(kThreadsN) void vscan_kernel(DenArgs p) {
                 }
             }
         }
-        // the last run's sum is the next chunk's carry (read only after a full chunk)
-        if (g == G - 1)
-#pragma unroll
-            for (int m = 0; m < 8; ++m) zc[buf ^ 1][c8 * 8 + m] = z[m];
-        __syncthreads();
         buf ^= 1;
     }
     if constexpr (SUMS) {
-        if (tid < D) (MODE == kMean ? p.msum : p.zseg)[((int64_t)chain * p.nseg + seg) * D + tid] = zc[buf][tid];
+        if (tid < D) (MODE == kMean ? p.msum : p.zseg)[((int64_t)chain * p.nseg + seg) * D + tid] = carry;
     }
 }
 
@@ -411,14 +420,14 @@ hipError_t launch_vs(const DenArgs &a, int mode, hipStream_t s) {
     const bool sums = mode == kZSeg || mode == kYSeg;
     const unsigned grid = (unsigned)a.chains * (unsigned)(sums ? a.nseg - 1 : a.nseg);
     switch (mode) {
-        case kMean: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kMean>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kKappa: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kKappa>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kDQN: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQN>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kZSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kZSeg>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kDen: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDen>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kDQ: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQ>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        case kYSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kYSeg>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
-        default: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDK>), dim3(grid), dim3(kThreadsN), 0, s, a); break;
+        case kMean: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kMean>), dim3(grid), dim3(vscan_threads(kMean)), 0, s, a); break;
+        case kKappa: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kKappa>), dim3(grid), dim3(vscan_threads(kKappa)), 0, s, a); break;
+        case kDQN: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQN>), dim3(grid), dim3(vscan_threads(kDQN)), 0, s, a); break;
+        case kZSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kZSeg>), dim3(grid), dim3(vscan_threads(kZSeg)), 0, s, a); break;
+        case kDen: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDen>), dim3(grid), dim3(vscan_threads(kDen)), 0, s, a); break;
+        case kDQ: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDQ>), dim3(grid), dim3(vscan_threads(kDQ)), 0, s, a); break;
+        case kYSeg: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kYSeg>), dim3(grid), dim3(vscan_threads(kYSeg)), 0, s, a); break;
+        default: hipLaunchKernelGGL((vscan_kernel<E, D, FMAP, kDK>), dim3(grid), dim3(vscan_threads(kDK)), 0, s, a); break;
     }
     return hipGetLastError();
 }
