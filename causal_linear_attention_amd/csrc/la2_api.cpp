@@ -253,9 +253,19 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
 // Segment start states of the scan with key role `b` (width D) and value role `c` (width W) in
 // direction `dir`, written to `ws` ([chains, nseg, D, W] fp32).  Only called for split chains.
 // `init` ([chains, D, W] or nullptr): the state the first segment starts from.
+// compose (and no init): leave the state pass's per-piece deltas in `ws` without the prefix launch, for
+// an output kernel that sums them itself.
+// A walk that sums the reverse deltas itself reads each later piece's 64 KiB at its start (four
+// memory round trips per piece before its first tile) instead of one prefix launch for all (~10 us):
+// 10 us faster at two pieces, no faster at 5-15 pieces.
+constexpr int kComposeMaxPieces = 2;
+bool compose_reverse(const Plan &p) {
+    return p.nseg > 1 && p.nsub - 1 - la2::state_index(0, p.sub, p.nsub, true) <= kComposeMaxPieces;
+}
+
 int segment_states(const void *b, const void *c, const float *decay, int64_t chains, int64_t H, int64_t T, int D,
                    int W, const Plan &pl, int dtype, la2::Dir dir, void *ws, hipStream_t s,
-                   const float *init = nullptr) {
+                   const float *init = nullptr, bool compose = false) {
     // the state pass runs the sub-segments: every state entry is one segment of its own
     Plan sp = pl;
     sp.seg_tiles = pl.seg_tiles / pl.sub;
@@ -267,6 +277,7 @@ int segment_states(const void *b, const void *c, const float *decay, int64_t cha
     args.seg_first = dir == la2::Dir::Forward ? 0 : pl.sub;
     args.seg_count = dir == la2::Dir::Forward ? (pl.nseg - 1) * pl.sub : pl.nsub - pl.sub;
     if (launch(args, D, sp, dtype, dir, la2::Mode::StateOnly, s) != hipSuccess) return LA2_ERR_HIP;
+    if (compose && init == nullptr) return LA2_OK;
     // a reverse init sits at the chain's last position: the last piece's length - 1 before its start
     const int64_t init_len = T - 1 - (int64_t)(pl.nsub - 1) * sp.seg_tiles * pl.TB;
     if (la2::launch_segment_prefix(args.states, decay, (int)chains, (int)H, pl.nsub, (int64_t)sp.seg_tiles * pl.TB,
@@ -767,7 +778,7 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         // states and final states (left in the workspace), and the reverse states at the segment ends.
         const Plan bp = bwd1_plan(pl, chains, T, d, d_v);
         if (bp.nseg > 1 && (st = segment_states(q, dout, nullptr, chains, H, T, D, DV, bp, dtype, la2::Dir::Reverse,
-                                                ws_r, s)) != LA2_OK)
+                                                ws_r, s, nullptr, compose_reverse(bp))) != LA2_OK)
             return st;
         la2::Bwd1Args a{};
         a.q = q;
@@ -788,6 +799,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
         a.r_states = bp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
         a.r_sub = bp.sub;
         a.r_nsub = bp.nsub;
+        a.r_compose = compose_reverse(bp);
+        a.r_piece_len = (int64_t)(bp.seg_tiles / bp.sub) * bp.TB;
         return la2::launch_bwd1_bf16(a, s) == hipSuccess ? LA2_OK : LA2_ERR_HIP;
     }
     // dq_t = S_t do_t          = forward scan with (query, key, value) = (do, v, k); its state is S^T, so
@@ -804,10 +817,12 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
     if (fused) {
         // dk_t = R_t v_t and dv_t = R_t^T k_t in one reverse pass, R_t = lam R_{t+1} + q_t do_t^T
         const Plan fp = make_plan(B, H, T, d, d_v, block, dtype, true);
+        // d = d_v = 128, no carried state: the walk, which sums the reverse deltas itself
+        const bool walk = d == 128 && d_v == 128 && !dstate_out && !dstate_in && !forced().legacy_dkdv;
         if (fp.nseg > 1 && (st = segment_states(q, dout, decay, chains, H, T, D, DV, fp, dtype, la2::Dir::Reverse,
-                                                ws_r, s, dstate_out)) != LA2_OK)
+                                                ws_r, s, dstate_out, walk && compose_reverse(fp))) != LA2_OK)
             return st;
-        if (d == 128 && d_v == 128 && !dstate_out && !dstate_in && !forced().legacy_dkdv) {
+        if (walk) {
             // d = d_v = 128, no carried state: the producer/consumer walk of the one-pass backward without
             // its dQ and S (la2_bwd1_bf16.hip), R from the reverse states at the segment ends
             la2::Bwd1Args a{};
@@ -824,6 +839,8 @@ int backward_impl(const void *q, const void *k, const void *v, const float *deca
             a.r_states = fp.nseg > 1 ? static_cast<const float *>(ws_r) : nullptr;
             a.r_sub = fp.sub;
             a.r_nsub = fp.nsub;
+            a.r_compose = compose_reverse(fp);
+            a.r_piece_len = (int64_t)(fp.seg_tiles / fp.sub) * fp.TB;
             a.decay = decay;
             a.H = (int)H;
             if (nk_dden && skip_dq && !decay && fp.nseg == 1) {

@@ -207,13 +207,46 @@ __device__ __forceinline__ void producer(const Bwd1Args &p, u16 *smem, int chain
 
     f32x16 sacc[HOLD ? 8 : 1];
     if constexpr (HOLD) {
+        if (!SK && g != nullptr && p.r_compose) {
+            // R at the segment's end from the deltas of the later pieces: run = lam^L run + dR[piece],
+            // from the chain's last piece down to the one after this segment (the segment prefix's
+            // recurrence, in the same order and fused multiply-adds)
+            const float f = DEC ? exp2f((float)p.r_piece_len * chain_l2(p, chain)) : 1.0f;
+            const int first = state_index(seg, p.r_sub, p.r_nsub, true) + 1;
+            const float *base = p.r_states + (int64_t)chain * p.r_nsub * D1 * D1;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int kb = kb0 + s / 4, nb = s % 4;
+            for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
+                for (int r = 0; r < 16; ++r) sacc[s][r] = 0.0f;
+            for (int pc = p.r_nsub - 1; pc >= first; --pc) {
+                const float *gd = base + (int64_t)pc * D1 * D1;
+                // two blocks' 32 loads in flight at a time (left to itself the compiler waits for each)
+#pragma unroll
+                for (int s0 = 0; s0 < 8; s0 += 2) {
+                    float t[2][16];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int kb = kb0 + (s0 + u) / 4, nb = (s0 + u) % 4;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            t[u][r] = gd[(int64_t)(kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * D1 + nb * 32 + col];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sacc[s0 + u][r] = fmaf(f, sacc[s0 + u][r], t[u][r]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int kb = kb0 + s / 4, nb = s % 4;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int d = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    sacc[s][r] = g != nullptr ? g[(int64_t)d * D1 + nb * 32 + col] : 0.0f;
+                }
             }
         }
     }
@@ -446,6 +479,8 @@ hipError_t launch_bwd1_bf16(const Bwd1Args &a, hipStream_t s) {
     const unsigned items = (unsigned)((int64_t)a.chains * a.nseg);
     if (a.dq != nullptr && a.decay != nullptr) return hipErrorInvalidValue;   // no one-pass walk with a decay
     if (a.decay != nullptr && a.H <= 0) return hipErrorInvalidValue;
+    if (a.r_compose && (a.r_states == nullptr || a.r_piece_len <= 0 || a.r_sub <= 0 || a.r_nsub <= 0))
+        return hipErrorInvalidValue;
     if (a.dden != nullptr) {
         // y starts from zero at the chain's end: unsplit chains only
         if (a.dq != nullptr || a.decay != nullptr || a.nseg != 1 || a.r_states != nullptr || a.den == nullptr)

@@ -184,6 +184,10 @@ struct Bwd1Args {
     const float *r_states; // fp32 [chains, r_nsub, D, D]: reverse states at the segments' ends, or nullptr
     int r_sub;
     int r_nsub;
+    // r_compose != 0: r_states holds the reverse state pass's per-piece deltas instead (no prefix ran),
+    // and each segment sums the deltas of the pieces after it, r_piece_len positions each, itself
+    int r_compose;
+    int64_t r_piece_len;
     // dq = nullptr: dk and dv only (the dK/dV pass of the two-pass backward; s_states, s_final unused),
     // with the per-head decay lam ([H] fp32, chain c is head c % H) or nullptr for lam = 1
     const float *decay;
