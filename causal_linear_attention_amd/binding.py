@@ -98,7 +98,7 @@ def _load_test_library():
     if _test_lib is None:
         lib = load_library(TEST_LIB_PATH)
         lib.la2_test_set_plan.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.la2_test_set_plan.restype = ctypes.c_int
         lib.la2_test_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                         ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -145,7 +145,7 @@ def reread_probe(q, k, v, o, item_bytes, mode, nontemporal, stream=None):
 
 @contextlib.contextmanager
 def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, norm_segment=0,
-                  two_pass_backward=False, legacy_forward=False, legacy_dkdv=False):
+                  two_pass_backward=False, legacy_forward=False, legacy_dkdv=False, reverse_prefix=False):
     """Run the wrappers on the test build of the library with forced plan choices (see
     include/la2_test_hooks.h; 0 / False = automatic).  For tests: the forced plans cover code paths
     that small shapes would not reach.  Not thread-safe."""
@@ -153,12 +153,12 @@ def plan_override(seg_tiles=0, state_sub=0, slice_width=0, separate_dkdv=False, 
     _load_test_library()
     _test_lib.la2_test_set_plan(int(seg_tiles), int(state_sub), int(slice_width), int(bool(separate_dkdv)),
                                 int(norm_segment), int(bool(two_pass_backward)), int(bool(legacy_forward)),
-                                int(bool(legacy_dkdv)))
+                                int(bool(legacy_dkdv)), int(bool(reverse_prefix)))
     _lib = _test_lib
     try:
         yield _test_lib
     finally:
-        _test_lib.la2_test_set_plan(0, 0, 0, 0, 0, 0, 0, 0)
+        _test_lib.la2_test_set_plan(0, 0, 0, 0, 0, 0, 0, 0, 0)
         _lib = _release
 
 

@@ -31,6 +31,8 @@ struct PlanOverride {
     int two_pass_backward;  // != 0: la2_backward_saved without decay by the dQ pass and the dK/dV pass
     int legacy_forward;     // != 0: forward-direction bf16 output passes on the 8-wave scan kernel only
     int legacy_dkdv;        // != 0: the fused dk/dv pass on its 8-wave kernel only
+    int reverse_prefix;     // != 0: the reverse prefix launch even where the backward walk would sum the
+                            //   deltas of its later pieces itself
 };
 
 #ifdef LA2_TEST_HOOKS
@@ -260,7 +262,7 @@ hipError_t launch(const la2::ScanArgs &args, int D, const Plan &pl, int dtype, l
 // 10 us faster at two pieces, no faster at 5-15 pieces.
 constexpr int kComposeMaxPieces = 2;
 bool compose_reverse(const Plan &p) {
-    return p.nseg > 1 && p.nsub - 1 - la2::state_index(0, p.sub, p.nsub, true) <= kComposeMaxPieces;
+    return p.nseg > 1 && !forced().reverse_prefix && p.nsub - 1 - la2::state_index(0, p.sub, p.nsub, true) <= kComposeMaxPieces;
 }
 
 int segment_states(const void *b, const void *c, const float *decay, int64_t chains, int64_t H, int64_t T, int D,
@@ -315,9 +317,9 @@ int la2_abi_version(void) { return LA2_ABI_VERSION; }
 
 #ifdef LA2_TEST_HOOKS
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv, int64_t norm_segment,
-                      int two_pass_backward, int legacy_forward, int legacy_dkdv) {
-    g_override = PlanOverride{seg_tiles, state_sub, slice_width, separate_dkdv, norm_segment, two_pass_backward,
-                              legacy_forward, legacy_dkdv};
+                      int two_pass_backward, int legacy_forward, int legacy_dkdv, int reverse_prefix) {
+    g_override = PlanOverride{seg_tiles,      state_sub,   slice_width, separate_dkdv, norm_segment,
+                              two_pass_backward, legacy_forward, legacy_dkdv, reverse_prefix};
     return LA2_OK;
 }
 #endif

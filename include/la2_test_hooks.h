@@ -35,9 +35,12 @@ extern "C" {
  *                  instead of the one fused launch
  *   legacy_dkdv:   non-zero runs the fused dK/dV pass at d = d_v = 128 on its eight-wave kernel instead
  *                  of the producer/consumer walk of the one-pass backward
+ *   reverse_prefix: non-zero launches the reverse segment prefix even where the backward walk would
+ *                  sum the state deltas of its (at most two) later pieces itself
  * Returns LA2_OK. */
 int la2_test_set_plan(int64_t seg_tiles, int state_sub, int slice_width, int separate_dkdv,
-                      int64_t norm_segment, int two_pass_backward, int legacy_forward, int legacy_dkdv);
+                      int64_t norm_segment, int two_pass_backward, int legacy_forward, int legacy_dkdv,
+                      int reverse_prefix);
 
 /* A plain HBM stream, for measuring what the tile kernels' read:write mixes can reach:
  * dst_j = src_0 + ... + src_{nsrc-1} (u32 lanes) over `bytes` bytes of each device buffer, read and
